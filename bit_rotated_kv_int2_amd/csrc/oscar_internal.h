@@ -1,0 +1,108 @@
+// Internal declarations shared by the translation units of liboscar.so.
+// Geometry of the page block and the bf16/fp16 helpers used on the device.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "oscar.h"
+
+namespace oscar {
+
+constexpr int kD = OSCAR_HEAD_DIM;          // head dimension
+constexpr int kPageTokens = OSCAR_PAGE_TOKENS;
+constexpr int kGroup = OSCAR_GROUP;
+constexpr int kPageBytes = OSCAR_PAGE_BYTES;
+constexpr int kKCodes = OSCAR_PAGE_KCODES;
+constexpr int kVCodes = OSCAR_PAGE_VCODES;
+constexpr int kKMeta = OSCAR_PAGE_KMETA;
+constexpr int kVMeta = OSCAR_PAGE_VMETA;
+constexpr int kMaxGroupHeads = 16;          // Hq / Hkv supported
+constexpr int kPartStride = 132;            // floats per (m, l, o[128]) partial, padded
+
+// Bit reversal of a 7-bit channel index (d = 128).
+__host__ __device__ constexpr int bitrev7(int p) {
+  return ((p & 1) << 6) | ((p & 2) << 4) | ((p & 4) << 2) | (p & 8) | ((p & 16) >> 2) |
+         ((p & 32) >> 4) | ((p & 64) >> 6);
+}
+
+// Metadata entry of token slot t: slots t, t+16, t+32, t+48 are adjacent so a
+// lane owning slot-column t&15 reads its four tokens with one 32-byte load.
+__host__ __device__ constexpr int meta_entry(int slot) { return 4 * (slot & 15) + (slot >> 4); }
+// Byte (within a 16-byte V channel row) that holds token slot t; bits 2*(t&3).
+__host__ __device__ constexpr int vcode_byte(int slot) { return 4 * ((slot >> 2) & 3) + (slot >> 4); }
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+__device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+__device__ __forceinline__ uint16_t f32_to_f16_rn(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// Orders LDS traffic between the lanes of one wave (compiler fence plus the
+// hardware wait); waves never wait for each other here.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Everything a kernel needs from oscar_params / oscar_kv_pool / oscar_rotation,
+// flattened into one by-value struct.
+struct PoolView {
+  uint16_t *sink_k, *sink_v, *recent_k, *recent_v;
+  uint8_t *pages;
+  const int32_t *block_table, *sink_slot;
+  int32_t *seq_lens, *err;
+  int32_t batch, max_pages, n_pages, n_sink_slots;
+  int32_t hkv, hq, sink, recent;
+  float sm_scale;
+};
+
+struct RotView {
+  const float *U_K, *U_V, *tau_K, *tau_V;
+};
+
+// Decode workspace carve-up (offsets in bytes from the workspace base).
+struct DecodePlan {
+  int n_splits;          // history splits per (sequence, kv head)
+  int pages_per_split;
+  int n_bf16_chunks;     // 64-token chunks covering sink + recent
+  size_t off_qrot;       // float [B][Hq][128] rotated queries
+  size_t off_qint;       // int8 MFMA operands [B][Hkv][MT][2][64][16]
+  size_t off_qconst;     // float [B][Hq][4]  {delta, Q0, Q1, unused}
+  size_t off_part;       // float [B][Hkv][n_splits][G][kPartStride]
+  size_t off_bpart;      // float [B][Hkv][n_bf16_chunks][G][kPartStride]
+  size_t total;
+};
+
+DecodePlan make_decode_plan(int batch, int hkv, int hq, int max_pages, int sink, int recent,
+                            int variant);
+
+// Launchers (return hipError_t of the launches).
+hipError_t launch_append(const PoolView &pv, const RotView &rv, const uint16_t *k_new,
+                         const uint16_t *v_new, int n_new, hipStream_t s);
+hipError_t launch_decode(const PoolView &pv, const RotView &rv, const uint16_t *q, float *out,
+                         uint8_t *ws, const DecodePlan &plan, int variant, hipStream_t s);
+
+struct Bf16View {
+  const uint16_t *k_pages, *v_pages;
+  const int32_t *block_table, *seq_lens;
+  int32_t *err;
+  int32_t batch, max_pages, n_pages, hkv, hq;
+  float sm_scale;
+};
+struct Bf16Plan {
+  int n_splits, pages_per_split;
+  size_t off_part, total;
+};
+Bf16Plan make_bf16_plan(int batch, int hkv, int hq, int max_pages);
+hipError_t launch_bf16_decode(const Bf16View &v, const uint16_t *q, float *out, uint8_t *ws,
+                              const Bf16Plan &plan, hipStream_t s);
+
+// Host calibration (float64).
+int calibrate_host(int d, int hkv, int hq, float sm_scale, const float *q_cal, int64_t n_q,
+                   const float *k_cal, const float *v_cal, int64_t n_kv, double quantile_k,
+                   double quantile_v, float *U_K, float *U_V, float *tau_K, float *tau_V,
+                   char *err, size_t err_len);
+
+}  // namespace oscar

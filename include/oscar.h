@@ -1,0 +1,223 @@
+/*
+ * oscar.h -- C ABI of liboscar.so: OSCAR rotated-INT2 KV-cache decode
+ * attention for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *   [A] youleyou.com article "超越 TurboQuant，显存压力终于得到缓解！Together AI
+ *       最新论文 OSCAR 直接挑战 TurboQuant …", section "OSCAR 的设计思路" and the
+ *       token-pool paragraphs that follow it.
+ *   [B] MarkTechPost article, Chinese translation, "Together AI 开源 OSCAR：一种
+ *       用于长上下文 LLM 服务的注意力感知 2 位 KV 缓存量化系统", sections
+ *       "OSCAR 有何不同做法" (method), "服务系统：混合精度缓存布局" (serving),
+ *       visual-guide steps 04 and 06.
+ *
+ * Conventions shared by every entry point
+ *   - Return value: OSCAR_OK (0) or a negative OSCAR_E* code.  On error a
+ *     message is available from oscar_last_error() (per thread) and nothing
+ *     has been launched.  No C++ exception crosses this boundary.
+ *   - Pointers inside oscar_rotation, oscar_kv_pool and oscar_bf16_cache, and
+ *     the tensor arguments of the decode/append calls, are DEVICE pointers
+ *     owned by the caller.  The library never allocates or frees them and
+ *     keeps no reference after the call returns.  oscar_calibrate_rotation
+ *     alone takes HOST pointers.
+ *   - Device calls are asynchronous on `stream` (a hipStream_t; NULL = the
+ *     default stream).  Faults inside a kernel surface at the caller's next
+ *     synchronisation.  Conditions only the device can see (a block-table
+ *     entry outside [0, n_pages), a sequence longer than the table) are
+ *     skipped by the kernels and reported by OR-ing OSCAR_DEVERR_* bits into
+ *     *pool->error_flags when that pointer is non-NULL.
+ *   - bf16 and fp16 values are passed as their uint16_t bit patterns.
+ *   - All tokens are row vectors; d = head_dim = 128.
+ */
+#ifndef OSCAR_H
+#define OSCAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  OSCAR_OK = 0,
+  OSCAR_EINVAL = -1,     /* invalid argument (message says which) */
+  OSCAR_ENOTSUP = -2,    /* valid but unsupported configuration */
+  OSCAR_EWORKSPACE = -3, /* workspace too small */
+  OSCAR_EHIP = -4        /* HIP runtime error at launch */
+};
+
+/* Bits OR-ed into *oscar_kv_pool.error_flags by the kernels. */
+enum {
+  OSCAR_DEVERR_PAGE = 1,     /* block-table entry outside [0, n_pages) */
+  OSCAR_DEVERR_LENGTH = 2,   /* sequence needs more pages than max_pages */
+  OSCAR_DEVERR_SINKSLOT = 4  /* sink_slot entry outside [0, n_sink_slots) */
+};
+
+/* Fixed geometry of this version. */
+#define OSCAR_HEAD_DIM 128
+#define OSCAR_PAGE_TOKENS 64
+#define OSCAR_GROUP 64
+/*
+ * One history page holds 64 token slots of one KV head, 5120 bytes:
+ *   [   0, 2048)  K codes, token-major: row t (32 bytes) is token slot t;
+ *                 byte j holds channels 4j..4j+3, channel 4j+i in bits
+ *                 [2i, 2i+2).
+ *   [2048, 4096)  V codes, channel-major: row c (16 bytes) is channel c;
+ *                 token slot t sits in byte 4*((t>>2)&3) + (t>>4), bits
+ *                 [2*(t&3), 2*(t&3)+2).  (This order lets one 32-bit load
+ *                 feed a 16x16x64 int8 MFMA operand directly.)
+ *   [4096, 4608)  K metadata: 64 entries of 4 fp16 {scale0, zero0, scale1,
+ *                 zero1} (group 0 = rotated channels 0..63, group 1 =
+ *                 64..127); token slot t is entry 4*(t&15) + (t>>4).
+ *   [4608, 5120)  V metadata, same layout.
+ * A page id p addresses pages + (p * num_kv_heads + h) * OSCAR_PAGE_BYTES.
+ * Codes are 0..3 and dequantise as code*scale + zero in the rotated basis.
+ */
+#define OSCAR_PAGE_BYTES 5120
+#define OSCAR_PAGE_KCODES 0
+#define OSCAR_PAGE_VCODES 2048
+#define OSCAR_PAGE_KMETA 4096
+#define OSCAR_PAGE_VMETA 4608
+
+/* Shape and softmax parameters, validated on every call. */
+typedef struct oscar_params {
+  int32_t head_dim;     /* must be 128 */
+  int32_t num_kv_heads; /* Hkv >= 1 */
+  int32_t num_q_heads;  /* Hq, a multiple of Hkv; Hq/Hkv <= 16 */
+  int32_t sink;         /* S0: BF16 sink tokens, multiple of 64, default 64 */
+  int32_t recent;       /* W: BF16 recent-window tokens, multiple of 64, default 256 */
+  int32_t page_tokens;  /* must be 64 */
+  int32_t group;        /* quantisation group G_K, must be 64 */
+  float sm_scale;       /* softmax scale, usually 1/sqrt(head_dim) */
+} oscar_params;
+
+/*
+ * Per-layer rotation artifact ([B] method: R_K = U_Q H P_br, R_V = U_S H P_br;
+ * [B] serving: clipping thresholds).  U_* are float32 [Hkv][d][d], row k
+ * column j = component k of eigenvector j, eigenvectors ordered by
+ * descending eigenvalue.  The composite rotation of a row vector x is
+ * x -> bitrev(FWHT(x U) / sqrt(d)).  tau_* are float32 [Hkv], finite,
+ * in (0, 60000].
+ */
+typedef struct oscar_rotation {
+  const float *U_K;
+  const float *U_V;
+  const float *tau_K;
+  const float *tau_V;
+} oscar_rotation;
+
+/*
+ * Mixed-precision KV pool of one layer ([A] token pool; [B] serving):
+ * positions [0, S0) in the BF16 sink, the last W positions in the BF16
+ * recent ring (slot = position mod W), everything between as rotated INT2
+ * history: history index i = position - S0 lives in page
+ * block_table[b][i / 64], slot i % 64.
+ */
+typedef struct oscar_kv_pool {
+  uint16_t *sink_k;            /* bf16 [n_sink_slots][Hkv][S0][d] */
+  uint16_t *sink_v;
+  uint16_t *recent_k;          /* bf16 [batch][Hkv][W][d] */
+  uint16_t *recent_v;
+  uint8_t *pages;              /* [n_pages][Hkv][OSCAR_PAGE_BYTES] */
+  const int32_t *block_table;  /* int32 [batch][max_pages] */
+  const int32_t *sink_slot;    /* int32 [batch]: sink slot of each sequence */
+  int32_t *seq_lens;           /* int32 [batch]: tokens currently stored */
+  int32_t *error_flags;        /* optional int32[1], OSCAR_DEVERR_* bits */
+  int32_t batch;
+  int32_t max_pages;
+  int32_t n_pages;
+  int32_t n_sink_slots;
+} oscar_kv_pool;
+
+/*
+ * Offline calibration of one layer ([B] method; [B] guide step 04).  HOST
+ * pointers, synchronous, float64 internally.
+ *   q_cal [Hq][n_q][d], k_cal and v_cal [Hkv][n_kv][d] (float32 holding bf16
+ *   values).  For each KV head: C_Q = uncentred covariance of the n_q * G
+ *   query rows of its G query heads; C_S = (1/(n_q G)) sum_h (S_h V)^T (S_h V)
+ *   with S_h = softmax(sm_scale Q_h K^T) over the calibration keys;
+ *   U = eigenvectors by descending eigenvalue, each column's largest-|.|
+ *   entry positive; tau = quantile (linear interpolation) of |x R| over all
+ *   rotated calibration entries, R built from the float32 U.
+ * Outputs U_K, U_V [Hkv][d][d] and tau_K, tau_V [Hkv].  OSCAR_EINVAL if
+ * n_q * G < d, n_kv < 1, a quantile is outside (0, 1), or a spectrum has a
+ * relative eigen-gap below 1e-10 (basis not unique).
+ */
+int32_t oscar_calibrate_rotation(const oscar_params *p, const float *q_cal, int64_t n_q,
+                                 const float *k_cal, const float *v_cal, int64_t n_kv,
+                                 double quantile_k, double quantile_v, float *U_K, float *U_V,
+                                 float *tau_K, float *tau_V);
+
+/*
+ * Append n_new tokens to every sequence of the pool ([A] token pool: new
+ * tokens enter the recent window and the oldest recent token is rotated,
+ * clipped, quantised, packed and demoted by a fused write kernel).
+ *   k_new, v_new: bf16 [batch][n_new][Hkv][d].
+ * Sequence b receives positions seq_lens[b] .. seq_lens[b]+n_new-1 (read on
+ * the device).  Every position that leaves the recent window -- old ring
+ * tokens and new tokens alike -- is written to history exactly as n_new
+ * single-token appends would write it (bit for bit), then seq_lens[b] grows
+ * by n_new.  The pages the new history needs must already be in the block
+ * table.  Concurrent appends that share a target page race.
+ */
+int32_t oscar_quantize_append(const oscar_params *p, const oscar_rotation *rot,
+                              const oscar_kv_pool *pool, const uint16_t *k_new,
+                              const uint16_t *v_new, int32_t n_new, void *stream);
+
+/*
+ * Decode attention of one query token per sequence over the whole pool
+ * ([A] token pool: INT2 and BF16 segments, merged by online softmax; [B]
+ * serving: read path).  q: bf16 [batch][Hq][d]; out: float32 [batch][Hq][d]
+ * = softmax(sm_scale q K^T) V over every stored token, with history keys
+ * and values dequantised and inverse-rotated (computed as (q R_K) against
+ * the rotated codes and R_V^T applied once to the merged history output).
+ * Query head h reads KV head h / (Hq/Hkv).  seq_lens is read on the device;
+ * a sequence of length 0 yields zeros.  workspace: device memory of at least
+ * oscar_decode_workspace_size() bytes, 256-byte aligned; it holds no state
+ * between calls.
+ */
+int32_t oscar_decode_attention(const oscar_params *p, const oscar_rotation *rot,
+                               const oscar_kv_pool *pool, const uint16_t *q, float *out,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+size_t oscar_decode_workspace_size(const oscar_params *p, int32_t batch, int32_t max_pages);
+
+/*
+ * In-house BF16 decode baseline on a paged all-BF16 cache (the comparison
+ * every speedup is quoted against): k_pages, v_pages bf16
+ * [n_pages][Hkv][64][d]; token position t of sequence b lives in page
+ * block_table[b][t / 64], slot t % 64.  Same q/out conventions as
+ * oscar_decode_attention.
+ */
+typedef struct oscar_bf16_cache {
+  const uint16_t *k_pages;
+  const uint16_t *v_pages;
+  const int32_t *block_table; /* int32 [batch][max_pages] */
+  const int32_t *seq_lens;    /* int32 [batch] */
+  int32_t *error_flags;       /* optional */
+  int32_t batch;
+  int32_t max_pages;
+  int32_t n_pages;
+} oscar_bf16_cache;
+
+int32_t oscar_bf16_decode_attention(const oscar_params *p, const oscar_bf16_cache *cache,
+                                    const uint16_t *q, float *out, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
+size_t oscar_bf16_decode_workspace_size(const oscar_params *p, int32_t batch, int32_t max_pages);
+
+/* Decode kernel selection: 0 = MFMA int8 path (default), 1 = VALU path. */
+int32_t oscar_set_decode_variant(int32_t variant);
+
+/* Message of the last error on the calling thread ("" if none). */
+const char *oscar_last_error(void);
+
+/* Library version, e.g. 1000 for 0.1.0. */
+int32_t oscar_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSCAR_H */

@@ -1,0 +1,243 @@
+"""GPU parity of the HIP path against the CPU oracle (needs an MI355X).
+
+Write path: codes and fp16 scale/zero bit-exact with the oracle; bulk appends
+bit-identical to sequential appends.  Decode: for every (sequence, query
+head), max |o_gpu - o_ref| <= 2e-3 * ||o_ref||_2 (float32 accumulation on the
+GPU, float64 oracle).  Inputs are seeded synthetic data from ``synth``; the
+rotation artifact fed to both sides comes from the oracle's calibration.
+"""
+import numpy as np
+import pytest
+
+from bit_rotated_kv_int2_amd import oscar as O
+from bit_rotated_kv_int2_amd import synth
+from oracle import oscar_ref as R
+from pool_helpers import (append_sequence, decode_check, gather_history, oracle_calibration,
+                          rotation_tensors)
+
+pytestmark = pytest.mark.gpu
+D = 128
+TOL = 2e-3
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _tokens(wl, seq, L, layer=0):
+    kb, vb = synth.kv_tokens(wl, layer, seq, 0, L)
+    return kb, vb
+
+
+def _f64(bits):
+    return synth.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _decode_gpu(params, rot, pool, q_bits, variant):
+    torch = _torch()
+    O.set_decode_variant(variant)
+    ws = O.alloc_workspace(O.decode_workspace_size(params, pool.batch, pool.max_pages))
+    q = torch.from_numpy(q_bits.view(np.int16)).cuda().contiguous()
+    out = torch.zeros((pool.batch, params.num_q_heads, D), dtype=torch.float32, device="cuda")
+    O.decode_attention(params, rot, pool, q, out, ws)
+    torch.cuda.synchronize()
+    O.set_decode_variant(0)
+    return out.cpu().numpy()
+
+
+def _oracle_decode(wl, cals, kb, vb, q_bits_b):
+    """Oracle output [Hq, d] for one sequence with tokens kb/vb [L, Hkv, d]."""
+    pools = [R.build_head_pool(_f64(kb[:, h]), _f64(vb[:, h]), cals[h]) for h in range(wl.n_kv)]
+    return R.decode_sequence(_f64(q_bits_b), pools, cals, 1 / np.sqrt(D)), pools
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    wl = synth.WORKLOADS["tiny-4k"]
+    cals = oracle_calibration(wl, n_cal=2048)
+    rot = rotation_tensors(cals)
+    params = O.make_params(wl.n_kv, wl.n_q)
+    kb, vb = _tokens(wl, 0, 4096)
+    q = synth.decode_queries(wl, 0)
+    return wl, cals, rot, params, kb, vb, q
+
+
+def _fresh_pool(params, n_pages, batch=1):
+    bt = np.arange(batch * n_pages, dtype=np.int32).reshape(batch, n_pages)
+    return O.KVPool(params, batch, batch * n_pages, bt)
+
+
+def test_write_bitexact_tiny(tiny):
+    wl, cals, rot, params, kb, vb, _ = tiny
+    L = 4096
+    n_hist = L - 64 - 256
+    pool = _fresh_pool(params, 59)
+    append_sequence(params, rot, pool, 0, kb, vb)
+    pages = pool.pages.cpu().numpy()
+    (kc, ks, kz), (vc, vs, vz) = gather_history(pages, pool.block_table.cpu().numpy()[0], 0, n_hist)
+    ref = R.build_head_pool(_f64(kb[:, 0]), _f64(vb[:, 0]), cals[0])
+    assert np.array_equal(kc, ref.hist_k.codes)
+    assert np.array_equal(ks.view(np.uint16), ref.hist_k.scale.view(np.uint16))
+    assert np.array_equal(kz.view(np.uint16), ref.hist_k.zero.view(np.uint16))
+    assert np.array_equal(vc, ref.hist_v.codes)
+    assert np.array_equal(vs.view(np.uint16), ref.hist_v.scale.view(np.uint16))
+    assert np.array_equal(vz.view(np.uint16), ref.hist_v.zero.view(np.uint16))
+    # BF16 windows hold the raw tokens
+    sink = pool.sink_k.cpu().numpy().view(np.uint16)[0, 0]
+    assert np.array_equal(sink, kb[:64, 0])
+    ring = pool.recent_v.cpu().numpy().view(np.uint16)[0, 0]
+    for pos in range(L - 256, L):
+        assert np.array_equal(ring[pos % 256], vb[pos, 0])
+    assert int(pool.seq_lens.cpu()[0]) == L
+    assert int(pool.error_flags.cpu()[0]) == 0
+
+
+def test_sequential_appends_equal_bulk(tiny):
+    wl, cals, rot, params, kb, vb, _ = tiny
+    L = 2500
+    a = _fresh_pool(params, 59)
+    append_sequence(params, rot, a, 0, kb[:L], vb[:L])
+    b = _fresh_pool(params, 59)
+    chunks = [1, 63, 1, 255, 1, 17, 300, 1, 1, 1, 64, 129, 700]
+    chunks.append(L - sum(chunks))
+    append_sequence(params, rot, b, 0, kb[:L], vb[:L], chunks=chunks)
+    assert np.array_equal(a.pages.cpu().numpy(), b.pages.cpu().numpy())
+    assert np.array_equal(a.recent_k.cpu().numpy(), b.recent_k.cpu().numpy())
+    assert np.array_equal(a.recent_v.cpu().numpy(), b.recent_v.cpu().numpy())
+    assert np.array_equal(a.sink_k.cpu().numpy(), b.sink_k.cpu().numpy())
+
+
+def test_single_token_appends(tiny):
+    """Decode-time appends one token at a time past the window (demotion path)."""
+    wl, cals, rot, params, kb, vb, _ = tiny
+    L0, L1 = 330, 400
+    a = _fresh_pool(params, 59)
+    append_sequence(params, rot, a, 0, kb[:L1], vb[:L1], chunks=[L0] + [1] * (L1 - L0))
+    pages = a.pages.cpu().numpy()
+    n_hist = L1 - 320
+    (kc, ks, kz), (vc, vs, vz) = gather_history(pages, a.block_table.cpu().numpy()[0], 0, n_hist)
+    ref = R.build_head_pool(_f64(kb[:L1, 0]), _f64(vb[:L1, 0]), cals[0])
+    assert np.array_equal(kc, ref.hist_k.codes) and np.array_equal(vc, ref.hist_v.codes)
+    assert np.array_equal(vs.view(np.uint16), ref.hist_v.scale.view(np.uint16))
+
+
+@pytest.mark.parametrize("variant", [0, 1])
+def test_decode_tiny(tiny, variant):
+    wl, cals, rot, params, kb, vb, q = tiny
+    pool = _fresh_pool(params, 59)
+    append_sequence(params, rot, pool, 0, kb, vb)
+    out = _decode_gpu(params, rot, pool, q, variant)
+    ref, _ = _oracle_decode(wl, cals, kb, vb, q[0])
+    r = decode_check(out[0], ref)
+    print(f"variant {variant}: max err / norm = {r:.3e}")
+    assert r <= TOL
+
+
+@pytest.mark.parametrize("L", [1, 63, 64, 65, 300, 320, 321, 383, 384, 385, 1000, 4095])
+def test_decode_edge_lengths(tiny, L):
+    wl, cals, rot, params, kb, vb, q = tiny
+    pool = _fresh_pool(params, 59)
+    append_sequence(params, rot, pool, 0, kb[:L], vb[:L])
+    ref, _ = _oracle_decode(wl, cals, kb[:L], vb[:L], q[0])
+    for variant in (0, 1):
+        out = _decode_gpu(params, rot, pool, q, variant)
+        assert decode_check(out[0], ref) <= TOL, (L, variant)
+
+
+def test_decode_empty_sequence(tiny):
+    wl, cals, rot, params, kb, vb, q = tiny
+    pool = _fresh_pool(params, 59)
+    out = _decode_gpu(params, rot, pool, q, 0)
+    assert np.all(out == 0)
+
+
+def test_batch_scattered_ragged():
+    """Several sequences, two KV heads (G = 4), pages scattered by a seeded
+    permutation, ragged lengths with partial last pages."""
+    wl = synth.Workload(90, "test-scattered", 3, 2, 8, 128, 700, 2222, n_cal=512, outliers="pairs10",
+                        scattered_pages=True)
+    cals = oracle_calibration(wl, n_cal=512)
+    rot = rotation_tensors(cals)
+    params = O.make_params(wl.n_kv, wl.n_q)
+    lens = np.array([700, 1500, 2222], np.int32)
+    bt, total = synth.block_table(wl, lens)
+    pool = O.KVPool(params, wl.batch, total, bt)
+    toks = []
+    for b in range(wl.batch):
+        kb, vb = synth.kv_tokens(wl, 0, b, 0, int(lens[b]))
+        toks.append((kb, vb))
+        append_sequence(params, rot, pool, b, kb, vb, chunks=[int(lens[b]) - 3, 1, 1, 1])
+    q = synth.decode_queries(wl, 0)
+    for variant in (0, 1):
+        out = _decode_gpu(params, rot, pool, q, variant)
+        for b in range(wl.batch):
+            ref, _ = _oracle_decode(wl, cals, toks[b][0], toks[b][1], q[b])
+            assert decode_check(out[b], ref) <= TOL, (b, variant)
+    assert int(pool.error_flags.cpu()[0]) == 0
+
+
+def test_shared_prefix_gqa12():
+    """G = 12 query heads per KV head; two sequences share the sink slot and
+    the prefix pages (same physical page ids), private suffixes."""
+    wl = synth.Workload(91, "test-prefix", 2, 1, 12, 128, 1600, 1600, n_cal=512, outliers="pairs10")
+    cals = oracle_calibration(wl, n_cal=512)
+    rot = rotation_tensors(cals)
+    params = O.make_params(wl.n_kv, wl.n_q)
+    prefix = 64 + 8 * 64            # sink + 8 whole pages
+    L = 1600
+    n_pages = (L - 320 + 63) // 64
+    bt = np.zeros((2, n_pages), np.int32)
+    bt[0] = np.arange(n_pages)
+    bt[1, :8] = np.arange(8)
+    bt[1, 8:] = np.arange(n_pages, 2 * n_pages - 8)
+    pool = O.KVPool(params, 2, 2 * n_pages - 8, bt, sink_slot=[0, 0], n_sink_slots=1)
+    pk, pv = synth.kv_tokens(wl, 0, 0, 0, prefix)
+    toks = []
+    for b in range(2):
+        sk, sv = synth.kv_tokens(wl, 0, 10 + b, 0, L - prefix)
+        kb = np.concatenate([pk, sk])
+        vb = np.concatenate([pv, sv])
+        toks.append((kb, vb))
+        append_sequence(params, rot, pool, b, kb, vb, chunks=[prefix, L - prefix])
+    q = synth.decode_queries(wl, 0)
+    for variant in (0, 1):
+        out = _decode_gpu(params, rot, pool, q, variant)
+        for b in range(2):
+            ref, _ = _oracle_decode(wl, cals, toks[b][0], toks[b][1], q[b])
+            assert decode_check(out[b], ref) <= TOL, (b, variant)
+
+
+def test_bad_block_table_entry_flagged(tiny):
+    wl, cals, rot, params, kb, vb, q = tiny
+    pool = _fresh_pool(params, 59)
+    append_sequence(params, rot, pool, 0, kb, vb)
+    torch = _torch()
+    bt = pool.block_table.clone()
+    pool.block_table[0, 5] = 1 << 20          # outside [0, n_pages): skipped, flagged
+    out = _decode_gpu(params, rot, pool, q, 0)
+    assert np.all(np.isfinite(out))
+    assert int(pool.error_flags.cpu()[0]) & O.DEVERR_PAGE
+    pool.block_table.copy_(bt)
+
+
+def test_bf16_baseline_decode(tiny):
+    """In-house BF16 decode on the raw bf16 tokens equals exact attention."""
+    torch = _torch()
+    wl, cals, rot, params, kb, vb, q = tiny
+    L = 4000
+    n_pages = (L + 63) // 64
+    cache = O.Bf16Cache(params, 1, n_pages, np.arange(n_pages, dtype=np.int32)[None])
+    kt = np.zeros((n_pages * 64, 1, D), np.uint16)
+    vt = np.zeros_like(kt)
+    kt[:L], vt[:L] = kb[:L], vb[:L]
+    cache.k_pages.copy_(torch.from_numpy(kt.reshape(n_pages, 64, 1, D).transpose(0, 2, 1, 3).copy().view(np.int16)))
+    cache.v_pages.copy_(torch.from_numpy(vt.reshape(n_pages, 64, 1, D).transpose(0, 2, 1, 3).copy().view(np.int16)))
+    cache.seq_lens.fill_(L)
+    ws = O.alloc_workspace(O.bf16_workspace_size(params, 1, n_pages))
+    qt = torch.from_numpy(q.view(np.int16)).cuda()
+    out = torch.zeros((1, wl.n_q, D), dtype=torch.float32, device="cuda")
+    O.bf16_decode_attention(params, cache, qt, out, ws)
+    torch.cuda.synchronize()
+    ref = R.attention_dense(_f64(q[0]), _f64(kb[:L, 0]), _f64(vb[:L, 0]), 1 / np.sqrt(D))
+    assert decode_check(out.cpu().numpy()[0], ref) <= TOL
