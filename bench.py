@@ -1,0 +1,410 @@
+#!/usr/bin/env python3
+"""INT2-KV decode attention on one MI355X: microseconds per step and achieved
+HBM GB/s at 100K context, batch 32 (default) and batch 1.
+
+A step is one pass of the whole hot path over one decode token per sequence:
+for every layer, the fused write kernel appends the new token (demoting the
+oldest recent-window token into rotated INT2 history), then decode attention
+runs over the mixed-precision pool (query pre-rotation, split-K INT2 history
+scan, BF16 sink/recent segment, log-sum-exp merge with R_V^T).
+
+All inputs are seeded synthetic data (bit_rotated_kv_int2_amd.synth) already
+resident in HBM when timing starts.  Per-layer caches are distinct, so every
+layer streams from HBM rather than the 256 MB last-level cache.
+
+Prints one JSON line.  ``--gpus N`` with N > 1 is refused: this build runs on
+one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "INT2-KV decode attention µs/step + achieved HBM GB/s at 100K ctx, batch 1/32"
+HBM_PEAK_GBPS = 8000.0
+D = 128
+HIST_BYTES_PER_TOKEN_HEAD = 80      # 64 B codes (K+V) + 16 B fp16 scale/zero (K+V)
+WIN_BYTES_PER_TOKEN_HEAD = 512      # bf16 K + V
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# workload construction (plumbing: device memory via torch, compute via liboscar)
+# ---------------------------------------------------------------------------
+
+def gpu_kv(torch, synth, wl, layer, seq, L):
+    """Seeded bf16 K/V bits [L, Hkv, d] (int16) of one sequence, on the GPU."""
+    g = synth.torch_kv_generator(wl, layer, seq, "cuda")
+    out = []
+    for tensor in (0, 1):
+        sc = torch.from_numpy(synth.outlier_scale(wl, layer, tensor)).cuda()
+        x = torch.randn((L, wl.n_kv, D), generator=g, device="cuda", dtype=torch.float32) * sc
+        out.append(x.to(torch.bfloat16).view(torch.int16).contiguous())
+        del x
+    return out[0], out[1]
+
+
+def calibrate_layer(O, synth, wl, layer, params, n_cal):
+    q, k, v = synth.calibration_set(wl, layer, n_cal=n_cal)
+    f = synth.bf16_bits_to_f32
+    UK, UV, tK, tV = O.calibrate_rotation(params, f(q), f(k), f(v))
+    return O.RotationTensors.from_numpy(UK, UV, tK, tV, "cuda")
+
+
+class Workbench:
+    def __init__(self, wl, n_layers, extra_tokens, n_cal, bf16_budget_gb):
+        import torch
+        from bit_rotated_kv_int2_amd import oscar as O
+        from bit_rotated_kv_int2_amd import synth
+        self.torch, self.O, self.synth = torch, O, synth
+        self.wl = wl
+        self.params = O.make_params(wl.n_kv, wl.n_q)
+        self.lengths = synth.sequence_lengths(wl)
+        self.bt, self.total_pages = synth.block_table(wl, self.lengths, extra_tokens)
+        self.n_layers = n_layers
+        self.layers = []
+        t0 = time.time()
+        for layer in range(n_layers):
+            rot = calibrate_layer(O, synth, wl, layer, self.params, n_cal)
+            pool = O.KVPool(self.params, wl.batch, self.total_pages, self.bt, zero_pages=False)
+            for b in range(wl.batch):
+                k, v = gpu_kv(torch, synth, wl, layer, b, int(self.lengths[b]))
+                O.quantize_append(self.params, rot, pool, k[None], v[None], seq=b)
+                del k, v
+            torch.cuda.synchronize()
+            assert int(pool.error_flags.item()) == 0
+            self.layers.append((rot, pool))
+            if layer % 6 == 5 or layer == n_layers - 1:
+                log(f"{wl.name}: built INT2 layer {layer + 1}/{n_layers} ({time.time() - t0:.1f}s)")
+        self.ws = O.alloc_workspace(O.decode_workspace_size(self.params, wl.batch, self.bt.shape[1]))
+        self.out = torch.zeros((wl.batch, wl.n_q, D), dtype=torch.float32, device="cuda")
+        # BF16 baseline caches holding the same token contents (as many layers as the budget allows)
+        per_layer = float(np.sum(self.lengths)) * wl.n_kv * WIN_BYTES_PER_TOKEN_HEAD
+        self.n_bf16 = int(max(1, min(n_layers, bf16_budget_gb * 1e9 // max(per_layer, 1))))
+        self.bf16 = []
+        pages16 = [(int(L) + 63) // 64 for L in self.lengths]
+        mp16 = max(pages16)
+        bt16 = np.full((wl.batch, mp16), -1, np.int32)
+        perm = synth.rng(wl, 0, synth.STREAM_PERM, 16).permutation(sum(pages16)).astype(np.int32)
+        nxt = 0
+        for b, n in enumerate(pages16):
+            bt16[b, :n] = perm[nxt:nxt + n]
+            nxt += n
+        self.bt16 = bt16
+        for layer in range(self.n_bf16):
+            cache = O.Bf16Cache(self.params, wl.batch, sum(pages16), bt16)
+            for b in range(wl.batch):
+                L = int(self.lengths[b])
+                k, v = gpu_kv(torch, synth, wl, layer, b, L)
+                n = pages16[b]
+                pad = n * 64 - L
+                for src, dst in ((k, cache.k_pages), (v, cache.v_pages)):
+                    if pad:
+                        src = torch.cat([src, torch.zeros((pad, wl.n_kv, D), dtype=src.dtype, device="cuda")])
+                    blk = src.view(n, 64, wl.n_kv, D).permute(0, 2, 1, 3)
+                    idx = torch.from_numpy(bt16[b, :n].astype(np.int64)).cuda()
+                    dst.index_copy_(0, idx, blk.contiguous())
+                del k, v
+            cache.seq_lens.copy_(torch.from_numpy(self.lengths.astype(np.int32)))
+            self.bf16.append(cache)
+        torch.cuda.synchronize()
+        self.ws16 = O.alloc_workspace(max(O.bf16_workspace_size(self.params, bb, mp16)
+                                          for bb in range(1, wl.batch + 1)))
+        log(f"{wl.name}: built {self.n_bf16} BF16 baseline layers ({time.time() - t0:.1f}s total)")
+
+    # --- byte accounting -----------------------------------------------------
+    def hist_bytes(self, lengths):
+        n_hist = np.maximum(0, lengths.astype(np.int64) - self.wl.sink - self.wl.recent)
+        return int(np.sum(n_hist)) * self.wl.n_kv * HIST_BYTES_PER_TOKEN_HEAD
+
+    def layer_step_bytes(self, lengths):
+        """Algorithmic HBM bytes of one layer of one step (append + decode)."""
+        wl = self.wl
+        win = np.minimum(lengths.astype(np.int64), wl.sink + wl.recent)
+        b = self.hist_bytes(lengths) + int(np.sum(win)) * wl.n_kv * WIN_BYTES_PER_TOKEN_HEAD
+        b += wl.batch * wl.n_q * D * (2 + 4)                      # q in, out
+        b += 2 * wl.n_kv * D * D * 4                              # U_K, U_V
+        b += wl.batch * wl.n_kv * 2 * (256 + 256 + 256 + 40)      # append: new in, ring in/out, codes+meta out
+        return b
+
+
+def run_workload(wb, steps, warmup, decode_reps, bf16_fit=None):
+    torch, O = wb.torch, wb.O
+    wl = wb.wl
+    nl = wb.n_layers
+    total = warmup + steps
+    # per-layer per-step new tokens and queries
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234 + wl.wid)
+    knew = [torch.randn((total, wl.batch, 1, wl.n_kv, D), generator=g, device="cuda").to(torch.bfloat16)
+            .view(torch.int16).contiguous() for _ in range(nl)]
+    vnew = [torch.randn((total, wl.batch, 1, wl.n_kv, D), generator=g, device="cuda").to(torch.bfloat16)
+            .view(torch.int16).contiguous() for _ in range(nl)]
+    qs = [torch.randn((total, wl.batch, wl.n_q, D), generator=g, device="cuda").to(torch.bfloat16)
+          .view(torch.int16).contiguous() for _ in range(nl)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps * nl)]
+    for a, b in ev:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    base = wb.lengths.astype(np.int64)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    wall0 = 0.0
+    for s in range(total):
+        if s == warmup:
+            torch.cuda.synchronize()
+            wall0 = time.perf_counter()
+            t_start.record()
+        for l, (rot, pool) in enumerate(wb.layers):
+            O.quantize_append(wb.params, rot, pool, knew[l][s], vnew[l][s])
+            if s >= warmup:
+                e0, e1 = ev[(s - warmup) * nl + l]
+                O.set_history_timing_events(e0, e1)
+            O.decode_attention(wb.params, rot, pool, qs[l][s], wb.out, wb.ws)
+            if s >= warmup:
+                O.set_history_timing_events(None, None)
+    t_stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = t_start.elapsed_time(t_stop) / steps
+    hist_us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]
+    for _, pool in wb.layers:
+        assert int(pool.error_flags.item()) == 0
+    # algorithmic bytes of the timed steps (lengths after the step's append)
+    step_bytes = [nl * wb.layer_step_bytes(base + s + 1) for s in range(warmup, total)]
+    hist_launch_bytes = [wb.hist_bytes(base + s + 1) for s in range(warmup, total)]
+
+    # decode-only per-layer time (no append), cycling through every layer
+    d0 = torch.cuda.Event(enable_timing=True)
+    d1 = torch.cuda.Event(enable_timing=True)
+    lens_now = base + total
+    d0.record()
+    for r in range(decode_reps):
+        for l, (rot, pool) in enumerate(wb.layers):
+            O.decode_attention(wb.params, rot, pool, qs[l][r % total], wb.out, wb.ws)
+    d1.record()
+    torch.cuda.synchronize()
+    decode_us = d0.elapsed_time(d1) * 1e3 / (decode_reps * nl)
+    decode_bytes = wb.layer_step_bytes(lens_now) - wl.batch * wl.n_kv * 2 * (256 + 256 + 256 + 40)
+
+    # BF16 baseline, same token contents, same shapes
+    b0 = torch.cuda.Event(enable_timing=True)
+    b1 = torch.cuda.Event(enable_timing=True)
+    n16 = max(decode_reps * nl // max(wb.n_bf16, 1), wb.n_bf16) // wb.n_bf16 * wb.n_bf16
+    q16 = qs[0][0]
+    for c in wb.bf16:   # warm
+        O.bf16_decode_attention(wb.params, c, q16, wb.out, wb.ws16)
+    b0.record()
+    for i in range(n16):
+        O.bf16_decode_attention(wb.params, wb.bf16[i % wb.n_bf16], q16, wb.out, wb.ws16)
+    b1.record()
+    torch.cuda.synchronize()
+    bf16_us = b0.elapsed_time(b1) * 1e3 / n16
+    bf16_bytes = int(np.sum(wb.lengths)) * wl.n_kv * WIN_BYTES_PER_TOKEN_HEAD
+    fit_us = None
+    if bf16_fit and bf16_fit < wl.batch:
+        views = []
+        for c in wb.bf16:
+            cc = c.c()
+            cc.batch = bf16_fit
+            views.append(cc)
+        import ctypes
+        stream = torch.cuda.current_stream().cuda_stream
+        f0 = torch.cuda.Event(enable_timing=True)
+        f1 = torch.cuda.Event(enable_timing=True)
+        f0.record()
+        for i in range(n16):
+            O._check(O.lib().oscar_bf16_decode_attention(ctypes.byref(wb.params), ctypes.byref(views[i % len(views)]),
+                                                         q16.data_ptr(), wb.out.data_ptr(), wb.ws16.data_ptr(),
+                                                         wb.ws16.numel(), stream))
+        f1.record()
+        torch.cuda.synchronize()
+        fit_us = f0.elapsed_time(f1) * 1e3 / n16
+
+    hist_mean_us = float(np.mean(hist_us))
+    hist_bytes_mean = float(np.mean(hist_launch_bytes))
+    return {
+        "step_ms": step_ms,
+        "wall_ms_per_step": wall * 1e3 / steps,
+        "value_gbps": float(np.mean(step_bytes)) / (step_ms * 1e-3) / 1e9,
+        "hist_kernel_us": hist_mean_us,
+        "hist_kernel_us_p10_p90": [float(np.percentile(hist_us, 10)), float(np.percentile(hist_us, 90))],
+        "hist_kernel_bytes": hist_bytes_mean,
+        "hist_kernel_gbps": hist_bytes_mean / (hist_mean_us * 1e-6) / 1e9,
+        "decode_us_per_layer": decode_us,
+        "decode_gbps": decode_bytes / (decode_us * 1e-6) / 1e9,
+        "bf16_us_per_layer": bf16_us,
+        "bf16_gbps": bf16_bytes / (bf16_us * 1e-6) / 1e9,
+        "speedup_vs_bf16_decode": bf16_us / decode_us,
+        "bytes_per_step": float(np.mean(step_bytes)),
+        "bf16_fit_us_per_layer": fit_us,
+    }
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle's decode on a bounded sample of the same workload
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(wl, pairs, reps):
+    import torch
+    from bit_rotated_kv_int2_amd import synth
+    from oracle import oscar_ref as R
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    lengths = synth.sequence_lengths(wl)
+    G = wl.n_q // wl.n_kv
+    q_all = synth.decode_queries(wl, 0)
+    qc, kc, vc = synth.calibration_set(wl, 0, n_cal=512)
+    f = synth.bf16_bits_to_f32
+    times, nbytes = [], 0
+    for (b, h) in pairs:
+        L = int(lengths[b])
+        k, v = gpu_kv(torch, synth, wl, 0, b, L)
+        kh = f(k[:, h].cpu().numpy().view(np.uint16)).astype(np.float64)
+        vh = f(v[:, h].cpu().numpy().view(np.uint16)).astype(np.float64)
+        del k, v
+        cal = R.calibrate_head(f(qc[h * G:(h + 1) * G]), f(kc[h]), f(vc[h]), 1 / np.sqrt(D))
+        pool = R.build_head_pool(kh, vh, cal)
+        q = f(q_all[b, h * G:(h + 1) * G]).astype(np.float64)
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            R.decode_head_dense(q, pool, cal, 1 / np.sqrt(D))
+            times.append(time.perf_counter() - t0)
+        nbytes += reps * (max(0, L - 320) * HIST_BYTES_PER_TOKEN_HEAD + min(L, 320) * WIN_BYTES_PER_TOKEN_HEAD)
+    total = float(np.sum(times))
+    return {"value": nbytes / total / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "seconds": total,
+            "us_per_head_decode": total / len(times) * 1e6,
+            "sample": f"oracle fp64 decode (dequantise + inverse-rotate + softmax attention) of "
+                      f"{len(pairs)} (sequence, KV head) pairs of {wl.name} at full length, "
+                      f"{reps} runs each; GB/s over the same algorithmic bytes as the GPU"}
+
+
+def effective_bpe(L, sink=64, recent=256, history_bits=2.0 + 32.0 / 64):
+    """Stored bits per KV element: BF16 windows + INT2 codes with fp16 scale and zero per 64 channels."""
+    win = min(L, sink + recent)
+    return (win * 16.0 + (L - win) * history_bits) / L
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3-8b-100k-b32-36l")
+    ap.add_argument("--layers", type=int, default=None, help="override the workload's layer count")
+    ap.add_argument("--decode-reps", type=int, default=5)
+    ap.add_argument("--n-cal", type=int, default=512)
+    ap.add_argument("--no-batch1", action="store_true", help="skip the batch-1 secondary workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variant", type=int, default=0, help="0 = MFMA int8 history kernel, 1 = VALU")
+    ap.add_argument("--bf16-budget-gb", type=float, default=48.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "multi-GPU sharding is design-only in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bit_rotated_kv_int2_amd import oscar as O
+    from bit_rotated_kv_int2_amd import synth
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    O.lib()   # fail loudly if the HIP library is missing
+    O.set_decode_variant(args.variant)
+
+    wl = synth.WORKLOADS[args.workload]
+    nl = args.layers or wl.layers
+    wb = Workbench(wl, nl, args.warmup + args.steps, args.n_cal, args.bf16_budget_gb)
+    bf16_fit = None
+    if wl.batch > 1:
+        # sequences an all-BF16 cache of the same layers fits in the HBM the INT2 pool occupies
+        int2_bytes = sum(p.pages.numel() + 2 * (p.recent_k.numel() + p.sink_k.numel()) * 2 for _, p in wb.layers)
+        per_seq_bf16 = float(np.mean(wb.lengths)) * wl.n_kv * WIN_BYTES_PER_TOKEN_HEAD * nl
+        bf16_fit = int(int2_bytes // per_seq_bf16)
+    r = run_workload(wb, args.steps, args.warmup, args.decode_reps, bf16_fit)
+    log(f"{wl.name}: {json.dumps(r)}")
+    del wb
+    torch.cuda.empty_cache()
+
+    batch1 = None
+    if not args.no_batch1 and wl.batch > 1:
+        wl1 = synth.WORKLOADS["qwen3-8b-100k-b1-36l"]
+        wb1 = Workbench(wl1, args.layers or wl1.layers, args.warmup + args.steps, args.n_cal, args.bf16_budget_gb)
+        r1 = run_workload(wb1, args.steps, args.warmup, args.decode_reps * 4)
+        log(f"{wl1.name}: {json.dumps(r1)}")
+        batch1 = {"workload": wl1.name, "us_per_step": r1["step_ms"] * 1e3, "gbps": r1["value_gbps"],
+                  "decode_us_per_layer": r1["decode_us_per_layer"], "decode_gbps": r1["decode_gbps"],
+                  "decode_frac_of_peak": r1["decode_gbps"] / HBM_PEAK_GBPS,
+                  "hist_kernel_us": r1["hist_kernel_us"], "hist_kernel_gbps": r1["hist_kernel_gbps"],
+                  "hist_kernel_frac_of_peak": r1["hist_kernel_gbps"] / HBM_PEAK_GBPS,
+                  "bf16_us_per_layer": r1["bf16_us_per_layer"], "bf16_gbps": r1["bf16_gbps"],
+                  "speedup_vs_bf16_decode": r1["speedup_vs_bf16_decode"]}
+        del wb1
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        pairs = [(0, 0), (1, 3), (2, 5), (3, 7)] if wl.batch >= 4 else [(0, h) for h in range(min(4, wl.n_kv))]
+        cpu = cpu_baseline(wl, pairs, reps=2)
+
+    line = {
+        "metric": METRIC,
+        "value": r["value_gbps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["step_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "dtype_detail": "INT2 history codes on int8xint8->int32 MFMA; fp32 softmax/accumulation; bf16 windows",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "layers": nl, "kv_heads": wl.n_kv,
+                   "q_heads": wl.n_q, "head_dim": D, "context": [wl.min_len, wl.max_len],
+                   "page_tokens": 64, "scattered_pages": wl.scattered_pages, "parallelism": "single-gpu"},
+        "us_per_step": r["step_ms"] * 1e3,
+        "step_contents": "per layer: append 1 token/sequence (fused rotate-clip-quantise-pack-demote) + decode attention",
+        "decode_us_per_layer": r["decode_us_per_layer"],
+        "decode_gbps": r["decode_gbps"],
+        "decode_frac_of_peak": r["decode_gbps"] / HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "kernel": "int2_mfma_kernel (split-K INT2 history scan)",
+                     "achieved": r["hist_kernel_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": r["hist_kernel_gbps"] / HBM_PEAK_GBPS, "traffic": None,
+                     "bytes_per_launch": r["hist_kernel_bytes"], "us_per_launch": r["hist_kernel_us"],
+                     "us_p10_p90": r["hist_kernel_us_p10_p90"]},
+        "bf16_baseline": {"us_per_layer": r["bf16_us_per_layer"], "gbps": r["bf16_gbps"],
+                          "speedup_vs_bf16_decode": r["speedup_vs_bf16_decode"],
+                          "bf16_batch_in_same_hbm": bf16_fit,
+                          "bf16_us_per_layer_at_that_batch": r["bf16_fit_us_per_layer"],
+                          "job_throughput_ratio": (None if not r["bf16_fit_us_per_layer"] else
+                                                   (wl.batch / r["decode_us_per_layer"]) /
+                                                   (bf16_fit / r["bf16_fit_us_per_layer"]))},
+        "effective_bits_per_kv_element": round(effective_bpe(float(np.mean(synth.sequence_lengths(wl)))), 4),
+        "pages_bits_per_kv_element": 2.28,
+        "batch1": batch1,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -22,8 +22,7 @@ SOURCES = [
     "oscar_api.cpp",
     "oscar_calibrate.cpp",
     "oscar_write.hip",
-    "oscar_decode.hip",
-    "oscar_decode_mfma.hip",
+    "oscar_decode_kernels.hip",
     "oscar_bf16.hip",
 ]
 

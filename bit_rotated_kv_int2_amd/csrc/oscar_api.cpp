@@ -12,6 +12,7 @@ namespace {
 
 thread_local char g_err[512] = "";
 int g_variant = 0;
+hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 
 int fail(int code, const char *fmt, ...) {
   va_list ap;
@@ -92,6 +93,14 @@ const char *oscar_last_error(void) { return g_err; }
 
 int32_t oscar_version(void) { return 1000; }
 
+int32_t oscar_set_history_timing_events(void *start_event, void *stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(OSCAR_EINVAL, "give both timing events or neither");
+  g_ev_start = (hipEvent_t)start_event;
+  g_ev_stop = (hipEvent_t)stop_event;
+  return ok();
+}
+
 int32_t oscar_set_decode_variant(int32_t variant) {
   if (variant != 0 && variant != 1) return fail(OSCAR_EINVAL, "variant must be 0 (MFMA) or 1 (VALU)");
   g_variant = variant;
@@ -153,7 +162,8 @@ int32_t oscar_decode_attention(const oscar_params *p, const oscar_rotation *rot,
   if (((uintptr_t)workspace) & 255) return fail(OSCAR_EINVAL, "workspace must be 256-byte aligned");
   oscar::PoolView pv = make_pv(p, pool);
   oscar::RotView rv{rot->U_K, rot->U_V, rot->tau_K, rot->tau_V};
-  hipError_t e = oscar::launch_decode(pv, rv, q, out, (uint8_t *)workspace, plan, g_variant, (hipStream_t)stream);
+  hipError_t e = oscar::launch_decode(pv, rv, q, out, (uint8_t *)workspace, plan, g_variant, (hipStream_t)stream,
+                                      g_ev_start, g_ev_stop);
   if (e != hipSuccess) return fail(OSCAR_EHIP, "decode launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -1,83 +1,74 @@
 // In-house BF16 decode attention on a paged all-BF16 KV cache: the baseline
 // every INT2 speedup is measured against (the pages compare OSCAR's INT2
-// history against a BF16 KV cache: [A] youleyou.com article on OSCAR, section
+// history with a BF16 KV cache: [A] youleyou.com article on OSCAR, section
 // "系统加速效果"; [B] MarkTechPost (zh) "Together AI 开源 OSCAR…", section "结果").
 //
-// Split-K over 64-token pages, four waves per workgroup on interleaved pages.
-//   QK on the matrix cores: v_mfma_f32_16x16x32_bf16, rows = query heads
-//   (up to 16), columns = 16 tokens, K = 128 channels; the bf16 query and
-//   keys are used as stored, products accumulate in float32.
-//   PV on the VALU in float32: lane (c8, tq) owns channels 8 c8 .. 8 c8 + 7
-//   and every fourth token, so each V row is read with 16-byte loads.
-#include "oscar_internal.h"
+// One launch: blocks of 256 threads over (sequence, KV head, split) of the
+// 64-token pages; each wave takes every fourth page of its split and runs the
+// shared BF16 chunk routine (bf16 MFMA logits, float32 VALU value sums).  The
+// last block of a (sequence, KV head) merges the split partials and writes
+// the output, so no second launch is needed.  Counters return to zero; the
+// workspace must be zero-filled before its first use.
+#include <stdlib.h>
+
+#include "oscar_wave.h"
 
 namespace oscar {
 namespace {
 
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-constexpr float kLog2e = 1.4426950408889634f;
-
 struct Bf16Args {
   Bf16View v;
   const uint16_t *q;
-  float *part;
+  float *out;
+  float *part;      // [B*Hkv][n_splits][G][kPartStride]
+  int *counters;    // [B*Hkv]
   int n_splits, pages_per_split;
 };
 
-__device__ __forceinline__ v8bf as_v8bf(uint4 u) { return __builtin_bit_cast(v8bf, u); }
+template <int GH>
+union Bf16BaseSmem {
+  struct {
+    float ps[4][GH][kPageTokens + 4];
+    float m[4][GH], l[4][GH];
+    float o[4][GH][kD];
+  } w;
+  struct {
+    float ws[GH][256], M[GH], l[GH];
+  } g;
+};
 
-template <int GH>   // GH >= G: heads per KV head, rounded up
+template <int GH>
 __global__ void __launch_bounds__(256) bf16_decode_kernel(Bf16Args a) {
   const Bf16View &cv = a.v;
-  const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int BH = cv.batch * cv.hkv;
+  const int bh = blockIdx.x % BH, split = blockIdx.x / BH;
+  const int b = bh / cv.hkv, kv = bh % cv.hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, q = lane >> 4;
   const int G = cv.hq / cv.hkv;
-  const int L = cv.seq_lens[b];
+  const int L = max(0, cv.seq_lens[b]);
   const int n_pages = (L + kPageTokens - 1) / kPageTokens;
   const int pg0 = split * a.pages_per_split;
-  const int pg1 = min(n_pages, pg0 + a.pages_per_split);
+  const int pg1 = min(min(n_pages, pg0 + a.pages_per_split), cv.max_pages);
+  if (n_pages > cv.max_pages && split == 0 && tid == 0 && cv.err) atomicOr(cv.err, OSCAR_DEVERR_LENGTH);
+  __shared__ Bf16BaseSmem<GH> sm;
 
-  __shared__ float ps[4][kMaxGroupHeads][kPageTokens + 4];
-  __shared__ float sm_m[4][kMaxGroupHeads], sm_l[4][kMaxGroupHeads];
-  __shared__ float sm_o[4][kMaxGroupHeads][kD];
-
-  // A operand: row = head (n), kgroup q, kstep ks: channels 32 q + 8 ks .. +8.
   v8bf Aq[4];
-  {
-    const int h = n;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      uint4 u = {0, 0, 0, 0};
-      if (h < G) u = *(const uint4 *)(a.q + ((size_t)b * cv.hq + kv * G + h) * kD + 32 * q + 8 * ks);
-      Aq[ks] = as_v8bf(u);
-    }
-  }
-  // running softmax per head (head = 4 q + i in the C layout, replicated)
-  float m[4], l[4];
+  load_bf16_query(a.q + ((size_t)b * cv.hq + (size_t)kv * G) * kD, G, Aq);
+  float m[4], l[4], mrow[GH], o[GH][8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     m[i] = -INFINITY;
     l[i] = 0.f;
   }
-  // PV accumulators: lane (c8 = n, tq = q): channels 8 n .. 8 n + 7, all heads
-  float o[GH][8];
 #pragma unroll
-  for (int h = 0; h < GH; ++h)
+  for (int h = 0; h < GH; ++h) {
+    mrow[h] = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[h][i] = 0.f;
-  float mrow[GH];     // running max of every head, for PV rescaling
-#pragma unroll
-  for (int h = 0; h < GH; ++h) mrow[h] = -INFINITY;
+    for (int c = 0; c < 8; ++c) o[h][c] = 0.f;
+  }
   const float sl2 = cv.sm_scale * kLog2e;
   bool bad = false;
-
   for (int pgi = pg0 + wave; pgi < pg1; pgi += 4) {
-    if (pgi >= cv.max_pages) {
-      bad = true;
-      break;
-    }
     const int phys = cv.block_table[(size_t)b * cv.max_pages + pgi];
     if (phys < 0 || phys >= cv.n_pages) {
       bad = true;
@@ -85,202 +76,89 @@ __global__ void __launch_bounds__(256) bf16_decode_kernel(Bf16Args a) {
     }
     const int valid = min(kPageTokens, L - pgi * kPageTokens);
     const size_t base = ((size_t)phys * cv.hkv + kv) * kPageTokens * kD;
-    const uint16_t *K = cv.k_pages + base;
-    const uint16_t *V = cv.v_pages + base;
-
-    // ---- logits: 4 tiles of 16 tokens ----
-    float lg[4][4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const uint16_t *kr = K + (size_t)(16 * tt + n) * kD + 32 * q;
-      v4f C = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const v8bf Bk = as_v8bf(*(const uint4 *)(kr + 8 * ks));
-        C = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aq[ks], Bk, C, 0, 0, 0);
-      }
-      const bool ok = (16 * tt + n) < valid;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lg[tt][i] = ok ? C[i] * sl2 : -INFINITY;
-    }
-    // per head (row 4 q + i): page max over tokens (tt and 16 lanes n)
-    float pm[4], e[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = fmaxf(fmaxf(lg[0][i], lg[1][i]), fmaxf(lg[2][i], lg[3][i]));
-      v = fmaxf(v, __shfl_xor(v, 1, 64));
-      v = fmaxf(v, __shfl_xor(v, 2, 64));
-      v = fmaxf(v, __shfl_xor(v, 4, 64));
-      v = fmaxf(v, __shfl_xor(v, 8, 64));
-      const float mn = fmaxf(m[i], v);
-      const float al = __builtin_amdgcn_exp2f(m[i] - mn);
-      float s = 0.f;
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        e[tt][i] = __builtin_amdgcn_exp2f(lg[tt][i] - mn);
-        s += e[tt][i];
-      }
-      s += __shfl_xor(s, 1, 64);
-      s += __shfl_xor(s, 2, 64);
-      s += __shfl_xor(s, 4, 64);
-      s += __shfl_xor(s, 8, 64);
-      l[i] = l[i] * al + s;
-      m[i] = mn;
-      pm[i] = mn;
-      const int h = 4 * q + i;
-      if (h < G) {
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) ps[wave][h][16 * tt + n] = e[tt][i];
-      }
-    }
-    // share the new running max of each head with the PV lanes
-    wave_lds_sync();
-    float mh[GH];
-#pragma unroll
-    for (int h = 0; h < GH; ++h) {
-      // head h lives in lanes 16 (h >> 2) .. in C row i = h & 3
-      const int src = 16 * (h >> 2);
-      const int i = h & 3;
-      float v = (i == 0) ? pm[0] : (i == 1) ? pm[1] : (i == 2) ? pm[2] : pm[3];
-      mh[h] = __shfl(v, src, 64);
-    }
-#pragma unroll
-    for (int h = 0; h < GH; ++h) {
-      if (h >= G) break;
-      const float al = __builtin_amdgcn_exp2f(mrow[h] - mh[h]);
-      mrow[h] = mh[h];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[h][i] *= al;
-    }
-    // ---- PV: lane (n = channel octet, q = token phase) ----
-    for (int t = q; t < valid; t += 4) {
-      const uint4 u = *(const uint4 *)(V + (size_t)t * kD + 8 * n);
-      float vf[8];
-      vf[0] = __uint_as_float(u.x << 16);
-      vf[1] = __uint_as_float(u.x & 0xFFFF0000u);
-      vf[2] = __uint_as_float(u.y << 16);
-      vf[3] = __uint_as_float(u.y & 0xFFFF0000u);
-      vf[4] = __uint_as_float(u.z << 16);
-      vf[5] = __uint_as_float(u.z & 0xFFFF0000u);
-      vf[6] = __uint_as_float(u.w << 16);
-      vf[7] = __uint_as_float(u.w & 0xFFFF0000u);
-#pragma unroll
-      for (int h = 0; h < GH; ++h) {
-        if (h >= G) break;
-        const float p = ps[wave][h][t];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[h][i] = fmaf(p, vf[i], o[h][i]);
-      }
-    }
-    wave_lds_sync();
+    bf16_chunk<GH>(cv.k_pages + base, cv.v_pages + base, valid, G, Aq, sl2, m, l, mrow, o, sm.w.ps[wave]);
   }
   if (bad && lane == 0 && cv.err) atomicOr(cv.err, OSCAR_DEVERR_PAGE);
+  float *parts = a.part + (size_t)bh * a.n_splits * G * kPartStride;
+  bf16_block_combine<GH>(G, m, l, o, sm.w.m, sm.w.l, sm.w.o, parts + (size_t)split * G * kPartStride);
 
-  // combine: PV partial sums over the 4 token phases q, then the 4 waves
-#pragma unroll
-  for (int h = 0; h < GH; ++h) {
-    if (h >= G) break;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float v = o[h][i];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      o[h][i] = v;
+  __shared__ int last_flag;
+  if (!arrive_last(&a.counters[bh], a.n_splits, &last_flag)) return;
+  const int S = a.n_splits;
+  for (int h = wave; h < G; h += 4) {
+    float M = -INFINITY;
+    for (int s = lane; s < S; s += 64) M = fmaxf(M, ld_coherent(parts + ((size_t)s * G + h) * kPartStride));
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    float lsum = 0.f;
+    for (int s = lane; s < S; s += 64) {
+      const float *p = parts + ((size_t)s * G + h) * kPartStride;
+      const float m0 = ld_coherent(p);
+      const float w = (M > -INFINITY && m0 > -INFINITY) ? exp2_fast(m0 - M) : 0.f;
+      sm.g.ws[h][s] = w;
+      lsum = fmaf(w, ld_coherent(p + 1), lsum);
     }
-  }
-  if (q == 0) {
-#pragma unroll
-    for (int h = 0; h < GH; ++h) {
-      if (h >= G) break;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sm_o[wave][h][8 * n + i] = o[h][i];
-    }
-  }
-  if (n == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * q + i;
-      if (h < G) {
-        sm_m[wave][h] = m[i];
-        sm_l[wave][h] = l[i];
-      }
+    for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
+    if (lane == 0) {
+      sm.g.M[h] = M;
+      sm.g.l[h] = lsum;
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < G * kD; idx += 256) {
+  for (int idx = tid; idx < G * kD; idx += blockDim.x) {
     const int h = idx / kD, c = idx % kD;
-    float M = -INFINITY;
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][h]);
-    float ov = 0.f, lv = 0.f;
-    if (M > -INFINITY) {
-      for (int w = 0; w < 4; ++w) {
-        if (sm_m[w][h] == -INFINITY) continue;
-        const float sc = __builtin_amdgcn_exp2f(sm_m[w][h] - M);
-        ov += sc * sm_o[w][h][c];
-        lv += sc * sm_l[w][h];
-      }
+    float o0 = 0.f, o1 = 0.f;
+    const float *p = parts + (size_t)h * kPartStride + 2 + c;
+    const size_t st = (size_t)G * kPartStride;
+    int s = 0;
+    for (; s + 2 <= S; s += 2) {
+      o0 = fmaf(sm.g.ws[h][s], ld_coherent(p + (size_t)s * st), o0);
+      o1 = fmaf(sm.g.ws[h][s + 1], ld_coherent(p + (size_t)(s + 1) * st), o1);
     }
-    float *dst = a.part + ((((size_t)b * cv.hkv + kv) * a.n_splits + split) * G + h) * kPartStride;
-    if (c == 0) {
-      dst[0] = M;   // log2 units
-      dst[1] = lv;
-    }
-    dst[2 + c] = ov;
+    if (s < S) o0 = fmaf(sm.g.ws[h][s], ld_coherent(p + (size_t)s * st), o0);
+    const float den = sm.g.l[h];
+    a.out[((size_t)b * cv.hq + (size_t)kv * G + h) * kD + c] = den > 0.f ? (o0 + o1) / den : 0.f;
   }
 }
 
-// grid (Hq, batch), block 128: merge the split partials of one query head.
-__global__ void __launch_bounds__(128) bf16_merge_kernel(Bf16View cv, const float *part, float *out,
-                                                         int n_splits) {
-  const int hq = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
-  const int G = cv.hq / cv.hkv;
-  const int kv = hq / G, h = hq % G;
-  auto P = [&](int s) { return part + ((((size_t)b * cv.hkv + kv) * n_splits + s) * G + h) * kPartStride; };
-  float M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, P(s)[0]);
-  float o = 0.f, l = 0.f;
-  if (M > -INFINITY) {
-    for (int s = 0; s < n_splits; ++s) {
-      const float *p = P(s);
-      if (p[0] == -INFINITY) continue;
-      const float w = __builtin_amdgcn_exp2f(p[0] - M);
-      o += w * p[2 + c];
-      l += w * p[1];
-    }
-  }
-  out[((size_t)b * cv.hq + hq) * kD + c] = (l > 0.f) ? o / l : 0.f;
+int bf16_target_blocks() {
+  static int v = [] {
+    const char *e = getenv("OSCAR_BF16_BLOCKS");
+    const int x = e ? atoi(e) : 0;
+    return x > 0 ? x : 1024;
+  }();
+  return v;
 }
 
 }  // namespace
 
 Bf16Plan make_bf16_plan(int batch, int hkv, int hq, int max_pages) {
-  (void)hq;
   Bf16Plan p{};
-  const long work = (long)batch * hkv * (max_pages > 0 ? max_pages : 1);
-  int pps = (int)((work + 2047) / 2048);
-  pps = pps < 4 ? 4 : pps;
-  p.pages_per_split = pps;
-  p.n_splits = max_pages > 0 ? (max_pages + pps - 1) / pps : 1;
-  p.off_part = 0;
   const int G = hq / hkv;
-  p.total = ((size_t)batch * hkv * p.n_splits * G * kPartStride * sizeof(float) + 255) & ~(size_t)255;
+  const int bh = batch * hkv;
+  int S = (bf16_target_blocks() + bh - 1) / bh;
+  const int max_by_pages = max_pages > 0 ? (max_pages + 3) / 4 : 1;
+  S = S < 1 ? 1 : S;
+  S = S > max_by_pages ? max_by_pages : S;
+  S = S > 256 ? 256 : S;
+  p.n_splits = S;
+  p.pages_per_split = max_pages > 0 ? (max_pages + S - 1) / S : 1;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  p.off_counters = 0;
+  p.off_part = al((size_t)bh * sizeof(int));
+  p.total = al(p.off_part + (size_t)bh * S * G * kPartStride * sizeof(float));
   return p;
 }
 
 hipError_t launch_bf16_decode(const Bf16View &v, const uint16_t *q, float *out, uint8_t *ws,
                               const Bf16Plan &plan, hipStream_t s) {
-  float *part = (float *)(ws + plan.off_part);
-  Bf16Args a{v, q, part, plan.n_splits, plan.pages_per_split};
-  const dim3 grid(plan.n_splits, v.hkv, v.batch), block(256);
+  Bf16Args a{v, q, out, (float *)(ws + plan.off_part), (int *)(ws + plan.off_counters), plan.n_splits,
+             plan.pages_per_split};
+  const dim3 grid(v.batch * v.hkv * plan.n_splits), block(256);
   const int G = v.hq / v.hkv;
   if (G <= 4) hipLaunchKernelGGL(bf16_decode_kernel<4>, grid, block, 0, s, a);
   else if (G <= 8) hipLaunchKernelGGL(bf16_decode_kernel<8>, grid, block, 0, s, a);
   else if (G <= 12) hipLaunchKernelGGL(bf16_decode_kernel<12>, grid, block, 0, s, a);
   else hipLaunchKernelGGL(bf16_decode_kernel<16>, grid, block, 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bf16_merge_kernel, dim3(v.hq, v.batch), dim3(128), 0, s, v, (const float *)part, out,
-                     plan.n_splits);
   return hipGetLastError();
 }
 

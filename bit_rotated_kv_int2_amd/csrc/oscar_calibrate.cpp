@@ -143,11 +143,12 @@ double quantile_linear(std::vector<double> &v, double qv) {
 
 // |x R| entries for every row of x [n][d] (float32 holding bf16 values),
 // R = U32 H P; the permutation does not change the multiset.
-void rotated_abs(int d, const float *x, int64_t n, const float *U32, std::vector<double> &out) {
+void rotated_abs_serial(int d, const float *x, int64_t n, const float *U32, std::vector<double> &out) {
   out.resize((size_t)n * d);
   const double c = 1.0 / std::sqrt((double)d);
-  parallel_for(n, [&](int, int64_t r) {
-    std::vector<double> y(d, 0.0);
+  std::vector<double> y(d);
+  for (int64_t r = 0; r < n; ++r) {
+    std::fill(y.begin(), y.end(), 0.0);
     const float *xr = x + (size_t)r * d;
     for (int k = 0; k < d; ++k) {
       const double xk = xr[k];
@@ -162,7 +163,7 @@ void rotated_abs(int d, const float *x, int64_t n, const float *U32, std::vector
           y[i + h] = a - b;
         }
     for (int j = 0; j < d; ++j) out[(size_t)r * d + j] = std::fabs(y[j] * c);
-  });
+  }
 }
 
 }  // namespace
@@ -173,6 +174,7 @@ int calibrate_host(int d, int hkv, int hq, float sm_scale, const float *q_cal, i
                    char *err, size_t err_len) {
   const int G = hq / hkv;
   const int T = n_threads();
+  std::vector<std::vector<double>> CQall(hkv), CSall(hkv);
   for (int kv = 0; kv < hkv; ++kv) {
     const float *K = k_cal + (size_t)kv * n_kv * d;
     const float *Vv = v_cal + (size_t)kv * n_kv * d;
@@ -219,32 +221,40 @@ int calibrate_host(int d, int hkv, int hq, float sm_scale, const float *q_cal, i
         for (int b = 0; b < d; ++b) CS[(size_t)a * d + b] += sa * sv[b];
       }
     });
-    std::vector<double> CQ((size_t)d * d, 0.0), CS((size_t)d * d, 0.0);
+    CQall[kv].assign((size_t)d * d, 0.0);
+    CSall[kv].assign((size_t)d * d, 0.0);
     for (int t = 0; t < T; ++t)
-      for (size_t i = 0; i < CQ.size(); ++i) {
-        CQ[i] += cq[t][i];
-        CS[i] += cs[t][i];
+      for (size_t i = 0; i < CQall[kv].size(); ++i) {
+        CQall[kv][i] += cq[t][i];
+        CSall[kv][i] += cs[t][i];
       }
-    for (size_t i = 0; i < CQ.size(); ++i) {
-      CQ[i] /= (double)rows;
-      CS[i] /= (double)rows;
+    for (size_t i = 0; i < CQall[kv].size(); ++i) {
+      CQall[kv][i] /= (double)rows;
+      CSall[kv][i] /= (double)rows;
     }
-    float *uk = U_K + (size_t)kv * d * d;
-    float *uv = U_V + (size_t)kv * d * d;
-    if (!sorted_basis(d, CQ, uk)) {
-      snprintf(err, err_len, "kv head %d: query covariance spectrum is degenerate", kv);
-      return OSCAR_EINVAL;
-    }
-    if (!sorted_basis(d, CS, uv)) {
-      snprintf(err, err_len, "kv head %d: score-weighted value covariance spectrum is degenerate", kv);
-      return OSCAR_EINVAL;
-    }
-    std::vector<double> vals;
-    rotated_abs(d, K, n_kv, uk, vals);
-    tau_K[kv] = (float)quantile_linear(vals, quantile_k);
-    rotated_abs(d, Vv, n_kv, uv, vals);
-    tau_V[kv] = (float)quantile_linear(vals, quantile_v);
   }
+  // Eigenbases and thresholds of all heads in parallel (2 * hkv independent jobs).
+  std::vector<int> bad(2 * hkv, 0);
+  std::vector<std::vector<double>> vals(2 * hkv);
+  parallel_for(2 * hkv, [&](int, int64_t job) {
+    const int kv = (int)(job >> 1);
+    const bool is_v = job & 1;
+    float *U = (is_v ? U_V : U_K) + (size_t)kv * d * d;
+    if (!sorted_basis(d, is_v ? CSall[kv] : CQall[kv], U)) {
+      bad[job] = 1;
+      return;
+    }
+    const float *X = (is_v ? v_cal : k_cal) + (size_t)kv * n_kv * d;
+    rotated_abs_serial(d, X, n_kv, U, vals[job]);
+    const double tq = quantile_linear(vals[job], is_v ? quantile_v : quantile_k);
+    (is_v ? tau_V : tau_K)[kv] = (float)tq;
+  });
+  for (int job = 0; job < 2 * hkv; ++job)
+    if (bad[job]) {
+      snprintf(err, err_len, "kv head %d: %s spectrum is degenerate", job >> 1,
+               (job & 1) ? "score-weighted value covariance" : "query covariance");
+      return OSCAR_EINVAL;
+    }
   return OSCAR_OK;
 }
 

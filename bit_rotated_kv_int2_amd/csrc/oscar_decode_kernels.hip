@@ -1,0 +1,886 @@
+// Decode attention over the mixed-precision pool on CDNA4: two launches.
+//
+// Sources: [A] youleyou.com article on OSCAR, token-pool paragraph under
+// "OSCAR 的设计思路" (INT2 segment: unpack, restore scale/zero, accumulate in
+// float; BF16 segment for sink/recent; online-softmax merge); [B]
+// MarkTechPost (zh) "Together AI 开源 OSCAR…", section
+// "服务系统：混合精度缓存布局" (rotated INT2 history with per-token asymmetric
+// 64-channel groups; the read path inverse-rotates inside attention), section
+// "OSCAR 有何不同做法" (R = U · H_Had · P_br) and section "结果" (decode is
+// KV-bandwidth bound at long context).
+//
+// pre  (grid B * Hkv, 256 threads): q~ = bitrev(FWHT(q U_K) / sqrt(d)) for
+//   the G query heads of a KV head, as a 15-bit fixed-point value split into
+//   the int8 operands of the logit MFMA, plus float copies for the VALU
+//   reference.
+// scan (grid B * Hkv * n_splits, NW waves per workgroup, one workgroup per CU
+//   at batch 1): the NW waves take interleaved history pages of one split;
+//   the 64-token BF16 chunks of the sink and the recent window are spread one
+//   per wave over the first workgroups, each writing its own partial; the
+//   last workgroup of a (sequence, KV head) merges the partials, applies
+//   R_V^T to the history part and writes the output.
+//
+// History page arithmetic (per wave, 64 tokens of one KV head):
+//   logits  v_mfma_i32_16x16x64_i8: rows (head, group, hi|lo) of the rotated
+//           query, columns 16 tokens, K = 128 channels; rows are masked to
+//           their group so the two scales stay apart;
+//   values  v_mfma_i32_16x16x64_i8: rows (head, group, hi|lo) of the weights
+//           w_t = 2^(l_t - m_ref) * scale_t quantised to 15 bits with a fixed
+//           per-head scale (scales are bounded by 2 tau_V / 3 after clipping),
+//           columns 16 channels, K = the 64 tokens; each page's exact int32
+//           result is added to float accumulators.  m_ref moves (and the
+//           running sums are rescaled) only when a logit exceeds it by more
+//           than a factor 2, so no per-page max or scale reduction is needed.
+//   Codes enter unscaled: the zero point is added as z * sum(q) (logits) and
+//   sum(p * z) (values).
+#include <stdlib.h>
+
+#include "oscar_wave.h"
+
+namespace oscar {
+namespace {
+
+constexpr float kWScale = 32639.0f;            // 15-bit weights, hi byte <= 127
+constexpr float kInvSqrtDf = 0.08838834764831845f;
+constexpr int kMaxSplits = 256;
+constexpr float kHeadroom = 1.0f;              // log2 headroom above m_ref
+
+struct DecArgs {
+  PoolView pv;
+  RotView rv;
+  const uint16_t *q;   // bf16 [B][Hq][d]
+  float *out;          // fp32 [B][Hq][d]
+  int *counters;       // [BH]
+  v4i *qop;            // [BH][MT * 2 * 64] int8 logit operands
+  float *qconst;       // [BH][GH][4]: delta, Q0, Q1 (per-group sums of q~)
+  float *qrot;         // [BH][GH][kD] float q~ (VALU reference)
+  float *part;         // [BH][n_splits + n_chunks][G][kPartStride]: history splits, then BF16 chunks
+  int n_splits, n_chunks, pages_per_split;
+};
+
+__device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// 16 two-bit codes -> int8 operand: register s, byte bb = bits [8 bb + 2 s, +2).
+__device__ __forceinline__ v4i unpack16(uint32_t w) {
+  v4i r;
+  r[0] = (int)(w & 0x03030303u);
+  r[1] = (int)((w >> 2) & 0x03030303u);
+  r[2] = (int)((w >> 4) & 0x03030303u);
+  r[3] = (int)((w >> 6) & 0x03030303u);
+  return r;
+}
+
+__device__ __forceinline__ float lo_h(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFF)); }
+__device__ __forceinline__ float hi_h(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+// Byte 1 / byte 0 of four words gathered into one word (word i -> byte i).
+__device__ __forceinline__ uint32_t gather_b1(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+  return __builtin_amdgcn_perm(w1, w0, 0x0C0C0501u) | __builtin_amdgcn_perm(w3, w2, 0x05010C0Cu);
+}
+__device__ __forceinline__ uint32_t gather_b0(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+  return __builtin_amdgcn_perm(w1, w0, 0x0C0C0400u) | __builtin_amdgcn_perm(w3, w2, 0x04000C0Cu);
+}
+
+// ===========================================================================
+// pre kernel
+// ===========================================================================
+template <int MT, int GH>
+struct QSmem {
+  float ys[MT * 4][kD];
+  v4i aq[MT * 2 * 64];
+};
+template <int MT, int GH>
+__device__ void run_query(const DecArgs &a, int b, int kv, QSmem<MT, GH> &sm) {
+  const PoolView &pv = a.pv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int G = pv.hq / pv.hkv;
+  const int bh = b * pv.hkv + kv;
+  const float *U = a.rv.U_K + (size_t)kv * kD * kD;
+  const uint16_t *qb = a.q + ((size_t)b * pv.hq + (size_t)kv * G) * kD;
+  // y[h][j] = sum_k q[h][k] U[k][j]: thread -> columns 4c..4c+3 and rows
+  // k = t % 8 + 8 i; all 16 loads in flight at once; 8-lane reduction.
+  {
+    const int c = tid >> 3, kk = tid & 7;
+    float4 u[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) u[i] = *(const float4 *)(U + (size_t)(kk + 8 * i) * kD + 4 * c);
+    for (int h = 0; h < G; ++h) {
+      const uint16_t *qr = qb + (size_t)h * kD;
+      float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float qk = bf16_to_f32(qr[kk + 8 * i]);
+        y0 = fmaf(qk, u[i].x, y0);
+        y1 = fmaf(qk, u[i].y, y1);
+        y2 = fmaf(qk, u[i].z, y2);
+        y3 = fmaf(qk, u[i].w, y3);
+      }
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        y0 += __shfl_xor(y0, o, 64);
+        y1 += __shfl_xor(y1, o, 64);
+        y2 += __shfl_xor(y2, o, 64);
+        y3 += __shfl_xor(y3, o, 64);
+      }
+      if (kk == 0) {
+        sm.ys[h][4 * c] = y0;
+        sm.ys[h][4 * c + 1] = y1;
+        sm.ys[h][4 * c + 2] = y2;
+        sm.ys[h][4 * c + 3] = y3;
+      }
+    }
+  }
+  for (int e = tid; e < MT * 2 * 64 * 4; e += blockDim.x) ((uint32_t *)sm.aq)[e] = 0;
+  __syncthreads();
+  for (int hs = 1; hs < kD; hs <<= 1) {
+    for (int e = tid; e < G * 64; e += blockDim.x) {
+      const int h = e >> 6, pr = e & 63;
+      const int i0 = (pr / hs) * (2 * hs) + (pr % hs);
+      const float x0 = sm.ys[h][i0], x1 = sm.ys[h][i0 + hs];
+      sm.ys[h][i0] = x0 + x1;
+      sm.ys[h][i0 + hs] = x0 - x1;
+    }
+    __syncthreads();
+  }
+  // one wave per head: rotated, permuted q~ -> float copy, fixed point, operands
+  for (int h = w; h < G; h += 4) {
+    const float v0 = sm.ys[h][bitrev7(lane)] * kInvSqrtDf;
+    const float v1 = sm.ys[h][bitrev7(lane + 64)] * kInvSqrtDf;
+    float *qr = a.qrot + ((size_t)bh * GH + h) * kD;
+    qr[lane] = v0;
+    qr[64 + lane] = v1;
+    float mx = fmaxf(fabsf(v0), fabsf(v1));
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    const float delta = mx > 0.f ? mx / 32639.0f : 1.0f;
+    const int q0 = max(-32639, min(32639, (int)rintf(v0 / delta)));
+    const int q1 = max(-32639, min(32639, (int)rintf(v1 / delta)));
+    int s0 = q0, s1 = q1;
+    for (int o = 32; o > 0; o >>= 1) {
+      s0 += __shfl_xor(s0, o, 64);
+      s1 += __shfl_xor(s1, o, 64);
+    }
+    if (lane == 0) {
+      float *qc = a.qconst + ((size_t)bh * GH + h) * 4;
+      qc[0] = delta;
+      qc[1] = delta * (float)s0;   // |sum| < 2^24: exact
+      qc[2] = delta * (float)s1;
+      qc[3] = 0.f;
+    }
+    const int mt = h >> 2;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int c = lane + 64 * half;
+      const int qi = half ? q1 : q0;
+      const int lo = (int)(int8_t)(qi & 0xFF);
+      const int hi = (qi - lo) >> 8;
+      // channel c -> kgroup c/32, kstep (c/16)%2, byte (c/4)%4 of register c%4
+      const int kg = c >> 5, ks = (c >> 4) & 1, bb = (c >> 2) & 3, s = c & 3;
+      const int g = c >> 6;
+      int8_t *base = (int8_t *)(sm.aq + (mt * 2 + ks) * 64);
+      const int r = 4 * (h & 3) + 2 * g;
+      base[(r + 16 * kg) * 16 + 4 * s + bb] = (int8_t)hi;
+      base[(r + 1 + 16 * kg) * 16 + 4 * s + bb] = (int8_t)lo;
+    }
+  }
+  __syncthreads();
+  v4i *dst = a.qop + (size_t)bh * MT * 2 * 64;
+  for (int e = tid; e < MT * 2 * 64; e += blockDim.x) dst[e] = sm.aq[e];
+}
+
+template <int MT, int GH>
+__global__ void __launch_bounds__(256) decode_pre_kernel(DecArgs a) {
+  __shared__ QSmem<MT, GH> sm;
+  const int bh = blockIdx.x;
+  run_query<MT, GH>(a, bh / a.pv.hkv, bh % a.pv.hkv, sm);
+}
+
+// ===========================================================================
+// scan kernel
+// ===========================================================================
+struct PageRegs {
+  uint2 kc[4];
+  uint4 km0, km1;
+  uint32_t vc[8];
+  uint4 vm0, vm1;
+};
+
+__device__ __forceinline__ void load_page(PageRegs &r, const uint8_t *P, int n, int q) {
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) r.kc[tt] = *(const uint2 *)(P + kKCodes + (16 * tt + n) * 32 + 8 * q);
+  r.km0 = *(const uint4 *)(P + kKMeta + 32 * n);
+  r.km1 = *(const uint4 *)(P + kKMeta + 32 * n + 16);
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) r.vc[nt] = *(const uint32_t *)(P + kVCodes + (16 * nt + n) * 16 + 4 * q);
+  r.vm0 = *(const uint4 *)(P + kVMeta + 32 * n);
+  r.vm1 = *(const uint4 *)(P + kVMeta + 32 * n + 16);
+}
+
+template <int MT>
+struct HistState {
+  float mref[MT];          // log2-domain reference max (row-uniform)
+  float lsum[MT], z0[MT], z1[MT];
+  float facc[MT][8];       // value sums in units of 1 / kw
+};
+
+template <int MT>
+__device__ __forceinline__ void rescale(HistState<MT> &st, int mt, float alpha) {
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) st.facc[mt][nt] *= alpha;
+  st.lsum[mt] *= alpha;
+  st.z0[mt] *= alpha;
+  st.z1[mt] *= alpha;
+}
+
+template <int MT, bool FULL>
+__device__ __forceinline__ void int2_page(const PageRegs &r, int valid, const v4i (&Aq)[MT][2],
+                                          const float (&qa)[MT], const float (&qb0)[MT],
+                                          const float (&qb1)[MT], float kw, HistState<MT> &st, v4i *wl) {
+  const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+  const uint32_t kmw[8] = {r.km0.x, r.km0.y, r.km0.z, r.km0.w, r.km1.x, r.km1.y, r.km1.z, r.km1.w};
+  const uint32_t vmw[8] = {r.vm0.x, r.vm0.y, r.vm0.z, r.vm0.w, r.vm1.x, r.vm1.y, r.vm1.z, r.vm1.w};
+  float lg[MT][4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const v4i B0 = unpack16(r.kc[tt].x);
+    const v4i B1 = unpack16(r.kc[tt].y);
+    const float s0 = lo_h(kmw[2 * tt]), z0 = hi_h(kmw[2 * tt]);
+    const float s1 = lo_h(kmw[2 * tt + 1]), z1 = hi_h(kmw[2 * tt + 1]);
+    const bool ok = FULL || (16 * tt + n) < valid;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      v4i C = mfma_i8(Aq[mt][0], B0, v4i{0, 0, 0, 0});
+      C = mfma_i8(Aq[mt][1], B1, C);
+      const float x0 = (float)(C[0] * 256 + C[1]);
+      const float x1 = (float)(C[2] * 256 + C[3]);
+      const float v = fmaf(fmaf(s0, x0, s1 * x1), qa[mt], fmaf(z0, qb0[mt], z1 * qb1[mt]));
+      lg[mt][tt] = ok ? v : -INFINITY;
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    // move the reference only when some logit exceeds it by the headroom
+    const float thr = st.mref[mt] + kHeadroom;
+    const bool over = lg[mt][0] > thr || lg[mt][1] > thr || lg[mt][2] > thr || lg[mt][3] > thr;
+    if (__builtin_amdgcn_ballot_w64(over)) {
+      float pm = fmaxf(fmaxf(lg[mt][0], lg[mt][1]), fmaxf(lg[mt][2], lg[mt][3]));
+      pm = row16_max(pm);
+      const float mnew = fmaxf(st.mref[mt], pm);
+      rescale<MT>(st, mt, exp2_fast(st.mref[mt] - mnew));
+      st.mref[mt] = mnew;
+    }
+    uint32_t u0[4], u1[4];
+    float es = 0.f, ez0 = 0.f, ez1 = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const bool ok = FULL || (16 * tt + n) < valid;
+      const float e = exp2_fast(lg[mt][tt] - st.mref[mt]);   // 0 for masked tokens
+      const float vs0 = lo_h(vmw[2 * tt]), vz0 = hi_h(vmw[2 * tt]);
+      const float vs1 = lo_h(vmw[2 * tt + 1]), vz1 = hi_h(vmw[2 * tt + 1]);
+      const float ek = ok ? e * kw : 0.f;
+      es += e;
+      ez0 = ok ? fmaf(e, vz0, ez0) : ez0;
+      ez1 = ok ? fmaf(e, vz1, ez1) : ez1;
+      // w + 128 = 256 hi + (lo + 128); w <= 32639 by the scale bound
+      u0[tt] = (uint32_t)fminf(fmaf(ek, vs0, 128.5f), 32767.0f);
+      u1[tt] = (uint32_t)fminf(fmaf(ek, vs1, 128.5f), 32767.0f);
+    }
+    st.lsum[mt] += es;
+    st.z0[mt] += ez0;
+    st.z1[mt] += ez1;
+    uint32_t *wd = (uint32_t *)(wl + mt * 64);
+    const int lb = 16 * (n >> 2), sub = n & 3;
+    wd[(4 * q + 0 + lb) * 4 + sub] = gather_b1(u0[0], u0[1], u0[2], u0[3]);
+    wd[(4 * q + 1 + lb) * 4 + sub] = gather_b0(u0[0], u0[1], u0[2], u0[3]) ^ 0x80808080u;
+    wd[(4 * q + 2 + lb) * 4 + sub] = gather_b1(u1[0], u1[1], u1[2], u1[3]);
+    wd[(4 * q + 3 + lb) * 4 + sub] = gather_b0(u1[0], u1[1], u1[2], u1[3]) ^ 0x80808080u;
+  }
+  wave_lds_sync();
+  v4i Aw[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) Aw[mt] = wl[mt * 64 + lane];
+  wave_lds_sync();
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+    const v4i Bv = unpack16(r.vc[nt]);
+    const int g = nt >> 2;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const v4i C = mfma_i8(Aw[mt], Bv, v4i{0, 0, 0, 0});
+      st.facc[mt][nt] += (float)(g ? C[2] * 256 + C[3] : C[0] * 256 + C[1]);
+    }
+  }
+}
+
+// VALU reference of the history scan: float32 FMAs on unpacked codes.
+struct ValuWave {
+  float *m, *l;          // [GH], wave-uniform values
+  float (*acc)[64][2];   // [GH][lane][2]
+};
+
+template <bool FULL>
+__device__ __forceinline__ void int2_page_valu(const uint8_t *P, int valid, int G, const float *qrot,
+                                               const float (*qsum)[2], float sl2, ValuWave st,
+                                               float (*pw)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int t = lane;
+  const uint4 k0 = *(const uint4 *)(P + kKCodes + t * 32);
+  const uint4 k1 = *(const uint4 *)(P + kKCodes + t * 32 + 16);
+  const uint2 km = *(const uint2 *)(P + kKMeta + meta_entry(t) * 8);
+  const uint2 vm = *(const uint2 *)(P + kVMeta + meta_entry(t) * 8);
+  const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+  const bool ok = FULL || t < valid;
+  const float ks0 = lo_h(km.x), kz0 = hi_h(km.x), ks1 = lo_h(km.y), kz1 = hi_h(km.y);
+  const float vs0 = lo_h(vm.x), vz0 = hi_h(vm.x), vs1 = lo_h(vm.y), vz1 = hi_h(vm.y);
+  const int c0 = 2 * lane, g = lane >> 5;
+  const uint4 r0 = *(const uint4 *)(P + kVCodes + c0 * 16);
+  const uint4 r1 = *(const uint4 *)(P + kVCodes + (c0 + 1) * 16);
+  const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w}, w1[4] = {r1.x, r1.y, r1.z, r1.w};
+#pragma unroll 1
+  for (int h = 0; h < G; ++h) {
+    const float *qr = qrot + (size_t)h * kD;
+    float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float code = (float)((kw[w] >> (2 * j)) & 3u);
+        if (w < 4) d0 = fmaf(qr[16 * w + j], code, d0);
+        else d1 = fmaf(qr[16 * w + j], code, d1);
+      }
+    }
+    float lg = (ks0 * d0 + kz0 * qsum[h][0] + ks1 * d1 + kz1 * qsum[h][1]) * sl2;
+    lg = ok ? lg : -INFINITY;
+    float pm = lg;
+    for (int o = 32; o > 0; o >>= 1) pm = fmaxf(pm, __shfl_xor(pm, o, 64));
+    const float mh = st.m[h];
+    const float mn = fmaxf(mh, pm);
+    const float alpha = exp2_fast(mh - mn);
+    const float p = ok ? exp2_fast(lg - mn) : 0.f;
+    float ls = p;
+    for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o, 64);
+    wave_lds_sync();
+    if (lane == 0) {
+      st.l[h] = st.l[h] * alpha + ls;
+      st.m[h] = mn;
+    }
+    pw[t][0] = ok ? p * vs0 : 0.f;
+    pw[t][1] = ok ? p * vz0 : 0.f;
+    pw[t][2] = ok ? p * vs1 : 0.f;
+    pw[t][3] = ok ? p * vz1 : 0.f;
+    wave_lds_sync();
+    float a0 = st.acc[h][lane][0] * alpha, a1 = st.acc[h][lane][1] * alpha;
+    // token t = 16 bb + 4 j + s sits in word j, byte bb, bits 2 s of a V row
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const int tt = 16 * bb + 4 * j + s4, sh = 8 * bb + 2 * s4;
+          const float cd0 = (float)((w0[j] >> sh) & 3u);
+          const float cd1 = (float)((w1[j] >> sh) & 3u);
+          const float ps = pw[tt][2 * g], pz = pw[tt][2 * g + 1];
+          a0 = fmaf(ps, cd0, a0 + pz);
+          a1 = fmaf(ps, cd1, a1 + pz);
+        }
+      }
+    }
+    st.acc[h][lane][0] = a0;
+    st.acc[h][lane][1] = a1;
+    wave_lds_sync();
+  }
+}
+
+// Waves per scan workgroup: 16 (four per SIMD) for one M-tile of heads, 8
+// (two per SIMD) otherwise, so that one workgroup fills a CU; the VALU
+// reference keeps per-wave value sums in LDS and uses 4.
+template <int MT, bool MFMA>
+constexpr int scan_waves() { return MFMA ? (MT == 1 ? 16 : 8) : 4; }
+
+template <int MT, int GH, int NW, bool MFMA>
+struct ScanSmem {
+  union WaveScratch {
+    v4i wl[MT * 64];                       // PV A operand (MFMA)
+    float pw[kPageTokens][4];              // p * scale, p * zero (VALU)
+    float ps[GH][kPageTokens + 4];         // BF16 chunk probabilities
+  } wave[NW];
+  float qsum[GH][2];                       // VALU: per-group sums of q~
+  float m[NW][MT * 4], l[NW][MT * 4], z[NW][MT * 4][2];
+  float o[NW][MT * 4][kD];
+  float vacc[MFMA ? 1 : NW][GH][64][2];    // VALU: per-wave running sums
+};
+
+template <int GH>
+struct MergeSmem {
+  float hm[GH], hl[GH];
+  float ws[GH][kMaxSplits];
+  float zs[GH][kD];
+  float ot[GH][kD];
+};
+
+template <int MT, int GH, int NW, bool MFMA>
+union ScanUnion {
+  ScanSmem<MT, GH, NW, MFMA> s;
+  MergeSmem<GH> g;
+};
+
+// One BF16 chunk (64 tokens of the sink or the recent ring) by one wave;
+// writes its (m, l, o) partial (log2 units, original basis).
+template <int GH>
+__device__ void bf16_chunk_partial(const DecArgs &a, int b, int kv, int c, float (*ps)[kPageTokens + 4],
+                                   float *dst) {
+  const PoolView &pv = a.pv;
+  const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+  const int G = pv.hq / pv.hkv;
+  const int L = max(0, pv.seq_lens[b]);
+  const int n_sink_chunks = pv.sink / kPageTokens;
+  const int slot = pv.sink_slot[b];
+  const bool slot_ok = slot >= 0 && slot < pv.n_sink_slots;
+  const uint16_t *K, *V;
+  int valid;
+  if (c < n_sink_chunks) {
+    if (!slot_ok && L > 0 && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_SINKSLOT);
+    valid = slot_ok ? max(0, min(kPageTokens, min(L, pv.sink) - c * kPageTokens)) : 0;
+    const size_t row = (((size_t)max(slot, 0) * pv.hkv + kv) * pv.sink + (size_t)c * kPageTokens) * kD;
+    K = pv.sink_k + row;
+    V = pv.sink_v + row;
+  } else {
+    // recent ring: valid slots are [a0, a0 + nr) mod W, a prefix of every chunk
+    const int r0 = max(pv.sink, L - pv.recent);
+    const int nr = max(0, L - r0);
+    const int a0 = r0 % pv.recent;
+    const int lo = (c - n_sink_chunks) * kPageTokens, hi = lo + kPageTokens;
+    const int e1 = min(a0 + nr, pv.recent);
+    const int e2 = max(0, a0 + nr - pv.recent);
+    valid = max(0, min(hi, e1) - max(lo, a0)) + max(0, min(hi, e2) - lo);
+    const size_t row = (((size_t)b * pv.hkv + kv) * pv.recent + lo) * kD;
+    K = pv.recent_k + row;
+    V = pv.recent_v + row;
+  }
+  float m[4], l[4], mrow[GH], o[GH][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.f;
+  }
+#pragma unroll
+  for (int h = 0; h < GH; ++h) {
+    mrow[h] = -INFINITY;
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) o[h][cc] = 0.f;
+  }
+  if (valid > 0) {
+    v8bf Aq[4];
+    load_bf16_query(a.q + ((size_t)b * pv.hq + (size_t)kv * G) * kD, G, Aq);
+    bf16_chunk<GH>(K, V, valid, G, Aq, pv.sm_scale * kLog2e, m, l, mrow, o, ps);
+  }
+#pragma unroll
+  for (int h = 0; h < GH; ++h) {
+    if (h >= G) break;
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      float v = o[h][cc];
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      if (q == 0) st_coherent(dst + (size_t)h * kPartStride + 2 + 8 * n + cc, v);
+    }
+  }
+  if (n == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * q + i;
+      if (h < G) {
+        st_coherent(dst + (size_t)h * kPartStride, m[i]);
+        st_coherent(dst + (size_t)h * kPartStride + 1, l[i]);
+      }
+    }
+  }
+}
+
+// Combine the NW waves' history state into the split's partial.
+template <int MT, int GH, int NW, bool MFMA>
+__device__ void write_split_partial(ScanSmem<MT, GH, NW, MFMA> &sm, int G, float *dst, bool with_z) {
+  const int tid = threadIdx.x;
+  for (int idx = tid; idx < G * kD; idx += blockDim.x) {
+    const int h = idx / kD, c = idx % kD;
+    float M = -INFINITY;
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.m[w][h]);
+    float o = 0.f, l = 0.f;
+    if (M > -INFINITY) {
+      for (int w = 0; w < NW; ++w) {
+        if (sm.m[w][h] == -INFINITY) continue;
+        const float sc = exp2_fast(sm.m[w][h] - M);
+        const float ov = MFMA ? sm.o[w][h][c] : sm.vacc[MFMA ? 0 : w][h][c >> 1][c & 1];
+        o += sc * (with_z ? ov + sm.z[w][h][c >> 6] : ov);
+        l += sc * sm.l[w][h];
+      }
+    }
+    float *d = dst + (size_t)h * kPartStride;
+    if (c == 0) {
+      st_coherent(d, M);
+      st_coherent(d + 1, l);
+    }
+    st_coherent(d + 2 + c, o);
+  }
+}
+
+template <int MT, int GH, int NW>
+__device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float *dst,
+                              ScanSmem<MT, GH, NW, true> &sm) {
+  const PoolView &pv = a.pv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, q = lane >> 4;
+  const int G = pv.hq / pv.hkv;
+  const int bh = b * pv.hkv + kv;
+  const int L = pv.seq_lens[b];
+  const int n_hist = max(0, L - pv.sink - pv.recent);
+  const int n_pages = (n_hist + kPageTokens - 1) / kPageTokens;
+  const int pg0 = split * a.pages_per_split;
+  const int pg1 = min(min(n_pages, pg0 + a.pages_per_split), pv.max_pages);
+  if (n_pages > pv.max_pages && split == 0 && tid == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_LENGTH);
+
+  const int32_t *btab = pv.block_table + (size_t)b * pv.max_pages;
+  const uint8_t *pbase = pv.pages + (size_t)kv * kPageBytes;
+  const size_t pstride = (size_t)pv.hkv * kPageBytes;
+  int pg = pg0 + wave;
+  PageRegs cur;
+  bool bad = false;
+  bool cur_ok = false;
+  if (pg < pg1) {
+    const int ph = btab[pg];
+    cur_ok = ph >= 0 && ph < pv.n_pages;
+    if (cur_ok) load_page(cur, pbase + (size_t)ph * pstride, n, q);
+    else bad = true;
+  }
+  v4i Aq[MT][2];
+  float qa[MT], qb0[MT], qb1[MT];
+  const float sl2 = pv.sm_scale * kLog2e;
+  const v4i *qop = a.qop + (size_t)bh * MT * 2 * 64;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    Aq[mt][0] = qop[(mt * 2 + 0) * 64 + lane];
+    Aq[mt][1] = qop[(mt * 2 + 1) * 64 + lane];
+    const int h = 4 * mt + q;
+    const float *qc = a.qconst + ((size_t)bh * GH + min(h, GH - 1)) * 4;
+    const bool hv = h < G;
+    qa[mt] = hv ? qc[0] * sl2 : 0.f;
+    qb0[mt] = hv ? qc[1] * sl2 : 0.f;
+    qb1[mt] = hv ? qc[2] * sl2 : 0.f;
+  }
+  // fixed weight scale: scale_t <= 2 tau_V / 3 (clipped range / 3), e <= 2^headroom
+  const float sbound = a.rv.tau_V[kv] * (2.0f / 3.0f) * 1.001f;
+  const float kw = kWScale / (sbound * 2.0f);
+  const float inv_kw = 1.0f / kw;
+  HistState<MT> st;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    st.mref[mt] = -INFINITY;
+    st.lsum[mt] = st.z0[mt] = st.z1[mt] = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) st.facc[mt][nt] = 0.f;
+  }
+  v4i *wl = sm.wave[wave].wl;
+  while (pg < pg1) {
+    if (cur_ok) {
+      const int valid = min(kPageTokens, n_hist - pg * kPageTokens);
+      if (valid == kPageTokens) int2_page<MT, true>(cur, valid, Aq, qa, qb0, qb1, kw, st, wl);
+      else int2_page<MT, false>(cur, valid, Aq, qa, qb0, qb1, kw, st, wl);
+    }
+    pg += NW;
+    if (pg < pg1) {
+      const int ph = btab[pg];
+      cur_ok = ph >= 0 && ph < pv.n_pages;
+      if (cur_ok) load_page(cur, pbase + (size_t)ph * pstride, n, q);
+      else bad = true;
+    }
+  }
+  if (bad && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const float l16 = row16_sum(st.lsum[mt]);
+    const float z0 = row16_sum(st.z0[mt]);
+    const float z1 = row16_sum(st.z1[mt]);
+    const int hh = 4 * mt + q;
+    if (n == 0) {
+      sm.m[wave][hh] = st.mref[mt];
+      sm.l[wave][hh] = l16;
+      sm.z[wave][hh][0] = z0;
+      sm.z[wave][hh][1] = z1;
+    }
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) sm.o[wave][hh][16 * nt + n] = st.facc[mt][nt] * inv_kw;
+  }
+  __syncthreads();
+  write_split_partial<MT, GH, NW, true>(sm, G, dst, true);
+}
+
+template <int MT, int GH, int NW>
+__device__ void run_scan_valu(const DecArgs &a, int b, int kv, int split, float *dst,
+                              ScanSmem<MT, GH, NW, false> &sm) {
+  const PoolView &pv = a.pv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = pv.hq / pv.hkv;
+  const int bh = b * pv.hkv + kv;
+  const int L = pv.seq_lens[b];
+  const int n_hist = max(0, L - pv.sink - pv.recent);
+  const int n_pages = (n_hist + kPageTokens - 1) / kPageTokens;
+  const int pg0 = split * a.pages_per_split;
+  const int pg1 = min(min(n_pages, pg0 + a.pages_per_split), pv.max_pages);
+  if (n_pages > pv.max_pages && split == 0 && tid == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_LENGTH);
+  const float *qrot = a.qrot + (size_t)bh * GH * kD;
+  for (int h = wave; h < G; h += NW) {
+    float s0 = qrot[h * kD + lane], s1 = qrot[h * kD + 64 + lane];
+    for (int o = 32; o > 0; o >>= 1) {
+      s0 += __shfl_xor(s0, o, 64);
+      s1 += __shfl_xor(s1, o, 64);
+    }
+    if (lane == 0) {
+      sm.qsum[h][0] = s0;
+      sm.qsum[h][1] = s1;
+    }
+  }
+  for (int e = tid; e < NW * MT * 4; e += blockDim.x) {
+    sm.m[e / (MT * 4)][e % (MT * 4)] = -INFINITY;
+    sm.l[e / (MT * 4)][e % (MT * 4)] = 0.f;
+  }
+  for (int e = tid; e < NW * GH * 64 * 2; e += blockDim.x) (&sm.vacc[0][0][0][0])[e] = 0.f;
+  __syncthreads();
+  const ValuWave st{sm.m[wave], sm.l[wave], sm.vacc[wave]};
+  const float sl2 = pv.sm_scale * kLog2e;
+  const int32_t *btab = pv.block_table + (size_t)b * pv.max_pages;
+  bool bad = false;
+  for (int pg = pg0 + wave; pg < pg1; pg += NW) {
+    const int ph = btab[pg];
+    if (ph < 0 || ph >= pv.n_pages) {
+      bad = true;
+      continue;
+    }
+    const uint8_t *P = pv.pages + ((size_t)ph * pv.hkv + kv) * kPageBytes;
+    const int valid = min(kPageTokens, n_hist - pg * kPageTokens);
+    if (valid == kPageTokens) int2_page_valu<true>(P, valid, G, qrot, sm.qsum, sl2, st, sm.wave[wave].pw);
+    else int2_page_valu<false>(P, valid, G, qrot, sm.qsum, sl2, st, sm.wave[wave].pw);
+  }
+  if (bad && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
+  __syncthreads();
+  write_split_partial<MT, GH, NW, false>(sm, G, dst, false);
+}
+
+// Merge of one (sequence, KV head): history splits (rotated basis) -> R_V^T;
+// BF16 chunks; combine; normalise.  U_V rows are fetched first so that their
+// latency overlaps the partial loads.
+template <int GH>
+__device__ void merge_item(const DecArgs &a, int b, int kv, const float *parts, MergeSmem<GH> &sm) {
+  const PoolView &pv = a.pv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const int G = pv.hq / pv.hkv;
+  const int S = a.n_splits, NC = a.n_chunks;
+  const float *bparts = parts + (size_t)S * G * kPartStride;
+  // threads 0..255 own row k = t / 2 of U_V, channels 64 (t & 1) .. + 64
+  const int krow = (tid >> 1) & (kD - 1), half = tid & 1;
+  const float4 *urow = (const float4 *)(a.rv.U_V + (size_t)kv * kD * kD + (size_t)krow * kD + 64 * half);
+  float4 u[16];
+  if (tid < 2 * kD) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) u[i] = urow[i];
+  }
+  // 1) per head: history split weights w_s = 2^(m_s - M); BF16 chunk max
+  for (int h = wave; h < G; h += nwaves) {
+    float M = -INFINITY;
+    for (int sp = lane; sp < S; sp += 64) {
+      const float m = ld_coherent(parts + ((size_t)sp * G + h) * kPartStride);
+      sm.ws[h][sp] = m;
+      M = fmaxf(M, m);
+    }
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    float l = 0.f;
+    for (int sp = lane; sp < S; sp += 64) {
+      const float m = sm.ws[h][sp];
+      const float w = (M > -INFINITY && m > -INFINITY) ? exp2_fast(m - M) : 0.f;
+      sm.ws[h][sp] = w;
+      l = fmaf(w, ld_coherent(parts + ((size_t)sp * G + h) * kPartStride + 1), l);
+    }
+    for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
+    if (lane == 0) {
+      sm.hm[h] = M;
+      sm.hl[h] = l;
+    }
+  }
+  __syncthreads();
+  // 2) weighted history sums, scattered through the permutation: (o P)[j] = o[bitrev(j)]
+  for (int idx = tid; idx < G * kD; idx += blockDim.x) {
+    const int h = idx / kD, c = idx % kD;
+    const float *p = parts + (size_t)h * kPartStride + 2 + c;
+    const size_t st = (size_t)G * kPartStride;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int sp = 0;
+    for (; sp + 8 <= S; sp += 8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(sm.ws[h][sp + i], ld_coherent(p + (size_t)(sp + i) * st), acc[i]);
+    }
+    for (; sp < S; ++sp) acc[0] = fmaf(sm.ws[h][sp], ld_coherent(p + (size_t)sp * st), acc[0]);
+    sm.zs[h][bitrev7(c)] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  }
+  __syncthreads();
+  for (int hs = 1; hs < kD; hs <<= 1) {
+    for (int e = tid; e < G * 64; e += blockDim.x) {
+      const int h = e >> 6, pr = e & 63;
+      const int i0 = (pr / hs) * (2 * hs) + (pr % hs);
+      const float x0 = sm.zs[h][i0], x1 = sm.zs[h][i0 + hs];
+      sm.zs[h][i0] = x0 + x1;
+      sm.zs[h][i0 + hs] = x0 - x1;
+    }
+    __syncthreads();
+  }
+  // 3) o_hist[h][k] = sum_j z[h][j] U_V[k][j] / sqrt(d)
+  if (tid < 2 * kD) {
+    for (int h = 0; h < G; ++h) {
+      const float4 *zr = (const float4 *)(&sm.zs[h][64 * half]);
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float4 z = zr[i];
+        s = fmaf(z.x, u[i].x, fmaf(z.y, u[i].y, fmaf(z.z, u[i].z, fmaf(z.w, u[i].w, s))));
+      }
+      s += __shfl_xor(s, 1, 64);
+      if (half == 0) sm.ot[h][krow] = s * kInvSqrtDf;
+    }
+  }
+  __syncthreads();
+  // 4) BF16 chunks and the history part, normalised
+  for (int idx = tid; idx < G * kD; idx += blockDim.x) {
+    const int h = idx / kD, c = idx % kD;
+    float Mb = -INFINITY;
+    for (int cc = 0; cc < NC; ++cc) Mb = fmaxf(Mb, ld_coherent(bparts + ((size_t)cc * G + h) * kPartStride));
+    const float Mh = sm.hm[h];
+    const float Mt = fmaxf(Mh, Mb);
+    float res = 0.f;
+    if (Mt > -INFINITY) {
+      const float wh = Mh > -INFINITY ? exp2_fast(Mh - Mt) : 0.f;
+      float num = wh * sm.ot[h][c], den = wh * sm.hl[h];
+      for (int cc = 0; cc < NC; ++cc) {
+        const float *pb = bparts + ((size_t)cc * G + h) * kPartStride;
+        const float mb = ld_coherent(pb);
+        if (mb == -INFINITY) continue;
+        const float wb = exp2_fast(mb - Mt);
+        num = fmaf(wb, ld_coherent(pb + 2 + c), num);
+        den = fmaf(wb, ld_coherent(pb + 1), den);
+      }
+      res = num / den;
+    }
+    a.out[((size_t)b * pv.hq + (size_t)kv * G + h) * kD + c] = res;
+  }
+}
+
+// Register budget: four waves per SIMD for one M-tile of heads (G <= 4), two
+// otherwise; the VALU reference takes what it needs.
+template <int MT, int GH, bool MFMA>
+__global__ void __launch_bounds__((64 * scan_waves<MT, MFMA>()))
+__attribute__((amdgpu_waves_per_eu(MFMA ? (MT == 1 ? 4 : 2) : 1)))
+decode_scan_kernel(DecArgs a) {
+  constexpr int NW = scan_waves<MT, MFMA>();
+  const PoolView &pv = a.pv;
+  const int BH = pv.batch * pv.hkv;
+  const int bh = blockIdx.x % BH, split = blockIdx.x / BH;
+  const int b = bh / pv.hkv, kv = bh % pv.hkv;
+  const int G = pv.hq / pv.hkv;
+  const int wave = threadIdx.x >> 6;
+  const int S = a.n_splits;
+  float *parts = a.part + (size_t)bh * (S + a.n_chunks) * G * kPartStride;
+  __shared__ ScanUnion<MT, GH, NW, MFMA> sm;
+  // BF16 chunk c runs on workgroup c % S, wave (c / S) % NW, before its pages
+  for (int c = split; c < a.n_chunks; c += S) {
+    if (((c / S) % NW) == wave)
+      bf16_chunk_partial<GH>(a, b, kv, c, sm.s.wave[wave].ps, parts + (size_t)(S + c) * G * kPartStride);
+  }
+  float *dst = parts + (size_t)split * G * kPartStride;
+  if constexpr (MFMA) run_scan_mfma<MT, GH, NW>(a, b, kv, split, dst, sm.s);
+  else run_scan_valu<MT, GH, NW>(a, b, kv, split, dst, sm.s);
+  __shared__ int last_flag;
+  if (!arrive_last(&a.counters[bh], S, &last_flag)) return;
+  merge_item<GH>(a, b, kv, parts, sm.g);
+}
+
+}  // namespace
+
+namespace {
+int target_blocks() {
+  // scan workgroups the grid aims for (one per CU); OSCAR_DECODE_BLOCKS
+  // overrides it (tuning only)
+  static int v = [] {
+    const char *e = getenv("OSCAR_DECODE_BLOCKS");
+    const int x = e ? atoi(e) : 0;
+    return x > 0 ? x : 256;
+  }();
+  return v;
+}
+int mt_of(int G) { return (G + 3) / 4; }
+int gh_of(int G) { return 4 * mt_of(G); }
+int nw_of(int G, int variant) { return variant != 0 ? 4 : (mt_of(G) == 1 ? 16 : 8); }
+}  // namespace
+
+DecodePlan make_decode_plan(int batch, int hkv, int hq, int max_pages, int sink, int recent, int variant) {
+  DecodePlan p{};
+  const int G = hq / hkv;
+  const int MT = mt_of(G), GH = gh_of(G), NW = nw_of(G, variant);
+  const int bh = batch * hkv;
+  int S = (target_blocks() + bh - 1) / bh;
+  const int max_by_pages = max_pages > 0 ? (max_pages + NW - 1) / NW : 1;   // >= 1 page per wave
+  S = S < 1 ? 1 : S;
+  S = S > max_by_pages ? max_by_pages : S;
+  S = S > kMaxSplits ? kMaxSplits : S;
+  p.n_splits = S;
+  p.n_chunks = sink / kPageTokens + recent / kPageTokens;
+  p.pages_per_split = max_pages > 0 ? (max_pages + S - 1) / S : 1;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  size_t off = 0;
+  p.off_counters = off;
+  off = al(off + (size_t)bh * sizeof(int));
+  p.off_qop = off;
+  off = al(off + (size_t)bh * MT * 2 * 64 * 16);
+  p.off_qconst = off;
+  off = al(off + (size_t)bh * GH * 4 * sizeof(float));
+  p.off_qrot = off;
+  off = al(off + (size_t)bh * GH * kD * sizeof(float));
+  p.off_part = off;
+  off = al(off + (size_t)bh * (S + p.n_chunks) * G * kPartStride * sizeof(float));
+  p.total = off;
+  return p;
+}
+
+hipError_t launch_decode(const PoolView &pv, const RotView &rv, const uint16_t *q, float *out,
+                         uint8_t *ws, const DecodePlan &plan, int variant, hipStream_t s,
+                         hipEvent_t ev_start, hipEvent_t ev_stop) {
+  const int G = pv.hq / pv.hkv;
+  const int BH = pv.batch * pv.hkv;
+  DecArgs a{pv, rv, q, out, (int *)(ws + plan.off_counters), (v4i *)(ws + plan.off_qop),
+            (float *)(ws + plan.off_qconst), (float *)(ws + plan.off_qrot), (float *)(ws + plan.off_part),
+            plan.n_splits, plan.n_chunks, plan.pages_per_split};
+  const bool mfma = variant == 0;
+  const dim3 sgrid(BH * plan.n_splits);
+  hipError_t e;
+#define OSCAR_LAUNCH(MT, GH)                                                                         \
+  do {                                                                                               \
+    hipLaunchKernelGGL((decode_pre_kernel<MT, GH>), dim3(BH), dim3(256), 0, s, a);                   \
+    if ((e = hipGetLastError()) != hipSuccess) return e;                                             \
+    if (ev_start && (e = hipEventRecord(ev_start, s)) != hipSuccess) return e;                       \
+    if (mfma)                                                                                        \
+      hipLaunchKernelGGL((decode_scan_kernel<MT, GH, true>), sgrid, dim3(64 * scan_waves<MT, true>()), \
+                         0, s, a);                                                                   \
+    else                                                                                             \
+      hipLaunchKernelGGL((decode_scan_kernel<MT, GH, false>), sgrid,                                 \
+                         dim3(64 * scan_waves<MT, false>()), 0, s, a);                               \
+  } while (0)
+  if (G <= 4) OSCAR_LAUNCH(1, 4);
+  else if (G <= 8) OSCAR_LAUNCH(2, 8);
+  else if (G <= 12) OSCAR_LAUNCH(3, 12);
+  else OSCAR_LAUNCH(4, 16);
+#undef OSCAR_LAUNCH
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev_stop && (e = hipEventRecord(ev_stop, s)) != hipSuccess) return e;
+  return hipSuccess;
+}
+
+}  // namespace oscar

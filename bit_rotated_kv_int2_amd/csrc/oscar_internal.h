@@ -46,6 +46,33 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Cross-workgroup hand-off without cache flushes.  Partials and counters that
+// another workgroup (possibly on another XCD, with its own L2) reads are moved
+// with agent-scope relaxed atomics, which are coherent at the memory side;
+// a writer waits for its stores to complete (vmcnt 0) before the counter
+// increment, so no L2 write-back or invalidate is needed.
+__device__ __forceinline__ void st_coherent(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stores_complete() { __builtin_amdgcn_s_waitcnt(0); }
+// Returns true in every thread of the workgroup that arrives last of `total`
+// at counter *c, and resets the counter for the next call.
+__device__ __forceinline__ bool arrive_last(int *c, int total, int *flag_lds) {
+  stores_complete();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = prev == total - 1;
+    if (last) __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag_lds = last;
+  }
+  __syncthreads();
+  return *flag_lds != 0;
+}
+
 // Everything a kernel needs from oscar_params / oscar_kv_pool / oscar_rotation,
 // flattened into one by-value struct.
 struct PoolView {
@@ -65,13 +92,13 @@ struct RotView {
 // Decode workspace carve-up (offsets in bytes from the workspace base).
 struct DecodePlan {
   int n_splits;          // history splits per (sequence, kv head)
+  int n_chunks;          // 64-token BF16 chunks (sink + recent window)
   int pages_per_split;
-  int n_bf16_chunks;     // 64-token chunks covering sink + recent
-  size_t off_qrot;       // float [B][Hq][128] rotated queries
-  size_t off_qint;       // int8 MFMA operands [B][Hkv][MT][2][64][16]
-  size_t off_qconst;     // float [B][Hq][4]  {delta, Q0, Q1, unused}
-  size_t off_part;       // float [B][Hkv][n_splits][G][kPartStride]
-  size_t off_bpart;      // float [B][Hkv][n_bf16_chunks][G][kPartStride]
+  size_t off_counters;   // int [B*Hkv] completion counters, zero between calls
+  size_t off_qop;        // int8 logit operands [B*Hkv][MT][2][64][16]
+  size_t off_qconst;     // float [B*Hkv][GH][4]
+  size_t off_qrot;       // float [B*Hkv][GH][128]
+  size_t off_part;       // float [B*Hkv][n_splits + n_chunks][G][kPartStride]
   size_t total;
 };
 
@@ -82,7 +109,8 @@ DecodePlan make_decode_plan(int batch, int hkv, int hq, int max_pages, int sink,
 hipError_t launch_append(const PoolView &pv, const RotView &rv, const uint16_t *k_new,
                          const uint16_t *v_new, int n_new, hipStream_t s);
 hipError_t launch_decode(const PoolView &pv, const RotView &rv, const uint16_t *q, float *out,
-                         uint8_t *ws, const DecodePlan &plan, int variant, hipStream_t s);
+                         uint8_t *ws, const DecodePlan &plan, int variant, hipStream_t s,
+                         hipEvent_t ev_start, hipEvent_t ev_stop);
 
 struct Bf16View {
   const uint16_t *k_pages, *v_pages;
@@ -93,7 +121,7 @@ struct Bf16View {
 };
 struct Bf16Plan {
   int n_splits, pages_per_split;
-  size_t off_part, total;
+  size_t off_counters, off_part, total;
 };
 Bf16Plan make_bf16_plan(int batch, int hkv, int hq, int max_pages);
 hipError_t launch_bf16_decode(const Bf16View &v, const uint16_t *q, float *out, uint8_t *ws,

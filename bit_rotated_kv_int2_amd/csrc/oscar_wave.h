@@ -1,0 +1,205 @@
+// Wave-level building blocks shared by the decode kernels: DPP row
+// reductions, byte gathers, and the BF16 64-token chunk attention used both
+// by the BF16 sink/recent segment and by the all-BF16 baseline.
+#pragma once
+
+#include "oscar_internal.h"
+
+namespace oscar {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// DPP controls (GFX9 encoding): quad_perm [1,0,3,2], [2,3,0,1], row_ror 4, 8.
+constexpr int kDppQuadSwap1 = 0xB1;
+constexpr int kDppQuadSwap2 = 0x4E;
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Reductions over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15); every
+// lane of the row receives the result.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dppf<kDppQuadSwap1>(v));
+  v = fmaxf(v, dppf<kDppQuadSwap2>(v));
+  v = fmaxf(v, dppf<kDppRowRor4>(v));
+  v = fmaxf(v, dppf<kDppRowRor8>(v));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dppf<kDppQuadSwap1>(v);
+  v += dppf<kDppQuadSwap2>(v);
+  v += dppf<kDppRowRor4>(v);
+  v += dppf<kDppRowRor8>(v);
+  return v;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ v8bf as_v8bf(uint4 u) { return __builtin_bit_cast(v8bf, u); }
+
+// ---------------------------------------------------------------------------
+// BF16 chunk attention for one wave.
+//   K, V: 64 bf16 rows of 128 channels (row t = token t), `valid` leading rows
+//   are real tokens.  Aq: the query operand of v_mfma_f32_16x16x32_bf16 with
+//   rows = query heads (lane n = head, kgroup q: channels 32 q + 8 ks ..).
+//   Running state (log2 units): m[i], l[i] for the head 4 q + i of the C
+//   layout, and o[h][8] for channels 8 n .. 8 n + 7 and the token phase q
+//   (summed over q at the end).  ps: this wave's [16][68] LDS scratch.
+// ---------------------------------------------------------------------------
+template <int GH>
+__device__ __forceinline__ void bf16_chunk(const uint16_t *K, const uint16_t *V, int valid, int G,
+                                           const v8bf (&Aq)[4], float sl2, float (&m)[4],
+                                           float (&l)[4], float (&mrow)[GH], float (&o)[GH][8],
+                                           float (*ps)[kPageTokens + 4]) {
+  const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+  float lg[4][4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const uint16_t *kr = K + (size_t)(16 * tt + n) * kD + 32 * q;
+    uint4 kk[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kk[ks] = *(const uint4 *)(kr + 8 * ks);
+    v4f C = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) C = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aq[ks], as_v8bf(kk[ks]), C, 0, 0, 0);
+    const bool ok = (16 * tt + n) < valid;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lg[tt][i] = ok ? C[i] * sl2 : -INFINITY;
+  }
+  float pm[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v = fmaxf(fmaxf(lg[0][i], lg[1][i]), fmaxf(lg[2][i], lg[3][i]));
+    v = row16_max(v);
+    const float mn = fmaxf(m[i], v);
+    const float al = exp2_fast(m[i] - mn);
+    float s = 0.f;
+    float e[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      e[tt] = exp2_fast(lg[tt][i] - mn);
+      s += e[tt];
+    }
+    s = row16_sum(s);
+    l[i] = l[i] * al + s;
+    m[i] = mn;
+    pm[i] = mn;
+    const int h = 4 * q + i;
+    if (h < G) {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) ps[h][16 * tt + n] = e[tt];
+    }
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int h = 0; h < GH; ++h) {
+    if (h >= G) break;
+    const int i = h & 3;
+    const float v = (i == 0) ? pm[0] : (i == 1) ? pm[1] : (i == 2) ? pm[2] : pm[3];
+    const float mh = __shfl(v, 16 * (h >> 2), 64);
+    const float al = exp2_fast(mrow[h] - mh);
+    mrow[h] = mh;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[h][c] *= al;
+  }
+  for (int t = q; t < valid; t += 4) {
+    const uint4 u = *(const uint4 *)(V + (size_t)t * kD + 8 * n);
+    float vf[8];
+    vf[0] = __uint_as_float(u.x << 16);
+    vf[1] = __uint_as_float(u.x & 0xFFFF0000u);
+    vf[2] = __uint_as_float(u.y << 16);
+    vf[3] = __uint_as_float(u.y & 0xFFFF0000u);
+    vf[4] = __uint_as_float(u.z << 16);
+    vf[5] = __uint_as_float(u.z & 0xFFFF0000u);
+    vf[6] = __uint_as_float(u.w << 16);
+    vf[7] = __uint_as_float(u.w & 0xFFFF0000u);
+#pragma unroll
+    for (int h = 0; h < GH; ++h) {
+      if (h >= G) break;
+      const float p = ps[h][t];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) o[h][c] = fmaf(p, vf[c], o[h][c]);
+    }
+  }
+  wave_lds_sync();
+}
+
+// Load the bf16 query rows of the G heads of one KV head as the A operand.
+__device__ __forceinline__ void load_bf16_query(const uint16_t *qbase, int G, v8bf (&Aq)[4]) {
+  const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    uint4 u = {0, 0, 0, 0};
+    if (n < G) u = *(const uint4 *)(qbase + (size_t)n * kD + 32 * q + 8 * ks);
+    Aq[ks] = as_v8bf(u);
+  }
+}
+
+// Sum the PV partials over the 4 token phases and combine the 4 waves of a
+// block into one (m, l, o) partial per head (m in log2 units).
+template <int GH>
+__device__ __forceinline__ void bf16_block_combine(int G, const float (&m)[4], const float (&l)[4],
+                                                   float (&o)[GH][8], float (*sm_m)[GH], float (*sm_l)[GH],
+                                                   float (*sm_o)[GH][kD], float *dst_base) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int h = 0; h < GH; ++h) {
+    if (h >= G) break;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float v = o[h][c];
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      o[h][c] = v;
+    }
+  }
+  if (q == 0) {
+#pragma unroll
+    for (int h = 0; h < GH; ++h) {
+      if (h >= G) break;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) sm_o[wave][h][8 * n + c] = o[h][c];
+    }
+  }
+  if (n == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * q + i;
+      if (h < G) {
+        sm_m[wave][h] = m[i];
+        sm_l[wave][h] = l[i];
+      }
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * kD; idx += blockDim.x) {
+    const int h = idx / kD, c = idx % kD;
+    float M = -INFINITY;
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][h]);
+    float ov = 0.f, lv = 0.f;
+    if (M > -INFINITY) {
+      for (int w = 0; w < 4; ++w) {
+        if (sm_m[w][h] == -INFINITY) continue;
+        const float sc = exp2_fast(sm_m[w][h] - M);
+        ov += sc * sm_o[w][h][c];
+        lv += sc * sm_l[w][h];
+      }
+    }
+    float *dst = dst_base + (size_t)h * kPartStride;
+    if (c == 0) {
+      st_coherent(dst, M);
+      st_coherent(dst + 1, lv);
+    }
+    st_coherent(dst + 2 + c, ov);
+  }
+}
+
+}  // namespace oscar

@@ -29,7 +29,7 @@ EXPORTED = [
     "oscar_calibrate_rotation", "oscar_quantize_append", "oscar_decode_attention",
     "oscar_decode_workspace_size", "oscar_bf16_decode_attention",
     "oscar_bf16_decode_workspace_size", "oscar_set_decode_variant", "oscar_last_error",
-    "oscar_version",
+    "oscar_version", "oscar_set_history_timing_events",
 ]
 
 
@@ -104,6 +104,8 @@ def lib():
     L.oscar_last_error.restype = ctypes.c_char_p
     L.oscar_version.argtypes = []
     L.oscar_version.restype = i32
+    L.oscar_set_history_timing_events.argtypes = [vp, vp]
+    L.oscar_set_history_timing_events.restype = i32
     _lib = L
     return L
 
@@ -137,6 +139,13 @@ def set_decode_variant(variant: int) -> None:
 
 def version() -> int:
     return int(lib().oscar_version())
+
+
+def set_history_timing_events(start_event=None, stop_event=None) -> None:
+    """torch.cuda.Event pair (recorded once so the handle exists) or None."""
+    a = None if start_event is None else int(start_event.cuda_event)
+    b = None if stop_event is None else int(stop_event.cuda_event)
+    _check(lib().oscar_set_history_timing_events(a, b))
 
 
 # ---------------------------------------------------------------------------
@@ -219,13 +228,29 @@ class KVPool:
                        _ptr(self.pages), _ptr(self.block_table), _ptr(self.sink_slot), _ptr(self.seq_lens),
                        _ptr(self.error_flags), self.batch, self.max_pages, self.n_pages, self.n_sink_slots)
 
+    def c_seq(self, b: int) -> KVPoolC:
+        """The same pool seen as a batch of one: sequence b alone."""
+        c = self.c()
+        c.recent_k = _ptr(self.recent_k[b])
+        c.recent_v = _ptr(self.recent_v[b])
+        c.block_table = _ptr(self.block_table[b])
+        c.sink_slot = _ptr(self.sink_slot[b:b + 1])
+        c.seq_lens = _ptr(self.seq_lens[b:b + 1])
+        c.batch = 1
+        return c
 
-def quantize_append(params: Params, rot: RotationTensors, pool: KVPool, k_new, v_new, stream=None):
-    """k_new, v_new: bf16 bit patterns (int16/uint16 tensor) [B, n_new, Hkv, d] on the device."""
+
+def quantize_append(params: Params, rot: RotationTensors, pool: KVPool, k_new, v_new, stream=None,
+                    seq: Optional[int] = None):
+    """k_new, v_new: bf16 bit patterns (int16/uint16 tensor) [B, n_new, Hkv, d] on the device.
+
+    With ``seq`` set, appends to that sequence only and k_new/v_new have batch 1.
+    """
     assert k_new.is_contiguous() and v_new.is_contiguous() and k_new.shape == v_new.shape
-    assert k_new.dim() == 4 and k_new.shape[0] == pool.batch and k_new.element_size() == 2
+    assert k_new.dim() == 4 and k_new.element_size() == 2
+    assert k_new.shape[0] == (1 if seq is not None else pool.batch)
     n_new = int(k_new.shape[1])
-    r, pc = rot.c(), pool.c()
+    r, pc = rot.c(), (pool.c() if seq is None else pool.c_seq(seq))
     _check(lib().oscar_quantize_append(ctypes.byref(params), ctypes.byref(r), ctypes.byref(pc),
                                        _ptr(k_new), _ptr(v_new), n_new, _stream_ptr(stream)))
 
@@ -235,8 +260,9 @@ def decode_workspace_size(params: Params, batch: int, max_pages: int) -> int:
 
 
 def alloc_workspace(nbytes: int, device="cuda"):
+    """Zero-filled device workspace (the decode's completion counters start at zero)."""
     import torch
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
 def decode_attention(params: Params, rot: RotationTensors, pool: KVPool, q, out, workspace, stream=None):

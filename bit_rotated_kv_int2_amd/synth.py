@@ -59,8 +59,8 @@ class Workload:
     def group_size(self) -> int:
         return self.n_q // self.n_kv
 
-    def max_pages(self) -> int:
-        hist = max(0, self.max_len - self.sink - self.recent)
+    def max_pages(self, extra_tokens: int = 0) -> int:
+        hist = max(0, self.max_len + extra_tokens - self.sink - self.recent)
         return (hist + self.page_tokens - 1) // self.page_tokens
 
 
@@ -157,15 +157,16 @@ def sequence_lengths(wl: Workload) -> np.ndarray:
     return g.integers(wl.min_len, wl.max_len, size=wl.batch, endpoint=True).astype(np.int32)
 
 
-def block_table(wl: Workload, lengths: np.ndarray):
+def block_table(wl: Workload, lengths: np.ndarray, extra_tokens: int = 0):
     """int32 [batch, max_pages] page ids (-1 = unused) and the page count.
 
-    With ``shared_prefix`` every sequence maps its first prefix pages to the
-    same physical pages.  With ``scattered_pages`` physical ids are a seeded
+    Pages are reserved for ``extra_tokens`` more tokens per sequence.  With
+    ``shared_prefix`` every sequence maps its first prefix pages to the same
+    physical pages.  With ``scattered_pages`` physical ids are a seeded
     permutation of the pool.
     """
-    mp = wl.max_pages()
-    need = [max(0, int(L) - wl.sink - wl.recent) for L in lengths]
+    mp = wl.max_pages(extra_tokens)
+    need = [max(0, int(L) + extra_tokens - wl.sink - wl.recent) for L in lengths]
     need = [(n + wl.page_tokens - 1) // wl.page_tokens for n in need]
     shared = 0
     if wl.shared_prefix:

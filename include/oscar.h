@@ -207,6 +207,15 @@ int32_t oscar_bf16_decode_attention(const oscar_params *p, const oscar_bf16_cach
 
 size_t oscar_bf16_decode_workspace_size(const oscar_params *p, int32_t batch, int32_t max_pages);
 
+/*
+ * Optional timing hook for benchmarks.  When both are non-NULL, every later
+ * oscar_decode_attention call records `start_event` immediately before and
+ * `stop_event` immediately after its INT2 history kernel, on the call's
+ * stream (hipEvent_t handles created by the caller with timing enabled).
+ * Pass NULL, NULL to disable.  Process-wide; not meant for concurrent use.
+ */
+int32_t oscar_set_history_timing_events(void *start_event, void *stop_event);
+
 /* Decode kernel selection: 0 = MFMA int8 path (default), 1 = VALU path. */
 int32_t oscar_set_decode_variant(int32_t variant);
 

@@ -293,12 +293,17 @@ def rotate_for_write(x: np.ndarray, U32: np.ndarray) -> np.ndarray:
     x = np.asarray(x, dtype=np.float64)
     U = np.asarray(U32, dtype=np.float32).astype(np.float64)
     n, d = x.shape
-    y = np.zeros((n, d))
-    for k in range(d):
-        y = y + x[:, k:k + 1] * U[k:k + 1, :]
-    y = fwht_butterfly(y) * inv_sqrt_dim(d)
-    y = y[:, bitrev_indices(d)]
-    return y.astype(np.float32)
+    out = np.empty((n, d), dtype=np.float32)
+    idx = bitrev_indices(d)
+    c = inv_sqrt_dim(d)
+    for r0 in range(0, n, 2048):               # row blocks only bound memory use
+        xb = x[r0:r0 + 2048]
+        y = np.zeros((xb.shape[0], d))
+        for k in range(d):
+            y += xb[:, k:k + 1] * U[k:k + 1, :]
+        y = fwht_butterfly(y) * c
+        out[r0:r0 + 2048] = y[:, idx].astype(np.float32)
+    return out
 
 
 @dataclass

@@ -241,3 +241,24 @@ def test_bf16_baseline_decode(tiny):
     torch.cuda.synchronize()
     ref = R.attention_dense(_f64(q[0]), _f64(kb[:L, 0]), _f64(vb[:L, 0]), 1 / np.sqrt(D))
     assert decode_check(out.cpu().numpy()[0], ref) <= TOL
+
+
+def test_decode_repeat_same_workspace(tiny):
+    """Consecutive decodes sharing one workspace give identical results (the
+    completion counters return to zero after every call)."""
+    torch = _torch()
+    wl, cals, rot, params, kb, vb, q = tiny
+    pool = _fresh_pool(params, 59)
+    append_sequence(params, rot, pool, 0, kb, vb)
+    ws = O.alloc_workspace(O.decode_workspace_size(params, 1, pool.max_pages))
+    qt = torch.from_numpy(q.view(np.int16)).cuda()
+    outs = []
+    for _ in range(3):
+        out = torch.zeros((1, wl.n_q, D), dtype=torch.float32, device="cuda")
+        O.decode_attention(params, rot, pool, qt, out, ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    ref, _ = _oracle_decode(wl, cals, kb, vb, q[0])
+    assert decode_check(outs[0].cpu().numpy()[0], ref) <= TOL
