@@ -73,6 +73,7 @@ oscar::PoolView make_pv(const oscar_params *p, const oscar_kv_pool *pool) {
   v.sink_slot = pool->sink_slot;
   v.seq_lens = pool->seq_lens;
   v.err = pool->error_flags;
+  v.app_cnt = pool->append_counters;
   v.batch = pool->batch;
   v.max_pages = pool->max_pages;
   v.n_pages = pool->n_pages;

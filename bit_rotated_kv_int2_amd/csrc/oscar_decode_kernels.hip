@@ -393,14 +393,19 @@ __device__ __forceinline__ void int2_page_valu(const uint8_t *P, int valid, int 
   }
 }
 
-// Waves per scan workgroup: 16 (four per SIMD) for one M-tile of heads, 8
+// Waves per scan workgroup: 12 (three per SIMD) for one M-tile of heads, 8
 // (two per SIMD) otherwise, so that one workgroup fills a CU; the VALU
 // reference keeps per-wave value sums in LDS and uses 4.
 template <int MT, bool MFMA>
-constexpr int scan_waves() { return MFMA ? (MT == 1 ? 16 : 8) : 4; }
+constexpr int scan_waves() { return MFMA ? (MT == 1 ? 12 : 8) : 4; }
+
+// History pages each MFMA wave keeps in flight as LDS DMA copies.
+template <int MT>
+constexpr int scan_prefetch() { return 2; }
 
 template <int MT, int GH, int NW, bool MFMA>
 struct ScanSmem {
+  static constexpr int PF = MFMA ? scan_prefetch<MT>() : 1;
   union WaveScratch {
     v4i wl[MT * 64];                       // PV A operand (MFMA)
     float pw[kPageTokens][4];              // p * scale, p * zero (VALU)
@@ -408,9 +413,42 @@ struct ScanSmem {
   } wave[NW];
   float qsum[GH][2];                       // VALU: per-group sums of q~
   float m[NW][MT * 4], l[NW][MT * 4], z[NW][MT * 4][2];
-  float o[NW][MT * 4][kD];
+  union {
+    uint4 pbuf[MFMA ? NW : 1][PF][kPageBytes / 16];   // page copies (during the scan)
+    float o[NW][MT * 4][kD];                          // per-wave value sums (after it)
+  };
   float vacc[MFMA ? 1 : NW][GH][64][2];    // VALU: per-wave running sums
 };
+
+// Page copies into LDS are issued as inline assembly so that the compiler
+// does not treat every later LDS access as dependent on them (it would wait
+// for all vector memory first); their completion is awaited explicitly with
+// wait_pages().  Vector-memory loads complete in issue order, so waits the
+// compiler places for its own loads stay correct (at worst longer).
+
+// s_waitcnt immediate that waits for vector-memory count <= n only.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Wait until at most n pages' copies (5 loads each) are outstanding.
+__device__ __forceinline__ void wait_pages(int n) {
+  if (n >= 2) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+  else if (n == 1) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Wait for this wave's LDS reads (a page buffer may then be refilled).
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Copy one 5120-byte page to LDS: five 1 KB DMA loads; lane i moves bytes
+// [16 i, 16 i + 16) of each kilobyte.  base and lds are wave-uniform.
+__device__ __forceinline__ void dma_page(uint64_t base, uint32_t lds, uint32_t lane_off) {
+#pragma unroll
+  for (int j = 0; j < kPageBytes / 1024; ++j)
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds + 1024u * j), "v"(lane_off + 1024u * j), "s"(base)
+                 : "memory", "m0");
+}
 
 template <int GH>
 struct MergeSmem {
@@ -529,8 +567,10 @@ __device__ void write_split_partial(ScanSmem<MT, GH, NW, MFMA> &sm, int G, float
 template <int MT, int GH, int NW>
 __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float *dst,
                               ScanSmem<MT, GH, NW, true> &sm) {
+  constexpr int PF = ScanSmem<MT, GH, NW, true>::PF;
   const PoolView &pv = a.pv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, q = lane >> 4;
   const int G = pv.hq / pv.hkv;
   const int bh = b * pv.hkv + kv;
@@ -541,19 +581,37 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   const int pg1 = min(min(n_pages, pg0 + a.pages_per_split), pv.max_pages);
   if (n_pages > pv.max_pages && split == 0 && tid == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_LENGTH);
 
-  const int32_t *btab = pv.block_table + (size_t)b * pv.max_pages;
+  // this wave's pages: first + i * NW, i < npg.  Lane k of bt holds the
+  // block-table entry of page 64 c + k, c = the chunk of the next page issued.
+  const int first = pg0 + wave;
+  const int npg = first < pg1 ? (pg1 - first + NW - 1) / NW : 0;
+  const int32_t *btw = pv.block_table + (size_t)b * pv.max_pages + first;
+  int bt = lane < npg ? btw[(size_t)lane * NW] : -1;
   const uint8_t *pbase = pv.pages + (size_t)kv * kPageBytes;
   const size_t pstride = (size_t)pv.hkv * kPageBytes;
-  int pg = pg0 + wave;
-  PageRegs cur;
+  uint4 (*bufs)[kPageBytes / 16] = sm.pbuf[wave];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4 *)bufs[0];
   bool bad = false;
-  bool cur_ok = false;
-  if (pg < pg1) {
-    const int ph = btab[pg];
-    cur_ok = ph >= 0 && ph < pv.n_pages;
-    if (cur_ok) load_page(cur, pbase + (size_t)ph * pstride, n, q);
-    else bad = true;
-  }
+  uint32_t inflight = 0;   // bit j: page i + j (i = next page consumed) has a copy in flight
+  int issued = 0;
+  auto issue = [&](int j) {   // copy page j (j < npg) into buffer j % PF
+    if ((j & 63) == 0 && j > 0) {
+      bt = j + lane < npg ? btw[(size_t)(j + lane) * NW] : -1;
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    const int ph = __builtin_amdgcn_readlane(bt, j & 63);
+    const bool ok = ph >= 0 && ph < pv.n_pages;
+    if (ok) {
+      const uint64_t base = (uint64_t)(uintptr_t)(pbase + (size_t)ph * pstride);
+      dma_page(base, lds0 + (uint32_t)(j % PF) * kPageBytes, 16u * lane);
+    } else {
+      bad = true;
+    }
+    return ok;
+  };
+  for (; issued < PF && issued < npg; ++issued)
+    if (issue(issued)) inflight |= 1u << issued;
+
   v4i Aq[MT][2];
   float qa[MT], qb0[MT], qb1[MT];
   const float sl2 = pv.sm_scale * kLog2e;
@@ -582,21 +640,31 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
     for (int nt = 0; nt < 8; ++nt) st.facc[mt][nt] = 0.f;
   }
   v4i *wl = sm.wave[wave].wl;
-  while (pg < pg1) {
-    if (cur_ok) {
-      const int valid = min(kPageTokens, n_hist - pg * kPageTokens);
+  // complete the query operands here (and with them the first copies), so that
+  // no wait for them is left inside the loop
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  for (int i = 0; i < npg; ++i) {
+    const bool ok = inflight & 1u;
+    PageRegs cur;
+    if (ok) {
+      // copies issued after page i that may still be outstanding
+      wait_pages(__builtin_popcount(inflight >> 1));
+      load_page(cur, (const uint8_t *)bufs[i % PF], n, q);
+      wait_lds_reads();
+    }
+    inflight >>= 1;
+    if (issued < npg) {
+      if (issue(issued)) inflight |= 1u << (PF - 1);
+      ++issued;
+    }
+    if (ok) {
+      const int valid = min(kPageTokens, n_hist - (first + i * NW) * kPageTokens);
       if (valid == kPageTokens) int2_page<MT, true>(cur, valid, Aq, qa, qb0, qb1, kw, st, wl);
       else int2_page<MT, false>(cur, valid, Aq, qa, qb0, qb1, kw, st, wl);
     }
-    pg += NW;
-    if (pg < pg1) {
-      const int ph = btab[pg];
-      cur_ok = ph >= 0 && ph < pv.n_pages;
-      if (cur_ok) load_page(cur, pbase + (size_t)ph * pstride, n, q);
-      else bad = true;
-    }
   }
   if (bad && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
+  __syncthreads();   // every wave is done with its page buffers (aliased by sm.o)
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const float l16 = row16_sum(st.lsum[mt]);
@@ -774,11 +842,11 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *parts, 
   }
 }
 
-// Register budget: four waves per SIMD for one M-tile of heads (G <= 4), two
+// Register budget: three waves per SIMD for one M-tile of heads (G <= 4), two
 // otherwise; the VALU reference takes what it needs.
 template <int MT, int GH, bool MFMA>
 __global__ void __launch_bounds__((64 * scan_waves<MT, MFMA>()))
-__attribute__((amdgpu_waves_per_eu(MFMA ? (MT == 1 ? 4 : 2) : 1)))
+__attribute__((amdgpu_waves_per_eu(MFMA ? (MT == 1 ? 3 : 2) : 1)))
 decode_scan_kernel(DecArgs a) {
   constexpr int NW = scan_waves<MT, MFMA>();
   const PoolView &pv = a.pv;
@@ -818,7 +886,7 @@ int target_blocks() {
 }
 int mt_of(int G) { return (G + 3) / 4; }
 int gh_of(int G) { return 4 * mt_of(G); }
-int nw_of(int G, int variant) { return variant != 0 ? 4 : (mt_of(G) == 1 ? 16 : 8); }
+int nw_of(int G, int variant) { return variant != 0 ? 4 : (mt_of(G) == 1 ? 12 : 8); }
 }  // namespace
 
 DecodePlan make_decode_plan(int batch, int hkv, int hq, int max_pages, int sink, int recent, int variant) {

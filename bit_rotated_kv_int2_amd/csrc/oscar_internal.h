@@ -79,7 +79,7 @@ struct PoolView {
   uint16_t *sink_k, *sink_v, *recent_k, *recent_v;
   uint8_t *pages;
   const int32_t *block_table, *sink_slot;
-  int32_t *seq_lens, *err;
+  int32_t *seq_lens, *err, *app_cnt;
   int32_t batch, max_pages, n_pages, n_sink_slots;
   int32_t hkv, hq, sink, recent;
   float sm_scale;

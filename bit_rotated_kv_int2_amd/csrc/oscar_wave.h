@@ -110,23 +110,37 @@ __device__ __forceinline__ void bf16_chunk(const uint16_t *K, const uint16_t *V,
 #pragma unroll
     for (int c = 0; c < 8; ++c) o[h][c] *= al;
   }
-  for (int t = q; t < valid; t += 4) {
-    const uint4 u = *(const uint4 *)(V + (size_t)t * kD + 8 * n);
-    float vf[8];
-    vf[0] = __uint_as_float(u.x << 16);
-    vf[1] = __uint_as_float(u.x & 0xFFFF0000u);
-    vf[2] = __uint_as_float(u.y << 16);
-    vf[3] = __uint_as_float(u.y & 0xFFFF0000u);
-    vf[4] = __uint_as_float(u.z << 16);
-    vf[5] = __uint_as_float(u.z & 0xFFFF0000u);
-    vf[6] = __uint_as_float(u.w << 16);
-    vf[7] = __uint_as_float(u.w & 0xFFFF0000u);
+  // Value rows: 16 tokens per lane (token phase q), issued 4 at a time so the
+  // loads overlap.  Rows past `valid` re-read the last valid row (finite data)
+  // and meet p = 0.
+  const int tmax = valid - 1;
 #pragma unroll
-    for (int h = 0; h < GH; ++h) {
-      if (h >= G) break;
-      const float p = ps[h][t];
+  for (int blk = 0; blk < 4; ++blk) {
+    uint4 u[4];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) o[h][c] = fmaf(p, vf[c], o[h][c]);
+    for (int i = 0; i < 4; ++i) {
+      const int t = min(q + 4 * (4 * blk + i), tmax);
+      u[i] = *(const uint4 *)(V + (size_t)t * kD + 8 * n);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = q + 4 * (4 * blk + i);
+      float vf[8];
+      vf[0] = __uint_as_float(u[i].x << 16);
+      vf[1] = __uint_as_float(u[i].x & 0xFFFF0000u);
+      vf[2] = __uint_as_float(u[i].y << 16);
+      vf[3] = __uint_as_float(u[i].y & 0xFFFF0000u);
+      vf[4] = __uint_as_float(u[i].z << 16);
+      vf[5] = __uint_as_float(u[i].z & 0xFFFF0000u);
+      vf[6] = __uint_as_float(u[i].w << 16);
+      vf[7] = __uint_as_float(u[i].w & 0xFFFF0000u);
+#pragma unroll
+      for (int h = 0; h < GH; ++h) {
+        if (h >= G) break;
+        const float p = ps[h][t];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[h][c] = fmaf(p, vf[c], o[h][c]);
+      }
     }
   }
   wave_lds_sync();

@@ -47,6 +47,25 @@ __device__ __forceinline__ float wave_min(float v) {
   return v;
 }
 
+// S6..S8 for output channel p of one token (this thread; the wave holds the
+// 64 channels of one group): clamp, group scale/zero, code.  Lane 0 of the
+// group writes the fp16 {scale, zero} pair to meta[group].
+__device__ __forceinline__ uint32_t quantize_code(float v, float tau, int p, uint32_t *meta) {
+  v = fminf(fmaxf(v, -tau), tau);
+  const float mx = wave_max(v), mn = wave_min(v);
+  const float s = __fdiv_rn(mx - mn, 3.0f);
+  const uint16_t s16 = f32_to_f16_rn(s), z16 = f32_to_f16_rn(mn);
+  const float sf = f16_to_f32(s16), zf = f16_to_f32(z16);
+  uint32_t code = 0;
+  if (sf != 0.0f) {
+    float r = rintf(__fdiv_rn(v - zf, sf));
+    r = fminf(fmaxf(r, 0.0f), 3.0f);
+    code = (uint32_t)r;
+  }
+  if ((p & 63) == 0) meta[p >> 6] = (uint32_t)s16 | ((uint32_t)z16 << 16);
+  return code;
+}
+
 // grid: (chunks, Hkv * 2, batch); block: 128 threads (thread j = channel j).
 // Demotes every position x with max(S0, p0 - W) <= x < p0 + n_new - W.
 __global__ void __launch_bounds__(kThreads) append_demote_kernel(AppendArgs a) {
@@ -124,28 +143,13 @@ __global__ void __launch_bounds__(kThreads) append_demote_kernel(AppendArgs a) {
   // S3..S8 per token; thread j = output channel p, wave = quantisation group.
   const float tau = (is_v ? a.rv.tau_V : a.rv.tau_K)[h];
   const int p = j;
-  const int g = p >> 6;
   uint8_t *page = pv.pages + ((size_t)phys * pv.hkv + h) * kPageBytes;
   uint32_t vbytes[4] = {0, 0, 0, 0};   // V: the 4 bytes of channel p this chunk touches
   uint32_t vmask[4] = {0, 0, 0, 0};
   for (int t = 0; t < nt; ++t) {
     const int slot = (t0 + t) % kPageTokens;
-    float v = (float)(ys[t][bitrev7(p)] * kInvSqrtD);
-    v = fminf(fmaxf(v, -tau), tau);
-    const float mx = wave_max(v), mn = wave_min(v);
-    const float s = __fdiv_rn(mx - mn, 3.0f);
-    const uint16_t s16 = f32_to_f16_rn(s), z16 = f32_to_f16_rn(mn);
-    const float sf = f16_to_f32(s16), zf = f16_to_f32(z16);
-    uint32_t code = 0;
-    if (sf != 0.0f) {
-      float r = rintf(__fdiv_rn(v - zf, sf));
-      r = fminf(fmaxf(r, 0.0f), 3.0f);
-      code = (uint32_t)r;
-    }
-    if ((p & 63) == 0) {
-      uint32_t *meta = (uint32_t *)(page + (is_v ? kVMeta : kKMeta) + meta_entry(slot) * 8);
-      meta[g] = (uint32_t)s16 | ((uint32_t)z16 << 16);
-    }
+    const float v = (float)(ys[t][bitrev7(p)] * kInvSqrtD);
+    const uint32_t code = quantize_code(v, tau, p, (uint32_t *)(page + (is_v ? kVMeta : kKMeta) + meta_entry(slot) * 8));
     if (!is_v) {
       // K codes: byte p/4 of the token row, four neighbouring lanes combine.
       uint32_t c = code << (2 * (p & 3));
@@ -168,6 +172,104 @@ __global__ void __launch_bounds__(kThreads) append_demote_kernel(AppendArgs a) {
       uint32_t val = vbytes[m];
       if (vmask[m] != 0xFF) val = (*dst & ~vmask[m]) | val;   // partial byte: keep other slots
       *dst = (uint8_t)val;
+    }
+  }
+}
+
+// Single-token append, one launch.  grid: (Hkv * 2, batch); block: 128
+// (thread j = channel j).  Block (h, K|V) of sequence b stores the new token
+// of head h (sink, or ring slot p0 mod W) and demotes the ring token that slot
+// held when it leaves the window; the last of the sequence's 2 Hkv blocks
+// (counted in app_cnt[b], which it resets) advances seq_lens[b].
+__global__ void __launch_bounds__(kThreads) append_one_kernel(AppendArgs a) {
+  const PoolView &pv = a.pv;
+  const int b = blockIdx.y, h = blockIdx.x >> 1, is_v = blockIdx.x & 1;
+  const int j = threadIdx.x;
+  const int p0 = pv.seq_lens[b];
+  __shared__ double xs[kD];
+  __shared__ double ys[kD];
+  if (p0 >= 0) {
+    const uint16_t nb = (is_v ? a.v_new : a.k_new)[((size_t)b * pv.hkv + h) * kD + j];
+    bool demote = false;
+    uint16_t old = 0;
+    if (p0 < pv.sink) {
+      const int ss = pv.sink_slot[b];
+      if (ss >= 0 && ss < pv.n_sink_slots)
+        (is_v ? pv.sink_v : pv.sink_k)[(((size_t)ss * pv.hkv + h) * pv.sink + p0) * kD + j] = nb;
+      else if (blockIdx.x == 0 && j == 0 && pv.err)
+        atomicOr(pv.err, OSCAR_DEVERR_SINKSLOT);
+    } else {
+      uint16_t *el = (is_v ? pv.recent_v : pv.recent_k) + (((size_t)b * pv.hkv + h) * pv.recent + p0 % pv.recent) * kD + j;
+      demote = p0 - pv.recent >= pv.sink;   // the slot's token leaves the window
+      if (demote) old = *el;
+      *el = nb;
+    }
+    int phys = -1;
+    if (demote) {
+      const int page_idx = (p0 - pv.recent - pv.sink) / kPageTokens;
+      if (page_idx >= pv.max_pages) {
+        if (j == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_LENGTH);
+      } else {
+        phys = pv.block_table[(size_t)b * pv.max_pages + page_idx];
+        if (phys < 0 || phys >= pv.n_pages) {
+          if (j == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
+          phys = -1;
+        }
+      }
+    }
+    if (phys >= 0) {   // block-uniform
+      const int slot = (p0 - pv.recent - pv.sink) % kPageTokens;
+      // S1: thread j takes column j of U; all 128 loads are issued together
+      const float *U = (is_v ? a.rv.U_V : a.rv.U_K) + (size_t)h * kD * kD + j;
+      float u[kD];
+#pragma unroll
+      for (int k = 0; k < kD; ++k) u[k] = U[(size_t)k * kD];
+      xs[j] = (double)bf16_to_f32(old);
+      __syncthreads();
+      double y = 0.0;
+#pragma unroll
+      for (int k = 0; k < kD; ++k) y = fma(xs[k], (double)u[k], y);
+      // S2: butterfly; stages 1..32 inside the wave, stage 64 through LDS
+#pragma unroll
+      for (int hs = 1; hs < 64; hs <<= 1) {
+        const double o = __shfl_xor(y, hs, 64);
+        y = (j & hs) ? o - y : y + o;
+      }
+      ys[j] = y;
+      __syncthreads();
+      {
+        const double o = ys[j ^ 64];
+        y = (j & 64) ? o - y : y + o;
+      }
+      __syncthreads();
+      ys[j] = y;
+      __syncthreads();
+      // S3..S8: thread j = output channel p
+      const int p = j;
+      const float tau = (is_v ? a.rv.tau_V : a.rv.tau_K)[h];
+      uint8_t *page = pv.pages + ((size_t)phys * pv.hkv + h) * kPageBytes;
+      const float v = (float)(ys[bitrev7(p)] * kInvSqrtD);
+      const uint32_t code = quantize_code(v, tau, p, (uint32_t *)(page + (is_v ? kVMeta : kKMeta) + meta_entry(slot) * 8));
+      if (!is_v) {
+        uint32_t c = code << (2 * (p & 3));
+        c |= __shfl_xor(c, 1, 64);
+        c |= __shfl_xor(c, 2, 64);
+        if ((p & 3) == 0) page[kKCodes + slot * 32 + (p >> 2)] = (uint8_t)c;
+      } else {
+        // one 2-bit field of a byte shared with three other slots
+        uint8_t *dst = page + kVCodes + p * 16 + vcode_byte(slot);
+        const uint32_t sh = 2 * (slot & 3);
+        *dst = (uint8_t)((*dst & ~(3u << sh)) | (code << sh));
+      }
+    }
+  }
+  __syncthreads();
+  if (j == 0) {
+    const int n = atomicAdd(&pv.app_cnt[b], 1);
+    if (n == 2 * pv.hkv - 1) {
+      pv.app_cnt[b] = 0;
+      if (p0 >= 0) pv.seq_lens[b] = p0 + 1;
+      else if (pv.err) atomicOr(pv.err, OSCAR_DEVERR_LENGTH);
     }
   }
 }
@@ -220,6 +322,10 @@ __global__ void __launch_bounds__(256) append_store_kernel(AppendArgs a) {
 hipError_t launch_append(const PoolView &pv, const RotView &rv, const uint16_t *k_new,
                          const uint16_t *v_new, int n_new, hipStream_t s) {
   AppendArgs a{pv, rv, k_new, v_new, n_new};
+  if (n_new == 1 && pv.app_cnt) {
+    hipLaunchKernelGGL(append_one_kernel, dim3(pv.hkv * 2, pv.batch), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  }
   const int chunks = (n_new + kChunk - 1) / kChunk + 1;
   hipLaunchKernelGGL(append_demote_kernel, dim3(chunks, pv.hkv * 2, pv.batch), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();

@@ -60,8 +60,8 @@ class KVPoolC(ctypes.Structure):
                 ("recent_k", ctypes.c_void_p), ("recent_v", ctypes.c_void_p),
                 ("pages", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
                 ("sink_slot", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
-                ("error_flags", ctypes.c_void_p), ("batch", ctypes.c_int32),
-                ("max_pages", ctypes.c_int32), ("n_pages", ctypes.c_int32),
+                ("error_flags", ctypes.c_void_p), ("append_counters", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("max_pages", ctypes.c_int32), ("n_pages", ctypes.c_int32),
                 ("n_sink_slots", ctypes.c_int32)]
 
 
@@ -222,11 +222,13 @@ class KVPool:
         self.pages = alloc((max(self.n_pages, 1), hkv, PAGE_BYTES), dtype=torch.uint8, device=device)
         self.seq_lens = torch.zeros(batch, dtype=torch.int32, device=device)
         self.error_flags = torch.zeros(1, dtype=torch.int32, device=device)
+        self.append_counters = torch.zeros(batch, dtype=torch.int32, device=device)
 
     def c(self) -> KVPoolC:
         return KVPoolC(_ptr(self.sink_k), _ptr(self.sink_v), _ptr(self.recent_k), _ptr(self.recent_v),
                        _ptr(self.pages), _ptr(self.block_table), _ptr(self.sink_slot), _ptr(self.seq_lens),
-                       _ptr(self.error_flags), self.batch, self.max_pages, self.n_pages, self.n_sink_slots)
+                       _ptr(self.error_flags), _ptr(self.append_counters), self.batch, self.max_pages,
+                       self.n_pages, self.n_sink_slots)
 
     def c_seq(self, b: int) -> KVPoolC:
         """The same pool seen as a batch of one: sequence b alone."""
@@ -236,6 +238,7 @@ class KVPool:
         c.block_table = _ptr(self.block_table[b])
         c.sink_slot = _ptr(self.sink_slot[b:b + 1])
         c.seq_lens = _ptr(self.seq_lens[b:b + 1])
+        c.append_counters = _ptr(self.append_counters[b:b + 1])
         c.batch = 1
         return c
 

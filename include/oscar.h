@@ -124,6 +124,10 @@ typedef struct oscar_kv_pool {
   const int32_t *sink_slot;    /* int32 [batch]: sink slot of each sequence */
   int32_t *seq_lens;           /* int32 [batch]: tokens currently stored */
   int32_t *error_flags;        /* optional int32[1], OSCAR_DEVERR_* bits */
+  int32_t *append_counters;    /* optional int32 [batch], zero-filled by the caller
+                                  once; single-token appends use it to let the
+                                  last block of a sequence advance seq_lens, and
+                                  leave it zero.  NULL selects a two-launch path. */
   int32_t batch;
   int32_t max_pages;
   int32_t n_pages;

@@ -49,7 +49,7 @@ def test_header_layout_constants_match_binding():
 
 def _fake_pool(batch=1):
     # non-NULL but never dereferenced: validation fails first
-    return O.KVPoolC(*([0x1000] * 9), batch, 4, 4, batch)
+    return O.KVPoolC(*([0x1000] * 10), batch, 4, 4, batch)
 
 
 def _call_decode(params, pool=None, ws_bytes=1 << 30):
