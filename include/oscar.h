@@ -178,8 +178,11 @@ int32_t oscar_quantize_append(const oscar_params *p, const oscar_rotation *rot,
  * the rotated codes and R_V^T applied once to the merged history output).
  * Query head h reads KV head h / (Hq/Hkv).  seq_lens is read on the device;
  * a sequence of length 0 yields zeros.  workspace: device memory of at least
- * oscar_decode_workspace_size() bytes, 256-byte aligned; it holds no state
- * between calls.
+ * oscar_decode_workspace_size() bytes, 256-byte aligned, ZERO-FILLED by the
+ * caller before its first use.  It holds completion counters that every call
+ * returns to zero, so it can be reused without clearing; calls that share a
+ * workspace must not overlap (same stream, or ordered).  The size depends on
+ * the decode variant selected when it is queried.
  */
 int32_t oscar_decode_attention(const oscar_params *p, const oscar_rotation *rot,
                                const oscar_kv_pool *pool, const uint16_t *q, float *out,
@@ -191,8 +194,8 @@ size_t oscar_decode_workspace_size(const oscar_params *p, int32_t batch, int32_t
  * In-house BF16 decode baseline on a paged all-BF16 cache (the comparison
  * every speedup is quoted against): k_pages, v_pages bf16
  * [n_pages][Hkv][64][d]; token position t of sequence b lives in page
- * block_table[b][t / 64], slot t % 64.  Same q/out conventions as
- * oscar_decode_attention.
+ * block_table[b][t / 64], slot t % 64.  Same q/out and workspace
+ * conventions as oscar_decode_attention (zero-filled before first use).
  */
 typedef struct oscar_bf16_cache {
   const uint16_t *k_pages;
