@@ -45,14 +45,7 @@ def log(msg):
 
 def gpu_kv(torch, synth, wl, layer, seq, L):
     """Seeded bf16 K/V bits [L, Hkv, d] (int16) of one sequence, on the GPU."""
-    g = synth.torch_kv_generator(wl, layer, seq, "cuda")
-    out = []
-    for tensor in (0, 1):
-        sc = torch.from_numpy(synth.outlier_scale(wl, layer, tensor)).cuda()
-        x = torch.randn((L, wl.n_kv, D), generator=g, device="cuda", dtype=torch.float32) * sc
-        out.append(x.to(torch.bfloat16).view(torch.int16).contiguous())
-        del x
-    return out[0], out[1]
+    return synth.gpu_sequence_kv(wl, layer, seq, L, "cuda")
 
 
 def calibrate_layer(O, synth, wl, layer, params, n_cal):

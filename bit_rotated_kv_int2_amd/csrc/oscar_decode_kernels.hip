@@ -40,7 +40,12 @@
 namespace oscar {
 namespace {
 
-constexpr float kWScale = 32639.0f;            // 15-bit weights, hi byte <= 127
+// Value weights are 23-bit fixed point per page: u = round(w * kWScale / wmax)
+// and u + 0x8080 = 65536 hi + 256 (mid + 128) + (lo + 128) with hi <= 127,
+// i.e. u + 0x8080 < 2^23.  kWScale keeps a margin below 2^23 - 0x8080 - 1 =
+// 8355711 because w * (kWScale / wmax) may round a few units above kWScale.
+constexpr float kWScale = 8355000.0f;
+constexpr float kWBias = 32896.5f;              // 0x8080 + 0.5 (round to nearest)
 constexpr float kInvSqrtDf = 0.08838834764831845f;
 constexpr int kMaxSplits = 256;
 constexpr float kHeadroom = 1.0f;              // log2 headroom above m_ref
@@ -75,7 +80,10 @@ __device__ __forceinline__ v4i unpack16(uint32_t w) {
 __device__ __forceinline__ float lo_h(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFF)); }
 __device__ __forceinline__ float hi_h(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
-// Byte 1 / byte 0 of four words gathered into one word (word i -> byte i).
+// Byte 2 / byte 1 / byte 0 of four words gathered into one word (word i -> byte i).
+__device__ __forceinline__ uint32_t gather_b2(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+  return __builtin_amdgcn_perm(w1, w0, 0x0C0C0602u) | __builtin_amdgcn_perm(w3, w2, 0x06020C0Cu);
+}
 __device__ __forceinline__ uint32_t gather_b1(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
   return __builtin_amdgcn_perm(w1, w0, 0x0C0C0501u) | __builtin_amdgcn_perm(w3, w2, 0x05010C0Cu);
 }
@@ -221,7 +229,7 @@ template <int MT>
 struct HistState {
   float mref[MT];          // log2-domain reference max (row-uniform)
   float lsum[MT], z0[MT], z1[MT];
-  float facc[MT][8];       // value sums in units of 1 / kw
+  float facc[MT][8];       // value sums (rotated basis, relative to 2^mref)
 };
 
 template <int MT>
@@ -233,10 +241,21 @@ __device__ __forceinline__ void rescale(HistState<MT> &st, int mt, float alpha) 
   st.z1[mt] *= alpha;
 }
 
+// One 64-token history page for MT M-tiles of 4 query heads.
+//
+// Logits: int8 MFMA of the 15-bit query (hi/lo rows, one per 64-channel
+// group) against the unpacked K codes; scale and zero per token and group.
+// Values: the weights w = 2^(l - m_ref) * scale_V of a head are quantised to
+// 23 bits against the page's largest weight of that head, split into
+// hi/mid/lo bytes (rows 4h, 4h+1, 4h+2 of the A operand of the token's
+// 64-channel group; row 4h+3 stays zero) and multiplied with the unpacked V
+// codes on the int8 MFMA.  Small weights must survive: at long context most
+// of the softmax mass can sit in weights far below the page maximum.  The
+// zero-point part sum(w * zero) stays in float.
 template <int MT, bool FULL>
 __device__ __forceinline__ void int2_page(const PageRegs &r, int valid, const v4i (&Aq)[MT][2],
                                           const float (&qa)[MT], const float (&qb0)[MT],
-                                          const float (&qb1)[MT], float kw, HistState<MT> &st, v4i *wl) {
+                                          const float (&qb1)[MT], HistState<MT> &st, v4i *wl) {
   const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
   const uint32_t kmw[8] = {r.km0.x, r.km0.y, r.km0.z, r.km0.w, r.km1.x, r.km1.y, r.km1.z, r.km1.w};
   const uint32_t vmw[8] = {r.vm0.x, r.vm0.y, r.vm0.z, r.vm0.w, r.vm1.x, r.vm1.y, r.vm1.z, r.vm1.w};
@@ -258,6 +277,7 @@ __device__ __forceinline__ void int2_page(const PageRegs &r, int valid, const v4
       lg[mt][tt] = ok ? v : -INFINITY;
     }
   }
+  float pscale[MT];   // per-head dequantisation step of this page's weights
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     // move the reference only when some logit exceeds it by the headroom
@@ -270,36 +290,53 @@ __device__ __forceinline__ void int2_page(const PageRegs &r, int valid, const v4
       rescale<MT>(st, mt, exp2_fast(st.mref[mt] - mnew));
       st.mref[mt] = mnew;
     }
-    uint32_t u0[4], u1[4];
-    float es = 0.f, ez0 = 0.f, ez1 = 0.f;
+    float w0[4], w1[4];
+    float es = 0.f, ez0 = 0.f, ez1 = 0.f, wmax = 0.f;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
+      // masked tokens: e = 0, and their (unwritten) metadata is not used
       const bool ok = FULL || (16 * tt + n) < valid;
-      const float e = exp2_fast(lg[mt][tt] - st.mref[mt]);   // 0 for masked tokens
+      const float e = exp2_fast(lg[mt][tt] - st.mref[mt]);
       const float vs0 = lo_h(vmw[2 * tt]), vz0 = hi_h(vmw[2 * tt]);
       const float vs1 = lo_h(vmw[2 * tt + 1]), vz1 = hi_h(vmw[2 * tt + 1]);
-      const float ek = ok ? e * kw : 0.f;
       es += e;
       ez0 = ok ? fmaf(e, vz0, ez0) : ez0;
       ez1 = ok ? fmaf(e, vz1, ez1) : ez1;
-      // w + 128 = 256 hi + (lo + 128); w <= 32639 by the scale bound
-      u0[tt] = (uint32_t)fminf(fmaf(ek, vs0, 128.5f), 32767.0f);
-      u1[tt] = (uint32_t)fminf(fmaf(ek, vs1, 128.5f), 32767.0f);
+      w0[tt] = ok ? e * vs0 : 0.f;
+      w1[tt] = ok ? e * vs1 : 0.f;
+      wmax = fmaxf(wmax, fmaxf(w0[tt], w1[tt]));
     }
     st.lsum[mt] += es;
     st.z0[mt] += ez0;
     st.z1[mt] += ez1;
-    uint32_t *wd = (uint32_t *)(wl + mt * 64);
+    wmax = row16_max(wmax);
+    const float kq = wmax > 0.f ? kWScale / wmax : 0.f;
+    pscale[mt] = wmax * (1.0f / kWScale);
+    uint32_t u0[4], u1[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      u0[tt] = (uint32_t)fmaf(w0[tt], kq, kWBias);
+      u1[tt] = (uint32_t)fmaf(w1[tt], kq, kWBias);
+    }
+    // lane (n, q): head q, tokens 16 tt + n -> A rows 4q + {hi, mid, lo},
+    // lane group n / 4, bytes 4 (n % 4) + tt
+    uint32_t *wd0 = (uint32_t *)(wl + (mt * 2 + 0) * 64);
+    uint32_t *wd1 = (uint32_t *)(wl + (mt * 2 + 1) * 64);
     const int lb = 16 * (n >> 2), sub = n & 3;
-    wd[(4 * q + 0 + lb) * 4 + sub] = gather_b1(u0[0], u0[1], u0[2], u0[3]);
-    wd[(4 * q + 1 + lb) * 4 + sub] = gather_b0(u0[0], u0[1], u0[2], u0[3]) ^ 0x80808080u;
-    wd[(4 * q + 2 + lb) * 4 + sub] = gather_b1(u1[0], u1[1], u1[2], u1[3]);
-    wd[(4 * q + 3 + lb) * 4 + sub] = gather_b0(u1[0], u1[1], u1[2], u1[3]) ^ 0x80808080u;
+    wd0[(4 * q + 0 + lb) * 4 + sub] = gather_b2(u0[0], u0[1], u0[2], u0[3]);
+    wd0[(4 * q + 1 + lb) * 4 + sub] = gather_b1(u0[0], u0[1], u0[2], u0[3]) ^ 0x80808080u;
+    wd0[(4 * q + 2 + lb) * 4 + sub] = gather_b0(u0[0], u0[1], u0[2], u0[3]) ^ 0x80808080u;
+    wd1[(4 * q + 0 + lb) * 4 + sub] = gather_b2(u1[0], u1[1], u1[2], u1[3]);
+    wd1[(4 * q + 1 + lb) * 4 + sub] = gather_b1(u1[0], u1[1], u1[2], u1[3]) ^ 0x80808080u;
+    wd1[(4 * q + 2 + lb) * 4 + sub] = gather_b0(u1[0], u1[1], u1[2], u1[3]) ^ 0x80808080u;
   }
   wave_lds_sync();
-  v4i Aw[MT];
+  v4i Aw[MT][2];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) Aw[mt] = wl[mt * 64 + lane];
+  for (int mt = 0; mt < MT; ++mt) {
+    Aw[mt][0] = wl[(mt * 2 + 0) * 64 + lane];
+    Aw[mt][1] = wl[(mt * 2 + 1) * 64 + lane];
+  }
   wave_lds_sync();
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
@@ -307,8 +344,9 @@ __device__ __forceinline__ void int2_page(const PageRegs &r, int valid, const v4
     const int g = nt >> 2;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const v4i C = mfma_i8(Aw[mt], Bv, v4i{0, 0, 0, 0});
-      st.facc[mt][nt] += (float)(g ? C[2] * 256 + C[3] : C[0] * 256 + C[1]);
+      const v4i C = mfma_i8(Aw[mt][g], Bv, v4i{0, 0, 0, 0});
+      const float val = fmaf((float)C[0], 65536.0f, (float)(C[1] * 256 + C[2]));
+      st.facc[mt][nt] = fmaf(val, pscale[mt], st.facc[mt][nt]);
     }
   }
 }
@@ -407,7 +445,7 @@ template <int MT, int GH, int NW, bool MFMA>
 struct ScanSmem {
   static constexpr int PF = MFMA ? scan_prefetch<MT>() : 1;
   union WaveScratch {
-    v4i wl[MT * 64];                       // PV A operand (MFMA)
+    v4i wl[MT * 2 * 64];                   // PV A operands, one per channel group (MFMA)
     float pw[kPageTokens][4];              // p * scale, p * zero (VALU)
     float ps[GH][kPageTokens + 4];         // BF16 chunk probabilities
   } wave[NW];
@@ -627,10 +665,6 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
     qb0[mt] = hv ? qc[1] * sl2 : 0.f;
     qb1[mt] = hv ? qc[2] * sl2 : 0.f;
   }
-  // fixed weight scale: scale_t <= 2 tau_V / 3 (clipped range / 3), e <= 2^headroom
-  const float sbound = a.rv.tau_V[kv] * (2.0f / 3.0f) * 1.001f;
-  const float kw = kWScale / (sbound * 2.0f);
-  const float inv_kw = 1.0f / kw;
   HistState<MT> st;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -640,6 +674,9 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
     for (int nt = 0; nt < 8; ++nt) st.facc[mt][nt] = 0.f;
   }
   v4i *wl = sm.wave[wave].wl;
+  // rows 4h + 3 of the weight operands stay zero; the rest is rewritten per page
+#pragma unroll
+  for (int i = 0; i < MT * 2; ++i) wl[i * 64 + lane] = v4i{0, 0, 0, 0};
   // complete the query operands here (and with them the first copies), so that
   // no wait for them is left inside the loop
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -659,8 +696,8 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
     }
     if (ok) {
       const int valid = min(kPageTokens, n_hist - (first + i * NW) * kPageTokens);
-      if (valid == kPageTokens) int2_page<MT, true>(cur, valid, Aq, qa, qb0, qb1, kw, st, wl);
-      else int2_page<MT, false>(cur, valid, Aq, qa, qb0, qb1, kw, st, wl);
+      if (valid == kPageTokens) int2_page<MT, true>(cur, valid, Aq, qa, qb0, qb1, st, wl);
+      else int2_page<MT, false>(cur, valid, Aq, qa, qb0, qb1, st, wl);
     }
   }
   if (bad && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
@@ -678,7 +715,7 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
       sm.z[wave][hh][1] = z1;
     }
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) sm.o[wave][hh][16 * nt + n] = st.facc[mt][nt] * inv_kw;
+    for (int nt = 0; nt < 8; ++nt) sm.o[wave][hh][16 * nt + n] = st.facc[mt][nt];
   }
   __syncthreads();
   write_split_partial<MT, GH, NW, true>(sm, G, dst, true);

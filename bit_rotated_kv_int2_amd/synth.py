@@ -190,3 +190,32 @@ def torch_kv_generator(wl: Workload, layer: int, seq: int, device):
     g = torch.Generator(device=device)
     g.manual_seed(((wl.wid * 1000 + layer) * 100000 + seq) * 7 + 1)
     return g
+
+
+def _gpu_kv_block(wl: Workload, layer: int, stream_seq: int, count: int, device):
+    import torch
+    g = torch_kv_generator(wl, layer, stream_seq, device)
+    out = []
+    for tensor in (0, 1):
+        sc = torch.from_numpy(outlier_scale(wl, layer, tensor)).to(device)
+        x = torch.randn((count, wl.n_kv, wl.head_dim), generator=g, device=device, dtype=torch.float32) * sc
+        out.append(x.to(torch.bfloat16).view(torch.int16).contiguous())
+        del x
+    return out[0], out[1]
+
+
+def gpu_sequence_kv(wl: Workload, layer: int, seq: int, L: int, device="cuda"):
+    """Seeded bf16 K and V bit patterns (int16 tensors [L, Hkv, d]) of one
+    sequence, generated on the device: N(0, 1) float32 times the layer's
+    outlier scale, rounded to bf16.  With ``shared_prefix`` the first
+    shared_prefix tokens come from one stream common to every sequence (seq
+    id = batch), the rest from the sequence's own stream."""
+    import torch
+    P = min(L, wl.shared_prefix)
+    if P == 0:
+        return _gpu_kv_block(wl, layer, seq, L, device)
+    kp, vp = _gpu_kv_block(wl, layer, wl.batch, P, device)
+    if L == P:
+        return kp, vp
+    ks, vs = _gpu_kv_block(wl, layer, seq, L - P, device)
+    return torch.cat([kp, ks]).contiguous(), torch.cat([vp, vs]).contiguous()
