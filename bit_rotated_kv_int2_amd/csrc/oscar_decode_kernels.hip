@@ -56,9 +56,8 @@ struct DecArgs {
   const uint16_t *q;   // bf16 [B][Hq][d]
   float *out;          // fp32 [B][Hq][d]
   int *counters;       // [BH]
-  v4i *qop;            // [BH][MT * 2 * 64] int8 logit operands
-  float *qconst;       // [BH][GH][4]: delta, Q0, Q1 (per-group sums of q~)
-  float *qrot;         // [BH][GH][kD] float q~ (VALU reference)
+  float *qconst;       // [BH][GH][4]: delta, Q0, Q1 (VALU variant)
+  float *qrot;         // [BH][GH][kD] float q~ (VALU variant)
   float *part;         // [BH][n_splits + n_chunks][G][kPartStride]: history splits, then BF16 chunks
   int n_splits, n_chunks, pages_per_split;
 };
@@ -77,8 +76,11 @@ __device__ __forceinline__ v4i unpack16(uint32_t w) {
   return r;
 }
 
-__device__ __forceinline__ float lo_h(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFF)); }
-__device__ __forceinline__ float hi_h(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+// fp16 halves of a word; written as a vector element so the compiler can fold
+// the conversion into mixed-precision FMAs (op_sel) instead of converting
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float lo_h(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w).x; }
+__device__ __forceinline__ float hi_h(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w).y; }
 
 // Byte 2 / byte 1 / byte 0 of four words gathered into one word (word i -> byte i).
 __device__ __forceinline__ uint32_t gather_b2(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
@@ -97,19 +99,26 @@ __device__ __forceinline__ uint32_t gather_b0(uint32_t w0, uint32_t w1, uint32_t
 template <int MT, int GH>
 struct QSmem {
   float ys[MT * 4][kD];
-  v4i aq[MT * 2 * 64];
+  v4i aq[MT * 2 * 64];     // int8 logit operands (hi/lo rows per head and group)
+  float qc[GH][4];         // delta, Q0, Q1 (per-group sums of the fixed-point q~)
 };
+
+// Query preparation for one (sequence, KV head), by the whole workgroup (any
+// multiple of 64 threads >= 256): q~ = bitrev(FWHT(q U_K) / sqrt(d)) for its
+// G query heads, then per head a 15-bit fixed-point copy split into hi/lo
+// int8 bytes laid out as the A operand of the logit MFMA (rows: head h ->
+// 4h + {group 0 hi, group 0 lo, group 1 hi, group 1 lo}).  Results stay in
+// `sm`; with `qrot` non-null the float q~ is also written there.
 template <int MT, int GH>
-__device__ void run_query(const DecArgs &a, int b, int kv, QSmem<MT, GH> &sm) {
+__device__ void query_prep(const DecArgs &a, int b, int kv, QSmem<MT, GH> &sm, float *qrot) {
   const PoolView &pv = a.pv;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
   const int G = pv.hq / pv.hkv;
-  const int bh = b * pv.hkv + kv;
   const float *U = a.rv.U_K + (size_t)kv * kD * kD;
   const uint16_t *qb = a.q + ((size_t)b * pv.hq + (size_t)kv * G) * kD;
-  // y[h][j] = sum_k q[h][k] U[k][j]: thread -> columns 4c..4c+3 and rows
-  // k = t % 8 + 8 i; all 16 loads in flight at once; 8-lane reduction.
-  {
+  // y[h][j] = sum_k q[h][k] U[k][j]: threads 0..255 -> columns 4c..4c+3 and
+  // rows k = t % 8 + 8 i; all 16 loads in flight at once; 8-lane reduction.
+  if (tid < 256) {
     const int c = tid >> 3, kk = tid & 7;
     float4 u[16];
 #pragma unroll
@@ -152,13 +161,14 @@ __device__ void run_query(const DecArgs &a, int b, int kv, QSmem<MT, GH> &sm) {
     }
     __syncthreads();
   }
-  // one wave per head: rotated, permuted q~ -> float copy, fixed point, operands
-  for (int h = w; h < G; h += 4) {
+  // one wave per head: rotated, permuted q~ -> fixed point -> operands
+  for (int h = w; h < G; h += nw) {
     const float v0 = sm.ys[h][bitrev7(lane)] * kInvSqrtDf;
     const float v1 = sm.ys[h][bitrev7(lane + 64)] * kInvSqrtDf;
-    float *qr = a.qrot + ((size_t)bh * GH + h) * kD;
-    qr[lane] = v0;
-    qr[64 + lane] = v1;
+    if (qrot) {
+      qrot[(size_t)h * kD + lane] = v0;
+      qrot[(size_t)h * kD + 64 + lane] = v1;
+    }
     float mx = fmaxf(fabsf(v0), fabsf(v1));
     for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
     const float delta = mx > 0.f ? mx / 32639.0f : 1.0f;
@@ -170,11 +180,10 @@ __device__ void run_query(const DecArgs &a, int b, int kv, QSmem<MT, GH> &sm) {
       s1 += __shfl_xor(s1, o, 64);
     }
     if (lane == 0) {
-      float *qc = a.qconst + ((size_t)bh * GH + h) * 4;
-      qc[0] = delta;
-      qc[1] = delta * (float)s0;   // |sum| < 2^24: exact
-      qc[2] = delta * (float)s1;
-      qc[3] = 0.f;
+      sm.qc[h][0] = delta;
+      sm.qc[h][1] = delta * (float)s0;   // |sum| < 2^24: exact
+      sm.qc[h][2] = delta * (float)s1;
+      sm.qc[h][3] = 0.f;
     }
     const int mt = h >> 2;
 #pragma unroll
@@ -193,15 +202,17 @@ __device__ void run_query(const DecArgs &a, int b, int kv, QSmem<MT, GH> &sm) {
     }
   }
   __syncthreads();
-  v4i *dst = a.qop + (size_t)bh * MT * 2 * 64;
-  for (int e = tid; e < MT * 2 * 64; e += blockDim.x) dst[e] = sm.aq[e];
 }
 
+// Query preparation for the VALU scan variant, which reads the float q~ and
+// the per-head constants from the workspace.
 template <int MT, int GH>
 __global__ void __launch_bounds__(256) decode_pre_kernel(DecArgs a) {
   __shared__ QSmem<MT, GH> sm;
   const int bh = blockIdx.x;
-  run_query<MT, GH>(a, bh / a.pv.hkv, bh % a.pv.hkv, sm);
+  query_prep<MT, GH>(a, bh / a.pv.hkv, bh % a.pv.hkv, sm, a.qrot + (size_t)bh * GH * kD);
+  const int G = a.pv.hq / a.pv.hkv;
+  for (int e = threadIdx.x; e < G * 4; e += blockDim.x) a.qconst[(size_t)bh * GH * 4 + e] = (&sm.qc[0][0])[e];
 }
 
 // ===========================================================================
@@ -310,7 +321,9 @@ __device__ __forceinline__ void int2_page(const PageRegs &r, int valid, const v4
     st.z0[mt] += ez0;
     st.z1[mt] += ez1;
     wmax = row16_max(wmax);
-    const float kq = wmax > 0.f ? kWScale / wmax : 0.f;
+    // approximate reciprocal: kq may exceed kWScale / wmax by an ulp, which
+    // the margin in kWScale absorbs; pscale is exact in the same sense
+    const float kq = wmax > 0.f ? kWScale * __builtin_amdgcn_rcpf(wmax) : 0.f;
     pscale[mt] = wmax * (1.0f / kWScale);
     uint32_t u0[4], u1[4];
 #pragma unroll
@@ -345,8 +358,9 @@ __device__ __forceinline__ void int2_page(const PageRegs &r, int valid, const v4
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const v4i C = mfma_i8(Aw[mt][g], Bv, v4i{0, 0, 0, 0});
-      const float val = fmaf((float)C[0], 65536.0f, (float)(C[1] * 256 + C[2]));
-      st.facc[mt][nt] = fmaf(val, pscale[mt], st.facc[mt][nt]);
+      // sum over 64 tokens of u * code <= 8355000 * 3 * 64 < 2^31: exact in int32
+      const int val = (int)(((unsigned)C[0] << 16) + ((unsigned)C[1] << 8) + (unsigned)C[2]);
+      st.facc[mt][nt] = fmaf((float)val, pscale[mt], st.facc[mt][nt]);
     }
   }
 }
@@ -448,7 +462,11 @@ struct ScanSmem {
     v4i wl[MT * 2 * 64];                   // PV A operands, one per channel group (MFMA)
     float pw[kPageTokens][4];              // p * scale, p * zero (VALU)
     float ps[GH][kPageTokens + 4];         // BF16 chunk probabilities
-  } wave[NW];
+  };
+  union {
+    WaveScratch wave[NW];
+    QSmem<MT, GH> q;                       // query preparation (before the scan)
+  };
   float qsum[GH][2];                       // VALU: per-group sums of q~
   float m[NW][MT * 4], l[NW][MT * 4], z[NW][MT * 4][2];
   union {
@@ -650,20 +668,29 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   for (; issued < PF && issued < npg; ++issued)
     if (issue(issued)) inflight |= 1u << issued;
 
+  // query operands, prepared by the workgroup while the first pages load
+  query_prep<MT, GH>(a, b, kv, sm.q, nullptr);
   v4i Aq[MT][2];
   float qa[MT], qb0[MT], qb1[MT];
   const float sl2 = pv.sm_scale * kLog2e;
-  const v4i *qop = a.qop + (size_t)bh * MT * 2 * 64;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    Aq[mt][0] = qop[(mt * 2 + 0) * 64 + lane];
-    Aq[mt][1] = qop[(mt * 2 + 1) * 64 + lane];
-    const int h = 4 * mt + q;
-    const float *qc = a.qconst + ((size_t)bh * GH + min(h, GH - 1)) * 4;
-    const bool hv = h < G;
-    qa[mt] = hv ? qc[0] * sl2 : 0.f;
-    qb0[mt] = hv ? qc[1] * sl2 : 0.f;
-    qb1[mt] = hv ? qc[2] * sl2 : 0.f;
+    Aq[mt][0] = sm.q.aq[(mt * 2 + 0) * 64 + lane];
+    Aq[mt][1] = sm.q.aq[(mt * 2 + 1) * 64 + lane];
+    const int h = min(4 * mt + q, GH - 1);
+    const bool hv = 4 * mt + q < G;
+    qa[mt] = hv ? sm.q.qc[h][0] * sl2 : 0.f;
+    qb0[mt] = hv ? sm.q.qc[h][1] * sl2 : 0.f;
+    qb1[mt] = hv ? sm.q.qc[h][2] * sl2 : 0.f;
+  }
+  __syncthreads();   // the query scratch is reused by the BF16 chunks and the weights
+  // BF16 chunk c (sink, then recent window) runs on workgroup c % S, wave (c / S) % NW
+  {
+    const int S = a.n_splits;
+    float *parts = a.part + (size_t)bh * (S + a.n_chunks) * G * kPartStride;
+    for (int c = split; c < a.n_chunks; c += S)
+      if (((c / S) % NW) == wave)
+        bf16_chunk_partial<GH>(a, b, kv, c, sm.wave[wave].ps, parts + (size_t)(S + c) * G * kPartStride);
   }
   HistState<MT> st;
 #pragma unroll
@@ -895,10 +922,12 @@ decode_scan_kernel(DecArgs a) {
   const int S = a.n_splits;
   float *parts = a.part + (size_t)bh * (S + a.n_chunks) * G * kPartStride;
   __shared__ ScanUnion<MT, GH, NW, MFMA> sm;
-  // BF16 chunk c runs on workgroup c % S, wave (c / S) % NW, before its pages
-  for (int c = split; c < a.n_chunks; c += S) {
-    if (((c / S) % NW) == wave)
-      bf16_chunk_partial<GH>(a, b, kv, c, sm.s.wave[wave].ps, parts + (size_t)(S + c) * G * kPartStride);
+  if constexpr (!MFMA) {
+    // BF16 chunk c runs on workgroup c % S, wave (c / S) % NW, before its pages
+    for (int c = split; c < a.n_chunks; c += S) {
+      if (((c / S) % NW) == wave)
+        bf16_chunk_partial<GH>(a, b, kv, c, sm.s.wave[wave].ps, parts + (size_t)(S + c) * G * kPartStride);
+    }
   }
   float *dst = parts + (size_t)split * G * kPartStride;
   if constexpr (MFMA) run_scan_mfma<MT, GH, NW>(a, b, kv, split, dst, sm.s);
@@ -943,8 +972,6 @@ DecodePlan make_decode_plan(int batch, int hkv, int hq, int max_pages, int sink,
   size_t off = 0;
   p.off_counters = off;
   off = al(off + (size_t)bh * sizeof(int));
-  p.off_qop = off;
-  off = al(off + (size_t)bh * MT * 2 * 64 * 16);
   p.off_qconst = off;
   off = al(off + (size_t)bh * GH * 4 * sizeof(float));
   p.off_qrot = off;
@@ -960,16 +987,18 @@ hipError_t launch_decode(const PoolView &pv, const RotView &rv, const uint16_t *
                          hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int G = pv.hq / pv.hkv;
   const int BH = pv.batch * pv.hkv;
-  DecArgs a{pv, rv, q, out, (int *)(ws + plan.off_counters), (v4i *)(ws + plan.off_qop),
-            (float *)(ws + plan.off_qconst), (float *)(ws + plan.off_qrot), (float *)(ws + plan.off_part),
+  DecArgs a{pv, rv, q, out, (int *)(ws + plan.off_counters), (float *)(ws + plan.off_qconst),
+            (float *)(ws + plan.off_qrot), (float *)(ws + plan.off_part),
             plan.n_splits, plan.n_chunks, plan.pages_per_split};
   const bool mfma = variant == 0;
   const dim3 sgrid(BH * plan.n_splits);
   hipError_t e;
 #define OSCAR_LAUNCH(MT, GH)                                                                         \
   do {                                                                                               \
-    hipLaunchKernelGGL((decode_pre_kernel<MT, GH>), dim3(BH), dim3(256), 0, s, a);                   \
-    if ((e = hipGetLastError()) != hipSuccess) return e;                                             \
+    if (!mfma) {                                                                                     \
+      hipLaunchKernelGGL((decode_pre_kernel<MT, GH>), dim3(BH), dim3(256), 0, s, a);                 \
+      if ((e = hipGetLastError()) != hipSuccess) return e;                                           \
+    }                                                                                                \
     if (ev_start && (e = hipEventRecord(ev_start, s)) != hipSuccess) return e;                       \
     if (mfma)                                                                                        \
       hipLaunchKernelGGL((decode_scan_kernel<MT, GH, true>), sgrid, dim3(64 * scan_waves<MT, true>()), \

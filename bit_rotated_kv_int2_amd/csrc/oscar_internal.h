@@ -95,7 +95,6 @@ struct DecodePlan {
   int n_chunks;          // 64-token BF16 chunks (sink + recent window)
   int pages_per_split;
   size_t off_counters;   // int [B*Hkv] completion counters, zero between calls
-  size_t off_qop;        // int8 logit operands [B*Hkv][MT][2][64][16]
   size_t off_qconst;     // float [B*Hkv][GH][4]
   size_t off_qrot;       // float [B*Hkv][GH][128]
   size_t off_part;       // float [B*Hkv][n_splits + n_chunks][G][kPartStride]
