@@ -38,6 +38,7 @@ int check_params(const oscar_params *p) {
     return fail(OSCAR_ENOTSUP, "at most %d query heads per KV head", oscar::kMaxGroupHeads);
   if (p->sink < 64 || p->sink % 64) return fail(OSCAR_ENOTSUP, "sink must be a positive multiple of 64");
   if (p->recent < 64 || p->recent % 64) return fail(OSCAR_ENOTSUP, "recent must be a positive multiple of 64");
+  if (p->sink + p->recent > 4096) return fail(OSCAR_ENOTSUP, "sink + recent must be <= 4096");
   if (p->page_tokens != OSCAR_PAGE_TOKENS) return fail(OSCAR_ENOTSUP, "page_tokens must be 64");
   if (p->group != OSCAR_GROUP) return fail(OSCAR_ENOTSUP, "group must be 64");
   if (!(p->sm_scale > 0.f) || !std::isfinite(p->sm_scale)) return fail(OSCAR_EINVAL, "sm_scale must be positive and finite");

@@ -48,6 +48,8 @@ constexpr float kWScale = 8355000.0f;
 constexpr float kWBias = 32896.5f;              // 0x8080 + 0.5 (round to nearest)
 constexpr float kInvSqrtDf = 0.08838834764831845f;
 constexpr int kMaxSplits = 256;
+constexpr int kMaxParts = 512;                 // history splits + BF16 tiles per (sequence, KV head)
+constexpr int kMergeSlices = 6;                // partial slices of the merge (slices x G <= 24)
 constexpr float kHeadroom = 1.0f;              // log2 headroom above m_ref
 
 struct DecArgs {
@@ -151,18 +153,20 @@ __device__ void query_prep(const DecArgs &a, int b, int kv, QSmem<MT, GH> &sm, f
   }
   for (int e = tid; e < MT * 2 * 64 * 4; e += blockDim.x) ((uint32_t *)sm.aq)[e] = 0;
   __syncthreads();
-  for (int hs = 1; hs < kD; hs <<= 1) {
-    for (int e = tid; e < G * 64; e += blockDim.x) {
-      const int h = e >> 6, pr = e & 63;
-      const int i0 = (pr / hs) * (2 * hs) + (pr % hs);
-      const float x0 = sm.ys[h][i0], x1 = sm.ys[h][i0 + hs];
-      sm.ys[h][i0] = x0 + x1;
-      sm.ys[h][i0 + hs] = x0 - x1;
-    }
-    __syncthreads();
-  }
-  // one wave per head: rotated, permuted q~ -> fixed point -> operands
+  // one wave per head: Walsh-Hadamard butterfly (lane l holds elements l and
+  // l + 64; stages 1..32 by lane exchange, stage 64 in registers), then the
+  // rotated, permuted q~ -> fixed point -> operands
   for (int h = w; h < G; h += nw) {
+    float x0 = sm.ys[h][lane], x1 = sm.ys[h][lane + 64];
+#pragma unroll
+    for (int hs = 1; hs < 64; hs <<= 1) {
+      const float o0 = __shfl_xor(x0, hs, 64), o1 = __shfl_xor(x1, hs, 64);
+      x0 = (lane & hs) ? o0 - x0 : x0 + o0;
+      x1 = (lane & hs) ? o1 - x1 : x1 + o1;
+    }
+    sm.ys[h][lane] = x0 + x1;
+    sm.ys[h][lane + 64] = x0 - x1;
+    wave_lds_sync();
     const float v0 = sm.ys[h][bitrev7(lane)] * kInvSqrtDf;
     const float v1 = sm.ys[h][bitrev7(lane + 64)] * kInvSqrtDf;
     if (qrot) {
@@ -461,7 +465,7 @@ struct ScanSmem {
   union WaveScratch {
     v4i wl[MT * 2 * 64];                   // PV A operands, one per channel group (MFMA)
     float pw[kPageTokens][4];              // p * scale, p * zero (VALU)
-    float ps[GH][kPageTokens + 4];         // BF16 chunk probabilities
+    float tile[GH][kD];                    // BF16 tile probabilities, then its o
   };
   union {
     WaveScratch wave[NW];
@@ -508,10 +512,13 @@ __device__ __forceinline__ void dma_page(uint64_t base, uint32_t lds, uint32_t l
 
 template <int GH>
 struct MergeSmem {
-  float hm[GH], hl[GH];
-  float ws[GH][kMaxSplits];
-  float zs[GH][kD];
-  float ot[GH][kD];
+  float ml[kMaxParts][GH][2];   // (m, l) of every partial: history splits, then BF16 tiles
+  float wgt[kMaxParts][GH];     // merge weight of every partial
+  float hs[GH][4];              // per head: history scale, tile scale, 1 / denominator
+  float zs[GH][kD];             // weighted history sum, bit-reversal permuted
+  float ot[GH][kD];             // history output in the original basis
+  float ob[GH][kD];             // weighted BF16 tile sum
+  float red[2][kMergeSlices * 4 * kD];   // per-slice sums (history, tiles)
 };
 
 template <int MT, int GH, int NW, bool MFMA>
@@ -520,32 +527,33 @@ union ScanUnion {
   MergeSmem<GH> g;
 };
 
-// One BF16 chunk (64 tokens of the sink or the recent ring) by one wave;
-// writes its (m, l, o) partial (log2 units, original basis).
+// BF16 window tiles: 16 tokens each, sink tiles first (kSinkTiles = sink / 16),
+// then the recent ring.  One wave computes one tile and writes its (m, l, o)
+// partial (log2 units, original basis) with coalesced stores.
 template <int GH>
-__device__ void bf16_chunk_partial(const DecArgs &a, int b, int kv, int c, float (*ps)[kPageTokens + 4],
-                                   float *dst) {
+__device__ void bf16_tile_partial(const DecArgs &a, int b, int kv, int u, float (*scratch)[kD], float *dst) {
   const PoolView &pv = a.pv;
   const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
   const int G = pv.hq / pv.hkv;
   const int L = max(0, pv.seq_lens[b]);
-  const int n_sink_chunks = pv.sink / kPageTokens;
+  const int n_sink_tiles = pv.sink / kTileTokens;
   const int slot = pv.sink_slot[b];
   const bool slot_ok = slot >= 0 && slot < pv.n_sink_slots;
   const uint16_t *K, *V;
   int valid;
-  if (c < n_sink_chunks) {
+  if (u < n_sink_tiles) {
     if (!slot_ok && L > 0 && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_SINKSLOT);
-    valid = slot_ok ? max(0, min(kPageTokens, min(L, pv.sink) - c * kPageTokens)) : 0;
-    const size_t row = (((size_t)max(slot, 0) * pv.hkv + kv) * pv.sink + (size_t)c * kPageTokens) * kD;
+    valid = slot_ok ? max(0, min(kTileTokens, min(L, pv.sink) - u * kTileTokens)) : 0;
+    const size_t row = (((size_t)max(slot, 0) * pv.hkv + kv) * pv.sink + (size_t)u * kTileTokens) * kD;
     K = pv.sink_k + row;
     V = pv.sink_v + row;
   } else {
-    // recent ring: valid slots are [a0, a0 + nr) mod W, a prefix of every chunk
+    // recent ring: valid slots are [a0, a0 + nr) mod W, a prefix of every
+    // tile (a0 is 0 mod 64 while the ring is filling; all slots once full)
     const int r0 = max(pv.sink, L - pv.recent);
     const int nr = max(0, L - r0);
     const int a0 = r0 % pv.recent;
-    const int lo = (c - n_sink_chunks) * kPageTokens, hi = lo + kPageTokens;
+    const int lo = (u - n_sink_tiles) * kTileTokens, hi = lo + kTileTokens;
     const int e1 = min(a0 + nr, pv.recent);
     const int e2 = max(0, a0 + nr - pv.recent);
     valid = max(0, min(hi, e1) - max(lo, a0)) + max(0, min(hi, e2) - lo);
@@ -553,32 +561,33 @@ __device__ void bf16_chunk_partial(const DecArgs &a, int b, int kv, int c, float
     K = pv.recent_k + row;
     V = pv.recent_v + row;
   }
-  float m[4], l[4], mrow[GH], o[GH][8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m[i] = -INFINITY;
-    l[i] = 0.f;
-  }
-#pragma unroll
-  for (int h = 0; h < GH; ++h) {
-    mrow[h] = -INFINITY;
-#pragma unroll
-    for (int cc = 0; cc < 8; ++cc) o[h][cc] = 0.f;
-  }
+  float m[4], l[4], o[GH][8];
   if (valid > 0) {
     v8bf Aq[4];
     load_bf16_query(a.q + ((size_t)b * pv.hq + (size_t)kv * G) * kD, G, Aq);
-    bf16_chunk<GH>(K, V, valid, G, Aq, pv.sm_scale * kLog2e, m, l, mrow, o, ps);
+    bf16_tile<GH>(K, V, valid, G, Aq, pv.sm_scale * kLog2e, m, l, o, scratch);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m[i] = -INFINITY;
+      l[i] = 0.f;
+    }
+#pragma unroll
+    for (int h = 0; h < GH; ++h) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) o[h][c] = 0.f;
+    }
   }
+  // sum the four token phases, stage o in LDS, store coalesced
 #pragma unroll
   for (int h = 0; h < GH; ++h) {
     if (h >= G) break;
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      float v = o[h][cc];
+    for (int c = 0; c < 8; ++c) {
+      float v = o[h][c];
       v += __shfl_xor(v, 16, 64);
       v += __shfl_xor(v, 32, 64);
-      if (q == 0) st_coherent(dst + (size_t)h * kPartStride + 2 + 8 * n + cc, v);
+      if (q == 0) scratch[h][8 * n + c] = v;
     }
   }
   if (n == 0) {
@@ -591,6 +600,9 @@ __device__ void bf16_chunk_partial(const DecArgs &a, int b, int kv, int c, float
       }
     }
   }
+  wave_lds_sync();
+  for (int e = lane; e < G * kD; e += 64) st_coherent(dst + (size_t)(e / kD) * kPartStride + 2 + e % kD, scratch[e / kD][e % kD]);
+  wave_lds_sync();
 }
 
 // Combine the NW waves' history state into the split's partial.
@@ -684,13 +696,14 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
     qb1[mt] = hv ? sm.q.qc[h][2] * sl2 : 0.f;
   }
   __syncthreads();   // the query scratch is reused by the BF16 chunks and the weights
-  // BF16 chunk c (sink, then recent window) runs on workgroup c % S, wave (c / S) % NW
+  // BF16 tile u (sink, then recent window) runs on workgroup u % S and, from
+  // the last wave down, on the waves that hold the fewest history pages
   {
     const int S = a.n_splits;
     float *parts = a.part + (size_t)bh * (S + a.n_chunks) * G * kPartStride;
-    for (int c = split; c < a.n_chunks; c += S)
-      if (((c / S) % NW) == wave)
-        bf16_chunk_partial<GH>(a, b, kv, c, sm.wave[wave].ps, parts + (size_t)(S + c) * G * kPartStride);
+    for (int u = split; u < a.n_chunks; u += S)
+      if (NW - 1 - (u / S) % NW == wave)
+        bf16_tile_partial<GH>(a, b, kv, u, sm.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
   }
   HistState<MT> st;
 #pragma unroll
@@ -799,17 +812,21 @@ __device__ void run_scan_valu(const DecArgs &a, int b, int kv, int split, float 
   write_split_partial<MT, GH, NW, false>(sm, G, dst, false);
 }
 
-// Merge of one (sequence, KV head): history splits (rotated basis) -> R_V^T;
-// BF16 chunks; combine; normalise.  U_V rows are fetched first so that their
-// latency overlaps the partial loads.
-template <int GH>
+// Merge of one (sequence, KV head), by the last workgroup to finish its
+// split: log-sum-exp merge of the history splits (rotated basis), then P, H
+// and U_V^T once; merge of the BF16 tiles; combine and normalise.  Partials
+// written by other workgroups are read with device-coherent loads, issued in
+// batches so that the merge costs a few memory round trips, not one per
+// partial.  U_V rows are fetched first so that their latency overlaps.
+template <int GH, int NT>
 __device__ void merge_item(const DecArgs &a, int b, int kv, const float *parts, MergeSmem<GH> &sm) {
+  // (head, channel pair) items per thread when each item takes all partials
+  constexpr int kItems = (GH * (kD / 2) + NT - 1) / NT;
   const PoolView &pv = a.pv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nwaves = blockDim.x >> 6;
   const int G = pv.hq / pv.hkv;
-  const int S = a.n_splits, NC = a.n_chunks;
-  const float *bparts = parts + (size_t)S * G * kPartStride;
+  const int S = a.n_splits, P = a.n_splits + a.n_chunks;
   // threads 0..255 own row k = t / 2 of U_V, channels 64 (t & 1) .. + 64
   const int krow = (tid >> 1) & (kD - 1), half = tid & 1;
   const float4 *urow = (const float4 *)(a.rv.U_V + (size_t)kv * kD * kD + (size_t)krow * kD + 64 * half);
@@ -818,55 +835,141 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *parts, 
 #pragma unroll
     for (int i = 0; i < 16; ++i) u[i] = urow[i];
   }
-  // 1) per head: history split weights w_s = 2^(m_s - M); BF16 chunk max
+  asm volatile("" ::: "memory");   // keep the U_V loads here, ahead of the partials
+  // 1) one round of device-coherent loads: the first kPer partials of each
+  // thread's slice (thread -> head, channel pair, slice; 8 bytes each) into
+  // registers, and the (m, l) headers of every partial into LDS.  Further
+  // rounds (only when P > kPer * slices) reload values in step 3.
+  constexpr int kPer = kItems == 1 ? 18 : 8;   // one round covers 3 x 18 = 54 partials at G = 4
+  const int npair = G * (kD / 2);
+  const int nsl = min(kMergeSlices, min(max(1, NT / npair), 24 / G));
+  const int nitem = npair * nsl;   // <= kItems * NT
+  const int rounds = (P + nsl * kPer - 1) / (nsl * kPer);
+  float2 val[kItems][kPer];
+#pragma unroll
+  for (int it = 0; it < kItems; ++it) {
+    const int e = tid + it * NT;
+    if (e >= nitem) break;
+    const int pr = e % npair, sl = e / npair;
+    const int h = pr / (kD / 2), c = 2 * (pr % (kD / 2));
+    const float *col = parts + (size_t)h * kPartStride + 2 + c;
+    const size_t st = (size_t)G * kPartStride;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int p = sl + nsl * j;
+      val[it][j] = p < P ? ld_coherent2(col + (size_t)p * st) : make_float2(0.f, 0.f);
+    }
+  }
+  for (int e = tid; e < P * G; e += blockDim.x) {   // partial e / G, head e % G
+    const float2 hv = ld_coherent2(parts + (size_t)e * kPartStride);
+    sm.ml[e / G][e % G][0] = hv.x;
+    sm.ml[e / G][e % G][1] = hv.y;
+  }
+  __syncthreads();
+  // 2) per head: maxima, weights, denominators
   for (int h = wave; h < G; h += nwaves) {
-    float M = -INFINITY;
-    for (int sp = lane; sp < S; sp += 64) {
-      const float m = ld_coherent(parts + ((size_t)sp * G + h) * kPartStride);
-      sm.ws[h][sp] = m;
-      M = fmaxf(M, m);
+    float Mh = -INFINITY, Mb = -INFINITY;
+    for (int p = lane; p < P; p += 64) {
+      const float m = sm.ml[p][h][0];
+      if (p < S) Mh = fmaxf(Mh, m);
+      else Mb = fmaxf(Mb, m);
     }
-    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-    float l = 0.f;
-    for (int sp = lane; sp < S; sp += 64) {
-      const float m = sm.ws[h][sp];
-      const float w = (M > -INFINITY && m > -INFINITY) ? exp2_fast(m - M) : 0.f;
-      sm.ws[h][sp] = w;
-      l = fmaf(w, ld_coherent(parts + ((size_t)sp * G + h) * kPartStride + 1), l);
+    for (int o = 32; o > 0; o >>= 1) {
+      Mh = fmaxf(Mh, __shfl_xor(Mh, o, 64));
+      Mb = fmaxf(Mb, __shfl_xor(Mb, o, 64));
     }
-    for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
+    float lh = 0.f, lb = 0.f;
+    for (int p = lane; p < P; p += 64) {
+      const float m = sm.ml[p][h][0];
+      const float ref = p < S ? Mh : Mb;
+      const float w = m > -INFINITY ? exp2_fast(m - ref) : 0.f;
+      sm.wgt[p][h] = w;
+      if (p < S) lh = fmaf(w, sm.ml[p][h][1], lh);
+      else lb = fmaf(w, sm.ml[p][h][1], lb);
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      lh += __shfl_xor(lh, o, 64);
+      lb += __shfl_xor(lb, o, 64);
+    }
     if (lane == 0) {
-      sm.hm[h] = M;
-      sm.hl[h] = l;
+      const float Mt = fmaxf(Mh, Mb);
+      const float ah = Mh > -INFINITY ? exp2_fast(Mh - Mt) : 0.f;
+      const float ab = Mb > -INFINITY ? exp2_fast(Mb - Mt) : 0.f;
+      const float den = ah * lh + ab * lb;
+      sm.hs[h][0] = ah;
+      sm.hs[h][1] = ab;
+      sm.hs[h][2] = den > 0.f ? 1.0f / den : 0.f;
     }
   }
   __syncthreads();
-  // 2) weighted history sums, scattered through the permutation: (o P)[j] = o[bitrev(j)]
+  // 3) weighted sums per slice (first round from registers, further rounds
+  // reload), then the slices are added in a fixed order
+#pragma unroll
+  for (int it = 0; it < kItems; ++it) {
+    const int e = tid + it * NT;
+    if (e >= nitem) break;
+    const int pr = e % npair, sl = e / npair;
+    const int h = pr / (kD / 2), c = 2 * (pr % (kD / 2));
+    const float *hb = parts + (size_t)h * kPartStride;
+    const size_t st = (size_t)G * kPartStride;
+    float hx = 0.f, hy = 0.f, bx = 0.f, by = 0.f;
+    for (int r = 0; r < rounds; ++r) {
+      const int p_base = nsl * kPer * r;
+      float2 v[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int p = p_base + sl + nsl * j;
+        v[j] = r == 0 ? val[it][j] : (p < P ? ld_coherent2(hb + (size_t)p * st + 2 + c) : make_float2(0.f, 0.f));
+      }
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int p = p_base + sl + nsl * j;
+        if (p < S) {
+          const float w = sm.wgt[p][h];
+          hx = fmaf(w, v[j].x, hx);
+          hy = fmaf(w, v[j].y, hy);
+        } else if (p < P) {
+          const float w = sm.wgt[p][h];
+          bx = fmaf(w, v[j].x, bx);
+          by = fmaf(w, v[j].y, by);
+        }
+      }
+    }
+    float *rh = sm.red[0] + (size_t)sl * G * kD + h * kD + c;
+    float *rb = sm.red[1] + (size_t)sl * G * kD + h * kD + c;
+    rh[0] = hx;
+    rh[1] = hy;
+    rb[0] = bx;
+    rb[1] = by;
+  }
+  __syncthreads();
   for (int idx = tid; idx < G * kD; idx += blockDim.x) {
     const int h = idx / kD, c = idx % kD;
-    const float *p = parts + (size_t)h * kPartStride + 2 + c;
-    const size_t st = (size_t)G * kPartStride;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int sp = 0;
-    for (; sp + 8 <= S; sp += 8) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(sm.ws[h][sp + i], ld_coherent(p + (size_t)(sp + i) * st), acc[i]);
+    float acc_h = 0.f, acc_b = 0.f;
+    for (int sl = 0; sl < nsl; ++sl) {
+      acc_h += sm.red[0][(size_t)sl * G * kD + idx];
+      acc_b += sm.red[1][(size_t)sl * G * kD + idx];
     }
-    for (; sp < S; ++sp) acc[0] = fmaf(sm.ws[h][sp], ld_coherent(p + (size_t)sp * st), acc[0]);
-    sm.zs[h][bitrev7(c)] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+    sm.zs[h][bitrev7(c)] = acc_h;   // (o P)[j] = o[bitrev(j)]
+    sm.ob[h][c] = acc_b;
   }
   __syncthreads();
-  for (int hs = 1; hs < kD; hs <<= 1) {
-    for (int e = tid; e < G * 64; e += blockDim.x) {
-      const int h = e >> 6, pr = e & 63;
-      const int i0 = (pr / hs) * (2 * hs) + (pr % hs);
-      const float x0 = sm.zs[h][i0], x1 = sm.zs[h][i0 + hs];
-      sm.zs[h][i0] = x0 + x1;
-      sm.zs[h][i0 + hs] = x0 - x1;
+  // Walsh-Hadamard butterfly of each head's permuted sum, one wave per head:
+  // lane l holds elements l and l + 64 (stage 64 in registers, the rest by
+  // lane exchanges)
+  for (int h = wave; h < G; h += nwaves) {
+    float x0 = sm.zs[h][lane], x1 = sm.zs[h][lane + 64];
+#pragma unroll
+    for (int hs = 1; hs < 64; hs <<= 1) {
+      const float o0 = __shfl_xor(x0, hs, 64), o1 = __shfl_xor(x1, hs, 64);
+      x0 = (lane & hs) ? o0 - x0 : x0 + o0;
+      x1 = (lane & hs) ? o1 - x1 : x1 + o1;
     }
-    __syncthreads();
+    sm.zs[h][lane] = x0 + x1;
+    sm.zs[h][lane + 64] = x0 - x1;
   }
-  // 3) o_hist[h][k] = sum_j z[h][j] U_V[k][j] / sqrt(d)
+  __syncthreads();
+  // 4) o_hist[h][k] = sum_j z[h][j] U_V[k][j] / sqrt(d)
   if (tid < 2 * kD) {
     for (int h = 0; h < G; ++h) {
       const float4 *zr = (const float4 *)(&sm.zs[h][64 * half]);
@@ -881,27 +984,10 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *parts, 
     }
   }
   __syncthreads();
-  // 4) BF16 chunks and the history part, normalised
+  // 5) combine and normalise
   for (int idx = tid; idx < G * kD; idx += blockDim.x) {
     const int h = idx / kD, c = idx % kD;
-    float Mb = -INFINITY;
-    for (int cc = 0; cc < NC; ++cc) Mb = fmaxf(Mb, ld_coherent(bparts + ((size_t)cc * G + h) * kPartStride));
-    const float Mh = sm.hm[h];
-    const float Mt = fmaxf(Mh, Mb);
-    float res = 0.f;
-    if (Mt > -INFINITY) {
-      const float wh = Mh > -INFINITY ? exp2_fast(Mh - Mt) : 0.f;
-      float num = wh * sm.ot[h][c], den = wh * sm.hl[h];
-      for (int cc = 0; cc < NC; ++cc) {
-        const float *pb = bparts + ((size_t)cc * G + h) * kPartStride;
-        const float mb = ld_coherent(pb);
-        if (mb == -INFINITY) continue;
-        const float wb = exp2_fast(mb - Mt);
-        num = fmaf(wb, ld_coherent(pb + 2 + c), num);
-        den = fmaf(wb, ld_coherent(pb + 1), den);
-      }
-      res = num / den;
-    }
+    const float res = (sm.hs[h][0] * sm.ot[h][c] + sm.hs[h][1] * sm.ob[h][c]) * sm.hs[h][2];
     a.out[((size_t)b * pv.hq + (size_t)kv * G + h) * kD + c] = res;
   }
 }
@@ -923,10 +1009,10 @@ decode_scan_kernel(DecArgs a) {
   float *parts = a.part + (size_t)bh * (S + a.n_chunks) * G * kPartStride;
   __shared__ ScanUnion<MT, GH, NW, MFMA> sm;
   if constexpr (!MFMA) {
-    // BF16 chunk c runs on workgroup c % S, wave (c / S) % NW, before its pages
-    for (int c = split; c < a.n_chunks; c += S) {
-      if (((c / S) % NW) == wave)
-        bf16_chunk_partial<GH>(a, b, kv, c, sm.s.wave[wave].ps, parts + (size_t)(S + c) * G * kPartStride);
+    // BF16 tile u runs on workgroup u % S, wave (u / S) % NW, before its pages
+    for (int u = split; u < a.n_chunks; u += S) {
+      if (((u / S) % NW) == wave)
+        bf16_tile_partial<GH>(a, b, kv, u, sm.s.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
     }
   }
   float *dst = parts + (size_t)split * G * kPartStride;
@@ -934,7 +1020,7 @@ decode_scan_kernel(DecArgs a) {
   else run_scan_valu<MT, GH, NW>(a, b, kv, split, dst, sm.s);
   __shared__ int last_flag;
   if (!arrive_last(&a.counters[bh], S, &last_flag)) return;
-  merge_item<GH>(a, b, kv, parts, sm.g);
+  merge_item<GH, 64 * NW>(a, b, kv, parts, sm.g);
 }
 
 }  // namespace
@@ -965,8 +1051,9 @@ DecodePlan make_decode_plan(int batch, int hkv, int hq, int max_pages, int sink,
   S = S < 1 ? 1 : S;
   S = S > max_by_pages ? max_by_pages : S;
   S = S > kMaxSplits ? kMaxSplits : S;
+  p.n_chunks = (sink + recent) / kTileTokens;
+  S = S > kMaxParts - p.n_chunks ? kMaxParts - p.n_chunks : S;
   p.n_splits = S;
-  p.n_chunks = sink / kPageTokens + recent / kPageTokens;
   p.pages_per_split = max_pages > 0 ? (max_pages + S - 1) / S : 1;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t off = 0;

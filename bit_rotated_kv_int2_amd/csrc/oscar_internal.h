@@ -20,6 +20,7 @@ constexpr int kKMeta = OSCAR_PAGE_KMETA;
 constexpr int kVMeta = OSCAR_PAGE_VMETA;
 constexpr int kMaxGroupHeads = 16;          // Hq / Hkv supported
 constexpr int kPartStride = 132;            // floats per (m, l, o[128]) partial, padded
+constexpr int kTileTokens = 16;             // BF16 window tokens per decode tile
 
 // Bit reversal of a 7-bit channel index (d = 128).
 __host__ __device__ constexpr int bitrev7(int p) {
@@ -57,6 +58,12 @@ __device__ __forceinline__ void st_coherent(float *p, float v) {
 __device__ __forceinline__ float ld_coherent(const float *p) {
   return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Two adjacent floats (8-byte aligned) in one device-coherent load.
+__device__ __forceinline__ float2 ld_coherent2(const float *p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t *>(const_cast<float *>(p)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
 __device__ __forceinline__ void stores_complete() { __builtin_amdgcn_s_waitcnt(0); }
 // Returns true in every thread of the workgroup that arrives last of `total`
 // at counter *c, and resets the counter for the next call.
@@ -92,7 +99,7 @@ struct RotView {
 // Decode workspace carve-up (offsets in bytes from the workspace base).
 struct DecodePlan {
   int n_splits;          // history splits per (sequence, kv head)
-  int n_chunks;          // 64-token BF16 chunks (sink + recent window)
+  int n_chunks;          // 16-token BF16 tiles (sink + recent window)
   int pages_per_split;
   size_t off_counters;   // int [B*Hkv] completion counters, zero between calls
   size_t off_qconst;     // float [B*Hkv][GH][4]

@@ -146,6 +146,65 @@ __device__ __forceinline__ void bf16_chunk(const uint16_t *K, const uint16_t *V,
   wave_lds_sync();
 }
 
+// BF16 attention of one 16-token tile for one wave, from a fresh state.
+//   K, V: 16 bf16 rows of 128 channels; the first `valid` (1..16) are real
+//   tokens (rows past them are re-read from row valid - 1 and masked).  All
+//   eight 16-byte loads per lane are issued together.  Outputs (log2 units):
+//   m[i], l[i] for head 4 q + i (row-uniform), o[h][8] = sum over this
+//   lane's token phase (tokens q, q + 4, q + 8, q + 12) of p V for channels
+//   8 n .. 8 n + 7, relative to m.  ps: [GH][>= 16] LDS scratch of the wave.
+template <int GH>
+__device__ __forceinline__ void bf16_tile(const uint16_t *K, const uint16_t *V, int valid, int G,
+                                          const v8bf (&Aq)[4], float sl2, float (&m)[4], float (&l)[4],
+                                          float (&o)[GH][8], float (*ps)[kD]) {
+  const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+  const uint16_t *kr = K + (size_t)min(n, valid - 1) * kD + 32 * q;
+  uint4 kk[4], vv[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) kk[ks] = *(const uint4 *)(kr + 8 * ks);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vv[i] = *(const uint4 *)(V + (size_t)min(q + 4 * i, valid - 1) * kD + 8 * n);
+  v4f C = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) C = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aq[ks], as_v8bf(kk[ks]), C, 0, 0, 0);
+  const bool ok = n < valid;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lg = ok ? C[i] * sl2 : -INFINITY;
+    m[i] = row16_max(lg);
+    const float e = exp2_fast(lg - m[i]);   // valid >= 1: m is finite
+    l[i] = row16_sum(e);
+    const int h = 4 * q + i;
+    if (h < G) ps[h][n] = e;
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int h = 0; h < GH; ++h) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[h][c] = 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float vf[8];
+    vf[0] = __uint_as_float(vv[i].x << 16);
+    vf[1] = __uint_as_float(vv[i].x & 0xFFFF0000u);
+    vf[2] = __uint_as_float(vv[i].y << 16);
+    vf[3] = __uint_as_float(vv[i].y & 0xFFFF0000u);
+    vf[4] = __uint_as_float(vv[i].z << 16);
+    vf[5] = __uint_as_float(vv[i].z & 0xFFFF0000u);
+    vf[6] = __uint_as_float(vv[i].w << 16);
+    vf[7] = __uint_as_float(vv[i].w & 0xFFFF0000u);
+#pragma unroll
+    for (int h = 0; h < GH; ++h) {
+      if (h >= G) break;
+      const float p = ps[h][q + 4 * i];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) o[h][c] = fmaf(p, vf[c], o[h][c]);
+    }
+  }
+  wave_lds_sync();
+}
+
 // Load the bf16 query rows of the G heads of one KV head as the A operand.
 __device__ __forceinline__ void load_bf16_query(const uint16_t *qbase, int G, v8bf (&Aq)[4]) {
   const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;

@@ -86,7 +86,8 @@ typedef struct oscar_params {
   int32_t num_kv_heads; /* Hkv >= 1 */
   int32_t num_q_heads;  /* Hq, a multiple of Hkv; Hq/Hkv <= 16 */
   int32_t sink;         /* S0: BF16 sink tokens, multiple of 64, default 64 */
-  int32_t recent;       /* W: BF16 recent-window tokens, multiple of 64, default 256 */
+  int32_t recent;       /* W: BF16 recent-window tokens, multiple of 64, default 256;
+                           sink + recent <= 4096 */
   int32_t page_tokens;  /* must be 64 */
   int32_t group;        /* quantisation group G_K, must be 64 */
   float sm_scale;       /* softmax scale, usually 1/sqrt(head_dim) */
