@@ -255,6 +255,84 @@ def run_workload(wb, steps, warmup, decode_reps, bf16_fit=None):
 
 
 # ---------------------------------------------------------------------------
+# Long shared prefix: bulk quantise-pack of the prefix, then decode
+# ---------------------------------------------------------------------------
+
+def run_prefix(n_cal, write_reps=5, decode_reps=20):
+    """Batch 16 x 131072 tokens, 8 KV / 96 query heads, one 98304-token
+    prefix on shared pages and one shared sink slot; one layer.
+
+    - The bulk prefill-time quantise-pack of the prefix (one append of 98304
+      tokens x 8 KV heads through the write kernels) is timed on its own,
+      write_reps times into the same pages (seq_lens reset in between).
+    - Then every sequence is completed and the decode attention timed.
+      Logical bytes count the shared pages once per sequence; unique bytes
+      count them once."""
+    import torch
+    from bit_rotated_kv_int2_amd import oscar as O
+    from bit_rotated_kv_int2_amd import synth
+    wl = synth.WORKLOADS["prefix-128k-b16-gqa12"]
+    params = O.make_params(wl.n_kv, wl.n_q)
+    rot = calibrate_layer(O, synth, wl, 0, params, n_cal)
+    lengths = synth.sequence_lengths(wl)
+    bt, total = synth.block_table(wl, lengths)
+    pool = O.KVPool(params, wl.batch, total, bt, sink_slot=np.zeros(wl.batch, np.int32), n_sink_slots=1,
+                    zero_pages=False)
+    P = wl.shared_prefix
+    kp, vp = gpu_kv(torch, synth, wl, 0, 0, P)
+    kp, vp = kp[None].contiguous(), vp[None].contiguous()
+    O.quantize_append(params, rot, pool, kp, vp, seq=0)   # warm
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(write_reps)]
+    for e0, e1 in ev:
+        pool.seq_lens.zero_()
+        e0.record()
+        O.quantize_append(params, rot, pool, kp, vp, seq=0)
+        e1.record()
+    torch.cuda.synchronize()
+    assert int(pool.error_flags.item()) == 0 and int(pool.seq_lens[0].item()) == P
+    write_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    del kp, vp
+    # complete sequence 0 with its private suffix, then every other sequence
+    k, v = gpu_kv(torch, synth, wl, 0, 0, int(lengths[0]))
+    O.quantize_append(params, rot, pool, k[P:][None].contiguous(), v[P:][None].contiguous(), seq=0)
+    del k, v
+    for b in range(1, wl.batch):
+        k, v = gpu_kv(torch, synth, wl, 0, b, int(lengths[b]))
+        O.quantize_append(params, rot, pool, k[None], v[None], seq=b)
+        del k, v
+    torch.cuda.synchronize()
+    assert int(pool.error_flags.item()) == 0
+    ws = O.alloc_workspace(O.decode_workspace_size(params, wl.batch, pool.max_pages))
+    out = torch.zeros((wl.batch, wl.n_q, D), dtype=torch.float32, device="cuda")
+    q = torch.from_numpy(synth.decode_queries(wl, 0).view(np.int16)).cuda()
+    O.decode_attention(params, rot, pool, q, out, ws)
+    d0 = torch.cuda.Event(enable_timing=True)
+    d1 = torch.cuda.Event(enable_timing=True)
+    d0.record()
+    for _ in range(decode_reps):
+        O.decode_attention(params, rot, pool, q, out, ws)
+    d1.record()
+    torch.cuda.synchronize()
+    assert int(pool.error_flags.item()) == 0
+    dec_us = d0.elapsed_time(d1) * 1e3 / decode_reps
+    n_hist = np.maximum(0, lengths.astype(np.int64) - wl.sink - wl.recent)
+    win = np.minimum(lengths.astype(np.int64), wl.sink + wl.recent)
+    out_bytes = wl.batch * wl.n_q * D * 4
+    logical = int(np.sum(n_hist)) * wl.n_kv * HIST_BYTES_PER_TOKEN_HEAD + \
+        int(np.sum(win)) * wl.n_kv * WIN_BYTES_PER_TOKEN_HEAD + out_bytes
+    shared_hist = (P - wl.sink) * wl.n_kv * HIST_BYTES_PER_TOKEN_HEAD
+    unique = logical - (wl.batch - 1) * shared_hist - (wl.batch - 1) * wl.sink * wl.n_kv * WIN_BYTES_PER_TOKEN_HEAD
+    return {"workload": wl.name, "prefix_tokens": P, "kv_heads": wl.n_kv,
+            "quantize_pack_ms": write_ms,
+            "quantize_pack_tokens_per_s": P / (write_ms * 1e-3),
+            "quantize_pack_token_heads_per_s": P * wl.n_kv / (write_ms * 1e-3),
+            "decode_us_per_layer": dec_us,
+            "decode_gbps_logical": logical / (dec_us * 1e-6) / 1e9,
+            "decode_gbps_unique": unique / (dec_us * 1e-6) / 1e9,
+            "note": "one layer; logical bytes read the shared prefix once per sequence, unique bytes once"}
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline: the oracle's decode on a bounded sample of the same workload
 # ---------------------------------------------------------------------------
 
@@ -313,7 +391,9 @@ def main():
     ap.add_argument("--n-cal", type=int, default=512)
     ap.add_argument("--no-batch1", action="store_true", help="skip the batch-1 secondary workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--variant", type=int, default=0, help="0 = MFMA int8 history kernel, 1 = VALU")
+    ap.add_argument("--no-prefix", action="store_true",
+                    help="skip the long shared-prefix workload (bulk quantise-pack + decode)")
+    ap.add_argument("--variant", type=int, default=0, help="0 = MFMA int8 history kernel, 1 = VALU, 2 = MFMA on the split grid only")
     ap.add_argument("--bf16-budget-gb", type=float, default=48.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="end with one plain device-to-device copy of this many MiB (scales HBM counters)")
@@ -362,6 +442,12 @@ def main():
         del wb1
         torch.cuda.empty_cache()
 
+    prefix = None
+    if not args.no_prefix:
+        prefix = run_prefix(args.n_cal)
+        log(f"prefix: {json.dumps(prefix)}")
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         # about 15 s of oracle decode: 8 (sequence, KV head) pairs at full length, 20 runs each
@@ -406,6 +492,7 @@ def main():
         "effective_bits_per_kv_element": round(effective_bpe(float(np.mean(synth.sequence_lengths(wl)))), 4),
         "pages_bits_per_kv_element": 2.28,
         "batch1": batch1,
+        "long_prefix": prefix,
         "cpu_baseline": cpu,
     }
     if args.copy_probe_mib:

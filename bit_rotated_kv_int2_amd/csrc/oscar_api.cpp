@@ -104,7 +104,8 @@ int32_t oscar_set_history_timing_events(void *start_event, void *stop_event) {
 }
 
 int32_t oscar_set_decode_variant(int32_t variant) {
-  if (variant != 0 && variant != 1) return fail(OSCAR_EINVAL, "variant must be 0 (MFMA) or 1 (VALU)");
+  if (variant < 0 || variant > 2)
+    return fail(OSCAR_EINVAL, "variant must be 0 (MFMA), 1 (VALU) or 2 (MFMA, grid partition)");
   g_variant = variant;
   return ok();
 }

@@ -60,8 +60,10 @@ struct DecArgs {
   int *counters;       // [BH]
   float *qconst;       // [BH][GH][4]: delta, Q0, Q1 (VALU variant)
   float *qrot;         // [BH][GH][kD] float q~ (VALU variant)
-  float *part;         // [BH][n_splits + n_chunks][G][kPartStride]: history splits, then BF16 chunks
-  int n_splits, n_chunks, pages_per_split;
+  float *part;         // grid path: [BH][n_splits + n_chunks][G][kPartStride] (history splits, then
+                       // BF16 tiles); balanced path: history partials [n_blocks + BH][G][kPartStride]
+  float *part_tile;    // balanced path: BF16 tile partials [BH][n_chunks][G][kPartStride]
+  int n_splits, n_chunks, pages_per_split, n_blocks;
 };
 
 __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
@@ -203,6 +205,104 @@ __device__ void query_prep(const DecArgs &a, int b, int kv, QSmem<MT, GH> &sm, f
       const int r = 4 * (h & 3) + 2 * g;
       base[(r + 16 * kg) * 16 + 4 * s + bb] = (int8_t)hi;
       base[(r + 1 + 16 * kg) * 16 + 4 * s + bb] = (int8_t)lo;
+    }
+  }
+  __syncthreads();
+}
+
+// Query preparation of up to K (sequence, KV head) items at once: thread
+// group k (threads 256 k .. 256 k + 255) forms item k's projections, then one
+// wave per (item, head) runs the butterfly and the quantisation.  ys is LDS
+// scratch [K][4][kD]; results go to aq[k] (A operands) and qc[k] (constants).
+// One M-tile of heads (G <= 4); needs blockDim.x >= 256 K.
+template <int K>
+__device__ void query_prep_multi(const DecArgs &a, const int (&bb)[K], const int (&kk)[K], int nitems,
+                                 float (*ys)[4][kD], v4i (*aq)[2 * 64], float (*qc)[4][4]) {
+  const PoolView &pv = a.pv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
+  const int G = pv.hq / pv.hkv;
+  const int grp = tid >> 8, t = tid & 255;
+  if (grp < nitems) {
+    int b = bb[0], kv = kk[0];
+#pragma unroll
+    for (int k = 1; k < K; ++k)
+      if (grp == k) b = bb[k], kv = kk[k];
+    const float *U = a.rv.U_K + (size_t)kv * kD * kD;
+    const uint16_t *qb = a.q + ((size_t)b * pv.hq + (size_t)kv * G) * kD;
+    const int c = t >> 3, k8 = t & 7;
+    float4 u[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) u[i] = *(const float4 *)(U + (size_t)(k8 + 8 * i) * kD + 4 * c);
+    for (int h = 0; h < G; ++h) {
+      const uint16_t *qr = qb + (size_t)h * kD;
+      float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float qv = bf16_to_f32(qr[k8 + 8 * i]);
+        y0 = fmaf(qv, u[i].x, y0);
+        y1 = fmaf(qv, u[i].y, y1);
+        y2 = fmaf(qv, u[i].z, y2);
+        y3 = fmaf(qv, u[i].w, y3);
+      }
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        y0 += __shfl_xor(y0, o, 64);
+        y1 += __shfl_xor(y1, o, 64);
+        y2 += __shfl_xor(y2, o, 64);
+        y3 += __shfl_xor(y3, o, 64);
+      }
+      if (k8 == 0) {
+        ys[grp][h][4 * c] = y0;
+        ys[grp][h][4 * c + 1] = y1;
+        ys[grp][h][4 * c + 2] = y2;
+        ys[grp][h][4 * c + 3] = y3;
+      }
+    }
+  }
+  for (int e = tid; e < nitems * 2 * 64 * 4; e += blockDim.x) ((uint32_t *)aq)[e] = 0;
+  __syncthreads();
+  for (int wi = w; wi < nitems * G; wi += nw) {
+    const int k = wi / G, h = wi % G;
+    float x0 = ys[k][h][lane], x1 = ys[k][h][lane + 64];
+#pragma unroll
+    for (int hs = 1; hs < 64; hs <<= 1) {
+      const float o0 = __shfl_xor(x0, hs, 64), o1 = __shfl_xor(x1, hs, 64);
+      x0 = (lane & hs) ? o0 - x0 : x0 + o0;
+      x1 = (lane & hs) ? o1 - x1 : x1 + o1;
+    }
+    ys[k][h][lane] = x0 + x1;
+    ys[k][h][lane + 64] = x0 - x1;
+    wave_lds_sync();
+    const float v0 = ys[k][h][bitrev7(lane)] * kInvSqrtDf;
+    const float v1 = ys[k][h][bitrev7(lane + 64)] * kInvSqrtDf;
+    float mx = fmaxf(fabsf(v0), fabsf(v1));
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    const float delta = mx > 0.f ? mx / 32639.0f : 1.0f;
+    const int q0 = max(-32639, min(32639, (int)rintf(v0 / delta)));
+    const int q1 = max(-32639, min(32639, (int)rintf(v1 / delta)));
+    int s0 = q0, s1 = q1;
+    for (int o = 32; o > 0; o >>= 1) {
+      s0 += __shfl_xor(s0, o, 64);
+      s1 += __shfl_xor(s1, o, 64);
+    }
+    if (lane == 0) {
+      qc[k][h][0] = delta;
+      qc[k][h][1] = delta * (float)s0;   // |sum| < 2^24: exact
+      qc[k][h][2] = delta * (float)s1;
+      qc[k][h][3] = 0.f;
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int c = lane + 64 * half;
+      const int qi = half ? q1 : q0;
+      const int lo = (int)(int8_t)(qi & 0xFF);
+      const int hi = (qi - lo) >> 8;
+      const int kg = c >> 5, ks = (c >> 4) & 1, bb8 = (c >> 2) & 3, sb = c & 3;
+      const int g = c >> 6;
+      int8_t *base = (int8_t *)(aq[k] + ks * 64);
+      const int r = 4 * h + 2 * g;
+      base[(r + 16 * kg) * 16 + 4 * sb + bb8] = (int8_t)hi;
+      base[(r + 1 + 16 * kg) * 16 + 4 * sb + bb8] = (int8_t)lo;
     }
   }
   __syncthreads();
@@ -499,19 +599,38 @@ __device__ __forceinline__ void wait_pages(int n) {
 // Wait for this wave's LDS reads (a page buffer may then be refilled).
 __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// Copy one 5120-byte page to LDS: five 1 KB DMA loads; lane i moves bytes
-// [16 i, 16 i + 16) of each kilobyte.  base and lds are wave-uniform.
-__device__ __forceinline__ void dma_page(uint64_t base, uint32_t lds, uint32_t lane_off) {
-#pragma unroll
-  for (int j = 0; j < kPageBytes / 1024; ++j)
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :
-                 : "s"(lds + 1024u * j), "v"(lane_off + 1024u * j), "s"(base)
-                 : "memory", "m0");
+// One 1 KB LDS-DMA copy: lane i moves bytes [16 i, 16 i + 16).  src and lds
+// are wave-uniform.  M0 (the LDS destination) is saved and restored inside
+// the asm, so the compiler's own use of M0 is unaffected.  The readfirstlane
+// builtin returns int: both halves of src go back through uint32_t so that
+// the low half is zero-extended (a sign-extended low half would set every
+// bit of the high half when its bit 31 is set).
+__device__ __forceinline__ void dma_1k(uint64_t src, uint32_t lds, uint32_t lane_off) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)src);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(src >> 32));
+  src = ((uint64_t)hi << 32) | (uint64_t)lo;
+  lds = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(lane_off), "s"(src)
+      : "memory");
 }
 
-template <int GH>
+// Copy one 5120-byte page to LDS: five 1 KB DMA copies (kilobyte j of the
+// page from base + 1024 j to lds + 1024 j; lane_off = 16 lane).
+__device__ __forceinline__ void dma_page(uint64_t base, uint32_t lds, uint32_t lane_off) {
+#pragma unroll
+  for (int j = 0; j < kPageBytes / 1024; ++j) dma_1k(base + 1024u * j, lds + 1024u * j, lane_off);
+}
+
+template <int GH, bool UVL = false>
 struct MergeSmem {
+  float uv[UVL ? kD : 1][kD];   // U_V of the KV head, staged by LDS DMA (UVL)
   float ml[kMaxParts][GH][2];   // (m, l) of every partial: history splits, then BF16 tiles
   float wgt[kMaxParts][GH];     // merge weight of every partial
   float hs[GH][4];              // per head: history scale, tile scale, 1 / denominator
@@ -632,80 +751,93 @@ __device__ void write_split_partial(ScanSmem<MT, GH, NW, MFMA> &sm, int G, float
   }
 }
 
-template <int MT, int GH, int NW>
-__device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float *dst,
-                              ScanSmem<MT, GH, NW, true> &sm) {
-  constexpr int PF = ScanSmem<MT, GH, NW, true>::PF;
-  const PoolView &pv = a.pv;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+// History page pipeline of one wave over the pages [pg0, pg1) of one
+// (sequence, KV head): the wave takes pages first + i * NW, i < npg, with up
+// to PF page copies in flight (LDS DMA).  Lane k of bt holds the block-table
+// entry of page index 64 c + k, c = the chunk of the next page issued.
+template <int NW, int PF>
+struct PagePipe {
+  const int32_t *btw;
+  const uint8_t *pbase;
+  size_t pstride;
+  uint4 (*bufs)[kPageBytes / 16];
+  uint32_t lds0;
+  int bt, first, npg, issued;
+  uint32_t inflight;   // bit j: page i + j (i = next page consumed) has a copy in flight
+  bool bad;
+};
+
+template <int NW, int PF>
+__device__ __forceinline__ void pipe_init(PagePipe<NW, PF> &p, const PoolView &pv, int b, int kv, int pg0, int pg1,
+                                          uint4 (*bufs)[kPageBytes / 16], int wave, int lane) {
+  p.first = pg0 + wave;
+  p.npg = p.first < pg1 ? (pg1 - p.first + NW - 1) / NW : 0;
+  p.btw = pv.block_table + (size_t)b * pv.max_pages + p.first;
+  p.bt = lane < p.npg ? p.btw[(size_t)lane * NW] : -1;
+  p.pbase = pv.pages + (size_t)kv * kPageBytes;
+  p.pstride = (size_t)pv.hkv * kPageBytes;
+  p.bufs = bufs;
+  p.lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4 *)bufs[0];
+  p.issued = 0;
+  p.inflight = 0;
+  p.bad = false;
+}
+
+// Start the copy of page j (j < npg) into buffer j % PF; false if its
+// block-table entry is out of range (then nothing is copied).
+template <int NW, int PF>
+__device__ __forceinline__ bool pipe_issue(PagePipe<NW, PF> &p, const PoolView &pv, int j, int lane) {
+  if ((j & 63) == 0 && j > 0) {
+    p.bt = j + lane < p.npg ? p.btw[(size_t)(j + lane) * NW] : -1;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+  const int ph = __builtin_amdgcn_readlane(p.bt, j & 63);
+  const bool ok = ph >= 0 && ph < pv.n_pages;
+  if (ok) {
+    const uint64_t base = (uint64_t)(uintptr_t)(p.pbase + (size_t)ph * p.pstride);
+    dma_page(base, p.lds0 + (uint32_t)(j % PF) * kPageBytes, 16u * lane);
+  } else {
+    p.bad = true;
+  }
+  return ok;
+}
+
+template <int NW, int PF>
+__device__ __forceinline__ void pipe_prologue(PagePipe<NW, PF> &p, const PoolView &pv, int lane) {
+  for (; p.issued < PF && p.issued < p.npg; ++p.issued)
+    if (pipe_issue(p, pv, p.issued, lane)) p.inflight |= 1u << p.issued;
+}
+
+// Consume every page of the pipeline (the prologue must have been issued).
+template <int MT, int NW, int PF>
+__device__ __forceinline__ void pipe_scan(PagePipe<NW, PF> &p, const PoolView &pv, int n_hist, const v4i (&Aq)[MT][2],
+                                          const float (&qa)[MT], const float (&qb0)[MT], const float (&qb1)[MT],
+                                          HistState<MT> &st, v4i *wl, int lane) {
   const int n = lane & 15, q = lane >> 4;
-  const int G = pv.hq / pv.hkv;
-  const int bh = b * pv.hkv + kv;
-  const int L = pv.seq_lens[b];
-  const int n_hist = max(0, L - pv.sink - pv.recent);
-  const int n_pages = (n_hist + kPageTokens - 1) / kPageTokens;
-  const int pg0 = split * a.pages_per_split;
-  const int pg1 = min(min(n_pages, pg0 + a.pages_per_split), pv.max_pages);
-  if (n_pages > pv.max_pages && split == 0 && tid == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_LENGTH);
-
-  // this wave's pages: first + i * NW, i < npg.  Lane k of bt holds the
-  // block-table entry of page 64 c + k, c = the chunk of the next page issued.
-  const int first = pg0 + wave;
-  const int npg = first < pg1 ? (pg1 - first + NW - 1) / NW : 0;
-  const int32_t *btw = pv.block_table + (size_t)b * pv.max_pages + first;
-  int bt = lane < npg ? btw[(size_t)lane * NW] : -1;
-  const uint8_t *pbase = pv.pages + (size_t)kv * kPageBytes;
-  const size_t pstride = (size_t)pv.hkv * kPageBytes;
-  uint4 (*bufs)[kPageBytes / 16] = sm.pbuf[wave];
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4 *)bufs[0];
-  bool bad = false;
-  uint32_t inflight = 0;   // bit j: page i + j (i = next page consumed) has a copy in flight
-  int issued = 0;
-  auto issue = [&](int j) {   // copy page j (j < npg) into buffer j % PF
-    if ((j & 63) == 0 && j > 0) {
-      bt = j + lane < npg ? btw[(size_t)(j + lane) * NW] : -1;
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    }
-    const int ph = __builtin_amdgcn_readlane(bt, j & 63);
-    const bool ok = ph >= 0 && ph < pv.n_pages;
+  for (int i = 0; i < p.npg; ++i) {
+    const bool ok = p.inflight & 1u;
+    PageRegs cur;
     if (ok) {
-      const uint64_t base = (uint64_t)(uintptr_t)(pbase + (size_t)ph * pstride);
-      dma_page(base, lds0 + (uint32_t)(j % PF) * kPageBytes, 16u * lane);
-    } else {
-      bad = true;
+      // copies issued after page i that may still be outstanding
+      wait_pages(__builtin_popcount(p.inflight >> 1));
+      load_page(cur, (const uint8_t *)p.bufs[i % PF], n, q);
+      wait_lds_reads();
     }
-    return ok;
-  };
-  for (; issued < PF && issued < npg; ++issued)
-    if (issue(issued)) inflight |= 1u << issued;
+    p.inflight >>= 1;
+    if (p.issued < p.npg) {
+      if (pipe_issue(p, pv, p.issued, lane)) p.inflight |= 1u << (PF - 1);
+      ++p.issued;
+    }
+    if (ok) {
+      const int valid = min(kPageTokens, n_hist - (p.first + i * NW) * kPageTokens);
+      if (valid == kPageTokens) int2_page<MT, true>(cur, valid, Aq, qa, qb0, qb1, st, wl);
+      else int2_page<MT, false>(cur, valid, Aq, qa, qb0, qb1, st, wl);
+    }
+  }
+}
 
-  // query operands, prepared by the workgroup while the first pages load
-  query_prep<MT, GH>(a, b, kv, sm.q, nullptr);
-  v4i Aq[MT][2];
-  float qa[MT], qb0[MT], qb1[MT];
-  const float sl2 = pv.sm_scale * kLog2e;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    Aq[mt][0] = sm.q.aq[(mt * 2 + 0) * 64 + lane];
-    Aq[mt][1] = sm.q.aq[(mt * 2 + 1) * 64 + lane];
-    const int h = min(4 * mt + q, GH - 1);
-    const bool hv = 4 * mt + q < G;
-    qa[mt] = hv ? sm.q.qc[h][0] * sl2 : 0.f;
-    qb0[mt] = hv ? sm.q.qc[h][1] * sl2 : 0.f;
-    qb1[mt] = hv ? sm.q.qc[h][2] * sl2 : 0.f;
-  }
-  __syncthreads();   // the query scratch is reused by the BF16 chunks and the weights
-  // BF16 tile u (sink, then recent window) runs on workgroup u % S and, from
-  // the last wave down, on the waves that hold the fewest history pages
-  {
-    const int S = a.n_splits;
-    float *parts = a.part + (size_t)bh * (S + a.n_chunks) * G * kPartStride;
-    for (int u = split; u < a.n_chunks; u += S)
-      if (NW - 1 - (u / S) % NW == wave)
-        bf16_tile_partial<GH>(a, b, kv, u, sm.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
-  }
-  HistState<MT> st;
+template <int MT>
+__device__ __forceinline__ void hist_reset(HistState<MT> &st) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     st.mref[mt] = -INFINITY;
@@ -713,35 +845,32 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) st.facc[mt][nt] = 0.f;
   }
-  v4i *wl = sm.wave[wave].wl;
-  // rows 4h + 3 of the weight operands stay zero; the rest is rewritten per page
+}
+
+// Query operands of one head group into registers, from prepared LDS copies.
+template <int MT, int GH>
+__device__ __forceinline__ void load_query_ops(const v4i *aq, const float (*qc)[4], int G, float sl2, int lane,
+                                               v4i (&Aq)[MT][2], float (&qa)[MT], float (&qb0)[MT],
+                                               float (&qb1)[MT]) {
+  const int q = lane >> 4;
 #pragma unroll
-  for (int i = 0; i < MT * 2; ++i) wl[i * 64 + lane] = v4i{0, 0, 0, 0};
-  // complete the query operands here (and with them the first copies), so that
-  // no wait for them is left inside the loop
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  for (int i = 0; i < npg; ++i) {
-    const bool ok = inflight & 1u;
-    PageRegs cur;
-    if (ok) {
-      // copies issued after page i that may still be outstanding
-      wait_pages(__builtin_popcount(inflight >> 1));
-      load_page(cur, (const uint8_t *)bufs[i % PF], n, q);
-      wait_lds_reads();
-    }
-    inflight >>= 1;
-    if (issued < npg) {
-      if (issue(issued)) inflight |= 1u << (PF - 1);
-      ++issued;
-    }
-    if (ok) {
-      const int valid = min(kPageTokens, n_hist - (first + i * NW) * kPageTokens);
-      if (valid == kPageTokens) int2_page<MT, true>(cur, valid, Aq, qa, qb0, qb1, st, wl);
-      else int2_page<MT, false>(cur, valid, Aq, qa, qb0, qb1, st, wl);
-    }
+  for (int mt = 0; mt < MT; ++mt) {
+    Aq[mt][0] = aq[(mt * 2 + 0) * 64 + lane];
+    Aq[mt][1] = aq[(mt * 2 + 1) * 64 + lane];
+    const int h = min(4 * mt + q, GH - 1);
+    const bool hv = 4 * mt + q < G;
+    qa[mt] = hv ? qc[h][0] * sl2 : 0.f;
+    qb0[mt] = hv ? qc[h][1] * sl2 : 0.f;
+    qb1[mt] = hv ? qc[h][2] * sl2 : 0.f;
   }
-  if (bad && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
-  __syncthreads();   // every wave is done with its page buffers (aliased by sm.o)
+}
+
+// Every wave's history state -> one (m, l, o) partial of the workgroup.
+// The page buffers must be idle (sm.o aliases them).
+template <int MT, int GH, int NW>
+__device__ void flush_partial(ScanSmem<MT, GH, NW, true> &sm, HistState<MT> &st, int G, float *dst) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, q = lane >> 4;
+  __syncthreads();
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const float l16 = row16_sum(st.lsum[mt]);
@@ -759,6 +888,55 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   }
   __syncthreads();
   write_split_partial<MT, GH, NW, true>(sm, G, dst, true);
+}
+
+template <int MT, int GH, int NW>
+__device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float *dst,
+                              ScanSmem<MT, GH, NW, true> &sm) {
+  constexpr int PF = ScanSmem<MT, GH, NW, true>::PF;
+  const PoolView &pv = a.pv;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = pv.hq / pv.hkv;
+  const int bh = b * pv.hkv + kv;
+  const int L = pv.seq_lens[b];
+  const int n_hist = max(0, L - pv.sink - pv.recent);
+  const int n_pages = (n_hist + kPageTokens - 1) / kPageTokens;
+  const int pg0 = split * a.pages_per_split;
+  const int pg1 = min(min(n_pages, pg0 + a.pages_per_split), pv.max_pages);
+  if (n_pages > pv.max_pages && split == 0 && tid == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_LENGTH);
+
+  PagePipe<NW, PF> pipe;
+  pipe_init(pipe, pv, b, kv, pg0, pg1, sm.pbuf[wave], wave, lane);
+  pipe_prologue(pipe, pv, lane);
+
+  // query operands, prepared by the workgroup while the first pages load
+  query_prep<MT, GH>(a, b, kv, sm.q, nullptr);
+  v4i Aq[MT][2];
+  float qa[MT], qb0[MT], qb1[MT];
+  load_query_ops<MT, GH>(sm.q.aq, sm.q.qc, G, pv.sm_scale * kLog2e, lane, Aq, qa, qb0, qb1);
+  __syncthreads();   // the query scratch is reused by the BF16 tiles and the weights
+  // BF16 tile u (sink, then recent window) runs on workgroup u % S and, from
+  // the last wave down, on the waves that hold the fewest history pages
+  {
+    const int S = a.n_splits;
+    float *parts = a.part + (size_t)bh * (S + a.n_chunks) * G * kPartStride;
+    for (int u = split; u < a.n_chunks; u += S)
+      if (NW - 1 - (u / S) % NW == wave)
+        bf16_tile_partial<GH>(a, b, kv, u, sm.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
+  }
+  HistState<MT> st;
+  hist_reset(st);
+  v4i *wl = sm.wave[wave].wl;
+  // rows 4h + 3 of the weight operands stay zero; the rest is rewritten per page
+#pragma unroll
+  for (int i = 0; i < MT * 2; ++i) wl[i * 64 + lane] = v4i{0, 0, 0, 0};
+  // complete the query operands here (and with them the first copies), so that
+  // no wait for them is left inside the loop
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  pipe_scan<MT, NW, PF>(pipe, pv, n_hist, Aq, qa, qb0, qb1, st, wl, lane);
+  if (pipe.bad && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
+  flush_partial<MT, GH, NW>(sm, st, G, dst);
 }
 
 template <int MT, int GH, int NW>
@@ -818,22 +996,34 @@ __device__ void run_scan_valu(const DecArgs &a, int b, int kv, int split, float 
 // written by other workgroups are read with device-coherent loads, issued in
 // batches so that the merge costs a few memory round trips, not one per
 // partial.  U_V rows are fetched first so that their latency overlaps.
-template <int GH, int NT>
-__device__ void merge_item(const DecArgs &a, int b, int kv, const float *parts, MergeSmem<GH> &sm) {
+template <int GH, int NT, bool UVL = false>
+__device__ void merge_item(const DecArgs &a, int b, int kv, const float *hist, int n_hist_parts, const float *tiles,
+                           int n_tile_parts, MergeSmem<GH, UVL> &sm) {
   // (head, channel pair) items per thread when each item takes all partials
   constexpr int kItems = (GH * (kD / 2) + NT - 1) / NT;
   const PoolView &pv = a.pv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nwaves = blockDim.x >> 6;
   const int G = pv.hq / pv.hkv;
-  const int S = a.n_splits, P = a.n_splits + a.n_chunks;
+  const int S = n_hist_parts, P = n_hist_parts + n_tile_parts;
+  // partial p: history split p < S, else BF16 tile p - S; [G][kPartStride] each
+  auto part_of = [&](int p) { return p < S ? hist + (size_t)p * G * kPartStride : tiles + (size_t)(p - S) * G * kPartStride; };
   // threads 0..255 own row k = t / 2 of U_V, channels 64 (t & 1) .. + 64
   const int krow = (tid >> 1) & (kD - 1), half = tid & 1;
   const float4 *urow = (const float4 *)(a.rv.U_V + (size_t)kv * kD * kD + (size_t)krow * kD + 64 * half);
-  float4 u[16];
-  if (tid < 2 * kD) {
+  float4 u[UVL ? 1 : 16];
+  if constexpr (UVL) {
+    // 64 KB of U_V into LDS, 1 KB per DMA copy, spread over the waves; the
+    // copies complete before step 4 reads them (explicit wait there)
+    const uint64_t src = (uint64_t)(uintptr_t)(a.rv.U_V + (size_t)kv * kD * kD);
+    const uint32_t dst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float *) & sm.uv[0][0];
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    for (int c = wv; c < kD * kD * 4 / 1024; c += nwaves) dma_1k(src + 1024u * c, dst + 1024u * c, 16u * lane);
+  } else {
+    if (tid < 2 * kD) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) u[i] = urow[i];
+      for (int i = 0; i < 16; ++i) u[i] = urow[i];
+    }
   }
   asm volatile("" ::: "memory");   // keep the U_V loads here, ahead of the partials
   // 1) one round of device-coherent loads: the first kPer partials of each
@@ -852,16 +1042,14 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *parts, 
     if (e >= nitem) break;
     const int pr = e % npair, sl = e / npair;
     const int h = pr / (kD / 2), c = 2 * (pr % (kD / 2));
-    const float *col = parts + (size_t)h * kPartStride + 2 + c;
-    const size_t st = (size_t)G * kPartStride;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int p = sl + nsl * j;
-      val[it][j] = p < P ? ld_coherent2(col + (size_t)p * st) : make_float2(0.f, 0.f);
+      val[it][j] = p < P ? ld_coherent2(part_of(p) + (size_t)h * kPartStride + 2 + c) : make_float2(0.f, 0.f);
     }
   }
   for (int e = tid; e < P * G; e += blockDim.x) {   // partial e / G, head e % G
-    const float2 hv = ld_coherent2(parts + (size_t)e * kPartStride);
+    const float2 hv = ld_coherent2(part_of(e / G) + (size_t)(e % G) * kPartStride);
     sm.ml[e / G][e % G][0] = hv.x;
     sm.ml[e / G][e % G][1] = hv.y;
   }
@@ -910,8 +1098,6 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *parts, 
     if (e >= nitem) break;
     const int pr = e % npair, sl = e / npair;
     const int h = pr / (kD / 2), c = 2 * (pr % (kD / 2));
-    const float *hb = parts + (size_t)h * kPartStride;
-    const size_t st = (size_t)G * kPartStride;
     float hx = 0.f, hy = 0.f, bx = 0.f, by = 0.f;
     for (int r = 0; r < rounds; ++r) {
       const int p_base = nsl * kPer * r;
@@ -919,7 +1105,8 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *parts, 
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
         const int p = p_base + sl + nsl * j;
-        v[j] = r == 0 ? val[it][j] : (p < P ? ld_coherent2(hb + (size_t)p * st + 2 + c) : make_float2(0.f, 0.f));
+        v[j] = r == 0 ? val[it][j]
+                      : (p < P ? ld_coherent2(part_of(p) + (size_t)h * kPartStride + 2 + c) : make_float2(0.f, 0.f));
       }
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
@@ -970,14 +1157,20 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *parts, 
   }
   __syncthreads();
   // 4) o_hist[h][k] = sum_j z[h][j] U_V[k][j] / sqrt(d)
+  if constexpr (UVL) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
   if (tid < 2 * kD) {
+    const float4 *ul = (const float4 *)(&sm.uv[UVL ? krow : 0][64 * half]);
     for (int h = 0; h < G; ++h) {
       const float4 *zr = (const float4 *)(&sm.zs[h][64 * half]);
       float s = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float4 z = zr[i];
-        s = fmaf(z.x, u[i].x, fmaf(z.y, u[i].y, fmaf(z.z, u[i].z, fmaf(z.w, u[i].w, s))));
+        const float4 uu = UVL ? ul[i] : u[UVL ? 0 : i];
+        s = fmaf(z.x, uu.x, fmaf(z.y, uu.y, fmaf(z.z, uu.z, fmaf(z.w, uu.w, s))));
       }
       s += __shfl_xor(s, 1, 64);
       if (half == 0) sm.ot[h][krow] = s * kInvSqrtDf;
@@ -1020,7 +1213,214 @@ decode_scan_kernel(DecArgs a) {
   else run_scan_valu<MT, GH, NW>(a, b, kv, split, dst, sm.s);
   __shared__ int last_flag;
   if (!arrive_last(&a.counters[bh], S, &last_flag)) return;
-  merge_item<GH, 64 * NW>(a, b, kv, parts, sm.g);
+  merge_item<GH, 64 * NW>(a, b, kv, parts, S, parts + (size_t)S * G * kPartStride, a.n_chunks, sm.g);
+}
+
+
+// ===========================================================================
+// balanced scan (one M-tile of heads, MFMA): every workgroup takes an equal
+// share of all work units (per (sequence, KV head): n_tiles BF16 tiles, then
+// its history pages), computed on the device from seq_lens, so sequences of
+// different lengths load the workgroups evenly.  A workgroup's share splits
+// into segments, one per (sequence, KV head) it touches; each segment yields
+// one history partial (slot = workgroup + bh, unique and ordered) and the
+// tile partials of the tiles it covers.  The last contributor of a
+// (sequence, KV head) merges after its own segments are done.
+// ===========================================================================
+// The balanced scan is switched off: an earlier build of its page copies
+// faulted the device (a sign-extended source address, corrected in dma_1k),
+// and this corrected build has not yet been run on the device.  Every shape
+// takes the grid path meanwhile.
+constexpr bool kBalancedScan = false;
+constexpr int kFlatPrep = 3;     // segments whose query operands are prepared together
+constexpr int kFlatMaxSeg = 96;  // segments per workgroup
+constexpr int kFlatMaxBatch = 4096;
+
+struct FlatSeg {
+  int b, kv, t0, t1, p0, p1, first_blk, last_blk;
+};
+
+template <int GH, int NW>
+struct FlatPrep {
+  v4i aq[kFlatPrep][2 * 64];
+  float qc[kFlatPrep][4][4];
+};
+
+template <int GH, int NW>
+union FlatUnion {
+  ScanSmem<1, GH, NW, true> s;
+  MergeSmem<GH, true> g;
+};
+
+__device__ __forceinline__ int seq_pages(const PoolView &pv, int b) {
+  const int L = max(0, pv.seq_lens[b]);
+  const int nh = max(0, L - pv.sink - pv.recent);
+  return min((nh + kPageTokens - 1) / kPageTokens, pv.max_pages);
+}
+
+// workgroup i owns units [start(i), start(i + 1)), start(i) = i U / NB
+__device__ __forceinline__ long long flat_start(long long i, long long U, long long NB) { return i * U / NB; }
+__device__ __forceinline__ int flat_block_of(long long x, long long U, int NB) {
+  long long i = x * NB / U;
+  if (i > NB - 1) i = NB - 1;
+  while (i + 1 < NB && flat_start(i + 1, U, NB) <= x) ++i;
+  while (i > 0 && flat_start(i, U, NB) > x) --i;
+  return (int)i;
+}
+
+template <int GH>
+__global__ void __launch_bounds__((64 * scan_waves<1, true>())) __attribute__((amdgpu_waves_per_eu(3)))
+decode_flat_kernel(DecArgs a) {
+  constexpr int NW = scan_waves<1, true>();
+  constexpr int PF = ScanSmem<1, GH, NW, true>::PF;
+  const PoolView &pv = a.pv;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = pv.hq / pv.hkv, Hkv = pv.hkv, B = pv.batch, NT = a.n_chunks, NB = a.n_blocks;
+  __shared__ FlatUnion<GH, NW> sm;
+  __shared__ FlatPrep<GH, NW> prep;
+  __shared__ FlatSeg segs[kFlatMaxSeg];
+  __shared__ int seg_info[4];   // nseg, nmerge
+  __shared__ int merge_list[kFlatMaxSeg];
+  __shared__ int last_flag;
+  __shared__ int wtot[NW];
+
+  // 1) units per sequence and their prefix sums (LDS scratch in the wave area)
+  int *pre = (int *)&sm.s.wave[0];   // [B + 1]
+  static_assert(sizeof(sm.s.wave) >= (kFlatMaxBatch + 1) * sizeof(int), "prefix scratch");
+  {
+    int carry = 0;
+    for (int base = 0; base < B; base += blockDim.x) {
+      const int b = base + tid;
+      int v = 0;
+      if (b < B) {
+        v = Hkv * (NT + seq_pages(pv, b));
+        if (blockIdx.x == 0 && pv.err) {
+          const int L = max(0, pv.seq_lens[b]);
+          const int nh = max(0, L - pv.sink - pv.recent);
+          if ((nh + kPageTokens - 1) / kPageTokens > pv.max_pages) atomicOr(pv.err, OSCAR_DEVERR_LENGTH);
+        }
+      }
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
+      }
+      if (lane == 63) wtot[wave] = v;
+      __syncthreads();
+      int off = carry;
+      for (int w2 = 0; w2 < wave; ++w2) off += wtot[w2];
+      if (b < B) pre[b + 1] = v + off;
+      int tot = 0;
+      for (int w2 = 0; w2 < NW; ++w2) tot += wtot[w2];
+      carry += tot;
+      __syncthreads();
+    }
+    if (tid == 0) pre[0] = 0;
+    __syncthreads();
+  }
+  const long long U = pre[B];
+  // workgroups in use: every one of them owns at least one unit, so each
+  // workgroup in [first_blk, last_blk] of a (sequence, KV head) contributes
+  const int NBe = (int)min((long long)NB, U);
+  if ((int)blockIdx.x >= NBe) return;
+  const long long start = flat_start(blockIdx.x, U, NBe), end = flat_start(blockIdx.x + 1, U, NBe);
+  // 2) segments (thread 0)
+  if (tid == 0) {
+    int lo = 0, hi = B - 1;   // sequence b with pre[b] <= start < pre[b + 1]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= start) lo = mid;
+      else hi = mid - 1;
+    }
+    int b = lo, n = 0;
+    long long x = start;
+    while (x < end && n < kFlatMaxSeg) {
+      const int ub = (pre[b + 1] - pre[b]) / Hkv;   // units of one (b, kv)
+      const int kv = (int)((x - pre[b]) / ub);
+      const long long u0 = pre[b] + (long long)kv * ub;   // first unit of (b, kv)
+      const int a0 = (int)(x - u0), a1 = (int)min((long long)ub, end - u0);
+      FlatSeg sg;
+      sg.b = b;
+      sg.kv = kv;
+      sg.t0 = min(a0, NT);
+      sg.t1 = min(a1, NT);
+      sg.p0 = max(a0, NT) - NT;
+      sg.p1 = max(a1, NT) - NT;
+      sg.first_blk = flat_block_of(u0, U, NBe);
+      sg.last_blk = flat_block_of(u0 + ub - 1, U, NBe);
+      segs[n++] = sg;
+      x = u0 + ub;
+      if (kv + 1 == Hkv) ++b;
+    }
+    seg_info[0] = n;
+    seg_info[1] = 0;
+  }
+  __syncthreads();
+  const int nseg = __builtin_amdgcn_readfirstlane(seg_info[0]);
+  const float sl2 = pv.sm_scale * kLog2e;
+
+  // 3) per segment: its page copies start, then (every kFlatPrep segments)
+  // the query operands of the next kFlatPrep segments are prepared side by
+  // side while the copies land
+  PagePipe<NW, PF> pipe;
+  v4i *wl = sm.s.wave[wave].wl;
+  for (int si = 0; si < nseg; ++si) {
+    FlatSeg sg = segs[si];
+    sg.b = __builtin_amdgcn_readfirstlane(sg.b);
+    sg.kv = __builtin_amdgcn_readfirstlane(sg.kv);
+    sg.t0 = __builtin_amdgcn_readfirstlane(sg.t0);
+    sg.t1 = __builtin_amdgcn_readfirstlane(sg.t1);
+    sg.p0 = __builtin_amdgcn_readfirstlane(sg.p0);
+    sg.p1 = __builtin_amdgcn_readfirstlane(sg.p1);
+    sg.first_blk = __builtin_amdgcn_readfirstlane(sg.first_blk);
+    sg.last_blk = __builtin_amdgcn_readfirstlane(sg.last_blk);
+    const int bh = sg.b * Hkv + sg.kv;
+    pipe_init(pipe, pv, sg.b, sg.kv, sg.p0, sg.p1, sm.s.pbuf[wave], wave, lane);
+    pipe_prologue(pipe, pv, lane);
+    if (si % kFlatPrep == 0) {
+      int bb[kFlatPrep], kk[kFlatPrep];
+#pragma unroll
+      for (int k = 0; k < kFlatPrep; ++k) {
+        const int sk = min(si + k, nseg - 1);
+        bb[k] = __builtin_amdgcn_readfirstlane(segs[sk].b);
+        kk[k] = __builtin_amdgcn_readfirstlane(segs[sk].kv);
+      }
+      query_prep_multi<kFlatPrep>(a, bb, kk, min(nseg - si, kFlatPrep), (float(*)[4][kD]) & sm.s.wave[0],
+                                  prep.aq, prep.qc);
+    }
+    const int slot = si % kFlatPrep;
+    v4i Aq[1][2];
+    float qa[1], qb0[1], qb1[1];
+    load_query_ops<1, GH>(prep.aq[slot], prep.qc[slot], G, sl2, lane, Aq, qa, qb0, qb1);
+    __syncthreads();   // operands read; the wave scratch is reused below
+    // BF16 tiles of this segment, from the last wave down
+    float *tile_parts = a.part_tile + (size_t)bh * NT * G * kPartStride;
+    for (int t = sg.t0; t < sg.t1; ++t)
+      if (NW - 1 - (t - sg.t0) % NW == wave)
+        bf16_tile_partial<GH>(a, sg.b, sg.kv, t, sm.s.wave[wave].tile, tile_parts + (size_t)t * G * kPartStride);
+    HistState<1> st;
+    hist_reset(st);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) wl[i * 64 + lane] = v4i{0, 0, 0, 0};
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    const int L = max(0, pv.seq_lens[sg.b]);
+    pipe_scan<1, NW, PF>(pipe, pv, max(0, L - pv.sink - pv.recent), Aq, qa, qb0, qb1, st, wl, lane);
+    if (pipe.bad && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
+    flush_partial<1, GH, NW>(sm.s, st, G, a.part + ((size_t)blockIdx.x + bh) * G * kPartStride);
+    if (arrive_last(&a.counters[bh], sg.last_blk - sg.first_blk + 1, &last_flag) && tid == 0)
+      merge_list[seg_info[1]++] = si;
+    __syncthreads();
+  }
+  // 4) merges of the (sequence, KV head) pairs this workgroup completed
+  const int nmerge = seg_info[1];
+  for (int mi = 0; mi < nmerge; ++mi) {
+    const FlatSeg sg = segs[merge_list[mi]];
+    const int bh = sg.b * Hkv + sg.kv;
+    merge_item<GH, 64 * NW, true>(a, sg.b, sg.kv, a.part + ((size_t)sg.first_blk + bh) * G * kPartStride,
+                            sg.last_blk - sg.first_blk + 1, a.part_tile + (size_t)bh * NT * G * kPartStride, NT,
+                            sm.g);
+    __syncthreads();
+  }
 }
 
 }  // namespace
@@ -1038,7 +1438,10 @@ int target_blocks() {
 }
 int mt_of(int G) { return (G + 3) / 4; }
 int gh_of(int G) { return 4 * mt_of(G); }
-int nw_of(int G, int variant) { return variant != 0 ? 4 : (mt_of(G) == 1 ? 12 : 8); }
+// variant 0: MFMA scan (balanced partition where it applies, else grid);
+// 2: MFMA scan on the grid partition only; 1: VALU scan on the grid
+bool is_mfma(int variant) { return variant != 1; }
+int nw_of(int G, int variant) { return !is_mfma(variant) ? 4 : (mt_of(G) == 1 ? 12 : 8); }
 }  // namespace
 
 DecodePlan make_decode_plan(int batch, int hkv, int hq, int max_pages, int sink, int recent, int variant) {
@@ -1046,25 +1449,45 @@ DecodePlan make_decode_plan(int batch, int hkv, int hq, int max_pages, int sink,
   const int G = hq / hkv;
   const int MT = mt_of(G), GH = gh_of(G), NW = nw_of(G, variant);
   const int bh = batch * hkv;
+  p.n_chunks = (sink + recent) / kTileTokens;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  // balanced path: one M-tile of heads on the MFMA scan, bounded segments
+  const long long NB = target_blocks();
+  const long long units_max = (long long)bh * (p.n_chunks + max(max_pages, 0));
+  const long long seg_bound = (units_max / NB + 1 + p.n_chunks - 1) / p.n_chunks + 2;
+  p.flat = kBalancedScan && variant == 0 && MT == 1 && batch <= kFlatMaxBatch && seg_bound <= kFlatMaxSeg &&
+           NB + p.n_chunks <= kMaxParts && units_max < (1LL << 30);
+  size_t off = 0;
+  p.off_counters = off;
+  off = al(off + (size_t)bh * sizeof(int));
+  if (p.flat) {
+    p.n_blocks = (int)NB;
+    p.n_splits = 0;
+    p.pages_per_split = 0;
+    p.off_qconst = p.off_qrot = off;
+    p.off_part = off;
+    off = al(off + (size_t)(NB + bh) * G * kPartStride * sizeof(float));
+    p.off_tile = off;
+    off = al(off + (size_t)bh * p.n_chunks * G * kPartStride * sizeof(float));
+    p.total = off;
+    return p;
+  }
   int S = (target_blocks() + bh - 1) / bh;
   const int max_by_pages = max_pages > 0 ? (max_pages + NW - 1) / NW : 1;   // >= 1 page per wave
   S = S < 1 ? 1 : S;
   S = S > max_by_pages ? max_by_pages : S;
   S = S > kMaxSplits ? kMaxSplits : S;
-  p.n_chunks = (sink + recent) / kTileTokens;
   S = S > kMaxParts - p.n_chunks ? kMaxParts - p.n_chunks : S;
   p.n_splits = S;
+  p.n_blocks = 0;
   p.pages_per_split = max_pages > 0 ? (max_pages + S - 1) / S : 1;
-  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  size_t off = 0;
-  p.off_counters = off;
-  off = al(off + (size_t)bh * sizeof(int));
   p.off_qconst = off;
   off = al(off + (size_t)bh * GH * 4 * sizeof(float));
   p.off_qrot = off;
   off = al(off + (size_t)bh * GH * kD * sizeof(float));
   p.off_part = off;
   off = al(off + (size_t)bh * (S + p.n_chunks) * G * kPartStride * sizeof(float));
+  p.off_tile = off;
   p.total = off;
   return p;
 }
@@ -1075,11 +1498,18 @@ hipError_t launch_decode(const PoolView &pv, const RotView &rv, const uint16_t *
   const int G = pv.hq / pv.hkv;
   const int BH = pv.batch * pv.hkv;
   DecArgs a{pv, rv, q, out, (int *)(ws + plan.off_counters), (float *)(ws + plan.off_qconst),
-            (float *)(ws + plan.off_qrot), (float *)(ws + plan.off_part),
-            plan.n_splits, plan.n_chunks, plan.pages_per_split};
-  const bool mfma = variant == 0;
-  const dim3 sgrid(BH * plan.n_splits);
+            (float *)(ws + plan.off_qrot), (float *)(ws + plan.off_part), (float *)(ws + plan.off_tile),
+            plan.n_splits, plan.n_chunks, plan.pages_per_split, plan.n_blocks};
+  const bool mfma = is_mfma(variant);
   hipError_t e;
+  if (plan.flat) {
+    if (ev_start && (e = hipEventRecord(ev_start, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_flat_kernel<4>, dim3(plan.n_blocks), dim3(64 * scan_waves<1, true>()), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (ev_stop && (e = hipEventRecord(ev_stop, s)) != hipSuccess) return e;
+    return hipSuccess;
+  }
+  const dim3 sgrid(BH * plan.n_splits);
 #define OSCAR_LAUNCH(MT, GH)                                                                         \
   do {                                                                                               \
     if (!mfma) {                                                                                     \

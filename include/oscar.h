@@ -224,7 +224,16 @@ size_t oscar_bf16_decode_workspace_size(const oscar_params *p, int32_t batch, in
  */
 int32_t oscar_set_history_timing_events(void *start_event, void *stop_event);
 
-/* Decode kernel selection: 0 = MFMA int8 path (default), 1 = VALU path. */
+/*
+ * Decode kernel selection (process-wide; OSCAR_EINVAL for other values):
+ *   0 = MFMA int8 history scan (default); for G <= 4 it may split the work
+ *       evenly over a fixed grid of workgroups (balanced partition, where
+ *       built in), else one workgroup per (sequence, KV head, split);
+ *   1 = VALU history scan (float arithmetic, reference speed);
+ *   2 = MFMA int8 history scan, always on the per-(sequence, KV head) split
+ *       grid.
+ * Results of 0 and 2 differ only in floating-point summation order.
+ */
 int32_t oscar_set_decode_variant(int32_t variant);
 
 /* Message of the last error on the calling thread ("" if none). */

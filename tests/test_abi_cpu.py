@@ -80,6 +80,9 @@ def test_validation_errors():
     assert L.oscar_quantize_append(ctypes.byref(p), None, ctypes.byref(pool),
                                    0x1000, 0x1000, 1, None) == O.OSCAR_EINVAL
     assert L.oscar_set_decode_variant(7) == O.OSCAR_EINVAL
+    assert L.oscar_set_decode_variant(-1) == O.OSCAR_EINVAL
+    for v in (2, 1, 0):
+        assert L.oscar_set_decode_variant(v) == 0
     assert L.oscar_decode_workspace_size(ctypes.byref(O.make_params(8, 30)), 1, 10) == 0
     with pytest.raises(O.OscarError):
         O.calibrate_rotation(O.make_params(1, 1), np.zeros((1, 8, 128), np.float32),

@@ -122,7 +122,7 @@ def test_single_token_appends(tiny):
     assert np.array_equal(vs.view(np.uint16), ref.hist_v.scale.view(np.uint16))
 
 
-@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("variant", [0, 1, 2])
 def test_decode_tiny(tiny, variant):
     wl, cals, rot, params, kb, vb, q = tiny
     pool = _fresh_pool(params, 59)
@@ -169,9 +169,44 @@ def test_batch_scattered_ragged():
         toks.append((kb, vb))
         append_sequence(params, rot, pool, b, kb, vb, chunks=[int(lens[b]) - 3, 1, 1, 1])
     q = synth.decode_queries(wl, 0)
-    for variant in (0, 1):
+    for variant in (0, 1, 2):
         out = _decode_gpu(params, rot, pool, q, variant)
         for b in range(wl.batch):
+            ref, _ = _oracle_decode(wl, cals, toks[b][0], toks[b][1], q[b])
+            assert decode_check(out[b], ref) <= TOL, (b, variant)
+    assert int(pool.error_flags.cpu()[0]) == 0
+
+
+@pytest.mark.skip(reason="balanced-partition scan switched off in the library: an earlier build of its "
+                         "page copies faulted the device (sign-extended DMA source address, corrected "
+                         "since) and the corrected build has not run on the device yet")
+def test_balanced_partition_ragged_batch():
+    """Sixteen sequences x eight KV heads (G = 4) of very different lengths
+    (empty, windows only, one partial page, up to 41 pages), pages scattered:
+    the balanced partition gives many workgroups two or three (sequence, KV
+    head) segments, and some segments tiles only.  Variant 0 (balanced) and
+    variant 2 (grid) must both match the oracle."""
+    wl = synth.Workload(91, "test-balanced", 16, 8, 32, 128, 0, 2950, n_cal=512, outliers="pairs10",
+                        scattered_pages=True)
+    cals = oracle_calibration(wl, n_cal=512)
+    rot = rotation_tensors(cals)
+    params = O.make_params(wl.n_kv, wl.n_q)
+    lens = np.array([0, 1, 70, 320, 321, 385, 900, 1800, 2950, 2222, 64, 2000, 1234, 333, 2949, 1500], np.int32)
+    bt, total = synth.block_table(wl, lens)
+    pool = O.KVPool(params, wl.batch, total, bt)
+    toks = []
+    for b in range(wl.batch):
+        kb, vb = synth.kv_tokens(wl, 0, b, 0, int(lens[b]))
+        toks.append((kb, vb))
+        if lens[b]:
+            append_sequence(params, rot, pool, b, kb, vb)
+    q = synth.decode_queries(wl, 0)
+    for variant in (0, 2):
+        out = _decode_gpu(params, rot, pool, q, variant)
+        for b in range(wl.batch):
+            if lens[b] == 0:
+                assert np.all(out[b] == 0), (b, variant)
+                continue
             ref, _ = _oracle_decode(wl, cals, toks[b][0], toks[b][1], q[b])
             assert decode_check(out[b], ref) <= TOL, (b, variant)
     assert int(pool.error_flags.cpu()[0]) == 0
