@@ -27,8 +27,8 @@
 namespace oscar {
 namespace {
 
-constexpr int kChunk = 16;        // history slots per workgroup (aligned to 16)
-constexpr int kThreads = 128;     // one thread per channel
+constexpr int kThreads = 128;     // single-token append: one thread per channel
+constexpr int kPageThreads = 256; // bulk demotion: four waves of 16 page slots
 constexpr double kInvSqrtD = 0x1.6a09e667f3bcdp-4;  // nearest double to 1/sqrt(128)
 
 struct AppendArgs {
@@ -47,10 +47,10 @@ __device__ __forceinline__ float wave_min(float v) {
   return v;
 }
 
-// S6..S8 for output channel p of one token (this thread; the wave holds the
-// 64 channels of one group): clamp, group scale/zero, code.  Lane 0 of the
-// group writes the fp16 {scale, zero} pair to meta[group].
-__device__ __forceinline__ uint32_t quantize_code(float v, float tau, int p, uint32_t *meta) {
+// S6..S8 for output channel p of one token (this lane; the wave holds the 64
+// channels of one group): clamp, group scale/zero, code.  Returns the code;
+// meta receives the fp16 {scale, zero} pair of the group (same on every lane).
+__device__ __forceinline__ uint32_t quantize_group(float v, float tau, uint32_t &meta) {
   v = fminf(fmaxf(v, -tau), tau);
   const float mx = wave_max(v), mn = wave_min(v);
   const float s = __fdiv_rn(mx - mn, 3.0f);
@@ -62,18 +62,32 @@ __device__ __forceinline__ uint32_t quantize_code(float v, float tau, int p, uin
     r = fminf(fmaxf(r, 0.0f), 3.0f);
     code = (uint32_t)r;
   }
-  if ((p & 63) == 0) meta[p >> 6] = (uint32_t)s16 | ((uint32_t)z16 << 16);
+  meta = (uint32_t)s16 | ((uint32_t)z16 << 16);
   return code;
 }
 
-// grid: (chunks, Hkv * 2, batch); block: 128 threads (thread j = channel j).
+// As quantize_group for output channel p; lane p % 64 == 0 stores the
+// group's fp16 {scale, zero} pair to meta[p / 64].
+__device__ __forceinline__ uint32_t quantize_code(float v, float tau, int p, uint32_t *meta) {
+  uint32_t m;
+  const uint32_t code = quantize_group(v, tau, m);
+  if ((p & 63) == 0) meta[p >> 6] = m;
+  return code;
+}
+
+// Bulk demotion, one 64-token history page of one (KV head, K|V) per
+// workgroup.  grid: (pages, Hkv * 2, batch); block: 256 threads.  Wave w owns
+// page slots 16 w .. 16 w + 15; lane l owns butterfly elements l and l + 64
+// of each of them (S1, S2) and output channels l and l + 64 (S5..S8).
 // Demotes every position x with max(S0, p0 - W) <= x < p0 + n_new - W.
-__global__ void __launch_bounds__(kThreads) append_demote_kernel(AppendArgs a) {
+__global__ void __launch_bounds__(kPageThreads) __attribute__((amdgpu_waves_per_eu(2)))
+append_demote_kernel(AppendArgs a) {
   const PoolView &pv = a.pv;
   const int b = blockIdx.z;
   const int h = blockIdx.y >> 1;
   const int is_v = blockIdx.y & 1;
-  const int j = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int p0 = pv.seq_lens[b];
   if (p0 < 0) return;                                       // flagged by the store kernel
   const int L = p0 + a.n_new;
@@ -81,98 +95,161 @@ __global__ void __launch_bounds__(kThreads) append_demote_kernel(AppendArgs a) {
   const int xb = L - pv.recent;
   if (xb <= xa) return;
   const int ha = xa - pv.sink, hb = xb - pv.sink;           // history index range
-  const int c0 = (ha / kChunk) * kChunk + blockIdx.x * kChunk;
-  const int t0 = max(c0, ha), t1 = min(c0 + kChunk, hb);
+  const int c0 = (ha / kPageTokens + (int)blockIdx.x) * kPageTokens;   // first index of this page
+  const int t0 = max(c0, ha), t1 = min(c0 + kPageTokens, hb);
   if (t1 <= t0) return;
-  const int nt = t1 - t0;
-
   const int page_idx = c0 / kPageTokens;
   if (page_idx >= pv.max_pages) {
-    if (j == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_LENGTH);
+    if (tid == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_LENGTH);
     return;
   }
   const int phys = pv.block_table[(size_t)b * pv.max_pages + page_idx];
   if (phys < 0 || phys >= pv.n_pages) {
-    if (j == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
+    if (tid == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
     return;
   }
+  __shared__ __align__(16) double xs[kPageTokens][kD];   // bf16 sources as float64, token-major
+  __shared__ __align__(16) uint8_t vst[kD][16];           // V code bytes of the page, channel-major
 
-  __shared__ double xs[kChunk][kD];
-  __shared__ double ys[kChunk][kD + 1];
-
-  // Gather the bf16 sources: ring slot for old recent tokens, input otherwise.
+  // Gather: each wave its own 16 slots (zeros outside [t0, t1)); lane l
+  // reads channels 2 l and 2 l + 1 of the token row.
   const uint16_t *ring = is_v ? pv.recent_v : pv.recent_k;
   const uint16_t *fresh = is_v ? a.v_new : a.k_new;
-  for (int t = 0; t < nt; ++t) {
-    const int x = t0 + t + pv.sink;
-    uint16_t bits;
-    if (x < p0)
-      bits = ring[(((size_t)b * pv.hkv + h) * pv.recent + (x % pv.recent)) * kD + j];
-    else
-      bits = fresh[(((size_t)b * a.n_new + (x - p0)) * pv.hkv + h) * kD + j];
-    xs[t][j] = (double)bf16_to_f32(bits);
+  for (int i = 0; i < 16; ++i) {
+    const int hx = c0 + 16 * w + i;   // history index of the slot
+    double2 d = {0.0, 0.0};
+    if (hx >= t0 && hx < t1) {
+      const int x = hx + pv.sink;
+      const uint16_t *row = x < p0 ? ring + (((size_t)b * pv.hkv + h) * pv.recent + (x % pv.recent)) * kD
+                                   : fresh + (((size_t)b * a.n_new + (x - p0)) * pv.hkv + h) * kD;
+      const uint32_t bits = ((const uint32_t *)row)[lane];
+      d.x = (double)bf16_to_f32((uint16_t)(bits & 0xFFFFu));
+      d.y = (double)bf16_to_f32((uint16_t)(bits >> 16));
+    }
+    *(double2 *)&xs[16 * w + i][2 * lane] = d;
   }
   __syncthreads();
 
-  // S1: projection onto the eigenbasis, float64, k ascending.
+  // S1: y_j = sum_k x_k U[k][j], float64, k ascending; U rows of the next
+  // eight k are loaded while the current eight are used.
   const float *U = (is_v ? a.rv.U_V : a.rv.U_K) + (size_t)h * kD * kD;
-  double acc[kChunk];
+  double acc[16][2];
 #pragma unroll
-  for (int t = 0; t < kChunk; ++t) acc[t] = 0.0;
-  for (int k = 0; k < kD; ++k) {
-    const double u = (double)U[k * kD + j];
+  for (int i = 0; i < 16; ++i) acc[i][0] = acc[i][1] = 0.0;
+  float uc[8][2], un[8][2];
 #pragma unroll
-    for (int t = 0; t < kChunk; ++t) acc[t] = fma(xs[t][k], u, acc[t]);
+  for (int kk = 0; kk < 8; ++kk) {
+    uc[kk][0] = U[kk * kD + lane];
+    uc[kk][1] = U[kk * kD + 64 + lane];
   }
+  for (int kb = 0; kb < kD / 8; ++kb) {
+    const int kn = kb + 1 < kD / 8 ? 8 * (kb + 1) : 8 * kb;   // last block reloads itself (unused)
 #pragma unroll
-  for (int t = 0; t < kChunk; ++t) ys[t][j] = acc[t];
-  __syncthreads();
-
-  // S2: butterfly.  Thread j owns pair (j & 63) for tokens with parity j >> 6.
-  for (int hs = 1; hs < kD; hs <<= 1) {
-    const int pr = j & 63;
-    const int i0 = (pr / hs) * (2 * hs) + (pr % hs);
-    for (int t = j >> 6; t < nt; t += 2) {
-      const double x0 = ys[t][i0], x1 = ys[t][i0 + hs];
-      ys[t][i0] = x0 + x1;
-      ys[t][i0 + hs] = x0 - x1;
+    for (int kk = 0; kk < 8; ++kk) {
+      un[kk][0] = U[(kn + kk) * kD + lane];
+      un[kk][1] = U[(kn + kk) * kD + 64 + lane];
     }
-    __syncthreads();
+#pragma unroll
+    for (int kp = 0; kp < 4; ++kp) {
+      const int k = 8 * kb + 2 * kp;
+      const double u00 = uc[2 * kp][0], u01 = uc[2 * kp][1];
+      const double u10 = uc[2 * kp + 1][0], u11 = uc[2 * kp + 1][1];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const double2 xv = *(const double2 *)&xs[16 * w + i][k];
+        acc[i][0] = fma(xv.x, u00, acc[i][0]);
+        acc[i][1] = fma(xv.x, u01, acc[i][1]);
+        acc[i][0] = fma(xv.y, u10, acc[i][0]);
+        acc[i][1] = fma(xv.y, u11, acc[i][1]);
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      uc[kk][0] = un[kk][0];
+      uc[kk][1] = un[kk][1];
+    }
   }
 
-  // S3..S8 per token; thread j = output channel p, wave = quantisation group.
+  // S2: butterfly stages h = 1 .. 32 across lanes, then h = 64 in registers.
+#pragma unroll
+  for (int hs = 1; hs < 64; hs <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const double o = __shfl_xor(acc[i][c], hs, 64);
+        acc[i][c] = (lane & hs) ? o - acc[i][c] : acc[i][c] + o;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const double x0 = acc[i][0], x1 = acc[i][1];
+    acc[i][0] = x0 + x1;
+    acc[i][1] = x0 - x1;
+  }
+
+  // S3..S8 per slot.  Output channel p takes element bitrev(p): lane l
+  // fetches the elements of channels l and l + 64 from their owner lanes.
   const float tau = (is_v ? a.rv.tau_V : a.rv.tau_K)[h];
-  const int p = j;
+  const int e0 = bitrev7(lane), e1 = bitrev7(lane + 64);
   uint8_t *page = pv.pages + ((size_t)phys * pv.hkv + h) * kPageBytes;
-  uint32_t vbytes[4] = {0, 0, 0, 0};   // V: the 4 bytes of channel p this chunk touches
-  uint32_t vmask[4] = {0, 0, 0, 0};
-  for (int t = 0; t < nt; ++t) {
-    const int slot = (t0 + t) % kPageTokens;
-    const float v = (float)(ys[t][bitrev7(p)] * kInvSqrtD);
-    const uint32_t code = quantize_code(v, tau, p, (uint32_t *)(page + (is_v ? kVMeta : kKMeta) + meta_entry(slot) * 8));
+  uint32_t vb[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};   // V: bytes 4 m + w of channels l, l + 64
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int slot = 16 * w + i;
+    const bool valid = c0 + slot >= t0 && c0 + slot < t1;   // wave-uniform
+    const float f0 = (float)(acc[i][0] * kInvSqrtD), f1 = (float)(acc[i][1] * kInvSqrtD);
+    const float g00 = __shfl(f0, e0 & 63, 64), g01 = __shfl(f1, e0 & 63, 64);
+    const float g10 = __shfl(f0, e1 & 63, 64), g11 = __shfl(f1, e1 & 63, 64);
+    uint32_t m0, m1;
+    const uint32_t code0 = quantize_group((e0 >> 6) ? g01 : g00, tau, m0);
+    const uint32_t code1 = quantize_group((e1 >> 6) ? g11 : g10, tau, m1);
+    if (!valid) continue;
+    if (lane == 0) *(uint2 *)(page + (is_v ? kVMeta : kKMeta) + meta_entry(slot) * 8) = make_uint2(m0, m1);
     if (!is_v) {
-      // K codes: byte p/4 of the token row, four neighbouring lanes combine.
-      uint32_t c = code << (2 * (p & 3));
-      c |= __shfl_xor(c, 1, 64);
-      c |= __shfl_xor(c, 2, 64);
-      if ((p & 3) == 0) page[kKCodes + slot * 32 + (p >> 2)] = (uint8_t)c;
+      // K row: dword q holds channels 16 q .. 16 q + 15, two bits each
+      uint32_t k0 = code0 << (2 * (lane & 15)), k1 = code1 << (2 * (lane & 15));
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        k0 |= __shfl_xor(k0, o, 64);
+        k1 |= __shfl_xor(k1, o, 64);
+      }
+      if ((lane & 15) == 0) {
+        uint32_t *row = (uint32_t *)(page + kKCodes + slot * 32);
+        row[lane >> 4] = k0;
+        row[4 + (lane >> 4)] = k1;
+      }
     } else {
-      const int m = (slot >> 2) & 3;   // chunks are 16-aligned: slot >> 4 fixed
-      vbytes[m] |= code << (2 * (slot & 3));
-      vmask[m] |= 3u << (2 * (slot & 3));
+      // V: slot 16 w + i sits in byte 4 (i / 4) + w of each channel row, bits 2 (i % 4)
+      vb[0][i >> 2] |= code0 << (2 * (i & 3));
+      vb[1][i >> 2] |= code1 << (2 * (i & 3));
     }
   }
-  if (is_v) {
-    const int a16 = (t0 % kPageTokens) >> 4;
-    uint8_t *row = page + kVCodes + p * 16;
+  if (!is_v) return;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      if (!vmask[m]) continue;
-      uint8_t *dst = row + 4 * m + a16;
-      uint32_t val = vbytes[m];
-      if (vmask[m] != 0xFF) val = (*dst & ~vmask[m]) | val;   // partial byte: keep other slots
-      *dst = (uint8_t)val;
+  for (int m = 0; m < 4; ++m) {
+    vst[lane][4 * m + w] = (uint8_t)vb[0][m];
+    vst[lane + 64][4 * m + w] = (uint8_t)vb[1][m];
+  }
+  __syncthreads();
+  if (tid < kD) {
+    uint4 *dst = (uint4 *)(page + kVCodes + tid * 16);
+    uint4 val = *(const uint4 *)vst[tid];
+    if (t0 != c0 || t1 != c0 + kPageTokens) {
+      // partial page: keep the bits of slots outside [t0 - c0, t1 - c0)
+      uint32_t mk[4] = {0, 0, 0, 0};
+      for (int s = t0 - c0; s < t1 - c0; ++s) {
+        const int byte = 4 * ((s >> 2) & 3) + (s >> 4);
+        mk[byte >> 2] |= 3u << (8 * (byte & 3) + 2 * (s & 3));
+      }
+      const uint4 old = *dst;
+      val.x = (old.x & ~mk[0]) | (val.x & mk[0]);
+      val.y = (old.y & ~mk[1]) | (val.y & mk[1]);
+      val.z = (old.z & ~mk[2]) | (val.z & mk[2]);
+      val.w = (old.w & ~mk[3]) | (val.w & mk[3]);
     }
+    *dst = val;
   }
 }
 
@@ -326,8 +403,10 @@ hipError_t launch_append(const PoolView &pv, const RotView &rv, const uint16_t *
     hipLaunchKernelGGL(append_one_kernel, dim3(pv.hkv * 2, pv.batch), dim3(kThreads), 0, s, a);
     return hipGetLastError();
   }
-  const int chunks = (n_new + kChunk - 1) / kChunk + 1;
-  hipLaunchKernelGGL(append_demote_kernel, dim3(chunks, pv.hkv * 2, pv.batch), dim3(kThreads), 0, s, a);
+  // the demoted range is at most n_new history slots: it spans at most
+  // n_new / 64 + 2 pages
+  const int pages = n_new / kPageTokens + 2;
+  hipLaunchKernelGGL(append_demote_kernel, dim3(pages, pv.hkv * 2, pv.batch), dim3(kPageThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(append_store_kernel, dim3(pv.batch), dim3(256), 0, s, a);
