@@ -32,6 +32,36 @@ METRIC = "INT2-KV decode attention µs/step + achieved HBM GB/s at 100K ctx, bat
 HBM_PEAK_GBPS = 8000.0
 D = 128
 HIST_BYTES_PER_TOKEN_HEAD = 80      # 64 B codes (K+V) + 16 B fp16 scale/zero (K+V)
+
+# HBM traffic of the scan kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
+# recorded with a hash of the kernel sources it was measured on; reported
+# only while those sources are unchanged.
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "bit_rotated_kv_int2_amd", "measured_traffic.json")
+TRAFFIC_SOURCES = ("bit_rotated_kv_int2_amd/csrc/oscar_decode_kernels.hip", "bit_rotated_kv_int2_amd/csrc/oscar_internal.h",
+                   "bit_rotated_kv_int2_amd/csrc/oscar_wave.h", "include/oscar.h")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """Scaled HBM bytes per scan launch for this workload, or None when the
+    kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except OSError:
+        return None
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch", {}).get(workload)
 WIN_BYTES_PER_TOKEN_HEAD = 512      # bf16 K + V
 
 
@@ -479,7 +509,7 @@ def main():
         "decode_frac_of_peak": r["decode_gbps"] / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "kernel": "decode_scan_kernel (split-K INT2 history + BF16 windows + merge)",
                      "achieved": r["scan_kernel_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": r["scan_kernel_gbps"] / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": r["scan_kernel_gbps"] / HBM_PEAK_GBPS, "traffic": measured_traffic(wl.name),
                      "bytes_per_launch": r["scan_kernel_bytes"], "us_per_launch": r["scan_kernel_us"],
                      "us_p10_p90": r["scan_kernel_us_p10_p90"]},
         "bf16_baseline": {"us_per_layer": r["bf16_us_per_layer"], "gbps": r["bf16_gbps"],
