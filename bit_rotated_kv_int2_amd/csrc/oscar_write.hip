@@ -351,47 +351,59 @@ __global__ void __launch_bounds__(kThreads) append_one_kernel(AppendArgs a) {
   }
 }
 
-// grid: (batch); block: 256.  Stores new tokens that stay BF16 (sink or the
-// final recent window), then advances seq_lens.  Runs after the demote kernel
-// on the same stream, so every ring slot has been read before it is reused.
+// grid: (blocks, batch); block: 256.  Stores the new tokens that stay BF16
+// (sink, or the final recent window): rows of 256 B, one per (token, KV
+// head, K|V), sink tokens first; workgroup x takes rows [16 x, 16 x + 16).
+// Runs after the demote kernel on the same stream, so every ring slot has
+// been read before it is reused.  seq_lens is advanced by the commit kernel.
+constexpr int kStoreRows = 16;
 __global__ void __launch_bounds__(256) append_store_kernel(AppendArgs a) {
   const PoolView &pv = a.pv;
-  const int b = blockIdx.x;
+  const int b = blockIdx.y;
   const int p0 = pv.seq_lens[b];
-  if (p0 < 0) {
-    if (threadIdx.x == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_LENGTH);
-    return;
-  }
+  if (p0 < 0) return;                                       // flagged by the commit kernel
   const int L = p0 + a.n_new;
   const int sink_slot = pv.sink_slot[b];
   const bool sink_ok = sink_slot >= 0 && sink_slot < pv.n_sink_slots;
-  if (!sink_ok && p0 < pv.sink && threadIdx.x == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_SINKSLOT);
+  if (!sink_ok && p0 < pv.sink && blockIdx.x == 0 && threadIdx.x == 0 && pv.err)
+    atomicOr(pv.err, OSCAR_DEVERR_SINKSLOT);
   const int n_sink_new = max(0, min(a.n_new, pv.sink - p0));
   const int i_ring0 = max(n_sink_new, L - pv.recent - p0);
-  // words of 8 bytes per token row: 128 bf16 = 32 x uint64
-  const int words = kD / 4;
-  for (int kv = 0; kv < 2; ++kv) {
-    const uint64_t *src = (const uint64_t *)(kv ? a.v_new : a.k_new);
-    uint64_t *sink = (uint64_t *)(kv ? pv.sink_v : pv.sink_k);
-    uint64_t *ring = (uint64_t *)(kv ? pv.recent_v : pv.recent_k);
-    if (sink_ok) {
-      for (int e = threadIdx.x; e < n_sink_new * pv.hkv * words; e += blockDim.x) {
-        const int w = e % words, h = (e / words) % pv.hkv, i = e / (words * pv.hkv);
-        const int pos = p0 + i;
-        sink[(((size_t)sink_slot * pv.hkv + h) * pv.sink + pos) * words + w] =
-            src[(((size_t)b * a.n_new + i) * pv.hkv + h) * words + w];
-      }
-    }
-    const int n_ring = a.n_new - i_ring0;
-    for (int e = threadIdx.x; e < n_ring * pv.hkv * words; e += blockDim.x) {
-      const int w = e % words, h = (e / words) % pv.hkv, i = i_ring0 + e / (words * pv.hkv);
-      const int pos = p0 + i;
-      ring[(((size_t)b * pv.hkv + h) * pv.recent + (pos % pv.recent)) * words + w] =
-          src[(((size_t)b * a.n_new + i) * pv.hkv + h) * words + w];
+  const int n_sink_st = sink_ok ? n_sink_new : 0;           // sink tokens stored
+  const int n_tok = n_sink_st + (a.n_new - i_ring0);
+  const int rows = n_tok * pv.hkv * 2;
+  const int words = kD / 4;                                 // 8-byte words per row
+  const int w = threadIdx.x & (words - 1);
+  const int r1 = min(rows, ((int)blockIdx.x + 1) * kStoreRows);
+  for (int r = (int)blockIdx.x * kStoreRows + (int)(threadIdx.x / words); r < r1; r += 256 / words) {
+    const int is_v = r & 1, h = (r >> 1) % pv.hkv, ti = (r >> 1) / pv.hkv;
+    const bool to_sink = ti < n_sink_st;
+    const int i = to_sink ? ti : i_ring0 + (ti - n_sink_st);   // index among the new tokens
+    const int pos = p0 + i;
+    const uint64_t *src = (const uint64_t *)(is_v ? a.v_new : a.k_new);
+    const uint64_t v = src[(((size_t)b * a.n_new + i) * pv.hkv + h) * words + w];
+    if (to_sink) {
+      uint64_t *sink = (uint64_t *)(is_v ? pv.sink_v : pv.sink_k);
+      sink[(((size_t)sink_slot * pv.hkv + h) * pv.sink + pos) * words + w] = v;
+    } else {
+      uint64_t *ring = (uint64_t *)(is_v ? pv.recent_v : pv.recent_k);
+      ring[(((size_t)b * pv.hkv + h) * pv.recent + (pos % pv.recent)) * words + w] = v;
     }
   }
-  __syncthreads();
-  if (threadIdx.x == 0) pv.seq_lens[b] = L;
+}
+
+// grid: 1; block: 256.  Advances seq_lens by n_new (after every kernel of
+// the append has read the old length); a negative length is flagged.
+__global__ void __launch_bounds__(256) append_commit_kernel(AppendArgs a) {
+  const PoolView &pv = a.pv;
+  for (int b = threadIdx.x; b < pv.batch; b += blockDim.x) {
+    const int p0 = pv.seq_lens[b];
+    if (p0 < 0) {
+      if (pv.err) atomicOr(pv.err, OSCAR_DEVERR_LENGTH);
+    } else {
+      pv.seq_lens[b] = p0 + a.n_new;
+    }
+  }
 }
 
 }  // namespace
@@ -409,7 +421,14 @@ hipError_t launch_append(const PoolView &pv, const RotView &rv, const uint16_t *
   hipLaunchKernelGGL(append_demote_kernel, dim3(pages, pv.hkv * 2, pv.batch), dim3(kPageThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(append_store_kernel, dim3(pv.batch), dim3(256), 0, s, a);
+  // BF16 rows stored: at most min(n_new, sink + recent) tokens x Hkv x 2
+  const long long store_rows = (long long)min(n_new, pv.sink + pv.recent) * pv.hkv * 2;
+  const int store_blocks = (int)((store_rows + kStoreRows - 1) / kStoreRows);
+  if (store_blocks > 0) {
+    hipLaunchKernelGGL(append_store_kernel, dim3(store_blocks, pv.batch), dim3(256), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(append_commit_kernel, dim3(1), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
