@@ -34,8 +34,9 @@ What the oracle computes
 2. The write path ([A] token pool paragraph, [B] serving): rotate a bf16
    token by R (fp64 U-projection with k ascending, fp64 butterfly, fp64
    scale, bit-reversal, round to float32), clip to +-tau, per-token
-   asymmetric INT2 over groups of 64 channels with float16 scale and zero,
-   pack four 2-bit codes per byte.
+   asymmetric INT2 over groups of 64 channels with an 8-bit zero and an
+   8-bit scale per group (fixed-point fractions of tau), pack four 2-bit
+   codes per byte.
 3. The pool ([A], [B] serving): BF16 sink (first 64 tokens), rotated INT2
    history, BF16 recent window (last 256 tokens).
 4. Decode attention over the pool: the literal form (each history token is
@@ -309,8 +310,28 @@ def rotate_for_write(x: np.ndarray, U32: np.ndarray) -> np.ndarray:
 @dataclass
 class QuantizedTokens:
     codes: np.ndarray      # uint8 [n, d], values 0..3
-    scale: np.ndarray      # float16 [n, d // group]
-    zero: np.ndarray       # float16 [n, d // group]
+    s8: np.ndarray         # uint8 [n, d // group]: scale code
+    z8: np.ndarray         # uint8 [n, d // group]: zero code
+    scale: np.ndarray      # float32 [n, d // group]: decoded scale  s8 * b
+    zero: np.ndarray       # float32 [n, d // group]: decoded zero   z8 * a - tau
+
+
+META_LEVELS = 255          # largest 8-bit zero / scale code
+
+
+def metadata_steps(tau: np.float32):
+    """Grid steps of the 8-bit zero and scale codes of one head.
+
+    After the clip every group lies in [-tau, tau]: its minimum in that
+    interval and its INT2 step s = (max - min) / 3 in [0, 2 tau / 3].  The
+    zero code z8 in 0..255 stands for z8 * a - tau with a = 2 tau / 255; the
+    scale code s8 for s8 * b with b = 2 tau / 765.  Each step is one float32
+    division of 2 tau (exact) by the integer, correctly rounded.
+    """
+    t = np.float32(tau)
+    a = np.float32((t + t) / np.float32(255.0))
+    b = np.float32((t + t) / np.float32(765.0))
+    return a, b
 
 
 def quantize_int2(xr: np.ndarray, tau: np.float32, group: int = GROUP_CHANNELS) -> QuantizedTokens:
@@ -319,11 +340,16 @@ def quantize_int2(xr: np.ndarray, tau: np.float32, group: int = GROUP_CHANNELS) 
     [B] serving: per-token asymmetric INT2 with G_K = 64 channels per group,
     after clipping to the calibration threshold.  Readings: groups are
     consecutive channels of the rotated, permuted vector; min-max range after
-    the clip; s = (max - min) / 3; the float zero point is the group minimum
-    (x^ = code * s + z); scale and zero are stored as float16 and the codes
-    are computed against the stored (rounded) values; round half to even and
-    clamp to [0, 3]; a zero stored scale gives all-zero codes.  All steps in
-    float32 (IEEE subtract and divide).
+    the clip; s = (max - min) / 3; the zero point is the group minimum
+    (x^ = code * s + z).  Metadata: 16 bits per group, the density that the
+    pages' 2.28 bits per element at 128K implies (2 code bits + 16 / 64 per
+    element, plus the BF16 windows).  Zero and scale are stored as 8-bit
+    codes on grids spanning [-tau, tau] and [0, 2 tau / 3] (see
+    ``metadata_steps``): z8 = rint((min + tau) / a), s8 = rint(s / b), each
+    clamped to [0, 255] (0 when tau is 0).  The codes are computed against
+    the decoded values z^ = z8 a - tau and s^ = s8 b: code = rint((x - z^) /
+    s^) clamped to [0, 3], all codes 0 if s^ == 0.  All steps in float32
+    (IEEE add, subtract, multiply and divide; round half to even).
     """
     xr = np.asarray(xr, dtype=np.float32)
     n, d = xr.shape
@@ -334,15 +360,19 @@ def quantize_int2(xr: np.ndarray, tau: np.float32, group: int = GROUP_CHANNELS) 
     mx = np.max(xc, axis=-1)
     mn = np.min(xc, axis=-1)
     s = (mx - mn) / np.float32(3.0)
-    s16 = s.astype(np.float16)
-    z16 = mn.astype(np.float16)
-    sf = s16.astype(np.float32)[..., None]
-    zf = z16.astype(np.float32)[..., None]
+    a, b = metadata_steps(t)
+    lev = np.float32(META_LEVELS)
+    z8 = np.clip(np.rint((mn + t) / a), 0, lev) if a > 0 else np.zeros_like(mn)
+    s8 = np.clip(np.rint(s / b), 0, lev) if b > 0 else np.zeros_like(s)
+    z8 = z8.astype(np.uint8)
+    s8 = s8.astype(np.uint8)
+    zf = z8.astype(np.float32) * a - t
+    sf = s8.astype(np.float32) * b
     with np.errstate(divide="ignore", invalid="ignore"):
-        q = np.rint((xc - zf) / sf)
-    q = np.where(sf == 0, np.float32(0), q)
+        q = np.rint((xc - zf[..., None]) / sf[..., None])
+    q = np.where(sf[..., None] == 0, np.float32(0), q)
     codes = np.clip(q, 0, INT2_LEVELS - 1).astype(np.uint8).reshape(n, d)
-    return QuantizedTokens(codes=codes, scale=s16, zero=z16)
+    return QuantizedTokens(codes=codes, s8=s8, z8=z8, scale=sf, zero=zf)
 
 
 def pack_codes(codes: np.ndarray) -> np.ndarray:
@@ -367,7 +397,7 @@ def unpack_codes(packed: np.ndarray) -> np.ndarray:
 
 def dequantize_int2(codes: np.ndarray, scale: np.ndarray, zero: np.ndarray,
                     group: int = GROUP_CHANNELS) -> np.ndarray:
-    """x^ = code * s + z per group, in float64 from the stored float16 s, z."""
+    """x^ = code * s + z per group, in float64 from the decoded float32 s, z."""
     c = np.asarray(codes, dtype=np.float64)
     n, d = c.shape
     s = np.asarray(scale, dtype=np.float64)[..., None]
@@ -536,6 +566,6 @@ def effective_bits_per_element(L: int, history_bits: float, sink: int = SINK_TOK
 
 
 def history_bits_per_element(d: int = 128, group: int = GROUP_CHANNELS,
-                             metadata_bits_per_group: int = 32) -> float:
+                             metadata_bits_per_group: int = 16) -> float:
     """2 code bits plus the per-group metadata spread over the group."""
     return 2.0 + metadata_bits_per_group / group

@@ -69,9 +69,11 @@ def test_bit_accounting_reproduces_page_figures():
         assert round(bpe, 2) == g[key]["value"], (key, bpe)
     share = 100.0 * (O.SINK_TOKENS + O.RECENT_TOKENS) / g["bf16_window_share_percent_128k"]["context_tokens"]
     assert round(share, 2) == g["bf16_window_share_percent_128k"]["value"]
-    # this build's fp16 scale + fp16 zero per 64-channel group
-    assert O.history_bits_per_element() == 2.5
-    assert abs(O.effective_bits_per_element(102400, 2.5) - 260320 / 102400) < 1e-12
+    # the stored format: 8-bit zero + 8-bit scale per 64-channel group
+    assert O.history_bits_per_element() == 2.25
+    assert abs(O.effective_bits_per_element(102400, 2.25) - (320 * 16 + 102080 * 2.25) / 102400) < 1e-12
+    qt = O.quantize_int2(np.zeros((3, D), np.float32), np.float32(1.0))
+    assert qt.s8.dtype == np.uint8 and qt.z8.dtype == np.uint8 and qt.s8.shape == (3, D // 64)
 
 
 # --- Hadamard and butterfly (P-c) and Lemma 1 (P-b) -------------------------
@@ -192,73 +194,78 @@ def test_pack_unpack_exhaustive():
 # --- quantiser (P-f) ----------------------------------------------------------
 
 def test_quantizer_grid_values_exact():
-    """Values on the grid z + k s (s, z exact in fp16) get code k exactly."""
+    """tau = 382.5: the zero grid (255 steps over [-tau, tau]) has step 3 and
+    the scale grid (255 steps over [0, 2 tau / 3]) step 1, both exact, so
+    zero = 3 z8 - 382.5 and scale = s8.  Values z + k s with the group's
+    minimum and maximum present come back with codes k, metadata (z8, s8)
+    and exact dequantised values."""
     g = np.random.default_rng(4)
-    k = g.integers(0, 4, size=(3, D))
-    k[:, 0] = 0
-    k[:, 1] = 3                      # make min and max present in both groups
-    k[:, 64] = 0
-    k[:, 65] = 3
-    s, z = np.float32(0.25), np.float32(-0.5)
-    x = (z + k * s).astype(np.float32)
-    qt = O.quantize_int2(x, np.float32(100.0))
-    assert np.array_equal(qt.codes, k)
-    assert np.all(qt.scale == np.float16(0.25)) and np.all(qt.zero == np.float16(-0.5))
-    assert np.array_equal(O.dequantize_int2(qt.codes, qt.scale, qt.zero), x.astype(np.float64))
+    tau = np.float32(382.5)
+    n = 64
+    z8 = g.integers(0, 200, size=(n, 2))
+    s8 = np.minimum(g.integers(1, 86, size=(n, 2)), (255 - z8) // 3)   # z + 3 s <= tau
+    k = g.integers(0, 4, size=(n, 2, 64))
+    k[:, :, 0] = 0
+    k[:, :, 1] = 3
+    x = (3.0 * z8[..., None] - 382.5 + k * s8[..., None]).reshape(n, D)
+    assert np.all(np.abs(x) <= 382.5)
+    qt = O.quantize_int2(x.astype(np.float32), tau)
+    assert np.array_equal(qt.z8, z8) and np.array_equal(qt.s8, s8)
+    assert np.array_equal(qt.codes, k.reshape(n, D))
+    assert np.array_equal(O.dequantize_int2(qt.codes, qt.scale, qt.zero), x)
 
 
 def test_quantizer_hand_example():
-    """A hand-worked group: min -1, max 2 -> s = 1, z = -1; x = 0.5 is a tie
-    between codes 1 and 2 and rounds to the even code 2; 1.4 -> 2; -0.6 -> 0."""
-    x = np.zeros((1, D), dtype=np.float32)
-    x[0, :64] = 0.0
-    x[0, 0], x[0, 1], x[0, 2], x[0, 3], x[0, 4] = -1.0, 2.0, 0.5, 1.4, -0.6
-    x[0, 64:] = 7.0                  # constant group above tau
-    qt = O.quantize_int2(x, np.float32(5.0))
-    assert qt.scale[0, 0] == np.float16(1.0) and qt.zero[0, 0] == np.float16(-1.0)
-    assert qt.codes[0, :5].tolist() == [0, 3, 2, 2, 0]
-    assert qt.codes[0, 5] == 1       # 0.0 -> (0 - -1)/1 = 1
-    # clipped constant group: all values become tau = 5, range 0
-    assert qt.scale[0, 1] == 0 and qt.zero[0, 1] == np.float16(5.0)
-    assert np.all(qt.codes[0, 64:] == 0)
+    """Hand-worked, tau = 382.5 (zero step 3, scale step 1):
+    group 0 = {-351.1, -320, -337, -331, -306.1, rest -330}: min -351.1 ->
+    (min + tau) / 3 = 10.467 -> z8 = 10, zero -352.5; range 45 -> s = 15 ->
+    s8 = 15.  Codes: (-351.1 + 352.5) / 15 = 0.093 -> 0; -320 -> 2.167 -> 2;
+    -337 -> 1.033 -> 1; -331 -> 1.433 -> 1; -306.1 -> 3.093 -> 3; -330 ->
+    1.5, a tie, to the even code 2.
+    group 1: every value 500 is clipped to tau: range 0 -> s8 = 0, all codes
+    0; (tau + tau) / 3 = 255 -> z8 = 255."""
+    x = np.full((1, D), -330.0, dtype=np.float32)
+    x[0, :5] = [-351.1, -320.0, -337.0, -331.0, -306.1]
+    x[0, 64:] = 500.0
+    qt = O.quantize_int2(x, np.float32(382.5))
+    assert qt.z8[0].tolist() == [10, 255] and qt.s8[0].tolist() == [15, 0]
+    assert qt.zero[0, 0] == np.float32(-352.5) and qt.scale[0, 0] == np.float32(15.0)
+    assert qt.codes[0, :6].tolist() == [0, 2, 1, 1, 3, 2]
+    assert np.all(qt.codes[0, 64:] == 0) and qt.scale[0, 1] == 0
+
+
+def test_quantizer_degenerate():
+    """tau = 0 clips everything to 0: all metadata and codes are 0.  A constant
+    group has scale code 0 and its zero within half a zero step."""
+    qt = O.quantize_int2(np.random.default_rng(9).standard_normal((4, D)).astype(np.float32), np.float32(0.0))
+    assert not qt.codes.any() and not qt.s8.any() and not qt.z8.any()
+    assert np.all(qt.zero == 0) and np.all(qt.scale == 0)
+    x = np.full((1, D), 0.37, dtype=np.float32)
+    qt = O.quantize_int2(x, np.float32(2.0))
+    assert np.all(qt.s8 == 0) and not qt.codes.any()
+    assert np.all(np.abs(qt.zero.astype(np.float64) - 0.37) <= 0.5 * 4.0 / 255 + 1e-6)
 
 
 def test_quantizer_properties():
+    """Random tokens: codes in [0, 3], group min -> code 0, group max -> code 3
+    (up to the metadata rounding), and every dequantised value within half a
+    scale step plus the metadata rounding (half a zero step 2 tau / 255, and
+    three times half a scale step 2 tau / 765) of the clipped value."""
     g = np.random.default_rng(5)
     x = (g.standard_normal((200, D)) * 3).astype(np.float32)
     tau = np.float32(4.0)
     qt = O.quantize_int2(x, tau)
-    xc = np.clip(x, -tau, tau).reshape(200, 2, 64)
+    xc = np.clip(x, -tau, tau).reshape(200, 2, 64).astype(np.float64)
     c = qt.codes.reshape(200, 2, 64)
     assert c.max() <= 3
-    am = np.argmin(xc, axis=-1)
-    ax = np.argmax(xc, axis=-1)
-    assert np.all(np.take_along_axis(c, am[..., None], -1) == 0)
-    assert np.all(np.take_along_axis(c, ax[..., None], -1) == 3)
-    xh = O.dequantize_int2(qt.codes, qt.scale, qt.zero).reshape(200, 2, 64)
-    s = qt.scale.astype(np.float64)[..., None]
+    zs, ss = 2 * 4.0 / 255, 2 * 4.0 / 765
     z = qt.zero.astype(np.float64)[..., None]
-    bound = s / 2 + np.abs(z - xc.min(-1, keepdims=True)) + 3 * 2.0 ** -11 * s + 1e-6
+    s = qt.scale.astype(np.float64)[..., None]
+    assert np.all(np.abs(z - xc.min(-1, keepdims=True)) <= zs / 2 * (1 + 1e-5))
+    assert np.all(np.abs(s - (xc.max(-1, keepdims=True) - xc.min(-1, keepdims=True)) / 3) <= ss / 2 * (1 + 1e-5))
+    xh = O.dequantize_int2(qt.codes, qt.scale, qt.zero).reshape(200, 2, 64)
+    bound = s / 2 + zs / 2 + 3 * ss / 2 + 1e-5
     assert np.all(np.abs(xh - xc) <= bound)
-
-
-def test_naive_int2_special_case():
-    """With tau above every value, quantize_int2 is plain per-token min-max
-    INT2; compare with an element-by-element loop written from that definition."""
-    g = np.random.default_rng(6)
-    x = g.standard_normal((4, D)).astype(np.float32)
-    qt = O.quantize_int2(x, np.float32(1e4))
-    for t in range(4):
-        for gi in range(2):
-            seg = [float(v) for v in x[t, gi * 64:(gi + 1) * 64]]
-            lo, hi = min(seg), max(seg)
-            s16 = np.float16(np.float32(np.float32(hi) - np.float32(lo)) / np.float32(3))
-            z16 = np.float16(lo)
-            assert qt.scale[t, gi] == s16 and qt.zero[t, gi] == z16
-            for j, v in enumerate(seg):
-                r = (np.float32(v) - np.float32(z16)) / np.float32(s16)
-                want = min(3, max(0, int(np.rint(r))))
-                assert qt.codes[t, gi * 64 + j] == want
 
 
 # --- write-path rotation ------------------------------------------------------
