@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "INT2-KV decode attention µs/step + achieved HBM GB/s at 100K ctx, batch 1/32"
 HBM_PEAK_GBPS = 8000.0
 D = 128
-HIST_BYTES_PER_TOKEN_HEAD = 80      # 64 B codes (K+V) + 16 B fp16 scale/zero (K+V)
+HIST_BYTES_PER_TOKEN_HEAD = 72      # 64 B codes (K+V) + 8 B metadata codes (K+V, 16 bits per group)
 
 # HBM traffic of the scan kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
 # recorded with a hash of the kernel sources it was measured on; reported
@@ -404,8 +404,8 @@ def cpu_baseline(wl, pairs, reps):
                       f"{reps} runs each; GB/s over the same algorithmic bytes as the GPU"}
 
 
-def effective_bpe(L, sink=64, recent=256, history_bits=2.0 + 32.0 / 64):
-    """Stored bits per KV element: BF16 windows + INT2 codes with fp16 scale and zero per 64 channels."""
+def effective_bpe(L, sink=64, recent=256, history_bits=2.0 + 16.0 / 64):
+    """Stored bits per KV element: BF16 windows + INT2 codes with 16 metadata bits per 64 channels."""
     win = min(L, sink + recent)
     return (win * 16.0 + (L - win) * history_bits) / L
 

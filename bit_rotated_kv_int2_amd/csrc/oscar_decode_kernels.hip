@@ -80,11 +80,17 @@ __device__ __forceinline__ v4i unpack16(uint32_t w) {
   return r;
 }
 
-// fp16 halves of a word; written as a vector element so the compiler can fold
-// the conversion into mixed-precision FMAs (op_sel) instead of converting
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ float lo_h(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w).x; }
-__device__ __forceinline__ float hi_h(uint32_t w) { return (float)__builtin_bit_cast(half2_t, w).y; }
+// Byte i of a word as a float (one v_cvt_f32_ubyte<i>).
+__device__ __forceinline__ float ubyte_f(uint32_t w, int i) { return (float)((w >> (8 * i)) & 0xFFu); }
+
+// Metadata grid steps of one KV head (zero z8 * a - tau, scale s8 * b).
+struct MetaSteps {
+  float ka, kb, ktau, va, vb, vtau;
+};
+__device__ __forceinline__ MetaSteps meta_steps(const RotView &rv, int kv) {
+  const float tk = rv.tau_K[kv], tv = rv.tau_V[kv];
+  return MetaSteps{meta_zero_step(tk), meta_scale_step(tk), tk, meta_zero_step(tv), meta_scale_step(tv), tv};
+}
 
 // Byte 2 / byte 1 / byte 0 of four words gathered into one word (word i -> byte i).
 __device__ __forceinline__ uint32_t gather_b2(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
@@ -324,20 +330,18 @@ __global__ void __launch_bounds__(256) decode_pre_kernel(DecArgs a) {
 // ===========================================================================
 struct PageRegs {
   uint2 kc[4];
-  uint4 km0, km1;
+  uint4 km;          // metadata of tokens 16 tt + n, tt = 0..3: {s8_0, z8_0, s8_1, z8_1}
   uint32_t vc[8];
-  uint4 vm0, vm1;
+  uint4 vm;
 };
 
 __device__ __forceinline__ void load_page(PageRegs &r, const uint8_t *P, int n, int q) {
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) r.kc[tt] = *(const uint2 *)(P + kKCodes + (16 * tt + n) * 32 + 8 * q);
-  r.km0 = *(const uint4 *)(P + kKMeta + 32 * n);
-  r.km1 = *(const uint4 *)(P + kKMeta + 32 * n + 16);
+  r.km = *(const uint4 *)(P + kKMeta + 16 * n);
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) r.vc[nt] = *(const uint32_t *)(P + kVCodes + (16 * nt + n) * 16 + 4 * q);
-  r.vm0 = *(const uint4 *)(P + kVMeta + 32 * n);
-  r.vm1 = *(const uint4 *)(P + kVMeta + 32 * n + 16);
+  r.vm = *(const uint4 *)(P + kVMeta + 16 * n);
 }
 
 template <int MT>
@@ -356,6 +360,19 @@ __device__ __forceinline__ void rescale(HistState<MT> &st, int mt, float alpha) 
   st.z1[mt] *= alpha;
 }
 
+// Logit operands of one wave: the int8 query (A operand, hi/lo rows per
+// group) and per-lane-row constants.  With metadata codes (s8, z8) of a
+// token, its logit (log2 units) is
+//   fma(fma(s8_0, x0, s8_1 x1), qa, fma(z8_0, qb0, fma(z8_1, qb1, qc)))
+// where x_g is the integer dot product of group g, qa = delta b sl2,
+// qb_g = Q_g a sl2 and qc = -tau (Q_0 + Q_1) sl2 (a, b: the head's zero and
+// scale steps; delta: the query's fixed-point step; Q_g: its group sums).
+template <int MT>
+struct QueryOps {
+  v4i A[MT][2];
+  float qa[MT], qb0[MT], qb1[MT], qc[MT];
+};
+
 // One 64-token history page for MT M-tiles of 4 query heads.
 //
 // Logits: int8 MFMA of the 15-bit query (hi/lo rows, one per 64-channel
@@ -368,27 +385,26 @@ __device__ __forceinline__ void rescale(HistState<MT> &st, int mt, float alpha) 
 // of the softmax mass can sit in weights far below the page maximum.  The
 // zero-point part sum(w * zero) stays in float.
 template <int MT, bool FULL>
-__device__ __forceinline__ void int2_page(const PageRegs &r, int valid, const v4i (&Aq)[MT][2],
-                                          const float (&qa)[MT], const float (&qb0)[MT],
-                                          const float (&qb1)[MT], HistState<MT> &st, v4i *wl) {
+__device__ __forceinline__ void int2_page(const PageRegs &r, int valid, const QueryOps<MT> &qo, HistState<MT> &st,
+                                          v4i *wl) {
   const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
-  const uint32_t kmw[8] = {r.km0.x, r.km0.y, r.km0.z, r.km0.w, r.km1.x, r.km1.y, r.km1.z, r.km1.w};
-  const uint32_t vmw[8] = {r.vm0.x, r.vm0.y, r.vm0.z, r.vm0.w, r.vm1.x, r.vm1.y, r.vm1.z, r.vm1.w};
+  const uint32_t kmw[4] = {r.km.x, r.km.y, r.km.z, r.km.w};
+  const uint32_t vmw[4] = {r.vm.x, r.vm.y, r.vm.z, r.vm.w};
   float lg[MT][4];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
     const v4i B0 = unpack16(r.kc[tt].x);
     const v4i B1 = unpack16(r.kc[tt].y);
-    const float s0 = lo_h(kmw[2 * tt]), z0 = hi_h(kmw[2 * tt]);
-    const float s1 = lo_h(kmw[2 * tt + 1]), z1 = hi_h(kmw[2 * tt + 1]);
+    const float s0 = ubyte_f(kmw[tt], 0), z0 = ubyte_f(kmw[tt], 1);
+    const float s1 = ubyte_f(kmw[tt], 2), z1 = ubyte_f(kmw[tt], 3);
     const bool ok = FULL || (16 * tt + n) < valid;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      v4i C = mfma_i8(Aq[mt][0], B0, v4i{0, 0, 0, 0});
-      C = mfma_i8(Aq[mt][1], B1, C);
+      v4i C = mfma_i8(qo.A[mt][0], B0, v4i{0, 0, 0, 0});
+      C = mfma_i8(qo.A[mt][1], B1, C);
       const float x0 = (float)(C[0] * 256 + C[1]);
       const float x1 = (float)(C[2] * 256 + C[3]);
-      const float v = fmaf(fmaf(s0, x0, s1 * x1), qa[mt], fmaf(z0, qb0[mt], z1 * qb1[mt]));
+      const float v = fmaf(fmaf(s0, x0, s1 * x1), qo.qa[mt], fmaf(z0, qo.qb0[mt], fmaf(z1, qo.qb1[mt], qo.qc[mt])));
       lg[mt][tt] = ok ? v : -INFINITY;
     }
   }
@@ -412,8 +428,8 @@ __device__ __forceinline__ void int2_page(const PageRegs &r, int valid, const v4
       // masked tokens: e = 0, and their (unwritten) metadata is not used
       const bool ok = FULL || (16 * tt + n) < valid;
       const float e = exp2_fast(lg[mt][tt] - st.mref[mt]);
-      const float vs0 = lo_h(vmw[2 * tt]), vz0 = hi_h(vmw[2 * tt]);
-      const float vs1 = lo_h(vmw[2 * tt + 1]), vz1 = hi_h(vmw[2 * tt + 1]);
+      const float vs0 = ubyte_f(vmw[tt], 0), vz0 = ubyte_f(vmw[tt], 1);
+      const float vs1 = ubyte_f(vmw[tt], 2), vz1 = ubyte_f(vmw[tt], 3);
       es += e;
       ez0 = ok ? fmaf(e, vz0, ez0) : ez0;
       ez1 = ok ? fmaf(e, vz1, ez1) : ez1;
@@ -477,18 +493,20 @@ struct ValuWave {
 
 template <bool FULL>
 __device__ __forceinline__ void int2_page_valu(const uint8_t *P, int valid, int G, const float *qrot,
-                                               const float (*qsum)[2], float sl2, ValuWave st,
-                                               float (*pw)[4]) {
+                                               const float (*qsum)[2], float sl2, const MetaSteps &ms,
+                                               ValuWave st, float (*pw)[4]) {
   const int lane = threadIdx.x & 63;
   const int t = lane;
   const uint4 k0 = *(const uint4 *)(P + kKCodes + t * 32);
   const uint4 k1 = *(const uint4 *)(P + kKCodes + t * 32 + 16);
-  const uint2 km = *(const uint2 *)(P + kKMeta + meta_entry(t) * 8);
-  const uint2 vm = *(const uint2 *)(P + kVMeta + meta_entry(t) * 8);
+  const uint32_t km = *(const uint32_t *)(P + kKMeta + meta_entry(t) * 4);
+  const uint32_t vm = *(const uint32_t *)(P + kVMeta + meta_entry(t) * 4);
   const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
   const bool ok = FULL || t < valid;
-  const float ks0 = lo_h(km.x), kz0 = hi_h(km.x), ks1 = lo_h(km.y), kz1 = hi_h(km.y);
-  const float vs0 = lo_h(vm.x), vz0 = hi_h(vm.x), vs1 = lo_h(vm.y), vz1 = hi_h(vm.y);
+  const float ks0 = ubyte_f(km, 0) * ms.kb, kz0 = ubyte_f(km, 1) * ms.ka - ms.ktau;
+  const float ks1 = ubyte_f(km, 2) * ms.kb, kz1 = ubyte_f(km, 3) * ms.ka - ms.ktau;
+  const float vs0 = ubyte_f(vm, 0) * ms.vb, vz0 = ubyte_f(vm, 1) * ms.va - ms.vtau;
+  const float vs1 = ubyte_f(vm, 2) * ms.vb, vz1 = ubyte_f(vm, 3) * ms.va - ms.vtau;
   const int c0 = 2 * lane, g = lane >> 5;
   const uint4 r0 = *(const uint4 *)(P + kVCodes + c0 * 16);
   const uint4 r1 = *(const uint4 *)(P + kVCodes + (c0 + 1) * 16);
@@ -621,11 +639,16 @@ __device__ __forceinline__ void dma_1k(uint64_t src, uint32_t lds, uint32_t lane
       : "memory");
 }
 
-// Copy one 5120-byte page to LDS: five 1 KB DMA copies (kilobyte j of the
-// page from base + 1024 j to lds + 1024 j; lane_off = 16 lane).
+// Copy one 4608-byte page to LDS: four 1 KB DMA copies (kilobyte j of the
+// page from base + 1024 j to lds + 1024 j; lane_off = 16 lane) and one
+// 512-byte copy of the metadata tail.
 __device__ __forceinline__ void dma_page(uint64_t base, uint32_t lds, uint32_t lane_off) {
+  static_assert(kPageBytes == 4 * 1024 + 512, "a page is four 1 KB copies and a 512-byte tail");
 #pragma unroll
-  for (int j = 0; j < kPageBytes / 1024; ++j) dma_1k(base + 1024u * j, lds + 1024u * j, lane_off);
+  for (int j = 0; j < 4; ++j) dma_1k(base + 1024u * j, lds + 1024u * j, lane_off);
+  // tail: lanes 0..31 move 16 bytes each (the instruction still counts once
+  // in vmcnt, so a page is five copies either way)
+  if (lane_off < 512u) dma_1k(base + 4096u, lds + 4096u, lane_off);
 }
 
 template <int GH, bool UVL = false>
@@ -700,13 +723,14 @@ __device__ void bf16_tile_partial(const DecArgs &a, int b, int kv, int u, float 
   // sum the four token phases, stage o in LDS, store coalesced
 #pragma unroll
   for (int h = 0; h < GH; ++h) {
-    if (h >= G) break;
+    if (h < G) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float v = o[h][c];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      if (q == 0) scratch[h][8 * n + c] = v;
+      for (int c = 0; c < 8; ++c) {
+        float v = o[h][c];
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        if (q == 0) scratch[h][8 * n + c] = v;
+      }
     }
   }
   if (n == 0) {
@@ -810,8 +834,7 @@ __device__ __forceinline__ void pipe_prologue(PagePipe<NW, PF> &p, const PoolVie
 
 // Consume every page of the pipeline (the prologue must have been issued).
 template <int MT, int NW, int PF>
-__device__ __forceinline__ void pipe_scan(PagePipe<NW, PF> &p, const PoolView &pv, int n_hist, const v4i (&Aq)[MT][2],
-                                          const float (&qa)[MT], const float (&qb0)[MT], const float (&qb1)[MT],
+__device__ __forceinline__ void pipe_scan(PagePipe<NW, PF> &p, const PoolView &pv, int n_hist, const QueryOps<MT> &qo,
                                           HistState<MT> &st, v4i *wl, int lane) {
   const int n = lane & 15, q = lane >> 4;
   for (int i = 0; i < p.npg; ++i) {
@@ -830,8 +853,8 @@ __device__ __forceinline__ void pipe_scan(PagePipe<NW, PF> &p, const PoolView &p
     }
     if (ok) {
       const int valid = min(kPageTokens, n_hist - (p.first + i * NW) * kPageTokens);
-      if (valid == kPageTokens) int2_page<MT, true>(cur, valid, Aq, qa, qb0, qb1, st, wl);
-      else int2_page<MT, false>(cur, valid, Aq, qa, qb0, qb1, st, wl);
+      if (valid == kPageTokens) int2_page<MT, true>(cur, valid, qo, st, wl);
+      else int2_page<MT, false>(cur, valid, qo, st, wl);
     }
   }
 }
@@ -847,32 +870,38 @@ __device__ __forceinline__ void hist_reset(HistState<MT> &st) {
   }
 }
 
-// Query operands of one head group into registers, from prepared LDS copies.
+// Query operands of one head group into registers, from prepared LDS copies
+// (qc[h] = {delta, Q_0, Q_1}), with the K metadata steps of the KV head
+// folded in (see QueryOps).
 template <int MT, int GH>
-__device__ __forceinline__ void load_query_ops(const v4i *aq, const float (*qc)[4], int G, float sl2, int lane,
-                                               v4i (&Aq)[MT][2], float (&qa)[MT], float (&qb0)[MT],
-                                               float (&qb1)[MT]) {
+__device__ __forceinline__ void load_query_ops(const v4i *aq, const float (*qc)[4], int G, float sl2,
+                                               const MetaSteps &ms, int lane, QueryOps<MT> &qo) {
   const int q = lane >> 4;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    Aq[mt][0] = aq[(mt * 2 + 0) * 64 + lane];
-    Aq[mt][1] = aq[(mt * 2 + 1) * 64 + lane];
+    qo.A[mt][0] = aq[(mt * 2 + 0) * 64 + lane];
+    qo.A[mt][1] = aq[(mt * 2 + 1) * 64 + lane];
     const int h = min(4 * mt + q, GH - 1);
     const bool hv = 4 * mt + q < G;
-    qa[mt] = hv ? qc[h][0] * sl2 : 0.f;
-    qb0[mt] = hv ? qc[h][1] * sl2 : 0.f;
-    qb1[mt] = hv ? qc[h][2] * sl2 : 0.f;
+    const float q0 = hv ? qc[h][1] * sl2 : 0.f, q1 = hv ? qc[h][2] * sl2 : 0.f;
+    qo.qa[mt] = hv ? qc[h][0] * sl2 * ms.kb : 0.f;
+    qo.qb0[mt] = q0 * ms.ka;
+    qo.qb1[mt] = q1 * ms.ka;
+    qo.qc[mt] = -ms.ktau * (q0 + q1);
   }
 }
 
 // Every wave's history state -> one (m, l, o) partial of the workgroup.
 // The page buffers must be idle (sm.o aliases them).
 template <int MT, int GH, int NW>
-__device__ void flush_partial(ScanSmem<MT, GH, NW, true> &sm, HistState<MT> &st, int G, float *dst) {
+__device__ void flush_partial(ScanSmem<MT, GH, NW, true> &sm, HistState<MT> &st, int G, const MetaSteps &ms,
+                              float *dst) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, q = lane >> 4;
   __syncthreads();
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
+    // value sums are kept in metadata code units: sum w s8 code and sum w z8
+    // become sum w (s8 b) code and sum w (z8 a - tau)
     const float l16 = row16_sum(st.lsum[mt]);
     const float z0 = row16_sum(st.z0[mt]);
     const float z1 = row16_sum(st.z1[mt]);
@@ -880,11 +909,11 @@ __device__ void flush_partial(ScanSmem<MT, GH, NW, true> &sm, HistState<MT> &st,
     if (n == 0) {
       sm.m[wave][hh] = st.mref[mt];
       sm.l[wave][hh] = l16;
-      sm.z[wave][hh][0] = z0;
-      sm.z[wave][hh][1] = z1;
+      sm.z[wave][hh][0] = fmaf(z0, ms.va, -ms.vtau * l16);
+      sm.z[wave][hh][1] = fmaf(z1, ms.va, -ms.vtau * l16);
     }
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) sm.o[wave][hh][16 * nt + n] = st.facc[mt][nt];
+    for (int nt = 0; nt < 8; ++nt) sm.o[wave][hh][16 * nt + n] = st.facc[mt][nt] * ms.vb;
   }
   __syncthreads();
   write_split_partial<MT, GH, NW, true>(sm, G, dst, true);
@@ -912,9 +941,9 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
 
   // query operands, prepared by the workgroup while the first pages load
   query_prep<MT, GH>(a, b, kv, sm.q, nullptr);
-  v4i Aq[MT][2];
-  float qa[MT], qb0[MT], qb1[MT];
-  load_query_ops<MT, GH>(sm.q.aq, sm.q.qc, G, pv.sm_scale * kLog2e, lane, Aq, qa, qb0, qb1);
+  const MetaSteps ms = meta_steps(a.rv, kv);
+  QueryOps<MT> qo;
+  load_query_ops<MT, GH>(sm.q.aq, sm.q.qc, G, pv.sm_scale * kLog2e, ms, lane, qo);
   __syncthreads();   // the query scratch is reused by the BF16 tiles and the weights
   // BF16 tile u (sink, then recent window) runs on workgroup u % S and, from
   // the last wave down, on the waves that hold the fewest history pages
@@ -934,9 +963,9 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   // complete the query operands here (and with them the first copies), so that
   // no wait for them is left inside the loop
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  pipe_scan<MT, NW, PF>(pipe, pv, n_hist, Aq, qa, qb0, qb1, st, wl, lane);
+  pipe_scan<MT, NW, PF>(pipe, pv, n_hist, qo, st, wl, lane);
   if (pipe.bad && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
-  flush_partial<MT, GH, NW>(sm, st, G, dst);
+  flush_partial<MT, GH, NW>(sm, st, G, ms, dst);
 }
 
 template <int MT, int GH, int NW>
@@ -972,6 +1001,7 @@ __device__ void run_scan_valu(const DecArgs &a, int b, int kv, int split, float 
   __syncthreads();
   const ValuWave st{sm.m[wave], sm.l[wave], sm.vacc[wave]};
   const float sl2 = pv.sm_scale * kLog2e;
+  const MetaSteps ms = meta_steps(a.rv, kv);
   const int32_t *btab = pv.block_table + (size_t)b * pv.max_pages;
   bool bad = false;
   for (int pg = pg0 + wave; pg < pg1; pg += NW) {
@@ -982,8 +1012,8 @@ __device__ void run_scan_valu(const DecArgs &a, int b, int kv, int split, float 
     }
     const uint8_t *P = pv.pages + ((size_t)ph * pv.hkv + kv) * kPageBytes;
     const int valid = min(kPageTokens, n_hist - pg * kPageTokens);
-    if (valid == kPageTokens) int2_page_valu<true>(P, valid, G, qrot, sm.qsum, sl2, st, sm.wave[wave].pw);
-    else int2_page_valu<false>(P, valid, G, qrot, sm.qsum, sl2, st, sm.wave[wave].pw);
+    if (valid == kPageTokens) int2_page_valu<true>(P, valid, G, qrot, sm.qsum, sl2, ms, st, sm.wave[wave].pw);
+    else int2_page_valu<false>(P, valid, G, qrot, sm.qsum, sl2, ms, st, sm.wave[wave].pw);
   }
   if (bad && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
   __syncthreads();
@@ -1389,9 +1419,9 @@ decode_flat_kernel(DecArgs a) {
                                   prep.aq, prep.qc);
     }
     const int slot = si % kFlatPrep;
-    v4i Aq[1][2];
-    float qa[1], qb0[1], qb1[1];
-    load_query_ops<1, GH>(prep.aq[slot], prep.qc[slot], G, sl2, lane, Aq, qa, qb0, qb1);
+    const MetaSteps ms = meta_steps(a.rv, sg.kv);
+    QueryOps<1> qo;
+    load_query_ops<1, GH>(prep.aq[slot], prep.qc[slot], G, sl2, ms, lane, qo);
     __syncthreads();   // operands read; the wave scratch is reused below
     // BF16 tiles of this segment, from the last wave down
     float *tile_parts = a.part_tile + (size_t)bh * NT * G * kPartStride;
@@ -1404,9 +1434,9 @@ decode_flat_kernel(DecArgs a) {
     for (int i = 0; i < 2; ++i) wl[i * 64 + lane] = v4i{0, 0, 0, 0};
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     const int L = max(0, pv.seq_lens[sg.b]);
-    pipe_scan<1, NW, PF>(pipe, pv, max(0, L - pv.sink - pv.recent), Aq, qa, qb0, qb1, st, wl, lane);
+    pipe_scan<1, NW, PF>(pipe, pv, max(0, L - pv.sink - pv.recent), qo, st, wl, lane);
     if (pipe.bad && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
-    flush_partial<1, GH, NW>(sm.s, st, G, a.part + ((size_t)blockIdx.x + bh) * G * kPartStride);
+    flush_partial<1, GH, NW>(sm.s, st, G, ms, a.part + ((size_t)blockIdx.x + bh) * G * kPartStride);
     if (arrive_last(&a.counters[bh], sg.last_blk - sg.first_blk + 1, &last_flag) && tid == 0)
       merge_list[seg_info[1]++] = si;
     __syncthreads();

@@ -1,5 +1,5 @@
 // Internal declarations shared by the translation units of liboscar.so.
-// Geometry of the page block and the bf16/fp16 helpers used on the device.
+// Geometry of the page block and the bf16 / metadata helpers used on the device.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -28,17 +28,18 @@ __host__ __device__ constexpr int bitrev7(int p) {
          ((p & 32) >> 4) | ((p & 64) >> 6);
 }
 
-// Metadata entry of token slot t: slots t, t+16, t+32, t+48 are adjacent so a
-// lane owning slot-column t&15 reads its four tokens with one 32-byte load.
+// Metadata entry (4 bytes) of token slot t: slots t, t+16, t+32, t+48 are
+// adjacent so a lane owning slot-column t&15 reads its four tokens with one
+// 16-byte load.
 __host__ __device__ constexpr int meta_entry(int slot) { return 4 * (slot & 15) + (slot >> 4); }
+// Grid steps of the 8-bit metadata of a head with clip threshold tau: a
+// group's zero is z8 * zero_step - tau, its scale s8 * scale_step.
+__device__ __forceinline__ float meta_zero_step(float tau) { return __fdiv_rn(tau + tau, 255.0f); }
+__device__ __forceinline__ float meta_scale_step(float tau) { return __fdiv_rn(tau + tau, 765.0f); }
 // Byte (within a 16-byte V channel row) that holds token slot t; bits 2*(t&3).
 __host__ __device__ constexpr int vcode_byte(int slot) { return 4 * ((slot >> 2) & 3) + (slot >> 4); }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
-__device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
-__device__ __forceinline__ uint16_t f32_to_f16_rn(float x) {
-  return __builtin_bit_cast(uint16_t, (_Float16)x);
-}
 
 // Orders LDS traffic between the lanes of one wave (compiler fence plus the
 // hardware wait); waves never wait for each other here.

@@ -9,17 +9,22 @@
 // per-token asymmetric INT2 with 64-channel groups) and section
 // "OSCAR 有何不同做法" (R = U · H_Had · P_br).
 //
-// Arithmetic order (fixed so that codes and fp16 metadata are reproducible
-// bit for bit by any implementation that follows it):
+// Arithmetic order (fixed so that codes and metadata are reproducible bit
+// for bit by any implementation that follows it):
 //   S1 y_j = sum_k x_k U[k][j], float64, k ascending (bf16 x float32
 //      products are exact in float64, so fma == multiply-then-add);
 //   S2 radix-2 butterfly, stages h = 1..64, (a, b) -> (a + b, a - b), float64;
 //   S3 multiply by the float64 nearest to 1/sqrt(128);
 //   S4 output channel p takes butterfly output bitrev(p);
 //   S5 round to float32; S6 clamp to [-tau, tau];
-//   S7 per 64-channel group: s = (max - min) / 3 (float32 IEEE),
-//      scale = fp16(s), zero = fp16(min), code = clamp(rint((x - zero)/scale),
-//      0, 3) in float32 with the stored values, all codes 0 if scale == 0.
+//   S7 per 64-channel group: s = (max - min) / 3 (float32 IEEE); with
+//      a = (tau + tau) / 255 and b = (tau + tau) / 765: z8 = clamp(rint((min +
+//      tau) / a), 0, 255), s8 = clamp(rint(s / b), 0, 255) (0 if tau is 0);
+//      zero = z8 a - tau, scale = s8 b; code = clamp(rint((x - zero) /
+//      scale), 0, 3), all codes 0 if scale == 0.  Everything float32 (16
+//      metadata bits per group: the density of the pages' 2.28 bits per
+//      element at 128K; the encoding relative to tau is this library's);
+//   S8 pack four codes per byte (page layout in oscar.h).
 #include "oscar_internal.h"
 
 #pragma clang fp contract(off)
@@ -48,30 +53,38 @@ __device__ __forceinline__ float wave_min(float v) {
 }
 
 // S6..S8 for output channel p of one token (this lane; the wave holds the 64
-// channels of one group): clamp, group scale/zero, code.  Returns the code;
-// meta receives the fp16 {scale, zero} pair of the group (same on every lane).
+// channels of one group): clamp, group metadata, code.  Returns the code;
+// meta receives the group's 16-bit metadata s8 | z8 << 8 (same on every
+// lane).  Zero and scale are 8-bit codes on grids over [-tau, tau] and
+// [0, 2 tau / 3] (steps a = 2 tau / 255, b = 2 tau / 765): z8 = rint((min +
+// tau) / a), s8 = rint(s / b), clamped to [0, 255] (0 when tau is 0); codes
+// use the decoded zero z8 a - tau and scale s8 b.
 __device__ __forceinline__ uint32_t quantize_group(float v, float tau, uint32_t &meta) {
   v = fminf(fmaxf(v, -tau), tau);
   const float mx = wave_max(v), mn = wave_min(v);
   const float s = __fdiv_rn(mx - mn, 3.0f);
-  const uint16_t s16 = f32_to_f16_rn(s), z16 = f32_to_f16_rn(mn);
-  const float sf = f16_to_f32(s16), zf = f16_to_f32(z16);
+  const float a = meta_zero_step(tau), b = meta_scale_step(tau);
+  uint32_t z8 = 0, s8 = 0;
+  if (a > 0.0f) z8 = (uint32_t)fminf(fmaxf(rintf(__fdiv_rn(mn + tau, a)), 0.0f), 255.0f);
+  if (b > 0.0f) s8 = (uint32_t)fminf(fmaxf(rintf(__fdiv_rn(s, b)), 0.0f), 255.0f);
+  const float zf = (float)z8 * a - tau;
+  const float sf = (float)s8 * b;
   uint32_t code = 0;
   if (sf != 0.0f) {
     float r = rintf(__fdiv_rn(v - zf, sf));
     r = fminf(fmaxf(r, 0.0f), 3.0f);
     code = (uint32_t)r;
   }
-  meta = (uint32_t)s16 | ((uint32_t)z16 << 16);
+  meta = s8 | (z8 << 8);
   return code;
 }
 
 // As quantize_group for output channel p; lane p % 64 == 0 stores the
-// group's fp16 {scale, zero} pair to meta[p / 64].
-__device__ __forceinline__ uint32_t quantize_code(float v, float tau, int p, uint32_t *meta) {
+// group's metadata to meta[p / 64] (the 4-byte entry of the token).
+__device__ __forceinline__ uint32_t quantize_code(float v, float tau, int p, uint16_t *meta) {
   uint32_t m;
   const uint32_t code = quantize_group(v, tau, m);
-  if ((p & 63) == 0) meta[p >> 6] = m;
+  if ((p & 63) == 0) meta[p >> 6] = (uint16_t)m;
   return code;
 }
 
@@ -206,7 +219,7 @@ append_demote_kernel(AppendArgs a) {
     const uint32_t code0 = quantize_group((e0 >> 6) ? g01 : g00, tau, m0);
     const uint32_t code1 = quantize_group((e1 >> 6) ? g11 : g10, tau, m1);
     if (!valid) continue;
-    if (lane == 0) *(uint2 *)(page + (is_v ? kVMeta : kKMeta) + meta_entry(slot) * 8) = make_uint2(m0, m1);
+    if (lane == 0) *(uint32_t *)(page + (is_v ? kVMeta : kKMeta) + meta_entry(slot) * 4) = m0 | (m1 << 16);
     if (!is_v) {
       // K row: dword q holds channels 16 q .. 16 q + 15, two bits each
       uint32_t k0 = code0 << (2 * (lane & 15)), k1 = code1 << (2 * (lane & 15));
@@ -326,7 +339,7 @@ __global__ void __launch_bounds__(kThreads) append_one_kernel(AppendArgs a) {
       const float tau = (is_v ? a.rv.tau_V : a.rv.tau_K)[h];
       uint8_t *page = pv.pages + ((size_t)phys * pv.hkv + h) * kPageBytes;
       const float v = (float)(ys[bitrev7(p)] * kInvSqrtD);
-      const uint32_t code = quantize_code(v, tau, p, (uint32_t *)(page + (is_v ? kVMeta : kKMeta) + meta_entry(slot) * 8));
+      const uint32_t code = quantize_code(v, tau, p, (uint16_t *)(page + (is_v ? kVMeta : kKMeta) + meta_entry(slot) * 4));
       if (!is_v) {
         uint32_t c = code << (2 * (p & 3));
         c |= __shfl_xor(c, 1, 64);

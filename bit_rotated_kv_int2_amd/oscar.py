@@ -22,8 +22,8 @@ LIB_PATH = os.path.join(HERE, "liboscar.so")
 
 OSCAR_OK, OSCAR_EINVAL, OSCAR_ENOTSUP, OSCAR_EWORKSPACE, OSCAR_EHIP = 0, -1, -2, -3, -4
 DEVERR_PAGE, DEVERR_LENGTH, DEVERR_SINKSLOT = 1, 2, 4
-HEAD_DIM, PAGE_TOKENS, GROUP, PAGE_BYTES = 128, 64, 64, 5120
-PAGE_KCODES, PAGE_VCODES, PAGE_KMETA, PAGE_VMETA = 0, 2048, 4096, 4608
+HEAD_DIM, PAGE_TOKENS, GROUP, PAGE_BYTES = 128, 64, 64, 4608
+PAGE_KCODES, PAGE_VCODES, PAGE_KMETA, PAGE_VMETA = 0, 2048, 4096, 4352
 
 EXPORTED = [
     "oscar_calibrate_rotation", "oscar_quantize_append", "oscar_decode_attention",

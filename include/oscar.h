@@ -26,7 +26,7 @@
  *     entry outside [0, n_pages), a sequence longer than the table) are
  *     skipped by the kernels and reported by OR-ing OSCAR_DEVERR_* bits into
  *     *pool->error_flags when that pointer is non-NULL.
- *   - bf16 and fp16 values are passed as their uint16_t bit patterns.
+ *   - bf16 values are passed as their uint16_t bit patterns.
  *   - All tokens are row vectors; d = head_dim = 128.
  */
 #ifndef OSCAR_H
@@ -59,7 +59,7 @@ enum {
 #define OSCAR_PAGE_TOKENS 64
 #define OSCAR_GROUP 64
 /*
- * One history page holds 64 token slots of one KV head, 5120 bytes:
+ * One history page holds 64 token slots of one KV head, 4608 bytes:
  *   [   0, 2048)  K codes, token-major: row t (32 bytes) is token slot t;
  *                 byte j holds channels 4j..4j+3, channel 4j+i in bits
  *                 [2i, 2i+2).
@@ -67,18 +67,21 @@ enum {
  *                 token slot t sits in byte 4*((t>>2)&3) + (t>>4), bits
  *                 [2*(t&3), 2*(t&3)+2).  (This order lets one 32-bit load
  *                 feed a 16x16x64 int8 MFMA operand directly.)
- *   [4096, 4608)  K metadata: 64 entries of 4 fp16 {scale0, zero0, scale1,
- *                 zero1} (group 0 = rotated channels 0..63, group 1 =
- *                 64..127); token slot t is entry 4*(t&15) + (t>>4).
- *   [4608, 5120)  V metadata, same layout.
+ *   [4096, 4352)  K metadata: 64 entries of 4 bytes {s8_0, z8_0, s8_1, z8_1}
+ *                 (group 0 = rotated channels 0..63, group 1 = 64..127);
+ *                 token slot t is entry 4*(t&15) + (t>>4).
+ *   [4352, 4608)  V metadata, same layout.
  * A page id p addresses pages + (p * num_kv_heads + h) * OSCAR_PAGE_BYTES.
- * Codes are 0..3 and dequantise as code*scale + zero in the rotated basis.
+ * Metadata codes are relative to the KV head's clip threshold tau (tau_K or
+ * tau_V of the rotation): with a = (2 tau) / 255 and b = (2 tau) / 765 (float32
+ * divisions), a group's zero is z8 * a - tau and its scale s8 * b.  Codes are
+ * 0..3 and dequantise as code * scale + zero in the rotated basis.
  */
-#define OSCAR_PAGE_BYTES 5120
+#define OSCAR_PAGE_BYTES 4608
 #define OSCAR_PAGE_KCODES 0
 #define OSCAR_PAGE_VCODES 2048
 #define OSCAR_PAGE_KMETA 4096
-#define OSCAR_PAGE_VMETA 4608
+#define OSCAR_PAGE_VMETA 4352
 
 /* Shape and softmax parameters, validated on every call. */
 typedef struct oscar_params {

@@ -35,19 +35,22 @@ def page_vcodes(page: np.ndarray) -> np.ndarray:
 
 
 def page_meta(page: np.ndarray, off: int):
-    """(scale [64, 2], zero [64, 2]) float16 of a metadata block."""
-    ent = page[off:off + 512].copy().view(np.float16).reshape(64, 4)
+    """(s8 [64, 2], z8 [64, 2]) uint8 metadata codes of a metadata block:
+    64 entries of 4 bytes {s8_0, z8_0, s8_1, z8_1}, slot t at entry
+    4 (t % 16) + t / 16."""
+    ent = page[off:off + 256].reshape(64, 4)
     idx = np.array([4 * (t & 15) + (t >> 4) for t in range(64)])
     e = ent[idx]
-    return e[:, [0, 2]], e[:, [1, 3]]
+    return e[:, [0, 2]].copy(), e[:, [1, 3]].copy()
 
 
 def gather_history(pages: np.ndarray, block_row: np.ndarray, kv: int, n_hist: int):
-    """Canonical codes/scale/zero of the first n_hist history tokens of one
-    sequence and KV head, read from the device page buffer copy."""
+    """Canonical codes and metadata codes (s8, z8) of the first n_hist
+    history tokens of one sequence and KV head, read from the device page
+    buffer copy."""
     kc, vc = np.zeros((n_hist, D), np.uint8), np.zeros((n_hist, D), np.uint8)
-    ks, kz = np.zeros((n_hist, 2), np.float16), np.zeros((n_hist, 2), np.float16)
-    vs, vz = np.zeros((n_hist, 2), np.float16), np.zeros((n_hist, 2), np.float16)
+    ks, kz = np.zeros((n_hist, 2), np.uint8), np.zeros((n_hist, 2), np.uint8)
+    vs, vz = np.zeros((n_hist, 2), np.uint8), np.zeros((n_hist, 2), np.uint8)
     for pg in range((n_hist + 63) // 64):
         page = pages[block_row[pg], kv]
         a, b = pg * 64, min(n_hist, pg * 64 + 64)

@@ -44,7 +44,7 @@ def test_header_layout_constants_match_binding():
         m = re.search(rf"#define {macro} (\d+)", text)
         assert m and int(m.group(1)) == val, macro
     # 64 tokens x (2 x 32 code bytes + 2 x 8 metadata bytes) per page
-    assert O.PAGE_BYTES == 64 * (32 + 32 + 8 + 8)
+    assert O.PAGE_BYTES == 64 * (32 + 32 + 4 + 4)
 
 
 def _fake_pool(batch=1):

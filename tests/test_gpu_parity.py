@@ -1,6 +1,6 @@
 """GPU parity of the HIP path against the CPU oracle (needs an MI355X).
 
-Write path: codes and fp16 scale/zero bit-exact with the oracle; bulk appends
+Write path: codes and metadata codes (s8, z8) bit-exact with the oracle; bulk appends
 bit-identical to sequential appends.  Decode: for every (sequence, query
 head), max |o_gpu - o_ref| <= 2e-3 * ||o_ref||_2 (float32 accumulation on the
 GPU, float64 oracle).  Inputs are seeded synthetic data from ``synth``; the
@@ -78,11 +78,11 @@ def test_write_bitexact_tiny(tiny):
     (kc, ks, kz), (vc, vs, vz) = gather_history(pages, pool.block_table.cpu().numpy()[0], 0, n_hist)
     ref = R.build_head_pool(_f64(kb[:, 0]), _f64(vb[:, 0]), cals[0])
     assert np.array_equal(kc, ref.hist_k.codes)
-    assert np.array_equal(ks.view(np.uint16), ref.hist_k.scale.view(np.uint16))
-    assert np.array_equal(kz.view(np.uint16), ref.hist_k.zero.view(np.uint16))
+    assert np.array_equal(ks, ref.hist_k.s8)
+    assert np.array_equal(kz, ref.hist_k.z8)
     assert np.array_equal(vc, ref.hist_v.codes)
-    assert np.array_equal(vs.view(np.uint16), ref.hist_v.scale.view(np.uint16))
-    assert np.array_equal(vz.view(np.uint16), ref.hist_v.zero.view(np.uint16))
+    assert np.array_equal(vs, ref.hist_v.s8)
+    assert np.array_equal(vz, ref.hist_v.z8)
     # BF16 windows hold the raw tokens
     sink = pool.sink_k.cpu().numpy().view(np.uint16)[0, 0]
     assert np.array_equal(sink, kb[:64, 0])
@@ -119,7 +119,7 @@ def test_single_token_appends(tiny):
     (kc, ks, kz), (vc, vs, vz) = gather_history(pages, a.block_table.cpu().numpy()[0], 0, n_hist)
     ref = R.build_head_pool(_f64(kb[:L1, 0]), _f64(vb[:L1, 0]), cals[0])
     assert np.array_equal(kc, ref.hist_k.codes) and np.array_equal(vc, ref.hist_v.codes)
-    assert np.array_equal(vs.view(np.uint16), ref.hist_v.scale.view(np.uint16))
+    assert np.array_equal(vs, ref.hist_v.s8)
 
 
 @pytest.mark.parametrize("variant", [0, 1, 2])
