@@ -119,8 +119,10 @@ struct QSmem {
 // int8 bytes laid out as the A operand of the logit MFMA (rows: head h ->
 // 4h + {group 0 hi, group 0 lo, group 1 hi, group 1 lo}).  Results stay in
 // `sm`; with `qrot` non-null the float q~ is also written there.
-template <int MT, int GH>
-__device__ void query_prep(const DecArgs &a, int b, int kv, QSmem<MT, GH> &sm, float *qrot) {
+// after_loads() runs on every thread once the global loads of the
+// preparation (threads 0..255) have been consumed, before the first barrier.
+template <int MT, int GH, typename AfterLoads>
+__device__ void query_prep(const DecArgs &a, int b, int kv, QSmem<MT, GH> &sm, float *qrot, AfterLoads after_loads) {
   const PoolView &pv = a.pv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
   const int G = pv.hq / pv.hkv;
@@ -159,6 +161,7 @@ __device__ void query_prep(const DecArgs &a, int b, int kv, QSmem<MT, GH> &sm, f
       }
     }
   }
+  after_loads();
   for (int e = tid; e < MT * 2 * 64 * 4; e += blockDim.x) ((uint32_t *)sm.aq)[e] = 0;
   __syncthreads();
   // one wave per head: Walsh-Hadamard butterfly (lane l holds elements l and
@@ -320,7 +323,7 @@ template <int MT, int GH>
 __global__ void __launch_bounds__(256) decode_pre_kernel(DecArgs a) {
   __shared__ QSmem<MT, GH> sm;
   const int bh = blockIdx.x;
-  query_prep<MT, GH>(a, bh / a.pv.hkv, bh % a.pv.hkv, sm, a.qrot + (size_t)bh * GH * kD);
+  query_prep<MT, GH>(a, bh / a.pv.hkv, bh % a.pv.hkv, sm, a.qrot + (size_t)bh * GH * kD, [] {});
   const int G = a.pv.hq / a.pv.hkv;
   for (int e = threadIdx.x; e < G * 4; e += blockDim.x) a.qconst[(size_t)bh * GH * 4 + e] = (&sm.qc[0][0])[e];
 }
@@ -935,18 +938,32 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   const int pg1 = min(min(n_pages, pg0 + a.pages_per_split), pv.max_pages);
   if (n_pages > pv.max_pages && split == 0 && tid == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_LENGTH);
 
+  // Vector-memory loads complete in issue order, so a load issued after the
+  // page copies waits for them.  Loads whose values are used after the
+  // copies start are therefore completed first: the metadata steps here, the
+  // query preparation's loads (threads 0..255) before those waves start
+  // their copies; the other waves start theirs at once.
+  const MetaSteps ms = meta_steps(a.rv, kv);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   PagePipe<NW, PF> pipe;
   pipe_init(pipe, pv, b, kv, pg0, pg1, sm.pbuf[wave], wave, lane);
-  pipe_prologue(pipe, pv, lane);
-
-  // query operands, prepared by the workgroup while the first pages load
-  query_prep<MT, GH>(a, b, kv, sm.q, nullptr);
-  const MetaSteps ms = meta_steps(a.rv, kv);
+  if (wave >= 4) pipe_prologue(pipe, pv, lane);
+  query_prep<MT, GH>(a, b, kv, sm.q, nullptr, [&] {
+    if (wave < 4) pipe_prologue(pipe, pv, lane);
+  });
   QueryOps<MT> qo;
   load_query_ops<MT, GH>(sm.q.aq, sm.q.qc, G, pv.sm_scale * kLog2e, ms, lane, qo);
-  __syncthreads();   // the query scratch is reused by the BF16 tiles and the weights
-  // BF16 tile u (sink, then recent window) runs on workgroup u % S and, from
-  // the last wave down, on the waves that hold the fewest history pages
+  __syncthreads();   // the query scratch is reused by the weights and the BF16 tiles
+  HistState<MT> st;
+  hist_reset(st);
+  v4i *wl = sm.wave[wave].wl;
+  // rows 4h + 3 of the weight operands stay zero; the rest is rewritten per page
+#pragma unroll
+  for (int i = 0; i < MT * 2; ++i) wl[i * 64 + lane] = v4i{0, 0, 0, 0};
+  pipe_scan<MT, NW, PF>(pipe, pv, n_hist, qo, st, wl, lane);
+  if (pipe.bad && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
+  // BF16 tile u (sink, then recent window) runs on workgroup u % S after the
+  // history pages, from the last wave down: the waves with the fewest pages
   {
     const int S = a.n_splits;
     float *parts = a.part + (size_t)bh * (S + a.n_chunks) * G * kPartStride;
@@ -954,17 +971,6 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
       if (NW - 1 - (u / S) % NW == wave)
         bf16_tile_partial<GH>(a, b, kv, u, sm.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
   }
-  HistState<MT> st;
-  hist_reset(st);
-  v4i *wl = sm.wave[wave].wl;
-  // rows 4h + 3 of the weight operands stay zero; the rest is rewritten per page
-#pragma unroll
-  for (int i = 0; i < MT * 2; ++i) wl[i * 64 + lane] = v4i{0, 0, 0, 0};
-  // complete the query operands here (and with them the first copies), so that
-  // no wait for them is left inside the loop
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  pipe_scan<MT, NW, PF>(pipe, pv, n_hist, qo, st, wl, lane);
-  if (pipe.bad && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
   flush_partial<MT, GH, NW>(sm, st, G, ms, dst);
 }
 
