@@ -782,6 +782,17 @@ __device__ void write_split_partial(ScanSmem<MT, GH, NW, MFMA> &sm, int G, float
 // (sequence, KV head): the wave takes pages first + i * NW, i < npg, with up
 // to PF page copies in flight (LDS DMA).  Lane k of bt holds the block-table
 // entry of page index 64 c + k, c = the chunk of the next page issued.
+// Complete the load of a block-table register and redefine it through an
+// empty asm: later reads of it (one readlane per page) then carry no
+// compiler wait.  Without this the compiler, unable to prove across the
+// loop that the refill load (every 64 pages) has landed, waits for every
+// outstanding vector-memory operation, page copies included, at each
+// page issue.
+__device__ __forceinline__ void bt_settle(int &bt) {
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  asm volatile("" : "+v"(bt));
+}
+
 template <int NW, int PF>
 struct PagePipe {
   const int32_t *btw;
@@ -801,6 +812,7 @@ __device__ __forceinline__ void pipe_init(PagePipe<NW, PF> &p, const PoolView &p
   p.npg = p.first < pg1 ? (pg1 - p.first + NW - 1) / NW : 0;
   p.btw = pv.block_table + (size_t)b * pv.max_pages + p.first;
   p.bt = lane < p.npg ? p.btw[(size_t)lane * NW] : -1;
+  bt_settle(p.bt);
   p.pbase = pv.pages + (size_t)kv * kPageBytes;
   p.pstride = (size_t)pv.hkv * kPageBytes;
   p.bufs = bufs;
@@ -816,7 +828,7 @@ template <int NW, int PF>
 __device__ __forceinline__ bool pipe_issue(PagePipe<NW, PF> &p, const PoolView &pv, int j, int lane) {
   if ((j & 63) == 0 && j > 0) {
     p.bt = j + lane < p.npg ? p.btw[(size_t)(j + lane) * NW] : -1;
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    bt_settle(p.bt);
   }
   const int ph = __builtin_amdgcn_readlane(p.bt, j & 63);
   const bool ok = ph >= 0 && ph < pv.n_pages;
