@@ -1062,18 +1062,14 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *hist, i
   float4 u[UVL ? 1 : 16];
   if constexpr (UVL) {
     // 64 KB of U_V into LDS, 1 KB per DMA copy, spread over the waves; the
-    // copies complete before step 4 reads them (explicit wait there)
+    // copies complete before step 4 reads them (explicit wait there).  They
+    // go first: the compiler's waits for the loads below cover them anyway.
     const uint64_t src = (uint64_t)(uintptr_t)(a.rv.U_V + (size_t)kv * kD * kD);
     const uint32_t dst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float *) & sm.uv[0][0];
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     for (int c = wv; c < kD * kD * 4 / 1024; c += nwaves) dma_1k(src + 1024u * c, dst + 1024u * c, 16u * lane);
-  } else {
-    if (tid < 2 * kD) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) u[i] = urow[i];
-    }
+    asm volatile("" ::: "memory");
   }
-  asm volatile("" ::: "memory");   // keep the U_V loads here, ahead of the partials
   // 1) one round of device-coherent loads: the first kPer partials of each
   // thread's slice (thread -> head, channel pair, slice; 8 bytes each) into
   // registers, and the (m, l) headers of every partial into LDS.  Further
@@ -1100,6 +1096,15 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *hist, i
     const float2 hv = ld_coherent2(part_of(e / G) + (size_t)(e % G) * kPartStride);
     sm.ml[e / G][e % G][0] = hv.x;
     sm.ml[e / G][e % G][1] = hv.y;
+  }
+  // U_V rows after the partials: loads complete in issue order, so the
+  // waits above do not include them; they are needed only in step 4
+  if constexpr (!UVL) {
+    asm volatile("" ::: "memory");
+    if (tid < 2 * kD) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) u[i] = urow[i];
+    }
   }
   __syncthreads();
   // 2) per head: maxima, weights, denominators

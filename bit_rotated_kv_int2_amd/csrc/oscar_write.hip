@@ -202,9 +202,56 @@ append_demote_kernel(AppendArgs a) {
     acc[i][1] = x0 - x1;
   }
 
-  // S3..S8 per slot.  Output channel p takes element bitrev(p): lane l
-  // fetches the elements of channels l and l + 64 from their owner lanes.
+  // S3, S5: the float32 values of the wave's 16 slots, in butterfly order,
+  // staged in its own rows of xs (free after S1).  Row stride 132 floats.
   const float tau = (is_v ? a.rv.tau_V : a.rv.tau_K)[h];
+  constexpr int kRow = 132;
+  float *ys = (float *)&xs[16 * w][0];
+  float4 *stat = (float4 *)(ys + 16 * kRow);       // per slot: zero0, scale0, zero1, scale1
+  uint32_t *smeta = (uint32_t *)(stat + 16);       // per slot: s8_0 | z8_0 << 8 | s8_1 << 16 | z8_1 << 24
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    ys[i * kRow + lane] = (float)(acc[i][0] * kInvSqrtD);
+    ys[i * kRow + 64 + lane] = (float)(acc[i][1] * kInvSqrtD);
+  }
+  wave_lds_sync();
+  // S6, S7 per slot and group, lane i < 16 taking slot 16 w + i.  Output
+  // channel p takes element bitrev(p), so group g (channels 64 g .. 64 g + 63)
+  // is the set of elements with e % 2 == g; min and max commute with the
+  // order and with the clamp to [-tau, tau] (monotone), which is applied to
+  // them.  Then the group metadata as in quantize_group.
+  if (lane < 16) {
+    const float4 *row = (const float4 *)(ys + lane * kRow);
+    float mx0 = -INFINITY, mn0 = INFINITY, mx1 = -INFINITY, mn1 = INFINITY;
+#pragma unroll 8
+    for (int j = 0; j < kD / 4; ++j) {
+      const float4 v = row[j];
+      mx0 = fmaxf(mx0, fmaxf(v.x, v.z));
+      mn0 = fminf(mn0, fminf(v.x, v.z));
+      mx1 = fmaxf(mx1, fmaxf(v.y, v.w));
+      mn1 = fminf(mn1, fminf(v.y, v.w));
+    }
+    float zf[2], sf[2];
+    uint32_t meta = 0;
+    const float mx[2] = {fminf(fmaxf(mx0, -tau), tau), fminf(fmaxf(mx1, -tau), tau)};
+    const float mn[2] = {fminf(fmaxf(mn0, -tau), tau), fminf(fmaxf(mn1, -tau), tau)};
+    const float za = meta_zero_step(tau), sb = meta_scale_step(tau);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const float sg = __fdiv_rn(mx[g] - mn[g], 3.0f);
+      uint32_t z8 = 0, s8 = 0;
+      if (za > 0.0f) z8 = (uint32_t)fminf(fmaxf(rintf(__fdiv_rn(mn[g] + tau, za)), 0.0f), 255.0f);
+      if (sb > 0.0f) s8 = (uint32_t)fminf(fmaxf(rintf(__fdiv_rn(sg, sb)), 0.0f), 255.0f);
+      zf[g] = (float)z8 * za - tau;
+      sf[g] = (float)s8 * sb;
+      meta |= (s8 | (z8 << 8)) << (16 * g);
+    }
+    stat[lane] = make_float4(zf[0], sf[0], zf[1], sf[1]);
+    smeta[lane] = meta;
+  }
+  wave_lds_sync();
+
+  // S7 codes and S8 packing: lane l takes output channels l and l + 64
   const int e0 = bitrev7(lane), e1 = bitrev7(lane + 64);
   uint8_t *page = pv.pages + ((size_t)phys * pv.hkv + h) * kPageBytes;
   uint32_t vb[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};   // V: bytes 4 m + w of channels l, l + 64
@@ -212,14 +259,14 @@ append_demote_kernel(AppendArgs a) {
   for (int i = 0; i < 16; ++i) {
     const int slot = 16 * w + i;
     const bool valid = c0 + slot >= t0 && c0 + slot < t1;   // wave-uniform
-    const float f0 = (float)(acc[i][0] * kInvSqrtD), f1 = (float)(acc[i][1] * kInvSqrtD);
-    const float g00 = __shfl(f0, e0 & 63, 64), g01 = __shfl(f1, e0 & 63, 64);
-    const float g10 = __shfl(f0, e1 & 63, 64), g11 = __shfl(f1, e1 & 63, 64);
-    uint32_t m0, m1;
-    const uint32_t code0 = quantize_group((e0 >> 6) ? g01 : g00, tau, m0);
-    const uint32_t code1 = quantize_group((e1 >> 6) ? g11 : g10, tau, m1);
     if (!valid) continue;
-    if (lane == 0) *(uint32_t *)(page + (is_v ? kVMeta : kKMeta) + meta_entry(slot) * 4) = m0 | (m1 << 16);
+    const float4 st = stat[i];
+    const float v0 = fminf(fmaxf(ys[i * kRow + e0], -tau), tau);
+    const float v1 = fminf(fmaxf(ys[i * kRow + e1], -tau), tau);
+    uint32_t code0 = 0, code1 = 0;
+    if (st.y != 0.0f) code0 = (uint32_t)fminf(fmaxf(rintf(__fdiv_rn(v0 - st.x, st.y)), 0.0f), 3.0f);
+    if (st.w != 0.0f) code1 = (uint32_t)fminf(fmaxf(rintf(__fdiv_rn(v1 - st.z, st.w)), 0.0f), 3.0f);
+    if (lane == 0) *(uint32_t *)(page + (is_v ? kVMeta : kKMeta) + meta_entry(slot) * 4) = smeta[i];
     if (!is_v) {
       // K row: dword q holds channels 16 q .. 16 q + 15, two bits each
       uint32_t k0 = code0 << (2 * (lane & 15)), k1 = code1 << (2 * (lane & 15));
