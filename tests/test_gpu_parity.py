@@ -297,3 +297,31 @@ def test_decode_repeat_same_workspace(tiny):
         assert torch.equal(o, outs[0])
     ref, _ = _oracle_decode(wl, cals, kb, vb, q[0])
     assert decode_check(outs[0].cpu().numpy()[0], ref) <= TOL
+
+
+@pytest.mark.parametrize("kind", ["naive", "clip", "hadamard"])
+def test_quantiser_variants_parity(tiny, kind):
+    """The quantiser variants of the diagnostics (naive INT2, clip only,
+    Hadamard only) differ from OSCAR only in U and tau, so the library runs
+    them unchanged: codes and metadata bit-exact, decode within tolerance."""
+    from oracle import variants as V
+    torch = _torch()
+    wl, cals, _, params, kb, vb, q = tiny
+    _, kc, vc = synth.calibration_set(wl, 0, n_cal=2048)
+    vcal = [V.variant_calibration(kind, cals[0], _f64(kc[0]), _f64(vc[0]))]
+    vrot = rotation_tensors(vcal)
+    pool = _fresh_pool(params, 59)
+    append_sequence(params, vrot, pool, 0, kb, vb)
+    torch.cuda.synchronize()
+    (kc_, ks, kz), (vc_, vs, vz) = gather_history(pool.pages.cpu().numpy(), pool.block_table.cpu().numpy()[0], 0,
+                                                  4096 - 320)
+    ref = R.build_head_pool(_f64(kb[:, 0]), _f64(vb[:, 0]), vcal[0])
+    assert np.array_equal(kc_, ref.hist_k.codes) and np.array_equal(vc_, ref.hist_v.codes)
+    assert np.array_equal(ks, ref.hist_k.s8) and np.array_equal(kz, ref.hist_k.z8)
+    assert np.array_equal(vs, ref.hist_v.s8) and np.array_equal(vz, ref.hist_v.z8)
+    out = _decode_gpu(params, vrot, pool, q, 0)
+    want = R.decode_sequence(_f64(q[0]), [ref], vcal, 1 / np.sqrt(D))
+    err = decode_check(out[0], want)
+    print(f"variant {kind}: max err / norm = {err:.3e}")
+    assert err <= TOL
+    assert int(pool.error_flags.cpu()[0]) == 0
