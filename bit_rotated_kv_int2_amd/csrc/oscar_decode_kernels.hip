@@ -45,7 +45,9 @@ namespace {
 // i.e. u + 0x8080 < 2^23.  kWScale keeps a margin below 2^23 - 0x8080 - 1 =
 // 8355711 because w * (kWScale / wmax) may round a few units above kWScale.
 constexpr float kWScale = 8355000.0f;
-constexpr float kWBias = 32896.5f;              // 0x8080 + 0.5 (round to nearest)
+// fma(w, kq, kWMagic) lies in [2^23, 2^24), where float32 spacing is 1: its
+// low 23 bits are u + 0x8080 rounded to nearest, with no conversion.
+constexpr float kWMagic = 8388608.0f + 32896.0f;   // 2^23 + 0x8080
 constexpr float kInvSqrtDf = 0.08838834764831845f;
 constexpr int kMaxSplits = 256;
 constexpr int kMaxParts = 512;                 // history splits + BF16 tiles per (sequence, KV head)
@@ -451,8 +453,8 @@ __device__ __forceinline__ void int2_page(const PageRegs &r, int valid, const Qu
     uint32_t u0[4], u1[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-      u0[tt] = (uint32_t)fmaf(w0[tt], kq, kWBias);
-      u1[tt] = (uint32_t)fmaf(w1[tt], kq, kWBias);
+      u0[tt] = __float_as_uint(fmaf(w0[tt], kq, kWMagic));   // bytes 0..2 = u + 0x8080
+      u1[tt] = __float_as_uint(fmaf(w1[tt], kq, kWMagic));
     }
     // lane (n, q): head q, tokens 16 tt + n -> A rows 4q + {hi, mid, lo},
     // lane group n / 4, bytes 4 (n % 4) + tt
