@@ -45,6 +45,9 @@ int check_params(const oscar_params *p) {
   return OSCAR_OK;
 }
 
+// Tensors whose rows the kernels read or write 16 bytes at a time.
+bool misaligned(const void *ptr) { return ((uintptr_t)ptr & 15u) != 0; }
+
 int check_pool(const oscar_params *p, const oscar_kv_pool *pool) {
   if (!pool) return fail(OSCAR_EINVAL, "pool is NULL");
   if (pool->batch < 1) return fail(OSCAR_EINVAL, "pool.batch must be >= 1");
@@ -54,12 +57,16 @@ int check_pool(const oscar_params *p, const oscar_kv_pool *pool) {
   if (pool->max_pages < 0 || pool->n_pages < 0 || pool->n_sink_slots < 1)
     return fail(OSCAR_EINVAL, "pool sizes must be non-negative (n_sink_slots >= 1)");
   if (pool->n_pages > 0 && !pool->pages) return fail(OSCAR_EINVAL, "pool.pages is NULL");
+  if (misaligned(pool->sink_k) || misaligned(pool->sink_v) || misaligned(pool->recent_k) ||
+      misaligned(pool->recent_v) || misaligned(pool->pages))
+    return fail(OSCAR_EINVAL, "pool tensors must be 16-byte aligned");
   (void)p;
   return OSCAR_OK;
 }
 
 int check_rot(const oscar_rotation *r) {
   if (!r || !r->U_K || !r->U_V || !r->tau_K || !r->tau_V) return fail(OSCAR_EINVAL, "rotation has a NULL pointer");
+  if (misaligned(r->U_K) || misaligned(r->U_V)) return fail(OSCAR_EINVAL, "U_K/U_V must be 16-byte aligned");
   return OSCAR_OK;
 }
 
@@ -138,6 +145,7 @@ int32_t oscar_quantize_append(const oscar_params *p, const oscar_rotation *rot,
   if ((rc = check_rot(rot)) || (rc = check_pool(p, pool))) return rc;
   if (n_new < 1) return fail(OSCAR_EINVAL, "n_new must be >= 1");
   if (!k_new || !v_new) return fail(OSCAR_EINVAL, "k_new/v_new is NULL");
+  if (misaligned(k_new) || misaligned(v_new)) return fail(OSCAR_EINVAL, "k_new/v_new must be 16-byte aligned");
   oscar::PoolView pv = make_pv(p, pool);
   oscar::RotView rv{rot->U_K, rot->U_V, rot->tau_K, rot->tau_V};
   hipError_t e = oscar::launch_append(pv, rv, k_new, v_new, n_new, (hipStream_t)stream);
@@ -158,6 +166,7 @@ int32_t oscar_decode_attention(const oscar_params *p, const oscar_rotation *rot,
   if (rc) return rc;
   if ((rc = check_rot(rot)) || (rc = check_pool(p, pool))) return rc;
   if (!q || !out) return fail(OSCAR_EINVAL, "q/out is NULL");
+  if (misaligned(q) || misaligned(out)) return fail(OSCAR_EINVAL, "q/out must be 16-byte aligned");
   const oscar::DecodePlan plan = oscar::make_decode_plan(pool->batch, p->num_kv_heads, p->num_q_heads,
                                                           pool->max_pages, p->sink, p->recent, g_variant);
   if (!workspace || workspace_bytes < plan.total)
@@ -184,7 +193,10 @@ int32_t oscar_bf16_decode_attention(const oscar_params *p, const oscar_bf16_cach
   if (!cache || !cache->k_pages || !cache->v_pages || !cache->block_table || !cache->seq_lens)
     return fail(OSCAR_EINVAL, "bf16 cache has a NULL pointer");
   if (cache->batch < 1 || cache->max_pages < 0 || cache->n_pages < 0) return fail(OSCAR_EINVAL, "bad bf16 cache sizes");
+  if (misaligned(cache->k_pages) || misaligned(cache->v_pages))
+    return fail(OSCAR_EINVAL, "bf16 cache pages must be 16-byte aligned");
   if (!q || !out) return fail(OSCAR_EINVAL, "q/out is NULL");
+  if (misaligned(q) || misaligned(out)) return fail(OSCAR_EINVAL, "q/out must be 16-byte aligned");
   const oscar::Bf16Plan plan = oscar::make_bf16_plan(cache->batch, p->num_kv_heads, p->num_q_heads, cache->max_pages);
   if (!workspace || workspace_bytes < plan.total)
     return fail(OSCAR_EWORKSPACE, "workspace of %zu bytes needed, %zu given", plan.total, workspace_bytes);

@@ -89,9 +89,11 @@ __device__ __forceinline__ float ubyte_f(uint32_t w, int i) { return (float)((w 
 struct MetaSteps {
   float ka, kb, ktau, va, vb, vtau;
 };
-__device__ __forceinline__ MetaSteps meta_steps(const RotView &rv, int kv) {
-  const float tk = rv.tau_K[kv], tv = rv.tau_V[kv];
+__device__ __forceinline__ MetaSteps meta_steps(float tk, float tv) {
   return MetaSteps{meta_zero_step(tk), meta_scale_step(tk), tk, meta_zero_step(tv), meta_scale_step(tv), tv};
+}
+__device__ __forceinline__ MetaSteps meta_steps(const RotView &rv, int kv) {
+  return meta_steps(rv.tau_K[kv], rv.tau_V[kv]);
 }
 
 // Byte 2 / byte 1 / byte 0 of four words gathered into one word (word i -> byte i).
@@ -131,35 +133,50 @@ __device__ void query_prep(const DecArgs &a, int b, int kv, QSmem<MT, GH> &sm, f
   const float *U = a.rv.U_K + (size_t)kv * kD * kD;
   const uint16_t *qb = a.q + ((size_t)b * pv.hq + (size_t)kv * G) * kD;
   // y[h][j] = sum_k q[h][k] U[k][j]: threads 0..255 -> columns 4c..4c+3 and
-  // rows k = t % 8 + 8 i; all 16 loads in flight at once; 8-lane reduction.
+  // rows k = 16 (t % 8) + i, i < 16; 8-lane reduction.  The 16 row loads of
+  // U and the query rows of four heads (two 16-byte loads per head) are all
+  // in flight at once: one memory round trip per four heads.
   if (tid < 256) {
     const int c = tid >> 3, kk = tid & 7;
     float4 u[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) u[i] = *(const float4 *)(U + (size_t)(kk + 8 * i) * kD + 4 * c);
-    for (int h = 0; h < G; ++h) {
-      const uint16_t *qr = qb + (size_t)h * kD;
-      float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
+    for (int i = 0; i < 16; ++i) u[i] = *(const float4 *)(U + (size_t)(16 * kk + i) * kD + 4 * c);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float qk = bf16_to_f32(qr[kk + 8 * i]);
-        y0 = fmaf(qk, u[i].x, y0);
-        y1 = fmaf(qk, u[i].y, y1);
-        y2 = fmaf(qk, u[i].z, y2);
-        y3 = fmaf(qk, u[i].w, y3);
+    for (int h0 = 0; h0 < GH; h0 += 4) {
+      uint4 qv[4][2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // heads past G load head G - 1 (in bounds) and are not stored
+        const uint4 *qr = (const uint4 *)(qb + (size_t)min(h0 + j, G - 1) * kD + 16 * kk);
+        qv[j][0] = qr[0];
+        qv[j][1] = qr[1];
       }
 #pragma unroll
-      for (int o = 1; o < 8; o <<= 1) {
-        y0 += __shfl_xor(y0, o, 64);
-        y1 += __shfl_xor(y1, o, 64);
-        y2 += __shfl_xor(y2, o, 64);
-        y3 += __shfl_xor(y3, o, 64);
-      }
-      if (kk == 0) {
-        sm.ys[h][4 * c] = y0;
-        sm.ys[h][4 * c + 1] = y1;
-        sm.ys[h][4 * c + 2] = y2;
-        sm.ys[h][4 * c + 3] = y3;
+      for (int j = 0; j < 4; ++j) {
+        float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint4 &w4 = qv[j][i >> 3];
+          const uint32_t w = (i & 6) == 0 ? w4.x : (i & 6) == 2 ? w4.y : (i & 6) == 4 ? w4.z : w4.w;
+          const float qk = __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+          y0 = fmaf(qk, u[i].x, y0);
+          y1 = fmaf(qk, u[i].y, y1);
+          y2 = fmaf(qk, u[i].z, y2);
+          y3 = fmaf(qk, u[i].w, y3);
+        }
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) {
+          y0 += __shfl_xor(y0, o, 64);
+          y1 += __shfl_xor(y1, o, 64);
+          y2 += __shfl_xor(y2, o, 64);
+          y3 += __shfl_xor(y3, o, 64);
+        }
+        if (kk == 0 && h0 + j < G) {
+          sm.ys[h0 + j][4 * c] = y0;
+          sm.ys[h0 + j][4 * c + 1] = y1;
+          sm.ys[h0 + j][4 * c + 2] = y2;
+          sm.ys[h0 + j][4 * c + 3] = y3;
+        }
       }
     }
   }
@@ -794,6 +811,11 @@ __device__ __forceinline__ void bt_settle(int &bt) {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   asm volatile("" : "+v"(bt));
 }
+// The same for the block-table register and two loaded floats together.
+__device__ __forceinline__ void bt_settle(int &bt, float &x, float &y) {
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  asm volatile("" : "+v"(bt), "+v"(x), "+v"(y));
+}
 
 template <int NW, int PF>
 struct PagePipe {
@@ -807,14 +829,15 @@ struct PagePipe {
   bool bad;
 };
 
+// Issues the first block-table load without waiting for it: a bt_settle of
+// p.bt must come before pipe_prologue.
 template <int NW, int PF>
 __device__ __forceinline__ void pipe_init(PagePipe<NW, PF> &p, const PoolView &pv, int b, int kv, int pg0, int pg1,
                                           uint4 (*bufs)[kPageBytes / 16], int wave, int lane) {
   p.first = pg0 + wave;
   p.npg = p.first < pg1 ? (pg1 - p.first + NW - 1) / NW : 0;
   p.btw = pv.block_table + (size_t)b * pv.max_pages + p.first;
-  p.bt = lane < p.npg ? p.btw[(size_t)lane * NW] : -1;
-  bt_settle(p.bt);
+  p.bt = lane < p.npg ? p.btw[(size_t)lane * NW] : -1;   // settled by the caller
   p.pbase = pv.pages + (size_t)kv * kPageBytes;
   p.pstride = (size_t)pv.hkv * kPageBytes;
   p.bufs = bufs;
@@ -953,21 +976,26 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   if (n_pages > pv.max_pages && split == 0 && tid == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_LENGTH);
 
   // Vector-memory loads complete in issue order, so a load issued after the
-  // page copies waits for them.  Loads whose values are used after the
-  // copies start are therefore completed first: the metadata steps here, the
-  // query preparation's loads (threads 0..255) before those waves start
-  // their copies; the other waves start theirs at once.
-  const MetaSteps ms = meta_steps(a.rv, kv);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  // page copies waits for them.  Every load whose value is used after the
+  // copies start is therefore issued first and completed in one round trip:
+  // the clip thresholds, the first block-table entries and (threads
+  // 0..255) the query preparation's loads.  The waves without preparation
+  // work start their copies as soon as those land.
+  float tk = a.rv.tau_K[kv], tv = a.rv.tau_V[kv];
   PagePipe<NW, PF> pipe;
   pipe_init(pipe, pv, b, kv, pg0, pg1, sm.pbuf[wave], wave, lane);
-  if (wave >= 4) pipe_prologue(pipe, pv, lane);
   query_prep<MT, GH>(a, b, kv, sm.q, nullptr, [&] {
-    if (wave < 4) pipe_prologue(pipe, pv, lane);
+    bt_settle(pipe.bt, tk, tv);
+    if (wave >= 4) pipe_prologue(pipe, pv, lane);
   });
+  const MetaSteps ms = meta_steps(tk, tv);
   QueryOps<MT> qo;
   load_query_ops<MT, GH>(sm.q.aq, sm.q.qc, G, pv.sm_scale * kLog2e, ms, lane, qo);
   __syncthreads();   // the query scratch is reused by the weights and the BF16 tiles
+  // the preparing waves start their copies only now: issuing them inside
+  // the preparation would stall those waves (the CU accepts copy requests
+  // at the memory rate) and with them every wave waiting on the preparation
+  if (wave < 4) pipe_prologue(pipe, pv, lane);
   HistState<MT> st;
   hist_reset(st);
   v4i *wl = sm.wave[wave].wl;
@@ -1431,6 +1459,7 @@ decode_flat_kernel(DecArgs a) {
     sg.last_blk = __builtin_amdgcn_readfirstlane(sg.last_blk);
     const int bh = sg.b * Hkv + sg.kv;
     pipe_init(pipe, pv, sg.b, sg.kv, sg.p0, sg.p1, sm.s.pbuf[wave], wave, lane);
+    bt_settle(pipe.bt);
     pipe_prologue(pipe, pv, lane);
     if (si % kFlatPrep == 0) {
       int bb[kFlatPrep], kk[kFlatPrep];

@@ -26,6 +26,9 @@
  *     entry outside [0, n_pages), a sequence longer than the table) are
  *     skipped by the kernels and reported by OR-ing OSCAR_DEVERR_* bits into
  *     *pool->error_flags when that pointer is non-NULL.
+ *   - Every float and bf16 device tensor (rotation factors, pool pages and
+ *     BF16 segments, q, out, new tokens) must be 16-byte aligned, as any
+ *     hipMalloc or torch allocation is; OSCAR_EINVAL otherwise.
  *   - bf16 values are passed as their uint16_t bit patterns.
  *   - All tokens are row vectors; d = head_dim = 128.
  */

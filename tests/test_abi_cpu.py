@@ -79,6 +79,17 @@ def test_validation_errors():
                                    0x1000, 0x1000, 0, None) == O.OSCAR_EINVAL
     assert L.oscar_quantize_append(ctypes.byref(p), None, ctypes.byref(pool),
                                    0x1000, 0x1000, 1, None) == O.OSCAR_EINVAL
+    # device tensors read 16 bytes at a time must be 16-byte aligned
+    assert L.oscar_decode_attention(ctypes.byref(p), ctypes.byref(rot), ctypes.byref(pool),
+                                    0x1008, 0x1000, 0x1000, 1 << 30, None) == O.OSCAR_EINVAL
+    assert b"aligned" in L.oscar_last_error()
+    assert L.oscar_decode_attention(ctypes.byref(p), ctypes.byref(O.Rotation(0x1004, 0x1000, 0x1000, 0x1000)),
+                                    ctypes.byref(pool), 0x1000, 0x1000, 0x1000, 1 << 30, None) == O.OSCAR_EINVAL
+    bad = _fake_pool()
+    bad.pages = 0x1002
+    assert _call_decode(p, pool=bad) == O.OSCAR_EINVAL
+    assert L.oscar_quantize_append(ctypes.byref(p), ctypes.byref(rot), ctypes.byref(pool),
+                                   0x1000, 0x1010 + 2, 1, None) == O.OSCAR_EINVAL
     assert L.oscar_set_decode_variant(7) == O.OSCAR_EINVAL
     assert L.oscar_set_decode_variant(-1) == O.OSCAR_EINVAL
     for v in (2, 1, 0):
