@@ -164,13 +164,18 @@ __device__ void query_prep(const DecArgs &a, int b, int kv, QSmem<MT, GH> &sm, f
           y2 = fmaf(qk, u[i].z, y2);
           y3 = fmaf(qk, u[i].w, y3);
         }
-#pragma unroll
-        for (int o = 1; o < 8; o <<= 1) {
-          y0 += __shfl_xor(y0, o, 64);
-          y1 += __shfl_xor(y1, o, 64);
-          y2 += __shfl_xor(y2, o, 64);
-          y3 += __shfl_xor(y3, o, 64);
-        }
+        y0 += lane_xor<1>(y0);
+        y1 += lane_xor<1>(y1);
+        y2 += lane_xor<1>(y2);
+        y3 += lane_xor<1>(y3);
+        y0 += lane_xor<2>(y0);
+        y1 += lane_xor<2>(y1);
+        y2 += lane_xor<2>(y2);
+        y3 += lane_xor<2>(y3);
+        y0 += lane_xor<4>(y0);
+        y1 += lane_xor<4>(y1);
+        y2 += lane_xor<4>(y2);
+        y3 += lane_xor<4>(y3);
         if (kk == 0 && h0 + j < G) {
           sm.ys[h0 + j][4 * c] = y0;
           sm.ys[h0 + j][4 * c + 1] = y1;
@@ -188,12 +193,7 @@ __device__ void query_prep(const DecArgs &a, int b, int kv, QSmem<MT, GH> &sm, f
   // rotated, permuted q~ -> fixed point -> operands
   for (int h = w; h < G; h += nw) {
     float x0 = sm.ys[h][lane], x1 = sm.ys[h][lane + 64];
-#pragma unroll
-    for (int hs = 1; hs < 64; hs <<= 1) {
-      const float o0 = __shfl_xor(x0, hs, 64), o1 = __shfl_xor(x1, hs, 64);
-      x0 = (lane & hs) ? o0 - x0 : x0 + o0;
-      x1 = (lane & hs) ? o1 - x1 : x1 + o1;
-    }
+    fwht_lane_stages(x0, x1, lane);
     sm.ys[h][lane] = x0 + x1;
     sm.ys[h][lane + 64] = x0 - x1;
     wave_lds_sync();
@@ -203,16 +203,11 @@ __device__ void query_prep(const DecArgs &a, int b, int kv, QSmem<MT, GH> &sm, f
       qrot[(size_t)h * kD + lane] = v0;
       qrot[(size_t)h * kD + 64 + lane] = v1;
     }
-    float mx = fmaxf(fabsf(v0), fabsf(v1));
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    const float mx = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
     const float delta = mx > 0.f ? mx / 32639.0f : 1.0f;
     const int q0 = max(-32639, min(32639, (int)rintf(v0 / delta)));
     const int q1 = max(-32639, min(32639, (int)rintf(v1 / delta)));
-    int s0 = q0, s1 = q1;
-    for (int o = 32; o > 0; o >>= 1) {
-      s0 += __shfl_xor(s0, o, 64);
-      s1 += __shfl_xor(s1, o, 64);
-    }
+    const int s0 = wave_sum_i(q0), s1 = wave_sum_i(q1);
     if (lane == 0) {
       sm.qc[h][0] = delta;
       sm.qc[h][1] = delta * (float)s0;   // |sum| < 2^24: exact
@@ -676,7 +671,7 @@ __device__ __forceinline__ void dma_page(uint64_t base, uint32_t lds, uint32_t l
 template <int GH, bool UVL = false>
 struct MergeSmem {
   float uv[UVL ? kD : 1][kD];   // U_V of the KV head, staged by LDS DMA (UVL)
-  float ml[kMaxParts][GH][2];   // (m, l) of every partial: history splits, then BF16 tiles
+  float ml[kMaxParts * GH][2];  // (m, l) of partial p, head h at p * G + h: history splits, then BF16 tiles
   float wgt[kMaxParts][GH];     // merge weight of every partial
   float hs[GH][4];              // per head: history scale, tile scale, 1 / denominator
   float zs[GH][kD];             // weighted history sum, bit-reversal permuted
@@ -749,8 +744,8 @@ __device__ void bf16_tile_partial(const DecArgs &a, int b, int kv, int u, float 
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         float v = o[h][c];
-        v += __shfl_xor(v, 16, 64);
-        v += __shfl_xor(v, 32, 64);
+        v += lane_xor<16>(v);
+        v += lane_xor<32>(v);
         if (q == 0) scratch[h][8 * n + c] = v;
       }
     }
@@ -1084,12 +1079,23 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *hist, i
   const int nwaves = blockDim.x >> 6;
   const int G = pv.hq / pv.hkv;
   const int S = n_hist_parts, P = n_hist_parts + n_tile_parts;
-  // partial p: history split p < S, else BF16 tile p - S; [G][kPartStride] each
-  auto part_of = [&](int p) { return p < S ? hist + (size_t)p * G * kPartStride : tiles + (size_t)(p - S) * G * kPartStride; };
-  // threads 0..255 own row k = t / 2 of U_V, channels 64 (t & 1) .. + 64
-  const int krow = (tid >> 1) & (kD - 1), half = tid & 1;
-  const float4 *urow = (const float4 *)(a.rv.U_V + (size_t)kv * kD * kD + (size_t)krow * kD + 64 * half);
-  float4 u[UVL ? 1 : 16];
+  // partial p: history split p < S, else BF16 tile p - S; [G][kPartStride]
+  // each.  Row (p, h) of the partials from wave-uniform p and h: scalar
+  // address arithmetic, the lanes add only their channel offset.
+  const int pstride = G * kPartStride;
+  auto row_at = [&](int p, int h) -> const float * {
+    return (p < S ? hist + (size_t)p * pstride : tiles + (size_t)(p - S) * pstride) + (size_t)h * kPartStride;
+  };
+  // U_V rows for step 4: the last kUT threads own row k = t' / kLPR
+  // (t' = t - (NT - kUT)), channels kCPL (t' % kLPR) .. + kCPL.  With 12
+  // waves these are waves 4..11, so waves 0..3 are free for step 2.
+  constexpr int kUT = NT >= 512 ? 512 : 256;
+  constexpr int kLPR = kUT / kD, kCPL = kD / kLPR;
+  const int ut = tid - (NT - kUT);
+  const bool uown = ut >= 0;
+  const int krow = (ut >= 0 ? ut : 0) / kLPR, upart = (ut >= 0 ? ut : 0) % kLPR;
+  const float4 *urow = (const float4 *)(a.rv.U_V + (size_t)kv * kD * kD + (size_t)krow * kD + kCPL * upart);
+  float4 u[UVL ? 1 : kCPL / 4];
   if constexpr (UVL) {
     // 64 KB of U_V into LDS, 1 KB per DMA copy, spread over the waves; the
     // copies complete before step 4 reads them (explicit wait there).  They
@@ -1114,54 +1120,54 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *hist, i
   for (int it = 0; it < kItems; ++it) {
     const int e = tid + it * NT;
     if (e >= nitem) break;
-    const int pr = e % npair, sl = e / npair;
-    const int h = pr / (kD / 2), c = 2 * (pr % (kD / 2));
+    // npair and NT are multiples of 64: slice and head are wave-uniform
+    const int pr = e % npair;
+    const int sl = __builtin_amdgcn_readfirstlane(e / npair);
+    const int h = __builtin_amdgcn_readfirstlane(pr / (kD / 2));
+    const int c = 2 * (pr % (kD / 2));
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int p = sl + nsl * j;
-      val[it][j] = p < P ? ld_coherent2(part_of(p) + (size_t)h * kPartStride + 2 + c) : make_float2(0.f, 0.f);
+      val[it][j] = p < P ? ld_coherent2(row_at(p, h) + 2 + c) : make_float2(0.f, 0.f);
     }
   }
   for (int e = tid; e < P * G; e += blockDim.x) {   // partial e / G, head e % G
-    const float2 hv = ld_coherent2(part_of(e / G) + (size_t)(e % G) * kPartStride);
-    sm.ml[e / G][e % G][0] = hv.x;
-    sm.ml[e / G][e % G][1] = hv.y;
-  }
-  // U_V rows after the partials: loads complete in issue order, so the
-  // waits above do not include them; they are needed only in step 4
-  if constexpr (!UVL) {
-    asm volatile("" ::: "memory");
-    if (tid < 2 * kD) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) u[i] = urow[i];
-    }
+    const float2 hv = ld_coherent2(e < S * G ? hist + (size_t)e * kPartStride : tiles + (size_t)(e - S * G) * kPartStride);
+    sm.ml[e][0] = hv.x;
+    sm.ml[e][1] = hv.y;
   }
   __syncthreads();
+  // U_V rows once every wave has issued its partial loads (the memory
+  // pipeline serves a CU's loads in order, so earlier they would delay the
+  // loads that step 2 waits for); they are needed only in step 4
+  if constexpr (!UVL) {
+    asm volatile("" ::: "memory");
+    if (uown) {
+#pragma unroll
+      for (int i = 0; i < kCPL / 4; ++i) u[i] = urow[i];
+    }
+  }
   // 2) per head: maxima, weights, denominators
   for (int h = wave; h < G; h += nwaves) {
     float Mh = -INFINITY, Mb = -INFINITY;
     for (int p = lane; p < P; p += 64) {
-      const float m = sm.ml[p][h][0];
+      const float m = sm.ml[p * G + h][0];
       if (p < S) Mh = fmaxf(Mh, m);
       else Mb = fmaxf(Mb, m);
     }
-    for (int o = 32; o > 0; o >>= 1) {
-      Mh = fmaxf(Mh, __shfl_xor(Mh, o, 64));
-      Mb = fmaxf(Mb, __shfl_xor(Mb, o, 64));
-    }
+    Mh = wave_max(Mh);
+    Mb = wave_max(Mb);
     float lh = 0.f, lb = 0.f;
     for (int p = lane; p < P; p += 64) {
-      const float m = sm.ml[p][h][0];
+      const float m = sm.ml[p * G + h][0];
       const float ref = p < S ? Mh : Mb;
       const float w = m > -INFINITY ? exp2_fast(m - ref) : 0.f;
       sm.wgt[p][h] = w;
-      if (p < S) lh = fmaf(w, sm.ml[p][h][1], lh);
-      else lb = fmaf(w, sm.ml[p][h][1], lb);
+      if (p < S) lh = fmaf(w, sm.ml[p * G + h][1], lh);
+      else lb = fmaf(w, sm.ml[p * G + h][1], lb);
     }
-    for (int o = 32; o > 0; o >>= 1) {
-      lh += __shfl_xor(lh, o, 64);
-      lb += __shfl_xor(lb, o, 64);
-    }
+    lh = wave_sum(lh);
+    lb = wave_sum(lb);
     if (lane == 0) {
       const float Mt = fmaxf(Mh, Mb);
       const float ah = Mh > -INFINITY ? exp2_fast(Mh - Mt) : 0.f;
@@ -1179,8 +1185,10 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *hist, i
   for (int it = 0; it < kItems; ++it) {
     const int e = tid + it * NT;
     if (e >= nitem) break;
-    const int pr = e % npair, sl = e / npair;
-    const int h = pr / (kD / 2), c = 2 * (pr % (kD / 2));
+    const int pr = e % npair;
+    const int sl = __builtin_amdgcn_readfirstlane(e / npair);
+    const int h = __builtin_amdgcn_readfirstlane(pr / (kD / 2));
+    const int c = 2 * (pr % (kD / 2));
     float hx = 0.f, hy = 0.f, bx = 0.f, by = 0.f;
     for (int r = 0; r < rounds; ++r) {
       const int p_base = nsl * kPer * r;
@@ -1189,7 +1197,7 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *hist, i
       for (int j = 0; j < kPer; ++j) {
         const int p = p_base + sl + nsl * j;
         v[j] = r == 0 ? val[it][j]
-                      : (p < P ? ld_coherent2(part_of(p) + (size_t)h * kPartStride + 2 + c) : make_float2(0.f, 0.f));
+                      : (p < P ? ld_coherent2(row_at(p, h) + 2 + c) : make_float2(0.f, 0.f));
       }
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
@@ -1229,12 +1237,7 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *hist, i
   // lane exchanges)
   for (int h = wave; h < G; h += nwaves) {
     float x0 = sm.zs[h][lane], x1 = sm.zs[h][lane + 64];
-#pragma unroll
-    for (int hs = 1; hs < 64; hs <<= 1) {
-      const float o0 = __shfl_xor(x0, hs, 64), o1 = __shfl_xor(x1, hs, 64);
-      x0 = (lane & hs) ? o0 - x0 : x0 + o0;
-      x1 = (lane & hs) ? o1 - x1 : x1 + o1;
-    }
+    fwht_lane_stages(x0, x1, lane);
     sm.zs[h][lane] = x0 + x1;
     sm.zs[h][lane + 64] = x0 - x1;
   }
@@ -1244,19 +1247,25 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *hist, i
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
-  if (tid < 2 * kD) {
-    const float4 *ul = (const float4 *)(&sm.uv[UVL ? krow : 0][64 * half]);
+  // two partial sums per head (independent FMA chains), then the kLPR
+  // lanes of a row are added
+  if (uown) {
+    const float4 *ul = (const float4 *)(&sm.uv[UVL ? krow : 0][kCPL * upart]);
     for (int h = 0; h < G; ++h) {
-      const float4 *zr = (const float4 *)(&sm.zs[h][64 * half]);
-      float s = 0.f;
+      const float4 *zr = (const float4 *)(&sm.zs[h][kCPL * upart]);
+      float sa = 0.f, sb = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float4 z = zr[i];
-        const float4 uu = UVL ? ul[i] : u[UVL ? 0 : i];
-        s = fmaf(z.x, uu.x, fmaf(z.y, uu.y, fmaf(z.z, uu.z, fmaf(z.w, uu.w, s))));
+      for (int i = 0; i < kCPL / 4; i += 2) {
+        const float4 za = zr[i], zb = zr[i + 1];
+        const float4 ua = UVL ? ul[i] : u[UVL ? 0 : i];
+        const float4 ub = UVL ? ul[i + 1] : u[UVL ? 0 : i + 1];
+        sa = fmaf(za.x, ua.x, fmaf(za.y, ua.y, fmaf(za.z, ua.z, fmaf(za.w, ua.w, sa))));
+        sb = fmaf(zb.x, ub.x, fmaf(zb.y, ub.y, fmaf(zb.z, ub.z, fmaf(zb.w, ub.w, sb))));
       }
-      s += __shfl_xor(s, 1, 64);
-      if (half == 0) sm.ot[h][krow] = s * kInvSqrtDf;
+      float s = sa + sb;
+      s += lane_xor<1>(s);
+      if constexpr (kLPR == 4) s += lane_xor<2>(s);
+      if (upart == 0) sm.ot[h][krow] = s * kInvSqrtDf;
     }
   }
   __syncthreads();

@@ -13,15 +13,61 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// DPP controls (GFX9 encoding): quad_perm [1,0,3,2], [2,3,0,1], row_ror 4, 8.
+// DPP controls (GFX9 encoding): quad_perm [1,0,3,2], [2,3,0,1], row_ror 4, 8, 12.
 constexpr int kDppQuadSwap1 = 0xB1;
 constexpr int kDppQuadSwap2 = 0x4E;
 constexpr int kDppRowRor4 = 0x124;
 constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowRor12 = 0x12C;
 
 template <int CTRL>
+__device__ __forceinline__ int dppi(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
 __device__ __forceinline__ float dppf(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, dppi<CTRL>(__builtin_bit_cast(int, v)));
+}
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// The value of lane (lane ^ M), M = 1, 2, ..., 32, by VALU lane movement
+// instead of an LDS permute: DPP inside a 16-lane row for M < 16, the
+// row-pair and half-wave swaps for M = 16, 32.  Where a movement delivers
+// the partner's value in one of two results (row rotations by 4 and 12,
+// the two outputs of a swap), the lane index is sent through the same
+// movement to pick the result that came from lane ^ M.
+template <int M>
+__device__ __forceinline__ int lane_xor_i(int v) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "lane_xor: M");
+  if constexpr (M == 1) {
+    return dppi<kDppQuadSwap1>(v);
+  } else if constexpr (M == 2) {
+    return dppi<kDppQuadSwap2>(v);
+  } else if constexpr (M == 8) {
+    return dppi<kDppRowRor8>(v);   // rotation by half a row: lane ^ 8 either way
+  } else if constexpr (M == 4) {
+    // both rotations by every lane before the choice: a DPP read from a
+    // lane that a branch has switched off yields 0
+    const int l = lane_id();
+    const int a = dppi<kDppRowRor4>(v), b = dppi<kDppRowRor12>(v);
+    return dppi<kDppRowRor4>(l) == (l ^ 4) ? a : b;
+  } else {
+    const int l = lane_id();
+    if constexpr (M == 16) {
+      const auto li = __builtin_amdgcn_permlane16_swap(l, l, false, false);
+      const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      return (int)li[0] == (l ^ 16) ? (int)r[0] : (int)r[1];
+    } else {
+      const auto li = __builtin_amdgcn_permlane32_swap(l, l, false, false);
+      const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      return (int)li[0] == (l ^ 32) ? (int)r[0] : (int)r[1];
+    }
+  }
+}
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  return __builtin_bit_cast(float, lane_xor_i<M>(__builtin_bit_cast(int, v)));
 }
 
 // Reductions over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15); every
@@ -39,6 +85,49 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dppf<kDppRowRor4>(v);
   v += dppf<kDppRowRor8>(v);
   return v;
+}
+
+// Stages 1, 2, ..., 32 of a 128-point Walsh-Hadamard butterfly whose
+// elements l and l + 64 sit in lane l; stage 64 (x0 +- x1) is the caller's.
+template <int M>
+__device__ __forceinline__ void fwht_lane_stage(float &x0, float &x1, int lane) {
+  const float o0 = lane_xor<M>(x0), o1 = lane_xor<M>(x1);
+  x0 = (lane & M) ? o0 - x0 : x0 + o0;
+  x1 = (lane & M) ? o1 - x1 : x1 + o1;
+}
+__device__ __forceinline__ void fwht_lane_stages(float &x0, float &x1, int lane) {
+  fwht_lane_stage<1>(x0, x1, lane);
+  fwht_lane_stage<2>(x0, x1, lane);
+  fwht_lane_stage<4>(x0, x1, lane);
+  fwht_lane_stage<8>(x0, x1, lane);
+  fwht_lane_stage<16>(x0, x1, lane);
+  fwht_lane_stage<32>(x0, x1, lane);
+}
+
+// Reductions over the whole wave; every lane receives the result.
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (a + b) + (c + d);
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+  v += dppi<kDppQuadSwap1>(v);
+  v += dppi<kDppQuadSwap2>(v);
+  v += dppi<kDppRowRor4>(v);
+  v += dppi<kDppRowRor8>(v);
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -229,8 +318,8 @@ __device__ __forceinline__ void bf16_block_combine(int G, const float (&m)[4], c
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       float v = o[h][c];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
+      v += lane_xor<16>(v);
+      v += lane_xor<32>(v);
       o[h][c] = v;
     }
   }
