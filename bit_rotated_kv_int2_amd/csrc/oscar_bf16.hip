@@ -107,7 +107,7 @@ __global__ void __launch_bounds__(256) bf16_decode_kernel(Bf16Args a) {
   for (int idx = tid; idx < G * kD; idx += blockDim.x) {
     const int h = idx / kD, c = idx % kD;
     float o0 = 0.f, o1 = 0.f;
-    const float *p = parts + (size_t)h * kPartStride + 2 + c;
+    const float *p = parts + (size_t)h * kPartStride + kPartO + c;
     const size_t st = (size_t)G * kPartStride;
     int s = 0;
     for (; s + 2 <= S; s += 2) {

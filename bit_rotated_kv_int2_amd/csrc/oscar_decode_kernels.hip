@@ -677,7 +677,7 @@ struct MergeSmem {
   float zs[GH][kD];             // weighted history sum, bit-reversal permuted
   float ot[GH][kD];             // history output in the original basis
   float ob[GH][kD];             // weighted BF16 tile sum
-  float red[2][kMergeSlices * 4 * kD];   // per-slice sums (history, tiles)
+  alignas(16) float red[2][kMergeSlices * 4 * kD];   // per-slice sums (history, tiles)
 };
 
 template <int MT, int GH, int NW, bool MFMA>
@@ -761,7 +761,7 @@ __device__ void bf16_tile_partial(const DecArgs &a, int b, int kv, int u, float 
     }
   }
   wave_lds_sync();
-  for (int e = lane; e < G * kD; e += 64) st_coherent(dst + (size_t)(e / kD) * kPartStride + 2 + e % kD, scratch[e / kD][e % kD]);
+  for (int e = lane; e < G * kD; e += 64) st_coherent(dst + (size_t)(e / kD) * kPartStride + kPartO + e % kD, scratch[e / kD][e % kD]);
   wave_lds_sync();
 }
 
@@ -788,7 +788,7 @@ __device__ void write_split_partial(ScanSmem<MT, GH, NW, MFMA> &sm, int G, float
       st_coherent(d, M);
       st_coherent(d + 1, l);
     }
-    st_coherent(d + 2 + c, o);
+    st_coherent(d + kPartO + c, o);
   }
 }
 
@@ -1072,8 +1072,9 @@ __device__ void run_scan_valu(const DecArgs &a, int b, int kv, int split, float 
 template <int GH, int NT, bool UVL = false>
 __device__ void merge_item(const DecArgs &a, int b, int kv, const float *hist, int n_hist_parts, const float *tiles,
                            int n_tile_parts, MergeSmem<GH, UVL> &sm) {
-  // (head, channel pair) items per thread when each item takes all partials
-  constexpr int kItems = (GH * (kD / 2) + NT - 1) / NT;
+  // (head, channel quad) items per thread when each item takes all partials
+  // (quads padded to whole waves)
+  constexpr int kItems = ((GH * (kD / 4) + 63) / 64 * 64 + NT - 1) / NT;
   const PoolView &pv = a.pv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nwaves = blockDim.x >> 6;
@@ -1083,8 +1084,12 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *hist, i
   // each.  Row (p, h) of the partials from wave-uniform p and h: scalar
   // address arithmetic, the lanes add only their channel offset.
   const int pstride = G * kPartStride;
-  auto row_at = [&](int p, int h) -> const float * {
-    return (p < S ? hist + (size_t)p * pstride : tiles + (size_t)(p - S) * pstride) + (size_t)h * kPartStride;
+  const __amdgpu_buffer_rsrc_t rs_hist = coherent_rsrc(hist, (uint32_t)(S * pstride * 4));
+  const __amdgpu_buffer_rsrc_t rs_tile = coherent_rsrc(tiles, (uint32_t)(n_tile_parts * pstride * 4));
+  // 16 bytes at float offset off of partial p (p wave-uniform)
+  auto part4 = [&](int p, uint32_t off) -> float4 {
+    return p < S ? ld_coherent4(rs_hist, 4u * off, (uint32_t)(p * pstride * 4))
+                 : ld_coherent4(rs_tile, 4u * off, (uint32_t)((p - S) * pstride * 4));
   };
   // U_V rows for step 4: the last kUT threads own row k = t' / kLPR
   // (t' = t - (NT - kUT)), channels kCPL (t' % kLPR) .. + kCPL.  With 12
@@ -1107,28 +1112,29 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *hist, i
     asm volatile("" ::: "memory");
   }
   // 1) one round of device-coherent loads: the first kPer partials of each
-  // thread's slice (thread -> head, channel pair, slice; 8 bytes each) into
+  // thread's slice (thread -> head, channel quad, slice; 16 bytes each) into
   // registers, and the (m, l) headers of every partial into LDS.  Further
-  // rounds (only when P > kPer * slices) reload values in step 3.
-  constexpr int kPer = kItems == 1 ? 18 : 8;   // one round covers 3 x 18 = 54 partials at G = 4
-  const int npair = G * (kD / 2);
-  const int nsl = min(kMergeSlices, min(max(1, NT / npair), 24 / G));
-  const int nitem = npair * nsl;   // <= kItems * NT
+  // rounds (only when P > kPer * slices) reload values in step 3.  The quads
+  // of a slice are padded to whole waves, so the slice (and with it the
+  // partial index) is wave-uniform; padding lanes load head 0 and are idle.
+  constexpr int kPer = 8;   // one round covers 6 x 8 = 48 partials at G = 4
+  const int nq = G * (kD / 4);
+  const int nqp = (nq + 63) & ~63;
+  const int nsl = min(kMergeSlices, min(max(1, NT / nqp), 24 / G));
+  const int nitem = nqp * nsl;   // <= kItems * NT
   const int rounds = (P + nsl * kPer - 1) / (nsl * kPer);
-  float2 val[kItems][kPer];
+  float4 val[kItems][kPer];
 #pragma unroll
   for (int it = 0; it < kItems; ++it) {
     const int e = tid + it * NT;
     if (e >= nitem) break;
-    // npair and NT are multiples of 64: slice and head are wave-uniform
-    const int pr = e % npair;
-    const int sl = __builtin_amdgcn_readfirstlane(e / npair);
-    const int h = __builtin_amdgcn_readfirstlane(pr / (kD / 2));
-    const int c = 2 * (pr % (kD / 2));
+    const int qd = e % nqp;
+    const int sl = __builtin_amdgcn_readfirstlane(e / nqp);
+    const uint32_t off = qd < nq ? (uint32_t)((qd >> 5) * kPartStride + kPartO + 4 * (qd & 31)) : (uint32_t)kPartO;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int p = sl + nsl * j;
-      val[it][j] = p < P ? ld_coherent2(row_at(p, h) + 2 + c) : make_float2(0.f, 0.f);
+      val[it][j] = p < P ? part4(p, off) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
   for (int e = tid; e < P * G; e += blockDim.x) {   // partial e / G, head e % G
@@ -1185,40 +1191,37 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *hist, i
   for (int it = 0; it < kItems; ++it) {
     const int e = tid + it * NT;
     if (e >= nitem) break;
-    const int pr = e % npair;
-    const int sl = __builtin_amdgcn_readfirstlane(e / npair);
-    const int h = __builtin_amdgcn_readfirstlane(pr / (kD / 2));
-    const int c = 2 * (pr % (kD / 2));
-    float hx = 0.f, hy = 0.f, bx = 0.f, by = 0.f;
+    const int qd = e % nqp;
+    const int sl = __builtin_amdgcn_readfirstlane(e / nqp);
+    const bool act = qd < nq;
+    const int h = act ? qd >> 5 : 0, c = 4 * (qd & 31);
+    const uint32_t off = (uint32_t)(h * kPartStride + kPartO + c);
+    float4 hs4 = make_float4(0.f, 0.f, 0.f, 0.f), bs4 = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int r = 0; r < rounds; ++r) {
       const int p_base = nsl * kPer * r;
-      float2 v[kPer];
+      float4 v[kPer];
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
         const int p = p_base + sl + nsl * j;
-        v[j] = r == 0 ? val[it][j]
-                      : (p < P ? ld_coherent2(row_at(p, h) + 2 + c) : make_float2(0.f, 0.f));
+        v[j] = r == 0 ? val[it][j] : (p < P ? part4(p, off) : make_float4(0.f, 0.f, 0.f, 0.f));
       }
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
         const int p = p_base + sl + nsl * j;
-        if (p < S) {
+        if (p < P) {
           const float w = sm.wgt[p][h];
-          hx = fmaf(w, v[j].x, hx);
-          hy = fmaf(w, v[j].y, hy);
-        } else if (p < P) {
-          const float w = sm.wgt[p][h];
-          bx = fmaf(w, v[j].x, bx);
-          by = fmaf(w, v[j].y, by);
+          float4 &acc = p < S ? hs4 : bs4;
+          acc.x = fmaf(w, v[j].x, acc.x);
+          acc.y = fmaf(w, v[j].y, acc.y);
+          acc.z = fmaf(w, v[j].z, acc.z);
+          acc.w = fmaf(w, v[j].w, acc.w);
         }
       }
     }
-    float *rh = sm.red[0] + (size_t)sl * G * kD + h * kD + c;
-    float *rb = sm.red[1] + (size_t)sl * G * kD + h * kD + c;
-    rh[0] = hx;
-    rh[1] = hy;
-    rb[0] = bx;
-    rb[1] = by;
+    if (act) {
+      *(float4 *)(sm.red[0] + (size_t)sl * G * kD + h * kD + c) = hs4;
+      *(float4 *)(sm.red[1] + (size_t)sl * G * kD + h * kD + c) = bs4;
+    }
   }
   __syncthreads();
   for (int idx = tid; idx < G * kD; idx += blockDim.x) {

@@ -19,7 +19,8 @@ constexpr int kVCodes = OSCAR_PAGE_VCODES;
 constexpr int kKMeta = OSCAR_PAGE_KMETA;
 constexpr int kVMeta = OSCAR_PAGE_VMETA;
 constexpr int kMaxGroupHeads = 16;          // Hq / Hkv supported
-constexpr int kPartStride = 132;            // floats per (m, l, o[128]) partial, padded
+constexpr int kPartStride = 132;            // floats per partial: m, l, 2 pad, o[128]
+constexpr int kPartO = 4;                   // offset of o in a partial (16-byte aligned)
 constexpr int kTileTokens = 16;             // BF16 window tokens per decode tile
 
 // Bit reversal of a 7-bit channel index (d = 128).
@@ -58,6 +59,16 @@ __device__ __forceinline__ void st_coherent(float *p, float v) {
 }
 __device__ __forceinline__ float ld_coherent(const float *p) {
   return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Buffer resource of n bytes at p for 16-byte device-coherent loads
+// (out-of-range offsets read 0); word 3 = raw 32-bit data format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const float *p, uint32_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p), 0, (int)n, 0x00020000);
+}
+// Four floats at byte offset voff + soff of a buffer, device-coherent
+// (cache policy SC1, as an agent-scope atomic load).
+__device__ __forceinline__ float4 ld_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 16));
 }
 // Two adjacent floats (8-byte aligned) in one device-coherent load.
 __device__ __forceinline__ float2 ld_coherent2(const float *p) {

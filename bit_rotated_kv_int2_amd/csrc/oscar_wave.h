@@ -360,7 +360,7 @@ __device__ __forceinline__ void bf16_block_combine(int G, const float (&m)[4], c
       st_coherent(dst, M);
       st_coherent(dst + 1, lv);
     }
-    st_coherent(dst + 2 + c, ov);
+    st_coherent(dst + kPartO + c, ov);
   }
 }
 
