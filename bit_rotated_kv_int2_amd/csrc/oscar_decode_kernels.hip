@@ -1117,7 +1117,7 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *hist, i
   // rounds (only when P > kPer * slices) reload values in step 3.  The quads
   // of a slice are padded to whole waves, so the slice (and with it the
   // partial index) is wave-uniform; padding lanes load head 0 and are idle.
-  constexpr int kPer = 8;   // one round covers 6 x 8 = 48 partials at G = 4
+  constexpr int kPer = 9;   // one round covers 6 x 9 = 54 partials at G = 4 (32 splits + 20 tiles at batch 1)
   const int nq = G * (kD / 4);
   const int nqp = (nq + 63) & ~63;
   const int nsl = min(kMergeSlices, min(max(1, NT / nqp), 24 / G));
