@@ -71,12 +71,18 @@ __device__ __forceinline__ float lane_xor(float v) {
 }
 
 // Reductions over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15); every
-// lane of the row receives the result.
+// lane of the row receives the result.  The maximum takes a plain DPP move
+// and the NaN-propagating maximum (one v_maximum3_f32 per step; fmaxf would
+// add a canonicalising max of the moved value).  Inputs are never NaN.
+template <int CTRL>
+__device__ __forceinline__ float movdppf(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dppf<kDppQuadSwap1>(v));
-  v = fmaxf(v, dppf<kDppQuadSwap2>(v));
-  v = fmaxf(v, dppf<kDppRowRor4>(v));
-  v = fmaxf(v, dppf<kDppRowRor8>(v));
+  v = __builtin_elementwise_maximum(v, movdppf<kDppQuadSwap1>(v));
+  v = __builtin_elementwise_maximum(v, movdppf<kDppQuadSwap2>(v));
+  v = __builtin_elementwise_maximum(v, movdppf<kDppRowRor4>(v));
+  v = __builtin_elementwise_maximum(v, movdppf<kDppRowRor8>(v));
   return v;
 }
 __device__ __forceinline__ float row16_sum(float v) {
