@@ -177,6 +177,35 @@ def test_batch_scattered_ragged():
     assert int(pool.error_flags.cpu()[0]) == 0
 
 
+@pytest.mark.parametrize("G", [1, 2, 3, 5, 8, 16])
+def test_decode_group_sizes(G):
+    """Query heads per KV head from 1 to 16: one, two and four M-tiles of
+    four heads, partly filled tiles (G = 1, 2, 3, 5), two KV heads, two
+    sequences of ragged length (partial last page); every decode variant."""
+    wl = synth.Workload(100 + G, f"test-g{G}", 2, 2, 2 * G, 128, 900, 1700, n_cal=256, outliers="pairs10",
+                        scattered_pages=True)
+    cals = oracle_calibration(wl, n_cal=256)
+    rot = rotation_tensors(cals)
+    params = O.make_params(wl.n_kv, wl.n_q)
+    lens = np.array([1700, 931], np.int32)
+    bt, total = synth.block_table(wl, lens)
+    pool = O.KVPool(params, wl.batch, total, bt)
+    toks = []
+    for b in range(wl.batch):
+        kb, vb = synth.kv_tokens(wl, 0, b, 0, int(lens[b]))
+        toks.append((kb, vb))
+        append_sequence(params, rot, pool, b, kb, vb, chunks=[int(lens[b]) - 1, 1])
+    q = synth.decode_queries(wl, 0)
+    refs = [_oracle_decode(wl, cals, toks[b][0], toks[b][1], q[b])[0] for b in range(wl.batch)]
+    for variant in (0, 1, 2):
+        out = _decode_gpu(params, rot, pool, q, variant)
+        for b in range(wl.batch):
+            err = decode_check(out[b], refs[b])
+            print(f"G {G} variant {variant} seq {b}: max err / norm = {err:.3e}", flush=True)
+            assert err <= TOL, (G, b, variant, err)
+    assert int(pool.error_flags.cpu()[0]) == 0
+
+
 @pytest.mark.skip(reason="balanced-partition scan switched off in the library: an earlier build of its "
                          "page copies faulted the device (sign-extended DMA source address, corrected "
                          "since) and the corrected build has not run on the device yet")
