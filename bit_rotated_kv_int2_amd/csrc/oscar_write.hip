@@ -322,45 +322,48 @@ __global__ void __launch_bounds__(kThreads) append_one_kernel(AppendArgs a) {
   const PoolView &pv = a.pv;
   const int b = blockIdx.y, h = blockIdx.x >> 1, is_v = blockIdx.x & 1;
   const int j = threadIdx.x;
+  // Loads that do not depend on the sequence length are issued together
+  // with it: the new token, the clip threshold and (S1) column j of U, all
+  // 128 loads at once.  The length then decides the ring slot and the page.
+  const uint16_t nb = (is_v ? a.v_new : a.k_new)[((size_t)b * pv.hkv + h) * kD + j];
+  const float tau = (is_v ? a.rv.tau_V : a.rv.tau_K)[h];
+  const float *U = (is_v ? a.rv.U_V : a.rv.U_K) + (size_t)h * kD * kD + j;
+  float u[kD];
+#pragma unroll
+  for (int k = 0; k < kD; ++k) u[k] = U[(size_t)k * kD];
   const int p0 = pv.seq_lens[b];
   __shared__ double xs[kD];
   __shared__ double ys[kD];
   if (p0 >= 0) {
-    const uint16_t nb = (is_v ? a.v_new : a.k_new)[((size_t)b * pv.hkv + h) * kD + j];
-    bool demote = false;
-    uint16_t old = 0;
-    if (p0 < pv.sink) {
+    // the ring slot's old token and the page's block-table entry are
+    // loaded together; the new token goes into the ring slot at the end
+    const bool in_ring = p0 >= pv.sink;
+    uint16_t *el = (is_v ? pv.recent_v : pv.recent_k) + (((size_t)b * pv.hkv + h) * pv.recent + p0 % pv.recent) * kD + j;
+    const bool demote = in_ring && p0 - pv.recent >= pv.sink;   // the slot's token leaves the window
+    const int page_idx = demote ? (p0 - pv.recent - pv.sink) / kPageTokens : 0;
+    const bool in_table = demote && page_idx < pv.max_pages;
+    int phys = in_table ? pv.block_table[(size_t)b * pv.max_pages + page_idx] : -1;
+    const uint16_t old_raw = *el;   // in bounds for any p0: no branch, no early wait
+    const uint16_t old = demote ? old_raw : 0;
+    if (!in_ring) {
       const int ss = pv.sink_slot[b];
       if (ss >= 0 && ss < pv.n_sink_slots)
         (is_v ? pv.sink_v : pv.sink_k)[(((size_t)ss * pv.hkv + h) * pv.sink + p0) * kD + j] = nb;
       else if (blockIdx.x == 0 && j == 0 && pv.err)
         atomicOr(pv.err, OSCAR_DEVERR_SINKSLOT);
-    } else {
-      uint16_t *el = (is_v ? pv.recent_v : pv.recent_k) + (((size_t)b * pv.hkv + h) * pv.recent + p0 % pv.recent) * kD + j;
-      demote = p0 - pv.recent >= pv.sink;   // the slot's token leaves the window
-      if (demote) old = *el;
-      *el = nb;
     }
-    int phys = -1;
-    if (demote) {
-      const int page_idx = (p0 - pv.recent - pv.sink) / kPageTokens;
-      if (page_idx >= pv.max_pages) {
-        if (j == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_LENGTH);
-      } else {
-        phys = pv.block_table[(size_t)b * pv.max_pages + page_idx];
-        if (phys < 0 || phys >= pv.n_pages) {
-          if (j == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
-          phys = -1;
-        }
-      }
+    if (demote && !in_table && j == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_LENGTH);
+    if (in_table && (phys < 0 || phys >= pv.n_pages)) {
+      if (j == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
+      phys = -1;
     }
     if (phys >= 0) {   // block-uniform
       const int slot = (p0 - pv.recent - pv.sink) % kPageTokens;
-      // S1: thread j takes column j of U; all 128 loads are issued together
-      const float *U = (is_v ? a.rv.U_V : a.rv.U_K) + (size_t)h * kD * kD + j;
-      float u[kD];
-#pragma unroll
-      for (int k = 0; k < kD; ++k) u[k] = U[(size_t)k * kD];
+      uint8_t *page = pv.pages + ((size_t)phys * pv.hkv + h) * kPageBytes;
+      // V: the code byte this thread rewrites holds three other slots'
+      // codes; its load goes out now, ahead of the projection
+      uint8_t *vdst = page + kVCodes + j * 16 + vcode_byte(slot);
+      const uint8_t vold = *vdst;   // in the page for K and V blocks alike: no branch
       xs[j] = (double)bf16_to_f32(old);
       __syncthreads();
       double y = 0.0;
@@ -383,8 +386,6 @@ __global__ void __launch_bounds__(kThreads) append_one_kernel(AppendArgs a) {
       __syncthreads();
       // S3..S8: thread j = output channel p
       const int p = j;
-      const float tau = (is_v ? a.rv.tau_V : a.rv.tau_K)[h];
-      uint8_t *page = pv.pages + ((size_t)phys * pv.hkv + h) * kPageBytes;
       const float v = (float)(ys[bitrev7(p)] * kInvSqrtD);
       const uint32_t code = quantize_code(v, tau, p, (uint16_t *)(page + (is_v ? kVMeta : kKMeta) + meta_entry(slot) * 4));
       if (!is_v) {
@@ -394,11 +395,11 @@ __global__ void __launch_bounds__(kThreads) append_one_kernel(AppendArgs a) {
         if ((p & 3) == 0) page[kKCodes + slot * 32 + (p >> 2)] = (uint8_t)c;
       } else {
         // one 2-bit field of a byte shared with three other slots
-        uint8_t *dst = page + kVCodes + p * 16 + vcode_byte(slot);
         const uint32_t sh = 2 * (slot & 3);
-        *dst = (uint8_t)((*dst & ~(3u << sh)) | (code << sh));
+        *vdst = (uint8_t)((vold & ~(3u << sh)) | (code << sh));
       }
     }
+    if (in_ring) *el = nb;
   }
   __syncthreads();
   if (j == 0) {
