@@ -987,10 +987,25 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   QueryOps<MT> qo;
   load_query_ops<MT, GH>(sm.q.aq, sm.q.qc, G, pv.sm_scale * kLog2e, ms, lane, qo);
   __syncthreads();   // the query scratch is reused by the weights and the BF16 tiles
-  // the preparing waves start their copies only now: issuing them inside
-  // the preparation would stall those waves (the CU accepts copy requests
-  // at the memory rate) and with them every wave waiting on the preparation
-  if (wave < 4) pipe_prologue(pipe, pv, lane);
+  // BF16 tiles: this workgroup takes tiles u = split + S k.  Tiles k < 4 run
+  // first on waves 3..0 (the preparing waves, whose history pages are the
+  // last to arrive, and which finish their pages before the others); the
+  // rest run after the history pages, from the last wave down.  An early
+  // tile goes before the wave's page copies: its loads would otherwise
+  // complete behind them.  (The tile scratch overlaps the query scratch,
+  // which is dead after the barrier above.)
+  const int S = a.n_splits;
+  float *parts = a.part + (size_t)bh * (S + a.n_chunks) * G * kPartStride;
+  constexpr int kEarlyTiles = 4;
+  if (wave < kEarlyTiles) {
+    const int u = split + S * (kEarlyTiles - 1 - wave);
+    if (u < a.n_chunks)
+      bf16_tile_partial<GH>(a, b, kv, u, sm.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
+    // the preparing waves start their copies only now: issuing them inside
+    // the preparation would stall those waves (the CU accepts copy requests
+    // at the memory rate) and with them every wave waiting on the preparation
+    pipe_prologue(pipe, pv, lane);
+  }
   HistState<MT> st;
   hist_reset(st);
   v4i *wl = sm.wave[wave].wl;
@@ -999,15 +1014,9 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   for (int i = 0; i < MT * 2; ++i) wl[i * 64 + lane] = v4i{0, 0, 0, 0};
   pipe_scan<MT, NW, PF>(pipe, pv, n_hist, qo, st, wl, lane);
   if (pipe.bad && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
-  // BF16 tile u (sink, then recent window) runs on workgroup u % S after the
-  // history pages, from the last wave down: the waves with the fewest pages
-  {
-    const int S = a.n_splits;
-    float *parts = a.part + (size_t)bh * (S + a.n_chunks) * G * kPartStride;
-    for (int u = split; u < a.n_chunks; u += S)
-      if (NW - 1 - (u / S) % NW == wave)
-        bf16_tile_partial<GH>(a, b, kv, u, sm.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
-  }
+  for (int u = split + S * kEarlyTiles; u < a.n_chunks; u += S)
+    if (NW - 1 - (u / S - kEarlyTiles) % NW == wave)
+      bf16_tile_partial<GH>(a, b, kv, u, sm.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
   flush_partial<MT, GH, NW>(sm, st, G, ms, dst);
 }
 
