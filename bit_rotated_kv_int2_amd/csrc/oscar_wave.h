@@ -69,6 +69,12 @@ template <int M>
 __device__ __forceinline__ float lane_xor(float v) {
   return __builtin_bit_cast(float, lane_xor_i<M>(__builtin_bit_cast(int, v)));
 }
+template <int M>
+__device__ __forceinline__ double lane_xor_d(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)lane_xor_i<M>((int)(uint32_t)b), hi = (uint32_t)lane_xor_i<M>((int)(uint32_t)(b >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
 
 // Reductions over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15); every
 // lane of the row receives the result.  The maximum takes a plain DPP move
@@ -118,6 +124,17 @@ __device__ __forceinline__ float wave_max(float v) {
   const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
   const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
   return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+__device__ __forceinline__ float wave_min(float v) {
+  v = __builtin_elementwise_minimum(v, movdppf<kDppQuadSwap1>(v));
+  v = __builtin_elementwise_minimum(v, movdppf<kDppQuadSwap2>(v));
+  v = __builtin_elementwise_minimum(v, movdppf<kDppRowRor4>(v));
+  v = __builtin_elementwise_minimum(v, movdppf<kDppRowRor8>(v));
+  const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return fminf(fminf(a, b), fminf(c, d));
 }
 __device__ __forceinline__ float wave_sum(float v) {
   v = row16_sum(v);

@@ -25,7 +25,10 @@
 //      metadata bits per group: the density of the pages' 2.28 bits per
 //      element at 128K; the encoding relative to tau is this library's);
 //   S8 pack four codes per byte (page layout in oscar.h).
+#include <type_traits>
+
 #include "oscar_internal.h"
+#include "oscar_wave.h"
 
 #pragma clang fp contract(off)
 
@@ -42,15 +45,6 @@ struct AppendArgs {
   const uint16_t *k_new, *v_new;
   int n_new;
 };
-
-__device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-__device__ __forceinline__ float wave_min(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
-  return v;
-}
 
 // S6..S8 for output channel p of one token (this lane; the wave holds the 64
 // channels of one group): clamp, group metadata, code.  Returns the code;
@@ -143,64 +137,75 @@ append_demote_kernel(AppendArgs a) {
   }
   __syncthreads();
 
-  // S1: y_j = sum_k x_k U[k][j], float64, k ascending; U rows of the next
-  // eight k are loaded while the current eight are used.
+  // S1: y_j = sum_k x_k U[k][j], float64, k ascending.  Half-wave hw takes
+  // slots 16 w + 8 hw + i (i < 8) and lane l = lane % 32 output columns
+  // 4 l .. 4 l + 3, so every 16-byte LDS read of two x values feeds eight
+  // FMAs (LDS delivery, not the FMA rate, bounded the one-read-per-four
+  // layout).  U rows of the next eight k are loaded while the current eight
+  // are used.
   const float *U = (is_v ? a.rv.U_V : a.rv.U_K) + (size_t)h * kD * kD;
-  double acc[16][2];
+  const int hw = lane >> 5, lq = lane & 31;
+  double acc[8][4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i][0] = acc[i][1] = 0.0;
-  float uc[8][2], un[8][2];
+  for (int i = 0; i < 8; ++i) acc[i][0] = acc[i][1] = acc[i][2] = acc[i][3] = 0.0;
+  float4 uc[8], un[8];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    uc[kk][0] = U[kk * kD + lane];
-    uc[kk][1] = U[kk * kD + 64 + lane];
-  }
+  for (int kk = 0; kk < 8; ++kk) uc[kk] = *(const float4 *)(U + kk * kD + 4 * lq);
   for (int kb = 0; kb < kD / 8; ++kb) {
     const int kn = kb + 1 < kD / 8 ? 8 * (kb + 1) : 8 * kb;   // last block reloads itself (unused)
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      un[kk][0] = U[(kn + kk) * kD + lane];
-      un[kk][1] = U[(kn + kk) * kD + 64 + lane];
-    }
+    for (int kk = 0; kk < 8; ++kk) un[kk] = *(const float4 *)(U + (kn + kk) * kD + 4 * lq);
 #pragma unroll
     for (int kp = 0; kp < 4; ++kp) {
       const int k = 8 * kb + 2 * kp;
-      const double u00 = uc[2 * kp][0], u01 = uc[2 * kp][1];
-      const double u10 = uc[2 * kp + 1][0], u11 = uc[2 * kp + 1][1];
+      const double u0[4] = {uc[2 * kp].x, uc[2 * kp].y, uc[2 * kp].z, uc[2 * kp].w};
+      const double u1[4] = {uc[2 * kp + 1].x, uc[2 * kp + 1].y, uc[2 * kp + 1].z, uc[2 * kp + 1].w};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const double2 xv = *(const double2 *)&xs[16 * w + i][k];
-        acc[i][0] = fma(xv.x, u00, acc[i][0]);
-        acc[i][1] = fma(xv.x, u01, acc[i][1]);
-        acc[i][0] = fma(xv.y, u10, acc[i][0]);
-        acc[i][1] = fma(xv.y, u11, acc[i][1]);
+      for (int i = 0; i < 8; ++i) {
+        const double2 xv = *(const double2 *)&xs[16 * w + 8 * hw + i][k];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc[i][c] = fma(xv.x, u0[c], acc[i][c]);
+          acc[i][c] = fma(xv.y, u1[c], acc[i][c]);
+        }
       }
     }
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      uc[kk][0] = un[kk][0];
-      uc[kk][1] = un[kk][1];
-    }
+    for (int kk = 0; kk < 8; ++kk) uc[kk] = un[kk];
   }
 
-  // S2: butterfly stages h = 1 .. 32 across lanes, then h = 64 in registers.
+  // S2: butterfly stages h = 1, 2 inside the lane's four columns, then
+  // h = 4 .. 64 across lanes of the half-wave (bit-exact lane moves), in
+  // ascending order of h: element pairs (a, b) at (e, e + h) -> (a + b, a - b).
 #pragma unroll
-  for (int hs = 1; hs < 64; hs <<= 1) {
+  for (int i = 0; i < 8; ++i) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int hs = 1; hs <= 2; hs <<= 1) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const double o = __shfl_xor(acc[i][c], hs, 64);
-        acc[i][c] = (lane & hs) ? o - acc[i][c] : acc[i][c] + o;
+      for (int c = 0; c < 4; ++c) {
+        if (c & hs) continue;
+        const double x0 = acc[i][c], x1 = acc[i][c + hs];
+        acc[i][c] = x0 + x1;
+        acc[i][c + hs] = x0 - x1;
       }
     }
   }
+  auto stage = [&](auto M) {
+    constexpr int m = decltype(M)::value;   // element bit 4 m <-> lane bit m
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const double x0 = acc[i][0], x1 = acc[i][1];
-    acc[i][0] = x0 + x1;
-    acc[i][1] = x0 - x1;
-  }
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const double o = lane_xor_d<m>(acc[i][c]);
+        acc[i][c] = (lq & m) ? o - acc[i][c] : acc[i][c] + o;
+      }
+    }
+  };
+  stage(std::integral_constant<int, 1>{});
+  stage(std::integral_constant<int, 2>{});
+  stage(std::integral_constant<int, 4>{});
+  stage(std::integral_constant<int, 8>{});
+  stage(std::integral_constant<int, 16>{});
 
   // S3, S5: the float32 values of the wave's 16 slots, in butterfly order,
   // staged in its own rows of xs (free after S1).  Row stride 132 floats.
@@ -210,9 +215,9 @@ append_demote_kernel(AppendArgs a) {
   float4 *stat = (float4 *)(ys + 16 * kRow);       // per slot: zero0, scale0, zero1, scale1
   uint32_t *smeta = (uint32_t *)(stat + 16);       // per slot: s8_0 | z8_0 << 8 | s8_1 << 16 | z8_1 << 24
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    ys[i * kRow + lane] = (float)(acc[i][0] * kInvSqrtD);
-    ys[i * kRow + 64 + lane] = (float)(acc[i][1] * kInvSqrtD);
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ys[(8 * hw + i) * kRow + 4 * lq + c] = (float)(acc[i][c] * kInvSqrtD);
   }
   wave_lds_sync();
   // S6, S7 per slot and group, lane i < 16 taking slot 16 w + i.  Output
@@ -270,11 +275,14 @@ append_demote_kernel(AppendArgs a) {
     if (!is_v) {
       // K row: dword q holds channels 16 q .. 16 q + 15, two bits each
       uint32_t k0 = code0 << (2 * (lane & 15)), k1 = code1 << (2 * (lane & 15));
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        k0 |= __shfl_xor(k0, o, 64);
-        k1 |= __shfl_xor(k1, o, 64);
-      }
+      k0 |= (uint32_t)lane_xor_i<1>((int)k0);
+      k1 |= (uint32_t)lane_xor_i<1>((int)k1);
+      k0 |= (uint32_t)lane_xor_i<2>((int)k0);
+      k1 |= (uint32_t)lane_xor_i<2>((int)k1);
+      k0 |= (uint32_t)lane_xor_i<4>((int)k0);
+      k1 |= (uint32_t)lane_xor_i<4>((int)k1);
+      k0 |= (uint32_t)lane_xor_i<8>((int)k0);
+      k1 |= (uint32_t)lane_xor_i<8>((int)k1);
       if ((lane & 15) == 0) {
         uint32_t *row = (uint32_t *)(page + kKCodes + slot * 32);
         row[lane >> 4] = k0;
@@ -370,11 +378,17 @@ __global__ void __launch_bounds__(kThreads) append_one_kernel(AppendArgs a) {
 #pragma unroll
       for (int k = 0; k < kD; ++k) y = fma(xs[k], (double)u[k], y);
       // S2: butterfly; stages 1..32 inside the wave, stage 64 through LDS
-#pragma unroll
-      for (int hs = 1; hs < 64; hs <<= 1) {
-        const double o = __shfl_xor(y, hs, 64);
+      auto stage1 = [&](auto M) {
+        constexpr int hs = decltype(M)::value;
+        const double o = lane_xor_d<hs>(y);
         y = (j & hs) ? o - y : y + o;
-      }
+      };
+      stage1(std::integral_constant<int, 1>{});
+      stage1(std::integral_constant<int, 2>{});
+      stage1(std::integral_constant<int, 4>{});
+      stage1(std::integral_constant<int, 8>{});
+      stage1(std::integral_constant<int, 16>{});
+      stage1(std::integral_constant<int, 32>{});
       ys[j] = y;
       __syncthreads();
       {
@@ -390,8 +404,8 @@ __global__ void __launch_bounds__(kThreads) append_one_kernel(AppendArgs a) {
       const uint32_t code = quantize_code(v, tau, p, (uint16_t *)(page + (is_v ? kVMeta : kKMeta) + meta_entry(slot) * 4));
       if (!is_v) {
         uint32_t c = code << (2 * (p & 3));
-        c |= __shfl_xor(c, 1, 64);
-        c |= __shfl_xor(c, 2, 64);
+        c |= (uint32_t)lane_xor_i<1>((int)c);
+        c |= (uint32_t)lane_xor_i<2>((int)c);
         if ((p & 3) == 0) page[kKCodes + slot * 32 + (p >> 2)] = (uint8_t)c;
       } else {
         // one 2-bit field of a byte shared with three other slots
