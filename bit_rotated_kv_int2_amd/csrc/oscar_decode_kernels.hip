@@ -1077,7 +1077,9 @@ __device__ void run_scan_valu(const DecArgs &a, int b, int kv, int split, float 
 // and U_V^T once; merge of the BF16 tiles; combine and normalise.  Partials
 // written by other workgroups are read with device-coherent loads, issued in
 // batches so that the merge costs a few memory round trips, not one per
-// partial.  U_V rows are fetched first so that their latency overlaps.
+// partial.  The U_V rows are loaded once the partial loads are out, by
+// threads that do not compute the per-head weights, so that their latency
+// overlaps the weights and the weighted sums.
 template <int GH, int NT, bool UVL = false>
 __device__ void merge_item(const DecArgs &a, int b, int kv, const float *hist, int n_hist_parts, const float *tiles,
                            int n_tile_parts, MergeSmem<GH, UVL> &sm) {
@@ -1090,8 +1092,9 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *hist, i
   const int G = pv.hq / pv.hkv;
   const int S = n_hist_parts, P = n_hist_parts + n_tile_parts;
   // partial p: history split p < S, else BF16 tile p - S; [G][kPartStride]
-  // each.  Row (p, h) of the partials from wave-uniform p and h: scalar
-  // address arithmetic, the lanes add only their channel offset.
+  // each.  A buffer resource per segment; the partial's offset (p is
+  // wave-uniform) goes in the scalar offset, the lane's (head, channels)
+  // offset in the vector offset.
   const int pstride = G * kPartStride;
   const __amdgpu_buffer_rsrc_t rs_hist = coherent_rsrc(hist, (uint32_t)(S * pstride * 4));
   const __amdgpu_buffer_rsrc_t rs_tile = coherent_rsrc(tiles, (uint32_t)(n_tile_parts * pstride * 4));
