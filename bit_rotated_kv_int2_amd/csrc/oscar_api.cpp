@@ -12,6 +12,7 @@ namespace {
 
 thread_local char g_err[512] = "";
 int g_variant = 0;
+int g_blocks = 0;
 hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 
 int fail(int code, const char *fmt, ...) {
@@ -117,6 +118,12 @@ int32_t oscar_set_decode_variant(int32_t variant) {
   return ok();
 }
 
+int32_t oscar_set_decode_blocks(int32_t blocks) {
+  if (blocks < 0 || blocks > 65536) return fail(OSCAR_EINVAL, "blocks must be in [0, 65536]");
+  g_blocks = blocks;
+  return ok();
+}
+
 int32_t oscar_calibrate_rotation(const oscar_params *p, const float *q_cal, int64_t n_q,
                                  const float *k_cal, const float *v_cal, int64_t n_kv,
                                  double quantile_k, double quantile_v, float *U_K, float *U_V,
@@ -155,7 +162,8 @@ int32_t oscar_quantize_append(const oscar_params *p, const oscar_rotation *rot,
 
 size_t oscar_decode_workspace_size(const oscar_params *p, int32_t batch, int32_t max_pages) {
   if (check_params(p) || batch < 1 || max_pages < 0) return 0;
-  return oscar::make_decode_plan(batch, p->num_kv_heads, p->num_q_heads, max_pages, p->sink, p->recent, g_variant)
+  return oscar::make_decode_plan(batch, p->num_kv_heads, p->num_q_heads, max_pages, p->sink, p->recent, g_variant,
+                                 g_blocks)
       .total;
 }
 
@@ -168,7 +176,7 @@ int32_t oscar_decode_attention(const oscar_params *p, const oscar_rotation *rot,
   if (!q || !out) return fail(OSCAR_EINVAL, "q/out is NULL");
   if (misaligned(q) || misaligned(out)) return fail(OSCAR_EINVAL, "q/out must be 16-byte aligned");
   const oscar::DecodePlan plan = oscar::make_decode_plan(pool->batch, p->num_kv_heads, p->num_q_heads,
-                                                          pool->max_pages, p->sink, p->recent, g_variant);
+                                                          pool->max_pages, p->sink, p->recent, g_variant, g_blocks);
   if (!workspace || workspace_bytes < plan.total)
     return fail(OSCAR_EWORKSPACE, "workspace of %zu bytes needed, %zu given", plan.total, workspace_bytes);
   if (((uintptr_t)workspace) & 255) return fail(OSCAR_EINVAL, "workspace must be 256-byte aligned");

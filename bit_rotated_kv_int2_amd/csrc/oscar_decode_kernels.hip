@@ -82,6 +82,19 @@ __device__ __forceinline__ v4i unpack16(uint32_t w) {
   return r;
 }
 
+// The same for value codes, with a mask and no shift where the field fits
+// in a signed byte: register s holds code * 4^s for s = 0, 1, 2 (at most 48)
+// and the plain code for s = 3.  The weights multiplied with register s are
+// divided by 4^s beforehand (see int2_page).
+__device__ __forceinline__ v4i unpack16_v(uint32_t w) {
+  v4i r;
+  r[0] = (int)(w & 0x03030303u);
+  r[1] = (int)(w & 0x0C0C0C0Cu);
+  r[2] = (int)(w & 0x30303030u);
+  r[3] = (int)((w >> 6) & 0x03030303u);
+  return r;
+}
+
 // Byte i of a word as a float (one v_cvt_f32_ubyte<i>).
 __device__ __forceinline__ float ubyte_f(uint32_t w, int i) { return (float)((w >> (8 * i)) & 0xFFu); }
 
@@ -405,6 +418,9 @@ template <int MT, bool FULL>
 __device__ __forceinline__ void int2_page(const PageRegs &r, int valid, const QueryOps<MT> &qo, HistState<MT> &st,
                                           v4i *wl) {
   const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+  // this lane's weights meet value-code register n % 4 (see unpack16_v)
+  // (kWScale / 4^s for s = n % 4 < 3, else kWScale: exponent steps 0, 2, 4, 0)
+  const float wsc = __int_as_float(__float_as_int(kWScale) - (int)(((0x00040200u >> (8 * (n & 3))) & 0xFFu) << 23));
   const uint32_t kmw[4] = {r.km.x, r.km.y, r.km.z, r.km.w};
   const uint32_t vmw[4] = {r.vm.x, r.vm.y, r.vm.z, r.vm.w};
   float lg[MT][4];
@@ -429,10 +445,8 @@ __device__ __forceinline__ void int2_page(const PageRegs &r, int valid, const Qu
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     // move the reference only when some logit exceeds it by the headroom
-    const float thr = st.mref[mt] + kHeadroom;
-    const bool over = lg[mt][0] > thr || lg[mt][1] > thr || lg[mt][2] > thr || lg[mt][3] > thr;
-    if (__builtin_amdgcn_ballot_w64(over)) {
-      float pm = fmaxf(fmaxf(lg[mt][0], lg[mt][1]), fmaxf(lg[mt][2], lg[mt][3]));
+    float pm = fmaxf(fmaxf(lg[mt][0], lg[mt][1]), fmaxf(lg[mt][2], lg[mt][3]));
+    if (__builtin_amdgcn_ballot_w64(pm > st.mref[mt] + kHeadroom)) {
       pm = row16_max(pm);
       const float mnew = fmaxf(st.mref[mt], pm);
       rescale<MT>(st, mt, exp2_fast(st.mref[mt] - mnew));
@@ -460,7 +474,7 @@ __device__ __forceinline__ void int2_page(const PageRegs &r, int valid, const Qu
     wmax = row16_max(wmax);
     // approximate reciprocal: kq may exceed kWScale / wmax by an ulp, which
     // the margin in kWScale absorbs; pscale is exact in the same sense
-    const float kq = wmax > 0.f ? kWScale * __builtin_amdgcn_rcpf(wmax) : 0.f;
+    const float kq = wmax > 0.f ? wsc * __builtin_amdgcn_rcpf(wmax) : 0.f;
     pscale[mt] = wmax * (1.0f / kWScale);
     uint32_t u0[4], u1[4];
 #pragma unroll
@@ -490,13 +504,17 @@ __device__ __forceinline__ void int2_page(const PageRegs &r, int valid, const Qu
   wave_lds_sync();
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
-    const v4i Bv = unpack16(r.vc[nt]);
+    const v4i Bv = unpack16_v(r.vc[nt]);
     const int g = nt >> 2;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const v4i C = mfma_i8(Aw[mt][g], Bv, v4i{0, 0, 0, 0});
       // sum over 64 tokens of u * code <= 8355000 * 3 * 64 < 2^31: exact in int32
-      const int val = (int)(((unsigned)C[0] << 16) + ((unsigned)C[1] << 8) + (unsigned)C[2]);
+      // two shift-adds; the empty asm (on a VALU result) keeps the compiler
+      // from re-associating them into two shifts and a three-way add
+      int t = (int)(((unsigned)C[0] << 8) + (unsigned)C[1]);
+      asm volatile("" : "+v"(t));
+      const int val = (int)(((unsigned)t << 8) + (unsigned)C[2]);
       st.facc[mt][nt] = fmaf((float)val, pscale[mt], st.facc[mt][nt]);
     }
   }
@@ -794,22 +812,28 @@ __device__ void write_split_partial(ScanSmem<MT, GH, NW, MFMA> &sm, int G, float
 
 // History page pipeline of one wave over the pages [pg0, pg1) of one
 // (sequence, KV head): the wave takes pages first + i * NW, i < npg, with up
-// to PF page copies in flight (LDS DMA).  Lane k of bt holds the block-table
-// entry of page index 64 c + k, c = the chunk of the next page issued.
-// Complete the load of a block-table register and redefine it through an
-// empty asm: later reads of it (one readlane per page) then carry no
+// to PF page copies in flight (LDS DMA).  The block-table entries of a span
+// of kBtSpan pages are loaded together, 64 per register (lane k of bt0 holds
+// the entry of the next page index with remainder k mod 64; bt1 and bt2 the
+// following 64 each, shifted down every 64 pages).  One span covers every
+// page of a wave up to 2.1 M tokens of history per workgroup, so the refill
+// (which drains the wave's copies) is rare.
+constexpr int kBtSpan = 192;
+// Complete the loads of the block-table registers and redefine them through
+// an empty asm: later reads of them (one readlane per page) then carry no
 // compiler wait.  Without this the compiler, unable to prove across the
-// loop that the refill load (every 64 pages) has landed, waits for every
-// outstanding vector-memory operation, page copies included, at each
-// page issue.
-__device__ __forceinline__ void bt_settle(int &bt) {
+// loop that a refill load has landed, waits for every outstanding
+// vector-memory operation, page copies included, at each page issue.
+template <typename P>
+__device__ __forceinline__ void bt_settle(P &p) {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  asm volatile("" : "+v"(bt));
+  asm volatile("" : "+v"(p.bt0), "+v"(p.bt1), "+v"(p.bt2));
 }
-// The same for the block-table register and two loaded floats together.
-__device__ __forceinline__ void bt_settle(int &bt, float &x, float &y) {
+// The same for the block-table registers and two loaded floats together.
+template <typename P>
+__device__ __forceinline__ void bt_settle(P &p, float &x, float &y) {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  asm volatile("" : "+v"(bt), "+v"(x), "+v"(y));
+  asm volatile("" : "+v"(p.bt0), "+v"(p.bt1), "+v"(p.bt2), "+v"(x), "+v"(y));
 }
 
 template <int NW, int PF>
@@ -819,20 +843,30 @@ struct PagePipe {
   size_t pstride;
   uint4 (*bufs)[kPageBytes / 16];
   uint32_t lds0;
-  int bt, first, npg, issued;
+  int bt0, bt1, bt2;
+  int first, npg, issued;
   uint32_t inflight;   // bit j: page i + j (i = next page consumed) has a copy in flight
   bool bad;
 };
 
-// Issues the first block-table load without waiting for it: a bt_settle of
-// p.bt must come before pipe_prologue.
+// Block-table entries of the span starting at page index j (loads only).
+template <int NW, int PF>
+__device__ __forceinline__ void bt_load(PagePipe<NW, PF> &p, int j, int lane) {
+  const int i = j + lane;
+  p.bt0 = i < p.npg ? p.btw[(size_t)i * NW] : -1;
+  p.bt1 = i + 64 < p.npg ? p.btw[(size_t)(i + 64) * NW] : -1;
+  p.bt2 = i + 128 < p.npg ? p.btw[(size_t)(i + 128) * NW] : -1;
+}
+
+// Issues the first block-table loads without waiting for them: a bt_settle
+// of p must come before pipe_prologue.
 template <int NW, int PF>
 __device__ __forceinline__ void pipe_init(PagePipe<NW, PF> &p, const PoolView &pv, int b, int kv, int pg0, int pg1,
                                           uint4 (*bufs)[kPageBytes / 16], int wave, int lane) {
   p.first = pg0 + wave;
   p.npg = p.first < pg1 ? (pg1 - p.first + NW - 1) / NW : 0;
   p.btw = pv.block_table + (size_t)b * pv.max_pages + p.first;
-  p.bt = lane < p.npg ? p.btw[(size_t)lane * NW] : -1;   // settled by the caller
+  bt_load(p, 0, lane);   // settled by the caller
   p.pbase = pv.pages + (size_t)kv * kPageBytes;
   p.pstride = (size_t)pv.hkv * kPageBytes;
   p.bufs = bufs;
@@ -847,10 +881,15 @@ __device__ __forceinline__ void pipe_init(PagePipe<NW, PF> &p, const PoolView &p
 template <int NW, int PF>
 __device__ __forceinline__ bool pipe_issue(PagePipe<NW, PF> &p, const PoolView &pv, int j, int lane) {
   if ((j & 63) == 0 && j > 0) {
-    p.bt = j + lane < p.npg ? p.btw[(size_t)(j + lane) * NW] : -1;
-    bt_settle(p.bt);
+    if (j % kBtSpan == 0) {
+      bt_load(p, j, lane);
+      bt_settle(p);
+    } else {   // next 64 entries of the span
+      p.bt0 = p.bt1;
+      p.bt1 = p.bt2;
+    }
   }
-  const int ph = __builtin_amdgcn_readlane(p.bt, j & 63);
+  const int ph = __builtin_amdgcn_readlane(p.bt0, j & 63);
   const bool ok = ph >= 0 && ph < pv.n_pages;
   if (ok) {
     const uint64_t base = (uint64_t)(uintptr_t)(p.pbase + (size_t)ph * p.pstride);
@@ -867,31 +906,41 @@ __device__ __forceinline__ void pipe_prologue(PagePipe<NW, PF> &p, const PoolVie
     if (pipe_issue(p, pv, p.issued, lane)) p.inflight |= 1u << p.issued;
 }
 
+// One page of the pipeline: wait for its copy, read it, refill the pipeline
+// and fold the page into the state.  A page whose copy was never issued (its
+// block-table entry is out of range) is skipped.
+template <int MT, int NW, int PF, bool FULL>
+__device__ __forceinline__ void pipe_step(PagePipe<NW, PF> &p, const PoolView &pv, int i, int n_hist,
+                                          const QueryOps<MT> &qo, HistState<MT> &st, v4i *wl, int lane) {
+  const int n = lane & 15, q = lane >> 4;
+  const bool ok = p.inflight & 1u;
+  PageRegs cur;
+  // copies issued after page i that may still be outstanding
+  wait_pages(__builtin_popcount(p.inflight >> 1));
+  load_page(cur, (const uint8_t *)p.bufs[i % PF], n, q);   // in bounds also when page i was skipped
+  wait_lds_reads();
+  p.inflight >>= 1;
+  if (p.issued < p.npg) {
+    if (pipe_issue(p, pv, p.issued, lane)) p.inflight |= 1u << (PF - 1);
+    ++p.issued;
+  }
+  if (ok) {
+    const int valid = FULL ? kPageTokens : min(kPageTokens, n_hist - (p.first + i * NW) * kPageTokens);
+    int2_page<MT, FULL>(cur, valid, qo, st, wl);
+  }
+}
+
 // Consume every page of the pipeline (the prologue must have been issued).
+// Only the last page of the history can be partly filled, so every page of
+// the wave but possibly its last runs the full-page path.
 template <int MT, int NW, int PF>
 __device__ __forceinline__ void pipe_scan(PagePipe<NW, PF> &p, const PoolView &pv, int n_hist, const QueryOps<MT> &qo,
                                           HistState<MT> &st, v4i *wl, int lane) {
-  const int n = lane & 15, q = lane >> 4;
-  for (int i = 0; i < p.npg; ++i) {
-    const bool ok = p.inflight & 1u;
-    PageRegs cur;
-    if (ok) {
-      // copies issued after page i that may still be outstanding
-      wait_pages(__builtin_popcount(p.inflight >> 1));
-      load_page(cur, (const uint8_t *)p.bufs[i % PF], n, q);
-      wait_lds_reads();
-    }
-    p.inflight >>= 1;
-    if (p.issued < p.npg) {
-      if (pipe_issue(p, pv, p.issued, lane)) p.inflight |= 1u << (PF - 1);
-      ++p.issued;
-    }
-    if (ok) {
-      const int valid = min(kPageTokens, n_hist - (p.first + i * NW) * kPageTokens);
-      if (valid == kPageTokens) int2_page<MT, true>(cur, valid, qo, st, wl);
-      else int2_page<MT, false>(cur, valid, qo, st, wl);
-    }
-  }
+  const int full_pages = n_hist / kPageTokens;   // global pages [0, full_pages) hold 64 tokens
+  const int nfull = min(p.npg, max(0, (full_pages - p.first + NW - 1) / NW));
+  int i = 0;
+  for (; i < nfull; ++i) pipe_step<MT, NW, PF, true>(p, pv, i, n_hist, qo, st, wl, lane);
+  for (; i < p.npg; ++i) pipe_step<MT, NW, PF, false>(p, pv, i, n_hist, qo, st, wl, lane);
 }
 
 template <int MT>
@@ -980,7 +1029,7 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   PagePipe<NW, PF> pipe;
   pipe_init(pipe, pv, b, kv, pg0, pg1, sm.pbuf[wave], wave, lane);
   query_prep<MT, GH>(a, b, kv, sm.q, nullptr, [&] {
-    bt_settle(pipe.bt, tk, tv);
+    bt_settle(pipe, tk, tv);
     if (wave >= 4) pipe_prologue(pipe, pv, lane);
   });
   const MetaSteps ms = meta_steps(tk, tv);
@@ -1483,7 +1532,7 @@ decode_flat_kernel(DecArgs a) {
     sg.last_blk = __builtin_amdgcn_readfirstlane(sg.last_blk);
     const int bh = sg.b * Hkv + sg.kv;
     pipe_init(pipe, pv, sg.b, sg.kv, sg.p0, sg.p1, sm.s.pbuf[wave], wave, lane);
-    bt_settle(pipe.bt);
+    bt_settle(pipe);
     pipe_prologue(pipe, pv, lane);
     if (si % kFlatPrep == 0) {
       int bb[kFlatPrep], kk[kFlatPrep];
@@ -1534,15 +1583,15 @@ decode_flat_kernel(DecArgs a) {
 }  // namespace
 
 namespace {
-int target_blocks() {
-  // scan workgroups the grid aims for (one per CU); OSCAR_DECODE_BLOCKS
-  // overrides it (tuning only)
+int target_blocks(int blocks) {
+  // scan workgroups the grid aims for: the caller's choice, else one per CU
+  // (OSCAR_DECODE_BLOCKS overrides the default; tuning only)
   static int v = [] {
     const char *e = getenv("OSCAR_DECODE_BLOCKS");
     const int x = e ? atoi(e) : 0;
     return x > 0 ? x : 256;
   }();
-  return v;
+  return blocks > 0 ? blocks : v;
 }
 int mt_of(int G) { return (G + 3) / 4; }
 int gh_of(int G) { return 4 * mt_of(G); }
@@ -1552,7 +1601,8 @@ bool is_mfma(int variant) { return variant != 1; }
 int nw_of(int G, int variant) { return !is_mfma(variant) ? 4 : (mt_of(G) == 1 ? 12 : 8); }
 }  // namespace
 
-DecodePlan make_decode_plan(int batch, int hkv, int hq, int max_pages, int sink, int recent, int variant) {
+DecodePlan make_decode_plan(int batch, int hkv, int hq, int max_pages, int sink, int recent, int variant,
+                            int blocks) {
   DecodePlan p{};
   const int G = hq / hkv;
   const int MT = mt_of(G), GH = gh_of(G), NW = nw_of(G, variant);
@@ -1560,7 +1610,7 @@ DecodePlan make_decode_plan(int batch, int hkv, int hq, int max_pages, int sink,
   p.n_chunks = (sink + recent) / kTileTokens;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   // balanced path: one M-tile of heads on the MFMA scan, bounded segments
-  const long long NB = target_blocks();
+  const long long NB = target_blocks(blocks);
   const long long units_max = (long long)bh * (p.n_chunks + max(max_pages, 0));
   const long long seg_bound = (units_max / NB + 1 + p.n_chunks - 1) / p.n_chunks + 2;
   p.flat = kBalancedScan && variant == 0 && MT == 1 && batch <= kFlatMaxBatch && seg_bound <= kFlatMaxSeg &&
@@ -1580,7 +1630,7 @@ DecodePlan make_decode_plan(int batch, int hkv, int hq, int max_pages, int sink,
     p.total = off;
     return p;
   }
-  int S = (target_blocks() + bh - 1) / bh;
+  int S = (target_blocks(blocks) + bh - 1) / bh;
   const int max_by_pages = max_pages > 0 ? (max_pages + NW - 1) / NW : 1;   // >= 1 page per wave
   S = S < 1 ? 1 : S;
   S = S > max_by_pages ? max_by_pages : S;

@@ -123,8 +123,9 @@ struct DecodePlan {
   size_t total;
 };
 
+// blocks: scan workgroups the grid aims for (0 = the default, one per CU).
 DecodePlan make_decode_plan(int batch, int hkv, int hq, int max_pages, int sink, int recent,
-                            int variant);
+                            int variant, int blocks);
 
 // Launchers (return hipError_t of the launches).
 hipError_t launch_append(const PoolView &pv, const RotView &rv, const uint16_t *k_new,

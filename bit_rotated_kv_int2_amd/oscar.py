@@ -28,7 +28,7 @@ PAGE_KCODES, PAGE_VCODES, PAGE_KMETA, PAGE_VMETA = 0, 2048, 4096, 4352
 EXPORTED = [
     "oscar_calibrate_rotation", "oscar_quantize_append", "oscar_decode_attention",
     "oscar_decode_workspace_size", "oscar_bf16_decode_attention",
-    "oscar_bf16_decode_workspace_size", "oscar_set_decode_variant", "oscar_last_error",
+    "oscar_bf16_decode_workspace_size", "oscar_set_decode_variant", "oscar_set_decode_blocks", "oscar_last_error",
     "oscar_version", "oscar_set_history_timing_events",
 ]
 
@@ -100,6 +100,8 @@ def lib():
     L.oscar_bf16_decode_workspace_size.restype = sz
     L.oscar_set_decode_variant.argtypes = [i32]
     L.oscar_set_decode_variant.restype = i32
+    L.oscar_set_decode_blocks.argtypes = [i32]
+    L.oscar_set_decode_blocks.restype = i32
     L.oscar_last_error.argtypes = []
     L.oscar_last_error.restype = ctypes.c_char_p
     L.oscar_version.argtypes = []
@@ -135,6 +137,11 @@ def _stream_ptr(stream) -> Optional[int]:
 
 def set_decode_variant(variant: int) -> None:
     _check(lib().oscar_set_decode_variant(int(variant)))
+
+
+def set_decode_blocks(blocks: int) -> None:
+    """Scan workgroups the split grid aims for (0 = one per compute unit)."""
+    _check(lib().oscar_set_decode_blocks(int(blocks)))
 
 
 def version() -> int:

@@ -242,6 +242,17 @@ int32_t oscar_set_history_timing_events(void *start_event, void *stop_event);
  */
 int32_t oscar_set_decode_variant(int32_t variant);
 
+/*
+ * Number of history-scan workgroups the split grid aims for (process-wide):
+ * each (sequence, KV head) gets ceil(blocks / (batch * Hkv)) splits, capped
+ * so every wave keeps at least one page.  0 (the default) aims for one
+ * workgroup per compute unit (256).  Like the variant, it sets the workspace
+ * size, so query oscar_decode_workspace_size() after changing it.  Results
+ * differ only in floating-point summation order.  OSCAR_EINVAL outside
+ * [0, 65536].
+ */
+int32_t oscar_set_decode_blocks(int32_t blocks);
+
 /* Message of the last error on the calling thread ("" if none). */
 const char *oscar_last_error(void);
 

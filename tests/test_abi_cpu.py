@@ -94,6 +94,14 @@ def test_validation_errors():
     assert L.oscar_set_decode_variant(-1) == O.OSCAR_EINVAL
     for v in (2, 1, 0):
         assert L.oscar_set_decode_variant(v) == 0
+    assert L.oscar_set_decode_blocks(-1) == O.OSCAR_EINVAL
+    assert L.oscar_set_decode_blocks(65537) == O.OSCAR_EINVAL
+    p8 = ctypes.byref(O.make_params(8, 32))
+    default_ws = L.oscar_decode_workspace_size(p8, 1, 1600)
+    assert L.oscar_set_decode_blocks(8) == 0           # one split per (sequence, KV head): fewer partials
+    assert 0 < L.oscar_decode_workspace_size(p8, 1, 1600) < default_ws
+    assert L.oscar_set_decode_blocks(0) == 0
+    assert L.oscar_decode_workspace_size(p8, 1, 1600) == default_ws
     assert L.oscar_decode_workspace_size(ctypes.byref(O.make_params(8, 30)), 1, 10) == 0
     with pytest.raises(O.OscarError):
         O.calibrate_rotation(O.make_params(1, 1), np.zeros((1, 8, 128), np.float32),

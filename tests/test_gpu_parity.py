@@ -272,6 +272,29 @@ def test_shared_prefix_gqa12():
             assert decode_check(out[b], ref) <= TOL, (b, variant)
 
 
+def test_single_workgroup_long_history(tiny):
+    """One scan workgroup over a 150K-token history on scattered pages: each of
+    its waves takes more than 192 pages, so the block-table entries it holds
+    in registers run out and are reloaded in the middle of the scan."""
+    wl, cals, rot, params, _, _, q = tiny
+    L = 150_000
+    kb, vb = _tokens(wl, 1, L)
+    n_pages = (L - 64 - 256 + 63) // 64
+    assert n_pages // 12 > 192
+    perm = np.random.default_rng(7).permutation(n_pages).astype(np.int32)
+    pool = O.KVPool(params, 1, n_pages, perm[None])
+    append_sequence(params, rot, pool, 0, kb, vb)
+    O.set_decode_blocks(1)
+    try:
+        out = _decode_gpu(params, rot, pool, q, 2)
+    finally:
+        O.set_decode_blocks(0)
+    ref, _ = _oracle_decode(wl, cals, kb, vb, q[0])
+    err = decode_check(out[0], ref)
+    print(f"150K tokens, one workgroup: err/||o|| = {err:.3e}")
+    assert err <= TOL
+
+
 def test_bad_block_table_entry_flagged(tiny):
     wl, cals, rot, params, kb, vb, q = tiny
     pool = _fresh_pool(params, 59)
