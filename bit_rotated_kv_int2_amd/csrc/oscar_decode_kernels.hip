@@ -424,17 +424,24 @@ __device__ __forceinline__ void int2_page(const PageRegs &r, int valid, const Qu
   const uint32_t kmw[4] = {r.km.x, r.km.y, r.km.z, r.km.w};
   const uint32_t vmw[4] = {r.vm.x, r.vm.y, r.vm.z, r.vm.w};
   float lg[MT][4];
+  // all products first, so that no logit waits on the product just issued
+  v4i CK[4][MT];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
     const v4i B0 = unpack16(r.kc[tt].x);
     const v4i B1 = unpack16(r.kc[tt].y);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      CK[tt][mt] = mfma_i8(qo.A[mt][1], B1, mfma_i8(qo.A[mt][0], B0, v4i{0, 0, 0, 0}));
+  }
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
     const float s0 = ubyte_f(kmw[tt], 0), z0 = ubyte_f(kmw[tt], 1);
     const float s1 = ubyte_f(kmw[tt], 2), z1 = ubyte_f(kmw[tt], 3);
     const bool ok = FULL || (16 * tt + n) < valid;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      v4i C = mfma_i8(qo.A[mt][0], B0, v4i{0, 0, 0, 0});
-      C = mfma_i8(qo.A[mt][1], B1, C);
+      const v4i C = CK[tt][mt];
       const float x0 = (float)(C[0] * 256 + C[1]);
       const float x1 = (float)(C[2] * 256 + C[3]);
       const float v = fmaf(fmaf(s0, x0, s1 * x1), qo.qa[mt], fmaf(z0, qo.qb0[mt], fmaf(z1, qo.qb1[mt], qo.qc[mt])));
@@ -502,19 +509,24 @@ __device__ __forceinline__ void int2_page(const PageRegs &r, int valid, const Qu
     Aw[mt][1] = wl[(mt * 2 + 1) * 64 + lane];
   }
   wave_lds_sync();
+  // all products first, so that no value combine waits on the product just issued
+  v4i C[8][MT];
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
     const v4i Bv = unpack16_v(r.vc[nt]);
-    const int g = nt >> 2;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) C[nt][mt] = mfma_i8(Aw[mt][nt >> 2], Bv, v4i{0, 0, 0, 0});
+  }
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const v4i C = mfma_i8(Aw[mt][g], Bv, v4i{0, 0, 0, 0});
       // sum over 64 tokens of u * code <= 8355000 * 3 * 64 < 2^31: exact in int32
       // two shift-adds; the empty asm (on a VALU result) keeps the compiler
       // from re-associating them into two shifts and a three-way add
-      int t = (int)(((unsigned)C[0] << 8) + (unsigned)C[1]);
-      asm volatile("" : "+v"(t));
-      const int val = (int)(((unsigned)t << 8) + (unsigned)C[2]);
+      int t = (int)(((unsigned)C[nt][mt][0] << 8) + (unsigned)C[nt][mt][1]);
+      asm("" : "+v"(t));
+      const int val = (int)(((unsigned)t << 8) + (unsigned)C[nt][mt][2]);
       st.facc[mt][nt] = fmaf((float)val, pscale[mt], st.facc[mt][nt]);
     }
   }
