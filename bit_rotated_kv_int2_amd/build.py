@@ -24,6 +24,7 @@ SOURCES = [
     "oscar_write.hip",
     "oscar_decode_kernels.hip",
     "oscar_bf16.hip",
+    "oscar_probe.hip",
 ]
 
 # Packed-FP32 VALU forms are disabled for all device code.

@@ -124,6 +124,15 @@ int32_t oscar_set_decode_blocks(int32_t blocks) {
   return ok();
 }
 
+int32_t oscar_stream_read_probe(const void *buf, size_t bytes, uint32_t *sink, int32_t grid, void *stream) {
+  if (!buf || !sink) return fail(OSCAR_EINVAL, "buf/sink is NULL");
+  if (misaligned(buf)) return fail(OSCAR_EINVAL, "buf must be 16-byte aligned");
+  if (grid < 1 || grid > 65536) return fail(OSCAR_EINVAL, "grid must be in [1, 65536]");
+  hipError_t e = oscar::launch_stream_read(buf, bytes, sink, grid, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(OSCAR_EHIP, "probe launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int32_t oscar_calibrate_rotation(const oscar_params *p, const float *q_cal, int64_t n_q,
                                  const float *k_cal, const float *v_cal, int64_t n_kv,
                                  double quantile_k, double quantile_v, float *U_K, float *U_V,

@@ -127,6 +127,10 @@ struct DecodePlan {
 DecodePlan make_decode_plan(int batch, int hkv, int hq, int max_pages, int sink, int recent,
                             int variant, int blocks);
 
+// Streaming-read probe: threads per workgroup and launcher.
+int probe_threads();
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, int grid, hipStream_t s);
+
 // Launchers (return hipError_t of the launches).
 hipError_t launch_append(const PoolView &pv, const RotView &rv, const uint16_t *k_new,
                          const uint16_t *v_new, int n_new, hipStream_t s);

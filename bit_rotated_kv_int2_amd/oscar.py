@@ -29,7 +29,7 @@ EXPORTED = [
     "oscar_calibrate_rotation", "oscar_quantize_append", "oscar_decode_attention",
     "oscar_decode_workspace_size", "oscar_bf16_decode_attention",
     "oscar_bf16_decode_workspace_size", "oscar_set_decode_variant", "oscar_set_decode_blocks", "oscar_last_error",
-    "oscar_version", "oscar_set_history_timing_events",
+    "oscar_version", "oscar_set_history_timing_events", "oscar_stream_read_probe",
 ]
 
 
@@ -102,6 +102,8 @@ def lib():
     L.oscar_set_decode_variant.restype = i32
     L.oscar_set_decode_blocks.argtypes = [i32]
     L.oscar_set_decode_blocks.restype = i32
+    L.oscar_stream_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, i32, ctypes.c_void_p]
+    L.oscar_stream_read_probe.restype = i32
     L.oscar_last_error.argtypes = []
     L.oscar_last_error.restype = ctypes.c_char_p
     L.oscar_version.argtypes = []
@@ -142,6 +144,13 @@ def set_decode_variant(variant: int) -> None:
 def set_decode_blocks(blocks: int) -> None:
     """Scan workgroups the split grid aims for (0 = one per compute unit)."""
     _check(lib().oscar_set_decode_blocks(int(blocks)))
+
+
+def stream_read_probe(buf, sink, grid: int, stream=None) -> None:
+    """Plain streaming read of the device tensor buf (measurement aid); sink: int32 [grid * 512]."""
+    assert buf.is_contiguous() and sink.is_contiguous() and sink.numel() >= grid * 512
+    _check(lib().oscar_stream_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), int(grid),
+                                         _stream_ptr(stream)))
 
 
 def version() -> int:

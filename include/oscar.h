@@ -253,6 +253,18 @@ int32_t oscar_set_decode_variant(int32_t variant);
  */
 int32_t oscar_set_decode_blocks(int32_t blocks);
 
+/*
+ * Measurement aid, not part of the attention path: one plain streaming read
+ * of `bytes` bytes of the device buffer `buf` (16-byte aligned; a tail
+ * shorter than 32 KB may be skipped) by `grid` workgroups of 512 threads,
+ * each thread reading four 16-byte words per step.  sink: device uint32
+ * [grid * 512], overwritten with per-thread checksums.  It gives the
+ * practical HBM read rate the history scan is compared against.  Enqueued
+ * on `stream`; OSCAR_EINVAL for NULL pointers, misalignment or grid outside
+ * [1, 65536].
+ */
+int32_t oscar_stream_read_probe(const void *buf, size_t bytes, uint32_t *sink, int32_t grid, void *stream);
+
 /* Message of the last error on the calling thread ("" if none). */
 const char *oscar_last_error(void);
 

@@ -94,6 +94,9 @@ def test_validation_errors():
     assert L.oscar_set_decode_variant(-1) == O.OSCAR_EINVAL
     for v in (2, 1, 0):
         assert L.oscar_set_decode_variant(v) == 0
+    assert L.oscar_stream_read_probe(None, 1024, 0x1000, 1, None) == O.OSCAR_EINVAL
+    assert L.oscar_stream_read_probe(0x1008, 1024, 0x1000, 1, None) == O.OSCAR_EINVAL
+    assert L.oscar_stream_read_probe(0x1000, 1024, 0x2000, 0, None) == O.OSCAR_EINVAL
     assert L.oscar_set_decode_blocks(-1) == O.OSCAR_EINVAL
     assert L.oscar_set_decode_blocks(65537) == O.OSCAR_EINVAL
     p8 = ctypes.byref(O.make_params(8, 32))

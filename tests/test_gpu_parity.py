@@ -377,3 +377,19 @@ def test_quantiser_variants_parity(tiny, kind):
     print(f"variant {kind}: max err / norm = {err:.3e}")
     assert err <= TOL
     assert int(pool.error_flags.cpu()[0]) == 0
+
+
+def test_stream_read_probe_reads_every_word():
+    """The streaming-read probe covers the whole buffer: the xor of its
+    per-thread checksums is the xor of every 32-bit word (16 MiB = two full
+    grid strides of 256 x 512 threads x 4 words of 16 bytes)."""
+    torch = _torch()
+    g = torch.Generator().manual_seed(3)
+    host = torch.randint(-2**31, 2**31 - 1, (4 << 20,), dtype=torch.int64, generator=g).to(torch.int32)
+    buf = host.cuda()
+    sink = torch.empty(256 * 512, dtype=torch.int32, device="cuda")
+    O.stream_read_probe(buf, sink, 256)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == want
