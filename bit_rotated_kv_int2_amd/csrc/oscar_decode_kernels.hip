@@ -1048,19 +1048,24 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   QueryOps<MT> qo;
   load_query_ops<MT, GH>(sm.q.aq, sm.q.qc, G, pv.sm_scale * kLog2e, ms, lane, qo);
   __syncthreads();   // the query scratch is reused by the weights and the BF16 tiles
-  // BF16 tiles: this workgroup takes tiles u = split + S k.  Tiles k < 4 run
-  // first on waves 3..0 (the preparing waves, whose history pages are the
-  // last to arrive, and which finish their pages before the others); the
-  // rest run after the history pages, from the last wave down.  An early
-  // tile goes before the wave's page copies: its loads would otherwise
-  // complete behind them.  (The tile scratch overlaps the query scratch,
-  // which is dead after the barrier above.)
+  // BF16 tiles: this workgroup takes tiles u = split + S k.  Short scans
+  // (under 16 pages per wave): tiles k < 4 run first on waves 3..0 (the
+  // preparing waves, whose history pages are the last to arrive, and which
+  // finish their pages before the others); the rest run after the history
+  // pages, from the last wave down.  An early tile goes before the wave's
+  // page copies: its loads would otherwise complete behind them.  Long
+  // scans: every tile runs after the pages on waves 0..3, which finish their
+  // pages well before the younger waves of their SIMDs (the oldest wave has
+  // issue priority), so the tiles hide behind the remaining page stream.
+  // (The tile scratch overlaps the query scratch, which is dead after the
+  // barrier above.)
   const int S = a.n_splits;
   float *parts = a.part + (size_t)bh * (S + a.n_chunks) * G * kPartStride;
-  constexpr int kEarlyTiles = 4;
-  if (wave < kEarlyTiles) {
-    const int u = split + S * (kEarlyTiles - 1 - wave);
-    if (u < a.n_chunks)
+  const bool long_scan = pg1 - pg0 >= 16 * NW;
+  const int early = long_scan ? 0 : 4;
+  if (wave < 4) {
+    const int u = split + S * (early - 1 - wave);
+    if (wave < early && u < a.n_chunks)
       bf16_tile_partial<GH>(a, b, kv, u, sm.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
     // the preparing waves start their copies only now: issuing them inside
     // the preparation would stall those waves (the CU accepts copy requests
@@ -1075,9 +1080,11 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   for (int i = 0; i < MT * 2; ++i) wl[i * 64 + lane] = v4i{0, 0, 0, 0};
   pipe_scan<MT, NW, PF>(pipe, pv, n_hist, qo, st, wl, lane);
   if (pipe.bad && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
-  for (int u = split + S * kEarlyTiles; u < a.n_chunks; u += S)
-    if (NW - 1 - (u / S - kEarlyTiles) % NW == wave)
+  for (int u = split + S * early; u < a.n_chunks; u += S) {
+    const int k = u / S - early;
+    if ((long_scan ? k % 4 : NW - 1 - k % NW) == wave)
       bf16_tile_partial<GH>(a, b, kv, u, sm.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
+  }
   flush_partial<MT, GH, NW>(sm, st, G, ms, dst);
 }
 
