@@ -955,6 +955,62 @@ __device__ __forceinline__ void pipe_scan(PagePipe<NW, PF> &p, const PoolView &p
   for (; i < p.npg; ++i) pipe_step<MT, NW, PF, false>(p, pv, i, n_hist, qo, st, wl, lane);
 }
 
+// Dynamic page order within a workgroup (long scans, one M-tile of heads):
+// the block-table entries of the workgroup's pages sit in LDS and each wave
+// takes the next page index from a shared counter whenever it frees a
+// buffer, so the waves of a SIMD (which otherwise finish in age order, the
+// oldest having issue priority) all run until the pages are gone.  The BF16
+// tiles are handed out the same way afterwards.
+constexpr int kDynMaxPages = 2048;
+struct DynPages {
+  int next_page, next_tile;
+  int bt[kDynMaxPages];   // block-table entries of pages pg0 + i
+};
+
+// Consume pages in the order the counter hands them out.  The wave starts
+// with the prologue's two copies (pages wave and wave + NW, both full) and
+// takes indices from dp->next_page (initialised to NW * PF) until they reach
+// nfull, the workgroup's full pages.  Returns true on the wave that drew
+// index nfull: it owns the workgroup's partly filled last page, if any.
+template <int MT, int NW, int PF>
+__device__ __forceinline__ bool pipe_scan_dyn(PagePipe<NW, PF> &p, const PoolView &pv, int nfull, DynPages *dp,
+                                              const QueryOps<MT> &qo, HistState<MT> &st, v4i *wl, int lane) {
+  static_assert(PF == 2, "the dynamic order is written for two page buffers");
+  const int n = lane & 15, q = lane >> 4;
+  bool own_tail = false;
+  bool have_cur = true, have_nxt = true;
+  int c = 0;   // buffer of the page consumed next; the other holds the one after it
+  while (have_cur) {
+    // copies issued after this page that may still be outstanding
+    wait_pages(__builtin_popcount(p.inflight >> 1));
+    PageRegs cur;
+    load_page(cur, (const uint8_t *)p.bufs[c], n, q);
+    int j = 0;
+    if (lane == 0) j = atomicAdd(&dp->next_page, 1);
+    j = __builtin_amdgcn_readfirstlane(j);
+    wait_lds_reads();   // buffer c is read: it may be refilled
+    const bool ok = p.inflight & 1u;
+    p.inflight >>= 1;
+    own_tail = own_tail || j == nfull;
+    const bool have_new = j < nfull;
+    if (have_new) {
+      const int ph = __builtin_amdgcn_readfirstlane(dp->bt[j]);
+      if (ph >= 0 && ph < pv.n_pages) {
+        dma_page((uint64_t)(uintptr_t)(p.pbase + (size_t)ph * p.pstride), p.lds0 + (uint32_t)c * kPageBytes,
+                 16u * lane);
+        p.inflight |= 1u << (PF - 1);
+      } else {
+        p.bad = true;
+      }
+    }
+    if (ok) int2_page<MT, true>(cur, kPageTokens, qo, st, wl);
+    have_cur = have_nxt;
+    have_nxt = have_new;
+    c ^= 1;
+  }
+  return own_tail;
+}
+
 template <int MT>
 __device__ __forceinline__ void hist_reset(HistState<MT> &st) {
 #pragma unroll
@@ -1015,9 +1071,9 @@ __device__ void flush_partial(ScanSmem<MT, GH, NW, true> &sm, HistState<MT> &st,
   write_split_partial<MT, GH, NW, true>(sm, G, dst, true);
 }
 
-template <int MT, int GH, int NW>
+template <int MT, int GH, int NW, bool DYN>
 __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float *dst,
-                              ScanSmem<MT, GH, NW, true> &sm) {
+                              ScanSmem<MT, GH, NW, true> &sm, DynPages *dp) {
   constexpr int PF = ScanSmem<MT, GH, NW, true>::PF;
   const PoolView &pv = a.pv;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1040,8 +1096,37 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   float tk = a.rv.tau_K[kv], tv = a.rv.tau_V[kv];
   PagePipe<NW, PF> pipe;
   pipe_init(pipe, pv, b, kv, pg0, pg1, sm.pbuf[wave], wave, lane);
+  // long scans (16 pages per wave and more) take the BF16 tiles after the
+  // pages and, where the workgroup's block-table entries fit in LDS, hand
+  // pages and tiles out dynamically
+  const int npg_wg = pg1 - pg0;
+  const bool long_scan = npg_wg >= 16 * NW;
+  const bool dyn = DYN && long_scan && npg_wg <= kDynMaxPages;
+  // pages [pg0, pg0 + nfull) hold 64 tokens (only the history's last page can hold fewer)
+  const int nfull = max(0, min(pg1, n_hist / kPageTokens) - pg0);
+  constexpr int kDynPer = (kDynMaxPages + 64 * NW - 1) / (64 * NW);
+  int dbt[kDynPer];
+  if (dyn) {
+    const int32_t *row = pv.block_table + (size_t)b * pv.max_pages + pg0;
+#pragma unroll
+    for (int r = 0; r < kDynPer; ++r) {
+      const int i = tid + r * 64 * NW;
+      dbt[r] = i < npg_wg ? row[i] : -1;
+    }
+  }
   query_prep<MT, GH>(a, b, kv, sm.q, nullptr, [&] {
     bt_settle(pipe, tk, tv);
+    if (dyn) {   // published by the barrier that follows in the preparation
+#pragma unroll
+      for (int r = 0; r < kDynPer; ++r) {
+        const int i = tid + r * 64 * NW;
+        if (i < npg_wg) dp->bt[i] = dbt[r];
+      }
+      if (tid == 0) {
+        dp->next_page = NW * PF;
+        dp->next_tile = 0;
+      }
+    }
     if (wave >= 4) pipe_prologue(pipe, pv, lane);
   });
   const MetaSteps ms = meta_steps(tk, tv);
@@ -1061,7 +1146,6 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   // barrier above.)
   const int S = a.n_splits;
   float *parts = a.part + (size_t)bh * (S + a.n_chunks) * G * kPartStride;
-  const bool long_scan = pg1 - pg0 >= 16 * NW;
   const int early = long_scan ? 0 : 4;
   if (wave < 4) {
     const int u = split + S * (early - 1 - wave);
@@ -1078,12 +1162,43 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   // rows 4h + 3 of the weight operands stay zero; the rest is rewritten per page
 #pragma unroll
   for (int i = 0; i < MT * 2; ++i) wl[i * 64 + lane] = v4i{0, 0, 0, 0};
-  pipe_scan<MT, NW, PF>(pipe, pv, n_hist, qo, st, wl, lane);
+  if (dyn) {
+    if (pipe_scan_dyn<MT, NW, PF>(pipe, pv, nfull, dp, qo, st, wl, lane) && nfull < npg_wg) {
+      // the partly filled last page, on the wave that drew its index (its
+      // buffers are idle: every copy it issued has been consumed)
+      const int ph = __builtin_amdgcn_readfirstlane(dp->bt[nfull]);
+      if (ph >= 0 && ph < pv.n_pages) {
+        dma_page((uint64_t)(uintptr_t)(pipe.pbase + (size_t)ph * pipe.pstride), pipe.lds0, 16u * lane);
+        wait_pages(0);
+        PageRegs cur;
+        load_page(cur, (const uint8_t *)pipe.bufs[0], lane & 15, lane >> 4);
+        wait_lds_reads();
+        int2_page<MT, false>(cur, n_hist - (pg0 + nfull) * kPageTokens, qo, st, wl);
+      } else {
+        pipe.bad = true;
+      }
+    }
+  } else {
+    pipe_scan<MT, NW, PF>(pipe, pv, n_hist, qo, st, wl, lane);
+  }
   if (pipe.bad && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
-  for (int u = split + S * early; u < a.n_chunks; u += S) {
-    const int k = u / S - early;
-    if ((long_scan ? k % 4 : NW - 1 - k % NW) == wave)
+  if (dyn) {
+    // this workgroup's tiles are u = split + S k, k < n_tiles
+    const int n_tiles = split < a.n_chunks ? (a.n_chunks - 1 - split) / S + 1 : 0;
+    for (;;) {
+      int k = 0;
+      if (lane == 0) k = atomicAdd(&dp->next_tile, 1);
+      k = __builtin_amdgcn_readfirstlane(k);
+      if (k >= n_tiles) break;
+      const int u = split + S * k;
       bf16_tile_partial<GH>(a, b, kv, u, sm.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
+    }
+  } else {
+    for (int u = split + S * early; u < a.n_chunks; u += S) {
+      const int k = u / S - early;
+      if ((long_scan ? k % 4 : NW - 1 - k % NW) == wave)
+        bf16_tile_partial<GH>(a, b, kv, u, sm.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
+    }
   }
   flush_partial<MT, GH, NW>(sm, st, G, ms, dst);
 }
@@ -1384,7 +1499,12 @@ decode_scan_kernel(DecArgs a) {
     }
   }
   float *dst = parts + (size_t)split * G * kPartStride;
-  if constexpr (MFMA) run_scan_mfma<MT, GH, NW>(a, b, kv, split, dst, sm.s);
+  if constexpr (MFMA && MT == 1) {
+    __shared__ DynPages dp;
+    run_scan_mfma<MT, GH, NW, true>(a, b, kv, split, dst, sm.s, &dp);
+  } else if constexpr (MFMA) {
+    run_scan_mfma<MT, GH, NW, false>(a, b, kv, split, dst, sm.s, nullptr);
+  }
   else run_scan_valu<MT, GH, NW>(a, b, kv, split, dst, sm.s);
   __shared__ int last_flag;
   if (!arrive_last(&a.counters[bh], S, &last_flag)) return;

@@ -295,6 +295,32 @@ def test_single_workgroup_long_history(tiny):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("blocks", [1, 2, 3])
+def test_dynamic_page_order(tiny, blocks):
+    """Workgroups of 192 and more pages hand their pages and BF16 tiles out to
+    the waves dynamically: one to three workgroups over a 40037-token history
+    (621 pages, the last one partly filled), so that the workgroups of the
+    later splits also take tiles u = split + S k and the last split owns the
+    partial page."""
+    wl, cals, rot, params, _, _, q = tiny
+    L = 40037
+    kb, vb = _tokens(wl, 2, L)
+    n_pages = (L - 64 - 256 + 63) // 64
+    assert n_pages // blocks >= 16 * 12 and (L - 320) % 64
+    perm = np.random.default_rng(11).permutation(n_pages).astype(np.int32)
+    pool = O.KVPool(params, 1, n_pages, perm[None])
+    append_sequence(params, rot, pool, 0, kb, vb)
+    O.set_decode_blocks(blocks)
+    try:
+        out = _decode_gpu(params, rot, pool, q, 2)
+    finally:
+        O.set_decode_blocks(0)
+    ref, _ = _oracle_decode(wl, cals, kb, vb, q[0])
+    err = decode_check(out[0], ref)
+    print(f"40037 tokens, {blocks} workgroup(s): err/||o|| = {err:.3e}")
+    assert err <= TOL
+
+
 def test_bad_block_table_entry_flagged(tiny):
     wl, cals, rot, params, kb, vb, q = tiny
     pool = _fresh_pool(params, 59)
