@@ -970,8 +970,11 @@ struct DynPages {
 // Consume pages in the order the counter hands them out.  The wave starts
 // with the prologue's two copies (pages wave and wave + NW, both full) and
 // takes indices from dp->next_page (initialised to NW * PF) until they reach
-// nfull, the workgroup's full pages.  Returns true on the wave that drew
-// index nfull: it owns the workgroup's partly filled last page, if any.
+// nfull, the workgroup's full pages.  Each index is drawn one page ahead, so
+// the counter's round trip overlaps the page's compute, and its
+// block-table entry is read together with the page.  Returns true on the
+// wave that drew index nfull: it owns the workgroup's partly filled last
+// page, if any.
 template <int MT, int NW, int PF>
 __device__ __forceinline__ bool pipe_scan_dyn(PagePipe<NW, PF> &p, const PoolView &pv, int nfull, DynPages *dp,
                                               const QueryOps<MT> &qo, HistState<MT> &st, v4i *wl, int lane) {
@@ -980,21 +983,21 @@ __device__ __forceinline__ bool pipe_scan_dyn(PagePipe<NW, PF> &p, const PoolVie
   bool own_tail = false;
   bool have_cur = true, have_nxt = true;
   int c = 0;   // buffer of the page consumed next; the other holds the one after it
+  int jn = 0;  // the index drawn for the next refill
+  if (lane == 0) jn = atomicAdd(&dp->next_page, 1);
   while (have_cur) {
     // copies issued after this page that may still be outstanding
     wait_pages(__builtin_popcount(p.inflight >> 1));
     PageRegs cur;
     load_page(cur, (const uint8_t *)p.bufs[c], n, q);
-    int j = 0;
-    if (lane == 0) j = atomicAdd(&dp->next_page, 1);
-    j = __builtin_amdgcn_readfirstlane(j);
+    const int j = __builtin_amdgcn_readfirstlane(jn);
+    const bool have_new = j < nfull;
+    const int ph = __builtin_amdgcn_readfirstlane(dp->bt[have_new ? j : 0]);
     wait_lds_reads();   // buffer c is read: it may be refilled
     const bool ok = p.inflight & 1u;
     p.inflight >>= 1;
     own_tail = own_tail || j == nfull;
-    const bool have_new = j < nfull;
     if (have_new) {
-      const int ph = __builtin_amdgcn_readfirstlane(dp->bt[j]);
       if (ph >= 0 && ph < pv.n_pages) {
         dma_page((uint64_t)(uintptr_t)(p.pbase + (size_t)ph * p.pstride), p.lds0 + (uint32_t)c * kPageBytes,
                  16u * lane);
@@ -1002,6 +1005,7 @@ __device__ __forceinline__ bool pipe_scan_dyn(PagePipe<NW, PF> &p, const PoolVie
       } else {
         p.bad = true;
       }
+      if (lane == 0) jn = atomicAdd(&dp->next_page, 1);
     }
     if (ok) int2_page<MT, true>(cur, kPageTokens, qo, st, wl);
     have_cur = have_nxt;
@@ -1503,6 +1507,8 @@ decode_scan_kernel(DecArgs a) {
     __shared__ DynPages dp;
     run_scan_mfma<MT, GH, NW, true>(a, b, kv, split, dst, sm.s, &dp);
   } else if constexpr (MFMA) {
+    // several M-tiles (8 waves, heavier pages): the static page order
+    // measured faster on the GQA-12 shared-prefix workload
     run_scan_mfma<MT, GH, NW, false>(a, b, kv, split, dst, sm.s, nullptr);
   }
   else run_scan_valu<MT, GH, NW>(a, b, kv, split, dst, sm.s);
