@@ -1100,12 +1100,14 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   float tk = a.rv.tau_K[kv], tv = a.rv.tau_V[kv];
   PagePipe<NW, PF> pipe;
   pipe_init(pipe, pv, b, kv, pg0, pg1, sm.pbuf[wave], wave, lane);
-  // long scans (16 pages per wave and more) take the BF16 tiles after the
-  // pages and, where the workgroup's block-table entries fit in LDS, hand
-  // pages and tiles out dynamically
+  // long scans (16 pages per wave and more) take every BF16 tile after the
+  // pages; where the workgroup has two rounds of prologue pages or more and
+  // its block-table entries fit in LDS, pages and the late tiles are handed
+  // out dynamically
   const int npg_wg = pg1 - pg0;
   const bool long_scan = npg_wg >= 16 * NW;
-  const bool dyn = DYN && long_scan && npg_wg <= kDynMaxPages;
+  const int early = long_scan ? 0 : 4;
+  const bool dyn = DYN && npg_wg >= 2 * NW * PF && npg_wg <= kDynMaxPages;
   // pages [pg0, pg0 + nfull) hold 64 tokens (only the history's last page can hold fewer)
   const int nfull = max(0, min(pg1, n_hist / kPageTokens) - pg0);
   constexpr int kDynPer = (kDynMaxPages + 64 * NW - 1) / (64 * NW);
@@ -1128,7 +1130,7 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
       }
       if (tid == 0) {
         dp->next_page = NW * PF;
-        dp->next_tile = 0;
+        dp->next_tile = early;   // tiles k < early run on waves 0..3 before their pages
       }
     }
     if (wave >= 4) pipe_prologue(pipe, pv, lane);
@@ -1150,7 +1152,6 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   // barrier above.)
   const int S = a.n_splits;
   float *parts = a.part + (size_t)bh * (S + a.n_chunks) * G * kPartStride;
-  const int early = long_scan ? 0 : 4;
   if (wave < 4) {
     const int u = split + S * (early - 1 - wave);
     if (wave < early && u < a.n_chunks)
@@ -1187,7 +1188,8 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   }
   if (pipe.bad && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
   if (dyn) {
-    // this workgroup's tiles are u = split + S k, k < n_tiles
+    // this workgroup's tiles are u = split + S k, k < n_tiles; the counter
+    // starts past the early ones
     const int n_tiles = split < a.n_chunks ? (a.n_chunks - 1 - split) / S + 1 : 0;
     for (;;) {
       int k = 0;

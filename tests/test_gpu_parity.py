@@ -295,18 +295,19 @@ def test_single_workgroup_long_history(tiny):
     assert err <= TOL
 
 
-@pytest.mark.parametrize("blocks", [1, 2, 3])
+@pytest.mark.parametrize("blocks", [1, 2, 3, 8])
 def test_dynamic_page_order(tiny, blocks):
-    """Workgroups of 192 and more pages hand their pages and BF16 tiles out to
-    the waves dynamically: one to three workgroups over a 40037-token history
-    (621 pages, the last one partly filled), so that the workgroups of the
-    later splits also take tiles u = split + S k and the last split owns the
-    partial page."""
+    """Workgroups of 48 and more pages hand their pages (and the BF16 tiles
+    not taken before the pages) out to the waves dynamically: one to eight
+    workgroups over a 40037-token history (621 pages, the last one partly
+    filled), so that the workgroups of the later splits also take tiles
+    u = split + S k and the last split owns the partial page.  With 8
+    workgroups (78 pages each) waves 0..3 take four tiles first."""
     wl, cals, rot, params, _, _, q = tiny
     L = 40037
     kb, vb = _tokens(wl, 2, L)
     n_pages = (L - 64 - 256 + 63) // 64
-    assert n_pages // blocks >= 16 * 12 and (L - 320) % 64
+    assert n_pages // blocks >= 2 * 12 * 2 and (L - 320) % 64
     perm = np.random.default_rng(11).permutation(n_pages).astype(np.int32)
     pool = O.KVPool(params, 1, n_pages, perm[None])
     append_sequence(params, rot, pool, 0, kb, vb)
