@@ -322,6 +322,30 @@ def test_dynamic_page_order(tiny, blocks):
     assert err <= TOL
 
 
+def test_dynamic_page_order_bad_entries_flagged(tiny):
+    """Out-of-range block-table entries on the dynamic page order (one
+    workgroup over 621 pages): a prologue page, a page handed out by the
+    counter and the partly filled last page are skipped and flagged, and the
+    output stays finite."""
+    wl, cals, rot, params, _, _, q = tiny
+    L = 40037
+    kb, vb = _tokens(wl, 2, L)
+    n_pages = (L - 64 - 256 + 63) // 64
+    pool = O.KVPool(params, 1, n_pages, np.arange(n_pages, dtype=np.int32)[None])
+    append_sequence(params, rot, pool, 0, kb, vb)
+    bt = pool.block_table.clone()
+    for i in (5, 300, n_pages - 1):
+        pool.block_table[0, i] = 1 << 20
+    O.set_decode_blocks(1)
+    try:
+        out = _decode_gpu(params, rot, pool, q, 2)
+    finally:
+        O.set_decode_blocks(0)
+        pool.block_table.copy_(bt)
+    assert np.all(np.isfinite(out))
+    assert int(pool.error_flags.cpu()[0]) & O.DEVERR_PAGE
+
+
 def test_bad_block_table_entry_flagged(tiny):
     wl, cals, rot, params, kb, vb, q = tiny
     pool = _fresh_pool(params, 59)
