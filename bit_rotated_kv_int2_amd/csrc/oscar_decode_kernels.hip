@@ -1515,7 +1515,14 @@ decode_scan_kernel(DecArgs a) {
   }
   else run_scan_valu<MT, GH, NW>(a, b, kv, split, dst, sm.s);
   __shared__ int last_flag;
-  if (!arrive_last(&a.counters[bh], S, &last_flag)) return;
+  if (S == 1) {
+    // the only workgroup of its (sequence, KV head): no counter round trip,
+    // only its own partial stores completed before any thread reads them
+    stores_complete();
+    __syncthreads();
+  } else if (!arrive_last(&a.counters[bh], S, &last_flag)) {
+    return;
+  }
   merge_item<GH, 64 * NW>(a, b, kv, parts, S, parts + (size_t)S * G * kPartStride, a.n_chunks, sm.g);
 }
 
