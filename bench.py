@@ -12,8 +12,8 @@ All inputs are seeded synthetic data (bit_rotated_kv_int2_amd.synth) already
 resident in HBM when timing starts.  Per-layer caches are distinct, so every
 layer streams from HBM rather than the 256 MB last-level cache.
 
-Prints one JSON line.  ``--gpus N`` with N > 1 is refused: this build runs on
-one GPU.
+Prints one JSON line.  ``--gpus N`` with N > 1 is refused: the benchmark
+measures one GPU.
 """
 from __future__ import annotations
 
@@ -457,7 +457,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "multi-GPU sharding is design-only in this build.", file=sys.stderr)
+              "sharding over several GPUs is not implemented.", file=sys.stderr)
         sys.exit(2)
 
     import torch
