@@ -177,6 +177,42 @@ def test_batch_scattered_ragged():
     assert int(pool.error_flags.cpu()[0]) == 0
 
 
+def test_ragged_batch_mixed_page_orders():
+    """One launch whose workgroups take different page orders: four
+    sequences of ragged length (3000 to 41000 tokens, two KV heads, pages
+    scattered) on two splits of ceil(636 / 2) pages, so that some
+    workgroups keep the static order (under 48 pages), some hand pages out
+    dynamically after four early tiles (48 to 191) and some are long scans
+    (192 and more, every tile after the pages)."""
+    wl = synth.Workload(95, "test-mixed-order", 4, 2, 8, 128, 3000, 41000, n_cal=512, outliers="pairs10",
+                        scattered_pages=True)
+    cals = oracle_calibration(wl, n_cal=512)
+    rot = rotation_tensors(cals)
+    params = O.make_params(wl.n_kv, wl.n_q)
+    lens = np.array([3000, 9000, 23000, 41000], np.int32)
+    n_pg = (lens - 320 + 63) // 64
+    pps = (int(n_pg.max()) + 1) // 2                # pages per split
+    per_wg = np.concatenate([np.minimum(n_pg, pps), np.maximum(n_pg - pps, 0)])
+    assert (per_wg[per_wg > 0] < 48).any() and ((per_wg >= 48) & (per_wg < 192)).any() and (per_wg >= 192).any()
+    bt, total = synth.block_table(wl, lens)
+    pool = O.KVPool(params, wl.batch, total, bt)
+    toks = []
+    for b in range(wl.batch):
+        kb, vb = synth.kv_tokens(wl, 0, b, 0, int(lens[b]))
+        toks.append((kb, vb))
+        append_sequence(params, rot, pool, b, kb, vb)
+    q = synth.decode_queries(wl, 0)
+    O.set_decode_blocks(2 * wl.batch * wl.n_kv)   # two splits per (sequence, KV head)
+    try:
+        out = _decode_gpu(params, rot, pool, q, 2)
+    finally:
+        O.set_decode_blocks(0)
+    for b in range(wl.batch):
+        ref, _ = _oracle_decode(wl, cals, toks[b][0], toks[b][1], q[b])
+        assert decode_check(out[b], ref) <= TOL, b
+    assert int(pool.error_flags.cpu()[0]) == 0
+
+
 @pytest.mark.parametrize("G", [1, 2, 3, 5, 8, 16])
 def test_decode_group_sizes(G):
     """Query heads per KV head from 1 to 16: one, two and four M-tiles of
