@@ -955,12 +955,13 @@ __device__ __forceinline__ void pipe_scan(PagePipe<NW, PF> &p, const PoolView &p
   for (; i < p.npg; ++i) pipe_step<MT, NW, PF, false>(p, pv, i, n_hist, qo, st, wl, lane);
 }
 
-// Dynamic page order within a workgroup (long scans, one M-tile of heads):
-// the block-table entries of the workgroup's pages sit in LDS and each wave
-// takes the next page index from a shared counter whenever it frees a
-// buffer, so the waves of a SIMD (which otherwise finish in age order, the
-// oldest having issue priority) all run until the pages are gone.  The BF16
-// tiles are handed out the same way afterwards.
+// Dynamic page order within a workgroup (48 to kDynMaxPages pages, one
+// M-tile of heads): the block-table entries of the workgroup's pages sit in
+// LDS and each wave takes the next page index from a shared counter
+// whenever it frees a buffer, so the waves of a SIMD (which otherwise
+// finish in age order, the oldest having issue priority) all run until the
+// pages are gone.  The BF16 tiles not taken before the pages are handed out
+// the same way afterwards.
 constexpr int kDynMaxPages = 2048;
 struct DynPages {
   int next_page, next_tile;
