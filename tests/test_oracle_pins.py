@@ -464,3 +464,94 @@ def test_calibration_thresholds_reasonable(small_cal):
     assert abs(np.mean(rk <= cal.tau_K) - 0.96) < 1e-3
     rv = np.abs(vf.astype(np.float64) @ O.composite_rotation(cal.U_V))
     assert abs(np.mean(rv <= cal.tau_V) - 0.92) < 1e-3
+
+
+# --- calibration wiring: which covariance feeds which basis -----------------
+
+def _one_hot_calibration_set(seed=21, n=256, G=2, scale=1e4):
+    """Queries that are large multiples of the calibration keys, one key per
+    query (a permutation per head): every softmax score row is exactly one-hot
+    in float64, so S V selects value rows and C_S = V^T V / n, while
+    C_Q = scale^2 K^T K / n."""
+    g = np.random.default_rng(seed)
+    K = g.standard_normal((n, D))
+    V = g.standard_normal((n, D)) * np.linspace(3.0, 0.5, D)[None, :]
+    q = np.stack([scale * K[g.permutation(n)] for _ in range(G)])
+    return q, K, V
+
+
+def _basis_matches(U, C, tol):
+    """True if the columns of U are the eigenvectors of C by descending
+    eigenvalue, up to sign (scipy's symmetric eigensolver as the reference)."""
+    w, E = scipy.linalg.eigh(C)
+    E = E[:, ::-1]
+    dots = np.abs(np.sum(E * np.asarray(U, dtype=np.float64), axis=0))
+    return bool(np.all(dots > 1.0 - tol))
+
+
+def test_calibrate_head_value_basis_from_score_weighted_values():
+    """[B] method: R_V comes from C_S = V^T S^T S V and R_K from C_Q.  With
+    one-hot scores C_S reduces to V^T V / n, so U_V must be the eigenbasis of
+    the value Gram matrix and U_K that of the key Gram matrix; a basis built
+    from the wrong operand (keys for values, or the query covariance) fails."""
+    q, K, V = _one_hot_calibration_set()
+    n = K.shape[0]
+    cal = O.calibrate_head(q, K, V, 1 / np.sqrt(D))
+    assert _basis_matches(cal.U_V, V.T @ V / n, 1e-5)
+    assert _basis_matches(cal.U_K, K.T @ K / n, 1e-5)
+    w = scipy.linalg.eigh(V.T @ V / n, eigvals_only=True)[::-1]
+    assert np.max(np.abs(cal.eig_V - w)) < 1e-10 * w[0]
+    # the plausible wiring mistakes would not pass the same check
+    assert not _basis_matches(cal.U_K, V.T @ V / n, 1e-5)
+    swapped = O.calibrate_head(q, V, K, 1 / np.sqrt(D))      # keys and values exchanged
+    assert not _basis_matches(swapped.U_V, V.T @ V / n, 1e-5)
+
+
+def test_lemma1_on_calibrated_value_rotation(small_cal):
+    """Lemma 1 ([B] method) on the calibrated value rotation: R_V^T C_S R_V has
+    the constant diagonal tr(C_S) / d only if U_V diagonalises the C_S of the
+    same calibration data.  The basis a key/value swap would give does not."""
+    cal, qf, kf, vf = small_cal
+    CS = O.score_weighted_value_covariance(qf, kf, vf, 1 / np.sqrt(D))
+    tr = np.trace(CS)
+    R = O.composite_rotation(cal.U_V)
+    assert np.max(np.abs(np.diag(R.T @ CS @ R) - tr / D)) < 1e-6 * tr
+    Dg = cal.U_V.astype(np.float64).T @ CS @ cal.U_V.astype(np.float64)
+    assert np.all(np.diff(np.diag(Dg)) <= 1e-6 * tr)          # descending eigenvalues
+    _, Uw = O.sorted_eigenbasis(O.score_weighted_value_covariance(qf, vf, kf, 1 / np.sqrt(D)))
+    Rw = O.composite_rotation(Uw.astype(np.float32))
+    assert np.max(np.abs(np.diag(Rw.T @ CS @ Rw) - tr / D)) > 1e-3 * tr
+
+
+# --- decode_sequence: query head h reads KV head h // G ----------------------
+
+def test_decode_sequence_gqa_head_mapping():
+    """Query head h reads KV head h // (Hq / Hkv) (grouped-query attention):
+    checked against torch SDPA's grouped-query mode over the oracle's
+    dequantised caches, with two KV heads holding different data."""
+    wl = synth.WORKLOADS["tiny-4k"]
+    qc, kc, vc = synth.calibration_set(wl, 0, n_cal=256)
+    f = synth.bf16_bits_to_f32
+    Hkv, G, L = 2, 3, 700
+    pools, cals = [], []
+    for kv in range(Hkv):
+        cal = O.calibrate_head(f(qc)[:G] * (1 + kv), f(kc)[0] * (1 - 0.4 * kv), f(vc)[0], 1 / np.sqrt(D))
+        kb, vb = synth.kv_tokens(wl, kv, kv, 0, L)      # layer / sequence index as a different seed
+        K = f(kb)[:, 0].astype(np.float64) * (1 + 2 * kv)
+        V = f(vb)[:, 0].astype(np.float64) + 3.0 * kv
+        pools.append(O.build_head_pool(K, V, cal))
+        cals.append(cal)
+    g = np.random.default_rng(22)
+    q = g.standard_normal((Hkv * G, D))
+    out = O.decode_sequence(q, pools, cals, 1 / np.sqrt(D))
+    caches = [O.dequantized_head_cache(p, c) for p, c in zip(pools, cals)]
+    Kt = torch.from_numpy(np.stack([c[0] for c in caches]))[None]
+    Vt = torch.from_numpy(np.stack([c[1] for c in caches]))[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None, :, None, :], Kt, Vt, scale=1 / np.sqrt(D), enable_gqa=True)[0, :, 0]
+    assert np.max(np.abs(out - ref.numpy())) < 1e-12
+    # the interleaved mapping h % Hkv gives a different answer on these heads
+    wrong = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None, :, None, :], Kt.repeat(1, G, 1, 1), Vt.repeat(1, G, 1, 1),
+        scale=1 / np.sqrt(D))[0, :, 0]
+    assert np.max(np.abs(out - wrong.numpy())) > 0.1
