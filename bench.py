@@ -36,7 +36,7 @@ HIST_BYTES_PER_TOKEN_HEAD = 72      # 64 B codes (K+V) + 8 B metadata codes (K+V
 # HBM traffic of the scan kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
 # recorded with a hash of the kernel sources it was measured on; reported
 # only while those sources are unchanged.
-TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "bit_rotated_kv_int2_amd", "measured_traffic.json")
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "decode_scan_kernel_traffic.json")
 TRAFFIC_SOURCES = ("bit_rotated_kv_int2_amd/csrc/oscar_decode_kernels.hip", "bit_rotated_kv_int2_amd/csrc/oscar_internal.h",
                    "bit_rotated_kv_int2_amd/csrc/oscar_wave.h", "include/oscar.h")
 
@@ -86,7 +86,7 @@ def calibrate_layer(O, synth, wl, layer, params, n_cal):
 
 
 class Workbench:
-    def __init__(self, wl, n_layers, extra_tokens, n_cal, bf16_budget_gb):
+    def __init__(self, wl, n_layers, extra_tokens, n_cal, bf16_budget_gb, variant=0):
         import torch
         from bit_rotated_kv_int2_amd import oscar as O
         from bit_rotated_kv_int2_amd import synth
@@ -110,7 +110,8 @@ class Workbench:
             self.layers.append((rot, pool))
             if layer % 6 == 5 or layer == n_layers - 1:
                 log(f"{wl.name}: built INT2 layer {layer + 1}/{n_layers} ({time.time() - t0:.1f}s)")
-        self.ws = O.alloc_workspace(O.decode_workspace_size(self.params, wl.batch, self.bt.shape[1]))
+        self.variant = variant
+        self.ws = O.alloc_workspace(O.decode_workspace_size(self.params, wl.batch, self.bt.shape[1], variant))
         self.out = torch.zeros((wl.batch, wl.n_q, D), dtype=torch.float32, device="cuda")
         # BF16 baseline caches holding the same token contents (as many layers as the budget allows)
         per_layer = float(np.sum(self.lengths)) * wl.n_kv * WIN_BYTES_PER_TOKEN_HEAD
@@ -200,12 +201,13 @@ def run_workload(wb, steps, warmup, decode_reps, bf16_fit=None):
             t_start.record()
         for l, (rot, pool) in enumerate(wb.layers):
             O.quantize_append(wb.params, rot, pool, knew[l][s], vnew[l][s])
+            # the decode is one kernel launch (MFMA variants) on torch's current
+            # stream, so events recorded on that stream around it time the kernel
             if s >= warmup:
-                e0, e1 = ev[(s - warmup) * nl + l]
-                O.set_history_timing_events(e0, e1)
-            O.decode_attention(wb.params, rot, pool, qs[l][s], wb.out, wb.ws)
+                ev[(s - warmup) * nl + l][0].record()
+            O.decode_attention(wb.params, rot, pool, qs[l][s], wb.out, wb.ws, variant=wb.variant)
             if s >= warmup:
-                O.set_history_timing_events(None, None)
+                ev[(s - warmup) * nl + l][1].record()
     t_stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -224,7 +226,7 @@ def run_workload(wb, steps, warmup, decode_reps, bf16_fit=None):
     d0.record()
     for r in range(decode_reps):
         for l, (rot, pool) in enumerate(wb.layers):
-            O.decode_attention(wb.params, rot, pool, qs[l][r % total], wb.out, wb.ws)
+            O.decode_attention(wb.params, rot, pool, qs[l][r % total], wb.out, wb.ws, variant=wb.variant)
     d1.record()
     torch.cuda.synchronize()
     decode_us = d0.elapsed_time(d1) * 1e3 / (decode_reps * nl)
@@ -410,20 +412,37 @@ def effective_bpe(L, sink=64, recent=256, history_bits=2.0 + 16.0 / 64):
     return (win * 16.0 + (L - win) * history_bits) / L
 
 
-def stream_read_ceiling(torch, O, gib=4, reps=5):
-    """Practical HBM read rate: a plain streaming-read kernel of the library over
-    a 4 GiB buffer (best of a few grid sizes, HIP events around `reps` launches)."""
+def _probe_lib():
+    """The benchmark-only streaming-read helper library (not part of liboscar.so)."""
+    import ctypes
+    from bit_rotated_kv_int2_amd import build as B
+    lib = ctypes.CDLL(B.PROBE_LIB_PATH)
+    lib.bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.c_void_p]
+    lib.bench_stream_read.restype = ctypes.c_int
+    return lib
+
+
+def stream_read_ceiling(torch, gib=4, reps=5):
+    """Practical HBM read rate: a plain streaming-read kernel over a 4 GiB
+    buffer (best of a few grid sizes, HIP events around `reps` launches)."""
+    probe = _probe_lib()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def read(buf, sink, grid):
+        rc = probe.bench_stream_read(buf.data_ptr(), buf.numel() * 4, sink.data_ptr(), grid, stream)
+        assert rc == 0, rc
     n = gib << 30
     buf = torch.empty(n // 4, dtype=torch.int32, device="cuda").random_()
     best = None
     for grid in (256, 512, 1024):
         sink = torch.empty(grid * 512, dtype=torch.int32, device="cuda")
-        O.stream_read_probe(buf, sink, grid)
+        read(buf, sink, grid)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
-            O.stream_read_probe(buf, sink, grid)
+            read(buf, sink, grid)
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
@@ -465,11 +484,10 @@ def main():
     from bit_rotated_kv_int2_amd import synth
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     O.lib()   # fail loudly if the HIP library is missing
-    O.set_decode_variant(args.variant)
 
     wl = synth.WORKLOADS[args.workload]
     nl = args.layers or wl.layers
-    wb = Workbench(wl, nl, args.warmup + args.steps, args.n_cal, args.bf16_budget_gb)
+    wb = Workbench(wl, nl, args.warmup + args.steps, args.n_cal, args.bf16_budget_gb, args.variant)
     bf16_fit = None
     if wl.batch > 1:
         # sequences an all-BF16 cache of the same layers fits in the HBM the INT2 pool occupies
@@ -484,7 +502,8 @@ def main():
     batch1 = None
     if not args.no_batch1 and wl.batch > 1:
         wl1 = synth.WORKLOADS["qwen3-8b-100k-b1-36l"]
-        wb1 = Workbench(wl1, args.layers or wl1.layers, args.warmup + args.steps, args.n_cal, args.bf16_budget_gb)
+        wb1 = Workbench(wl1, args.layers or wl1.layers, args.warmup + args.steps, args.n_cal, args.bf16_budget_gb,
+                        args.variant)
         r1 = run_workload(wb1, args.steps, args.warmup, args.decode_reps * 4)
         log(f"{wl1.name}: {json.dumps(r1)}")
         batch1 = {"workload": wl1.name, "us_per_step": r1["step_ms"] * 1e3, "gbps": r1["value_gbps"],
@@ -503,7 +522,7 @@ def main():
         log(f"prefix: {json.dumps(prefix)}")
         torch.cuda.empty_cache()
 
-    ceiling = stream_read_ceiling(torch, O)
+    ceiling = stream_read_ceiling(torch)
     log(f"stream read ceiling: {json.dumps(ceiling)}")
 
     cpu = None

@@ -24,8 +24,12 @@ SOURCES = [
     "oscar_write.hip",
     "oscar_decode_kernels.hip",
     "oscar_bf16.hip",
-    "oscar_probe.hip",
 ]
+
+# Benchmark-only helper library (streaming-read probe); liboscar.so does not
+# contain or load it.
+PROBE_SOURCE = "bench_read_probe.hip"
+PROBE_LIB_PATH = os.path.join(HERE, "libbench_probe.so")
 
 # Packed-FP32 VALU forms are disabled for all device code.
 HIPCC_FLAGS = [
@@ -79,7 +83,19 @@ def build(verbose: bool = False, jobs: int = 6) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB_PATH)
+    _build_probe(verbose)
     return LIB_PATH
+
+
+def _build_probe(verbose: bool) -> None:
+    tmp = PROBE_LIB_PATH + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-x", "hip", "-shared", os.path.join(CSRC, PROBE_SOURCE), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PROBE_SOURCE}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB_PATH)
 
 
 if __name__ == "__main__":

@@ -1,12 +1,12 @@
-// Plain streaming read of a device buffer: the practical HBM read rate that
-// the history scan's bandwidth is compared against (a measurement aid, not
-// part of the attention path).
+// Benchmark helper, not part of liboscar.so: a plain streaming read of a
+// device buffer, built into its own library (libbench_probe.so) that only the
+// benchmark and its test load.  Its rate is the practical HBM read ceiling
+// that the history scan's bandwidth is reported against, next to the
+// published peak.
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
-#include "oscar_internal.h"
-
-namespace oscar {
 namespace {
 
 constexpr int kProbeThreads = 512;
@@ -33,12 +33,17 @@ __global__ void __launch_bounds__(kProbeThreads) stream_read_kernel(const uint4 
 
 }  // namespace
 
-int probe_threads() { return kProbeThreads; }
+extern "C" {
 
-hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(kProbeThreads), 0, s, (const uint4 *)buf, bytes / 16,
-                     sink);
-  return hipGetLastError();
+// One streaming read of `bytes` bytes of buf (16-byte aligned; a tail shorter
+// than 32 KB may be skipped) by `grid` workgroups of 512 threads; sink is
+// uint32 [grid * 512], overwritten with per-thread checksums.  Enqueued on
+// `stream`.  Returns 0, -1 for bad arguments, or a hipError_t value.
+int bench_stream_read(const void *buf, size_t bytes, uint32_t *sink, int grid, void *stream) {
+  if (!buf || !sink || ((uintptr_t)buf & 15u) || grid < 1 || grid > 65536) return -1;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(kProbeThreads), 0, (hipStream_t)stream,
+                     (const uint4 *)buf, bytes / 16, sink);
+  return (int)hipGetLastError();
 }
 
-}  // namespace oscar
+}  // extern "C"

@@ -11,9 +11,6 @@
 namespace {
 
 thread_local char g_err[512] = "";
-int g_variant = 0;
-int g_blocks = 0;
-hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 
 int fail(int code, const char *fmt, ...) {
   va_list ap;
@@ -71,6 +68,17 @@ int check_rot(const oscar_rotation *r) {
   return OSCAR_OK;
 }
 
+// Decode options: NULL means every field 0 (the defaults).
+int check_opts(const oscar_decode_options *o, oscar_decode_options *out) {
+  *out = oscar_decode_options{0, 0};
+  if (!o) return OSCAR_OK;
+  if (o->variant < 0 || o->variant > 2)
+    return fail(OSCAR_EINVAL, "options.variant must be 0 (MFMA), 1 (VALU) or 2 (MFMA, grid partition)");
+  if (o->blocks < 0 || o->blocks > 65536) return fail(OSCAR_EINVAL, "options.blocks must be in [0, 65536]");
+  *out = *o;
+  return OSCAR_OK;
+}
+
 oscar::PoolView make_pv(const oscar_params *p, const oscar_kv_pool *pool) {
   oscar::PoolView v{};
   v.sink_k = pool->sink_k;
@@ -102,36 +110,6 @@ extern "C" {
 const char *oscar_last_error(void) { return g_err; }
 
 int32_t oscar_version(void) { return 1000; }
-
-int32_t oscar_set_history_timing_events(void *start_event, void *stop_event) {
-  if ((start_event == nullptr) != (stop_event == nullptr))
-    return fail(OSCAR_EINVAL, "give both timing events or neither");
-  g_ev_start = (hipEvent_t)start_event;
-  g_ev_stop = (hipEvent_t)stop_event;
-  return ok();
-}
-
-int32_t oscar_set_decode_variant(int32_t variant) {
-  if (variant < 0 || variant > 2)
-    return fail(OSCAR_EINVAL, "variant must be 0 (MFMA), 1 (VALU) or 2 (MFMA, grid partition)");
-  g_variant = variant;
-  return ok();
-}
-
-int32_t oscar_set_decode_blocks(int32_t blocks) {
-  if (blocks < 0 || blocks > 65536) return fail(OSCAR_EINVAL, "blocks must be in [0, 65536]");
-  g_blocks = blocks;
-  return ok();
-}
-
-int32_t oscar_stream_read_probe(const void *buf, size_t bytes, uint32_t *sink, int32_t grid, void *stream) {
-  if (!buf || !sink) return fail(OSCAR_EINVAL, "buf/sink is NULL");
-  if (misaligned(buf)) return fail(OSCAR_EINVAL, "buf must be 16-byte aligned");
-  if (grid < 1 || grid > 65536) return fail(OSCAR_EINVAL, "grid must be in [1, 65536]");
-  hipError_t e = oscar::launch_stream_read(buf, bytes, sink, grid, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(OSCAR_EHIP, "probe launch failed: %s", hipGetErrorString(e));
-  return ok();
-}
 
 int32_t oscar_calibrate_rotation(const oscar_params *p, const float *q_cal, int64_t n_q,
                                  const float *k_cal, const float *v_cal, int64_t n_kv,
@@ -169,30 +147,36 @@ int32_t oscar_quantize_append(const oscar_params *p, const oscar_rotation *rot,
   return ok();
 }
 
-size_t oscar_decode_workspace_size(const oscar_params *p, int32_t batch, int32_t max_pages) {
-  if (check_params(p) || batch < 1 || max_pages < 0) return 0;
-  return oscar::make_decode_plan(batch, p->num_kv_heads, p->num_q_heads, max_pages, p->sink, p->recent, g_variant,
-                                 g_blocks)
+size_t oscar_decode_workspace_size(const oscar_params *p, int32_t batch, int32_t max_pages,
+                                   const oscar_decode_options *opts) {
+  oscar_decode_options o;
+  if (check_params(p) || batch < 1 || max_pages < 0 || check_opts(opts, &o)) return 0;
+  return oscar::make_decode_plan(batch, p->num_kv_heads, p->num_q_heads, max_pages, p->sink, p->recent, o.variant,
+                                 o.blocks)
       .total;
 }
 
 int32_t oscar_decode_attention(const oscar_params *p, const oscar_rotation *rot,
                                const oscar_kv_pool *pool, const uint16_t *q, float *out,
-                               void *workspace, size_t workspace_bytes, void *stream) {
+                               const oscar_decode_options *opts, void *workspace,
+                               size_t workspace_bytes, void *stream) {
   int rc = check_params(p);
   if (rc) return rc;
   if ((rc = check_rot(rot)) || (rc = check_pool(p, pool))) return rc;
+  oscar_decode_options o;
+  if ((rc = check_opts(opts, &o))) return rc;
   if (!q || !out) return fail(OSCAR_EINVAL, "q/out is NULL");
   if (misaligned(q) || misaligned(out)) return fail(OSCAR_EINVAL, "q/out must be 16-byte aligned");
   const oscar::DecodePlan plan = oscar::make_decode_plan(pool->batch, p->num_kv_heads, p->num_q_heads,
-                                                          pool->max_pages, p->sink, p->recent, g_variant, g_blocks);
+                                                          pool->max_pages, p->sink, p->recent, o.variant, o.blocks);
   if (!workspace || workspace_bytes < plan.total)
     return fail(OSCAR_EWORKSPACE, "workspace of %zu bytes needed, %zu given", plan.total, workspace_bytes);
   if (((uintptr_t)workspace) & 255) return fail(OSCAR_EINVAL, "workspace must be 256-byte aligned");
   oscar::PoolView pv = make_pv(p, pool);
   oscar::RotView rv{rot->U_K, rot->U_V, rot->tau_K, rot->tau_V};
-  hipError_t e = oscar::launch_decode(pv, rv, q, out, (uint8_t *)workspace, plan, g_variant, (hipStream_t)stream,
-                                      g_ev_start, g_ev_stop);
+  hipError_t e = oscar::launch_decode(pv, rv, q, out, (uint8_t *)workspace,
+                                      (int *)((uint8_t *)workspace + plan.off_counters), plan, o.variant,
+                                      (hipStream_t)stream);
   if (e != hipSuccess) return fail(OSCAR_EHIP, "decode launch failed: %s", hipGetErrorString(e));
   return ok();
 }

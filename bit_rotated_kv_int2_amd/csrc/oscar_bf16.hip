@@ -9,8 +9,6 @@
 // last block of a (sequence, KV head) merges the split partials and writes
 // the output, so no second launch is needed.  Counters return to zero; the
 // workspace must be zero-filled before its first use.
-#include <stdlib.h>
-
 #include "oscar_wave.h"
 
 namespace oscar {
@@ -120,14 +118,8 @@ __global__ void __launch_bounds__(256) bf16_decode_kernel(Bf16Args a) {
   }
 }
 
-int bf16_target_blocks() {
-  static int v = [] {
-    const char *e = getenv("OSCAR_BF16_BLOCKS");
-    const int x = e ? atoi(e) : 0;
-    return x > 0 ? x : 1024;
-  }();
-  return v;
-}
+// workgroups the baseline's split grid aims for (four per CU)
+constexpr int kBf16Blocks = 1024;
 
 }  // namespace
 
@@ -135,7 +127,7 @@ Bf16Plan make_bf16_plan(int batch, int hkv, int hq, int max_pages) {
   Bf16Plan p{};
   const int G = hq / hkv;
   const int bh = batch * hkv;
-  int S = (bf16_target_blocks() + bh - 1) / bh;
+  int S = (kBf16Blocks + bh - 1) / bh;
   const int max_by_pages = max_pages > 0 ? (max_pages + 3) / 4 : 1;
   S = S < 1 ? 1 : S;
   S = S > max_by_pages ? max_by_pages : S;

@@ -33,8 +33,6 @@
 //           than a factor 2, so no per-page max or scale reduction is needed.
 //   Codes enter unscaled: the zero point is added as z * sum(q) (logits) and
 //   sum(p * z) (values).
-#include <stdlib.h>
-
 #include "oscar_wave.h"
 
 namespace oscar {
@@ -1738,16 +1736,8 @@ decode_flat_kernel(DecArgs a) {
 }  // namespace
 
 namespace {
-int target_blocks(int blocks) {
-  // scan workgroups the grid aims for: the caller's choice, else one per CU
-  // (OSCAR_DECODE_BLOCKS overrides the default; tuning only)
-  static int v = [] {
-    const char *e = getenv("OSCAR_DECODE_BLOCKS");
-    const int x = e ? atoi(e) : 0;
-    return x > 0 ? x : 256;
-  }();
-  return blocks > 0 ? blocks : v;
-}
+// scan workgroups the grid aims for: the caller's choice, else one per CU
+int target_blocks(int blocks) { return blocks > 0 ? blocks : 256; }
 int mt_of(int G) { return (G + 3) / 4; }
 int gh_of(int G) { return 4 * mt_of(G); }
 // variant 0: MFMA scan (balanced partition where it applies, else grid);
@@ -1806,21 +1796,17 @@ DecodePlan make_decode_plan(int batch, int hkv, int hq, int max_pages, int sink,
 }
 
 hipError_t launch_decode(const PoolView &pv, const RotView &rv, const uint16_t *q, float *out,
-                         uint8_t *ws, const DecodePlan &plan, int variant, hipStream_t s,
-                         hipEvent_t ev_start, hipEvent_t ev_stop) {
+                         uint8_t *ws, int *counters, const DecodePlan &plan, int variant, hipStream_t s) {
   const int G = pv.hq / pv.hkv;
   const int BH = pv.batch * pv.hkv;
-  DecArgs a{pv, rv, q, out, (int *)(ws + plan.off_counters), (float *)(ws + plan.off_qconst),
+  DecArgs a{pv, rv, q, out, counters, (float *)(ws + plan.off_qconst),
             (float *)(ws + plan.off_qrot), (float *)(ws + plan.off_part), (float *)(ws + plan.off_tile),
             plan.n_splits, plan.n_chunks, plan.pages_per_split, plan.n_blocks};
   const bool mfma = is_mfma(variant);
   hipError_t e;
   if (plan.flat) {
-    if (ev_start && (e = hipEventRecord(ev_start, s)) != hipSuccess) return e;
     hipLaunchKernelGGL(decode_flat_kernel<4>, dim3(plan.n_blocks), dim3(64 * scan_waves<1, true>()), 0, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (ev_stop && (e = hipEventRecord(ev_stop, s)) != hipSuccess) return e;
-    return hipSuccess;
+    return hipGetLastError();
   }
   const dim3 sgrid(BH * plan.n_splits);
 #define OSCAR_LAUNCH(MT, GH)                                                                         \
@@ -1829,7 +1815,6 @@ hipError_t launch_decode(const PoolView &pv, const RotView &rv, const uint16_t *
       hipLaunchKernelGGL((decode_pre_kernel<MT, GH>), dim3(BH), dim3(256), 0, s, a);                 \
       if ((e = hipGetLastError()) != hipSuccess) return e;                                           \
     }                                                                                                \
-    if (ev_start && (e = hipEventRecord(ev_start, s)) != hipSuccess) return e;                       \
     if (mfma)                                                                                        \
       hipLaunchKernelGGL((decode_scan_kernel<MT, GH, true>), sgrid, dim3(64 * scan_waves<MT, true>()), \
                          0, s, a);                                                                   \
@@ -1842,9 +1827,7 @@ hipError_t launch_decode(const PoolView &pv, const RotView &rv, const uint16_t *
   else if (G <= 12) OSCAR_LAUNCH(3, 12);
   else OSCAR_LAUNCH(4, 16);
 #undef OSCAR_LAUNCH
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev_stop && (e = hipEventRecord(ev_stop, s)) != hipSuccess) return e;
-  return hipSuccess;
+  return hipGetLastError();
 }
 
 }  // namespace oscar

@@ -127,16 +127,13 @@ struct DecodePlan {
 DecodePlan make_decode_plan(int batch, int hkv, int hq, int max_pages, int sink, int recent,
                             int variant, int blocks);
 
-// Streaming-read probe: threads per workgroup and launcher.
-int probe_threads();
-hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, int grid, hipStream_t s);
-
 // Launchers (return hipError_t of the launches).
 hipError_t launch_append(const PoolView &pv, const RotView &rv, const uint16_t *k_new,
                          const uint16_t *v_new, int n_new, hipStream_t s);
+// ws: base of the plan's offsets; counters: the plan's completion counters
+// (ws + plan.off_counters for a caller's workspace).
 hipError_t launch_decode(const PoolView &pv, const RotView &rv, const uint16_t *q, float *out,
-                         uint8_t *ws, const DecodePlan &plan, int variant, hipStream_t s,
-                         hipEvent_t ev_start, hipEvent_t ev_stop);
+                         uint8_t *ws, int *counters, const DecodePlan &plan, int variant, hipStream_t s);
 
 struct Bf16View {
   const uint16_t *k_pages, *v_pages;

@@ -28,8 +28,7 @@ PAGE_KCODES, PAGE_VCODES, PAGE_KMETA, PAGE_VMETA = 0, 2048, 4096, 4352
 EXPORTED = [
     "oscar_calibrate_rotation", "oscar_quantize_append", "oscar_decode_attention",
     "oscar_decode_workspace_size", "oscar_bf16_decode_attention",
-    "oscar_bf16_decode_workspace_size", "oscar_set_decode_variant", "oscar_set_decode_blocks", "oscar_last_error",
-    "oscar_version", "oscar_set_history_timing_events", "oscar_stream_read_probe",
+    "oscar_bf16_decode_workspace_size", "oscar_last_error", "oscar_version",
 ]
 
 
@@ -65,6 +64,10 @@ class KVPoolC(ctypes.Structure):
                 ("n_sink_slots", ctypes.c_int32)]
 
 
+class DecodeOptions(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int32), ("blocks", ctypes.c_int32)]
+
+
 class Bf16CacheC(ctypes.Structure):
     _fields_ = [("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p),
                 ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
@@ -90,26 +93,18 @@ def lib():
     L.oscar_calibrate_rotation.restype = i32
     L.oscar_quantize_append.argtypes = [P(Params), P(Rotation), P(KVPoolC), vp, vp, i32, vp]
     L.oscar_quantize_append.restype = i32
-    L.oscar_decode_attention.argtypes = [P(Params), P(Rotation), P(KVPoolC), vp, vp, vp, sz, vp]
+    L.oscar_decode_attention.argtypes = [P(Params), P(Rotation), P(KVPoolC), vp, vp, P(DecodeOptions), vp, sz, vp]
     L.oscar_decode_attention.restype = i32
-    L.oscar_decode_workspace_size.argtypes = [P(Params), i32, i32]
+    L.oscar_decode_workspace_size.argtypes = [P(Params), i32, i32, P(DecodeOptions)]
     L.oscar_decode_workspace_size.restype = sz
     L.oscar_bf16_decode_attention.argtypes = [P(Params), P(Bf16CacheC), vp, vp, vp, sz, vp]
     L.oscar_bf16_decode_attention.restype = i32
     L.oscar_bf16_decode_workspace_size.argtypes = [P(Params), i32, i32]
     L.oscar_bf16_decode_workspace_size.restype = sz
-    L.oscar_set_decode_variant.argtypes = [i32]
-    L.oscar_set_decode_variant.restype = i32
-    L.oscar_set_decode_blocks.argtypes = [i32]
-    L.oscar_set_decode_blocks.restype = i32
-    L.oscar_stream_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, i32, ctypes.c_void_p]
-    L.oscar_stream_read_probe.restype = i32
     L.oscar_last_error.argtypes = []
     L.oscar_last_error.restype = ctypes.c_char_p
     L.oscar_version.argtypes = []
     L.oscar_version.restype = i32
-    L.oscar_set_history_timing_events.argtypes = [vp, vp]
-    L.oscar_set_history_timing_events.restype = i32
     _lib = L
     return L
 
@@ -137,31 +132,8 @@ def _stream_ptr(stream) -> Optional[int]:
     return int(stream.cuda_stream)
 
 
-def set_decode_variant(variant: int) -> None:
-    _check(lib().oscar_set_decode_variant(int(variant)))
-
-
-def set_decode_blocks(blocks: int) -> None:
-    """Scan workgroups the split grid aims for (0 = one per compute unit)."""
-    _check(lib().oscar_set_decode_blocks(int(blocks)))
-
-
-def stream_read_probe(buf, sink, grid: int, stream=None) -> None:
-    """Plain streaming read of the device tensor buf (measurement aid); sink: int32 [grid * 512]."""
-    assert buf.is_contiguous() and sink.is_contiguous() and sink.numel() >= grid * 512
-    _check(lib().oscar_stream_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), int(grid),
-                                         _stream_ptr(stream)))
-
-
 def version() -> int:
     return int(lib().oscar_version())
-
-
-def set_history_timing_events(start_event=None, stop_event=None) -> None:
-    """torch.cuda.Event pair (recorded once so the handle exists) or None."""
-    a = None if start_event is None else int(start_event.cuda_event)
-    b = None if stop_event is None else int(stop_event.cuda_event)
-    _check(lib().oscar_set_history_timing_events(a, b))
 
 
 # ---------------------------------------------------------------------------
@@ -274,8 +246,14 @@ def quantize_append(params: Params, rot: RotationTensors, pool: KVPool, k_new, v
                                        _ptr(k_new), _ptr(v_new), n_new, _stream_ptr(stream)))
 
 
-def decode_workspace_size(params: Params, batch: int, max_pages: int) -> int:
-    return int(lib().oscar_decode_workspace_size(ctypes.byref(params), batch, max_pages))
+def decode_options(variant: int = 0, blocks: int = 0) -> DecodeOptions:
+    """Per-call decode choices (see oscar_decode_options in include/oscar.h)."""
+    return DecodeOptions(int(variant), int(blocks))
+
+
+def decode_workspace_size(params: Params, batch: int, max_pages: int, variant: int = 0, blocks: int = 0) -> int:
+    opts = decode_options(variant, blocks)
+    return int(lib().oscar_decode_workspace_size(ctypes.byref(params), batch, max_pages, ctypes.byref(opts)))
 
 
 def alloc_workspace(nbytes: int, device="cuda"):
@@ -284,12 +262,16 @@ def alloc_workspace(nbytes: int, device="cuda"):
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
-def decode_attention(params: Params, rot: RotationTensors, pool: KVPool, q, out, workspace, stream=None):
-    """q: bf16 bits [B, Hq, d]; out: float32 [B, Hq, d]; workspace: uint8 device tensor."""
+def decode_attention(params: Params, rot: RotationTensors, pool: KVPool, q, out, workspace, stream=None,
+                     variant: int = 0, blocks: int = 0):
+    """q: bf16 bits [B, Hq, d]; out: float32 [B, Hq, d]; workspace: uint8 device tensor
+    sized by decode_workspace_size with the same variant and blocks."""
     assert q.is_contiguous() and out.is_contiguous() and q.element_size() == 2
     r, pc = rot.c(), pool.c()
+    opts = decode_options(variant, blocks)
     _check(lib().oscar_decode_attention(ctypes.byref(params), ctypes.byref(r), ctypes.byref(pc), _ptr(q),
-                                        _ptr(out), _ptr(workspace), workspace.numel(), _stream_ptr(stream)))
+                                        _ptr(out), ctypes.byref(opts), _ptr(workspace), workspace.numel(),
+                                        _stream_ptr(stream)))
 
 
 class Bf16Cache:

@@ -177,6 +177,32 @@ int32_t oscar_quantize_append(const oscar_params *p, const oscar_rotation *rot,
                               const uint16_t *v_new, int32_t n_new, void *stream);
 
 /*
+ * Per-call choices of the decode kernels.  Pass NULL for the defaults
+ * (every field 0).  Nothing is kept between calls: the library holds no
+ * process-wide decode settings.
+ *   variant: 0 = MFMA int8 history scan (default); for G <= 4 it may split
+ *            the work evenly over a fixed grid of workgroups (balanced
+ *            partition, where built in), else one workgroup per (sequence,
+ *            KV head, split);
+ *            1 = VALU history scan (float arithmetic, reference speed);
+ *            2 = MFMA int8 history scan, always on the per-(sequence, KV
+ *            head) split grid.
+ *            Results of 0 and 2 differ only in floating-point summation
+ *            order.  OSCAR_EINVAL for other values.
+ *   blocks:  history-scan workgroups the split grid aims for: each
+ *            (sequence, KV head) gets ceil(blocks / (batch * Hkv)) splits,
+ *            capped so every wave keeps at least one page.  0 aims for one
+ *            workgroup per compute unit (256).  Results differ only in
+ *            floating-point summation order.  OSCAR_EINVAL outside
+ *            [0, 65536].
+ * The workspace size depends on both, so size it with the same options.
+ */
+typedef struct oscar_decode_options {
+  int32_t variant;
+  int32_t blocks;
+} oscar_decode_options;
+
+/*
  * Decode attention of one query token per sequence over the whole pool
  * ([A] token pool: INT2 and BF16 segments, merged by online softmax; [B]
  * serving: read path).  q: bf16 [batch][Hq][d]; out: float32 [batch][Hq][d]
@@ -184,18 +210,24 @@ int32_t oscar_quantize_append(const oscar_params *p, const oscar_rotation *rot,
  * and values dequantised and inverse-rotated (computed as (q R_K) against
  * the rotated codes and R_V^T applied once to the merged history output).
  * Query head h reads KV head h / (Hq/Hkv).  seq_lens is read on the device;
- * a sequence of length 0 yields zeros.  workspace: device memory of at least
- * oscar_decode_workspace_size() bytes, 256-byte aligned, ZERO-FILLED by the
- * caller before its first use.  It holds completion counters that every call
- * returns to zero, so it can be reused without clearing; calls that share a
- * workspace must not overlap (same stream, or ordered).  The size depends on
- * the decode variant selected when it is queried.
+ * a sequence of length 0 yields zeros.  opts: NULL or the kernel choices
+ * above.  workspace: device memory of at least
+ * oscar_decode_workspace_size(p, batch, max_pages, opts) bytes, 256-byte
+ * aligned, ZERO-FILLED by the caller before its first use.  It holds
+ * completion counters that every call returns to zero, so it can be reused
+ * without clearing; calls that share a workspace must not overlap (same
+ * stream, or ordered).  With variant 0 or 2 the call is one kernel launch
+ * on `stream`.
  */
 int32_t oscar_decode_attention(const oscar_params *p, const oscar_rotation *rot,
                                const oscar_kv_pool *pool, const uint16_t *q, float *out,
-                               void *workspace, size_t workspace_bytes, void *stream);
+                               const oscar_decode_options *opts, void *workspace,
+                               size_t workspace_bytes, void *stream);
 
-size_t oscar_decode_workspace_size(const oscar_params *p, int32_t batch, int32_t max_pages);
+/* Workspace bytes oscar_decode_attention needs for this shape and these
+ * options (NULL = defaults); 0 for invalid parameters or options. */
+size_t oscar_decode_workspace_size(const oscar_params *p, int32_t batch, int32_t max_pages,
+                                   const oscar_decode_options *opts);
 
 /*
  * In-house BF16 decode baseline on a paged all-BF16 cache (the comparison
@@ -220,50 +252,6 @@ int32_t oscar_bf16_decode_attention(const oscar_params *p, const oscar_bf16_cach
                                     size_t workspace_bytes, void *stream);
 
 size_t oscar_bf16_decode_workspace_size(const oscar_params *p, int32_t batch, int32_t max_pages);
-
-/*
- * Optional timing hook for benchmarks.  When both are non-NULL, every later
- * oscar_decode_attention call records `start_event` immediately before and
- * `stop_event` immediately after its INT2 history kernel, on the call's
- * stream (hipEvent_t handles created by the caller with timing enabled).
- * Pass NULL, NULL to disable.  Process-wide; not meant for concurrent use.
- */
-int32_t oscar_set_history_timing_events(void *start_event, void *stop_event);
-
-/*
- * Decode kernel selection (process-wide; OSCAR_EINVAL for other values):
- *   0 = MFMA int8 history scan (default); for G <= 4 it may split the work
- *       evenly over a fixed grid of workgroups (balanced partition, where
- *       built in), else one workgroup per (sequence, KV head, split);
- *   1 = VALU history scan (float arithmetic, reference speed);
- *   2 = MFMA int8 history scan, always on the per-(sequence, KV head) split
- *       grid.
- * Results of 0 and 2 differ only in floating-point summation order.
- */
-int32_t oscar_set_decode_variant(int32_t variant);
-
-/*
- * Number of history-scan workgroups the split grid aims for (process-wide):
- * each (sequence, KV head) gets ceil(blocks / (batch * Hkv)) splits, capped
- * so every wave keeps at least one page.  0 (the default) aims for one
- * workgroup per compute unit (256).  Like the variant, it sets the workspace
- * size, so query oscar_decode_workspace_size() after changing it.  Results
- * differ only in floating-point summation order.  OSCAR_EINVAL outside
- * [0, 65536].
- */
-int32_t oscar_set_decode_blocks(int32_t blocks);
-
-/*
- * Measurement aid, not part of the attention path: one plain streaming read
- * of `bytes` bytes of the device buffer `buf` (16-byte aligned; a tail
- * shorter than 32 KB may be skipped) by `grid` workgroups of 512 threads,
- * each thread reading four 16-byte words per step.  sink: device uint32
- * [grid * 512], overwritten with per-thread checksums.  It gives the
- * practical HBM read rate the history scan is compared against.  Enqueued
- * on `stream`; OSCAR_EINVAL for NULL pointers, misalignment or grid outside
- * [1, 65536].
- */
-int32_t oscar_stream_read_probe(const void *buf, size_t bytes, uint32_t *sink, int32_t grid, void *stream);
 
 /* Message of the last error on the calling thread ("" if none). */
 const char *oscar_last_error(void);

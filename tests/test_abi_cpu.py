@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) >= 9
+    assert len(names) >= 8
     lib = ctypes.CDLL(O.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -52,12 +52,13 @@ def _fake_pool(batch=1):
     return O.KVPoolC(*([0x1000] * 10), batch, 4, 4, batch)
 
 
-def _call_decode(params, pool=None, ws_bytes=1 << 30):
+def _call_decode(params, pool=None, ws_bytes=1 << 30, opts=None):
     L = O.lib()
     rot = O.Rotation(0x1000, 0x1000, 0x1000, 0x1000)
     pool = pool or _fake_pool()
     return L.oscar_decode_attention(ctypes.byref(params), ctypes.byref(rot), ctypes.byref(pool),
-                                    0x1000, 0x1000, 0x1000, ws_bytes, None)
+                                    0x1000, 0x1000, None if opts is None else ctypes.byref(opts),
+                                    0x1000, ws_bytes, None)
 
 
 def test_validation_errors():
@@ -81,31 +82,29 @@ def test_validation_errors():
                                    0x1000, 0x1000, 1, None) == O.OSCAR_EINVAL
     # device tensors read 16 bytes at a time must be 16-byte aligned
     assert L.oscar_decode_attention(ctypes.byref(p), ctypes.byref(rot), ctypes.byref(pool),
-                                    0x1008, 0x1000, 0x1000, 1 << 30, None) == O.OSCAR_EINVAL
+                                    0x1008, 0x1000, None, 0x1000, 1 << 30, None) == O.OSCAR_EINVAL
     assert b"aligned" in L.oscar_last_error()
     assert L.oscar_decode_attention(ctypes.byref(p), ctypes.byref(O.Rotation(0x1004, 0x1000, 0x1000, 0x1000)),
-                                    ctypes.byref(pool), 0x1000, 0x1000, 0x1000, 1 << 30, None) == O.OSCAR_EINVAL
+                                    ctypes.byref(pool), 0x1000, 0x1000, None, 0x1000, 1 << 30, None) == O.OSCAR_EINVAL
     bad = _fake_pool()
     bad.pages = 0x1002
     assert _call_decode(p, pool=bad) == O.OSCAR_EINVAL
     assert L.oscar_quantize_append(ctypes.byref(p), ctypes.byref(rot), ctypes.byref(pool),
                                    0x1000, 0x1010 + 2, 1, None) == O.OSCAR_EINVAL
-    assert L.oscar_set_decode_variant(7) == O.OSCAR_EINVAL
-    assert L.oscar_set_decode_variant(-1) == O.OSCAR_EINVAL
-    for v in (2, 1, 0):
-        assert L.oscar_set_decode_variant(v) == 0
-    assert L.oscar_stream_read_probe(None, 1024, 0x1000, 1, None) == O.OSCAR_EINVAL
-    assert L.oscar_stream_read_probe(0x1008, 1024, 0x1000, 1, None) == O.OSCAR_EINVAL
-    assert L.oscar_stream_read_probe(0x1000, 1024, 0x2000, 0, None) == O.OSCAR_EINVAL
-    assert L.oscar_set_decode_blocks(-1) == O.OSCAR_EINVAL
-    assert L.oscar_set_decode_blocks(65537) == O.OSCAR_EINVAL
-    p8 = ctypes.byref(O.make_params(8, 32))
-    default_ws = L.oscar_decode_workspace_size(p8, 1, 1600)
-    assert L.oscar_set_decode_blocks(8) == 0           # one split per (sequence, KV head): fewer partials
-    assert 0 < L.oscar_decode_workspace_size(p8, 1, 1600) < default_ws
-    assert L.oscar_set_decode_blocks(0) == 0
-    assert L.oscar_decode_workspace_size(p8, 1, 1600) == default_ws
-    assert L.oscar_decode_workspace_size(ctypes.byref(O.make_params(8, 30)), 1, 10) == 0
+    # per-call decode options: checked before anything else is looked at
+    for bad_opts in (O.decode_options(7, 0), O.decode_options(-1, 0), O.decode_options(0, -1),
+                     O.decode_options(0, 65537)):
+        assert _call_decode(p, opts=bad_opts) == O.OSCAR_EINVAL
+        assert b"options" in L.oscar_last_error()
+    p8 = O.make_params(8, 32)
+    ws = lambda opts: L.oscar_decode_workspace_size(ctypes.byref(p8), 1, 1600,
+                                                    None if opts is None else ctypes.byref(opts))
+    default_ws = ws(None)
+    assert default_ws == ws(O.decode_options(0, 0)) == ws(O.decode_options(0, 256))
+    assert 0 < ws(O.decode_options(0, 8)) < default_ws       # one split per (sequence, KV head): fewer partials
+    assert ws(O.decode_options(0, -1)) == 0 and ws(O.decode_options(3, 0)) == 0
+    assert ws(None) == default_ws                           # nothing is kept between calls
+    assert L.oscar_decode_workspace_size(ctypes.byref(O.make_params(8, 30)), 1, 10, None) == 0
     with pytest.raises(O.OscarError):
         O.calibrate_rotation(O.make_params(1, 1), np.zeros((1, 8, 128), np.float32),
                              np.zeros((1, 8, 128), np.float32), np.zeros((1, 8, 128), np.float32))

@@ -50,7 +50,6 @@ def _build_pool(wl, lengths, cals, extra_tokens=0):
 
 def _decode(params, rot, pool, q_bits):
     import torch
-    O.set_decode_variant(0)
     ws = O.alloc_workspace(O.decode_workspace_size(params, pool.batch, pool.max_pages))
     q = torch.from_numpy(q_bits.view(np.int16)).cuda().contiguous()
     out = torch.zeros((pool.batch, params.num_q_heads, D), dtype=torch.float32, device="cuda")

@@ -34,15 +34,13 @@ def _f64(bits):
     return synth.bf16_bits_to_f32(bits).astype(np.float64)
 
 
-def _decode_gpu(params, rot, pool, q_bits, variant):
+def _decode_gpu(params, rot, pool, q_bits, variant, blocks=0):
     torch = _torch()
-    O.set_decode_variant(variant)
-    ws = O.alloc_workspace(O.decode_workspace_size(params, pool.batch, pool.max_pages))
+    ws = O.alloc_workspace(O.decode_workspace_size(params, pool.batch, pool.max_pages, variant, blocks))
     q = torch.from_numpy(q_bits.view(np.int16)).cuda().contiguous()
     out = torch.zeros((pool.batch, params.num_q_heads, D), dtype=torch.float32, device="cuda")
-    O.decode_attention(params, rot, pool, q, out, ws)
+    O.decode_attention(params, rot, pool, q, out, ws, variant=variant, blocks=blocks)
     torch.cuda.synchronize()
-    O.set_decode_variant(0)
     return out.cpu().numpy()
 
 
@@ -202,11 +200,7 @@ def test_ragged_batch_mixed_page_orders():
         toks.append((kb, vb))
         append_sequence(params, rot, pool, b, kb, vb)
     q = synth.decode_queries(wl, 0)
-    O.set_decode_blocks(2 * wl.batch * wl.n_kv)   # two splits per (sequence, KV head)
-    try:
-        out = _decode_gpu(params, rot, pool, q, 2)
-    finally:
-        O.set_decode_blocks(0)
+    out = _decode_gpu(params, rot, pool, q, 2, blocks=2 * wl.batch * wl.n_kv)   # two splits per (sequence, KV head)
     for b in range(wl.batch):
         ref, _ = _oracle_decode(wl, cals, toks[b][0], toks[b][1], q[b])
         assert decode_check(out[b], ref) <= TOL, b
@@ -320,11 +314,7 @@ def test_single_workgroup_long_history(tiny):
     perm = np.random.default_rng(7).permutation(n_pages).astype(np.int32)
     pool = O.KVPool(params, 1, n_pages, perm[None])
     append_sequence(params, rot, pool, 0, kb, vb)
-    O.set_decode_blocks(1)
-    try:
-        out = _decode_gpu(params, rot, pool, q, 2)
-    finally:
-        O.set_decode_blocks(0)
+    out = _decode_gpu(params, rot, pool, q, 2, blocks=1)
     ref, _ = _oracle_decode(wl, cals, kb, vb, q[0])
     err = decode_check(out[0], ref)
     print(f"150K tokens, one workgroup: err/||o|| = {err:.3e}")
@@ -347,11 +337,7 @@ def test_dynamic_page_order(tiny, blocks):
     perm = np.random.default_rng(11).permutation(n_pages).astype(np.int32)
     pool = O.KVPool(params, 1, n_pages, perm[None])
     append_sequence(params, rot, pool, 0, kb, vb)
-    O.set_decode_blocks(blocks)
-    try:
-        out = _decode_gpu(params, rot, pool, q, 2)
-    finally:
-        O.set_decode_blocks(0)
+    out = _decode_gpu(params, rot, pool, q, 2, blocks=blocks)
     ref, _ = _oracle_decode(wl, cals, kb, vb, q[0])
     err = decode_check(out[0], ref)
     print(f"40037 tokens, {blocks} workgroup(s): err/||o|| = {err:.3e}")
@@ -372,11 +358,9 @@ def test_dynamic_page_order_bad_entries_flagged(tiny):
     bt = pool.block_table.clone()
     for i in (5, 300, n_pages - 1):
         pool.block_table[0, i] = 1 << 20
-    O.set_decode_blocks(1)
     try:
-        out = _decode_gpu(params, rot, pool, q, 2)
+        out = _decode_gpu(params, rot, pool, q, 2, blocks=1)
     finally:
-        O.set_decode_blocks(0)
         pool.block_table.copy_(bt)
     assert np.all(np.isfinite(out))
     assert int(pool.error_flags.cpu()[0]) & O.DEVERR_PAGE
@@ -467,15 +451,23 @@ def test_quantiser_variants_parity(tiny, kind):
 
 
 def test_stream_read_probe_reads_every_word():
-    """The streaming-read probe covers the whole buffer: the xor of its
-    per-thread checksums is the xor of every 32-bit word (16 MiB = two full
-    grid strides of 256 x 512 threads x 4 words of 16 bytes)."""
+    """The benchmark's streaming-read probe (its own helper library) covers the
+    whole buffer: the xor of its per-thread checksums is the xor of every
+    32-bit word (16 MiB = two full grid strides of 256 x 512 threads x 4
+    words of 16 bytes)."""
+    import ctypes
+    from bit_rotated_kv_int2_amd import build as B
     torch = _torch()
+    probe = ctypes.CDLL(B.PROBE_LIB_PATH)
+    probe.bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_void_p]
+    probe.bench_stream_read.restype = ctypes.c_int
     g = torch.Generator().manual_seed(3)
     host = torch.randint(-2**31, 2**31 - 1, (4 << 20,), dtype=torch.int64, generator=g).to(torch.int32)
     buf = host.cuda()
     sink = torch.empty(256 * 512, dtype=torch.int32, device="cuda")
-    O.stream_read_probe(buf, sink, 256)
+    assert probe.bench_stream_read(buf.data_ptr(), buf.numel() * 4, sink.data_ptr(), 256,
+                                   torch.cuda.current_stream().cuda_stream) == 0
     torch.cuda.synchronize()
     want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
