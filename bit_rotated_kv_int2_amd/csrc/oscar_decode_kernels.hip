@@ -60,10 +60,9 @@ struct DecArgs {
   int *counters;       // [BH]
   float *qconst;       // [BH][GH][4]: delta, Q0, Q1 (VALU variant)
   float *qrot;         // [BH][GH][kD] float q~ (VALU variant)
-  float *part;         // grid path: [BH][n_splits + n_chunks][G][kPartStride] (history splits, then
-                       // BF16 tiles); balanced path: history partials [n_blocks + BH][G][kPartStride]
-  float *part_tile;    // balanced path: BF16 tile partials [BH][n_chunks][G][kPartStride]
-  int n_splits, n_chunks, pages_per_split, n_blocks;
+  float *part;         // [BH][n_parts][G][kPartStride]: history splits, then (several M-tiles, VALU)
+                       // BF16 tiles; one M-tile on MFMA folds its tiles into its split's partial
+  int n_splits, n_chunks, pages_per_split, n_parts;
 };
 
 __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
@@ -239,104 +238,6 @@ __device__ void query_prep(const DecArgs &a, int b, int kv, QSmem<MT, GH> &sm, f
       const int r = 4 * (h & 3) + 2 * g;
       base[(r + 16 * kg) * 16 + 4 * s + bb] = (int8_t)hi;
       base[(r + 1 + 16 * kg) * 16 + 4 * s + bb] = (int8_t)lo;
-    }
-  }
-  __syncthreads();
-}
-
-// Query preparation of up to K (sequence, KV head) items at once: thread
-// group k (threads 256 k .. 256 k + 255) forms item k's projections, then one
-// wave per (item, head) runs the butterfly and the quantisation.  ys is LDS
-// scratch [K][4][kD]; results go to aq[k] (A operands) and qc[k] (constants).
-// One M-tile of heads (G <= 4); needs blockDim.x >= 256 K.
-template <int K>
-__device__ void query_prep_multi(const DecArgs &a, const int (&bb)[K], const int (&kk)[K], int nitems,
-                                 float (*ys)[4][kD], v4i (*aq)[2 * 64], float (*qc)[4][4]) {
-  const PoolView &pv = a.pv;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
-  const int G = pv.hq / pv.hkv;
-  const int grp = tid >> 8, t = tid & 255;
-  if (grp < nitems) {
-    int b = bb[0], kv = kk[0];
-#pragma unroll
-    for (int k = 1; k < K; ++k)
-      if (grp == k) b = bb[k], kv = kk[k];
-    const float *U = a.rv.U_K + (size_t)kv * kD * kD;
-    const uint16_t *qb = a.q + ((size_t)b * pv.hq + (size_t)kv * G) * kD;
-    const int c = t >> 3, k8 = t & 7;
-    float4 u[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) u[i] = *(const float4 *)(U + (size_t)(k8 + 8 * i) * kD + 4 * c);
-    for (int h = 0; h < G; ++h) {
-      const uint16_t *qr = qb + (size_t)h * kD;
-      float y0 = 0.f, y1 = 0.f, y2 = 0.f, y3 = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float qv = bf16_to_f32(qr[k8 + 8 * i]);
-        y0 = fmaf(qv, u[i].x, y0);
-        y1 = fmaf(qv, u[i].y, y1);
-        y2 = fmaf(qv, u[i].z, y2);
-        y3 = fmaf(qv, u[i].w, y3);
-      }
-#pragma unroll
-      for (int o = 1; o < 8; o <<= 1) {
-        y0 += __shfl_xor(y0, o, 64);
-        y1 += __shfl_xor(y1, o, 64);
-        y2 += __shfl_xor(y2, o, 64);
-        y3 += __shfl_xor(y3, o, 64);
-      }
-      if (k8 == 0) {
-        ys[grp][h][4 * c] = y0;
-        ys[grp][h][4 * c + 1] = y1;
-        ys[grp][h][4 * c + 2] = y2;
-        ys[grp][h][4 * c + 3] = y3;
-      }
-    }
-  }
-  for (int e = tid; e < nitems * 2 * 64 * 4; e += blockDim.x) ((uint32_t *)aq)[e] = 0;
-  __syncthreads();
-  for (int wi = w; wi < nitems * G; wi += nw) {
-    const int k = wi / G, h = wi % G;
-    float x0 = ys[k][h][lane], x1 = ys[k][h][lane + 64];
-#pragma unroll
-    for (int hs = 1; hs < 64; hs <<= 1) {
-      const float o0 = __shfl_xor(x0, hs, 64), o1 = __shfl_xor(x1, hs, 64);
-      x0 = (lane & hs) ? o0 - x0 : x0 + o0;
-      x1 = (lane & hs) ? o1 - x1 : x1 + o1;
-    }
-    ys[k][h][lane] = x0 + x1;
-    ys[k][h][lane + 64] = x0 - x1;
-    wave_lds_sync();
-    const float v0 = ys[k][h][bitrev7(lane)] * kInvSqrtDf;
-    const float v1 = ys[k][h][bitrev7(lane + 64)] * kInvSqrtDf;
-    float mx = fmaxf(fabsf(v0), fabsf(v1));
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-    const float delta = mx > 0.f ? mx / 32639.0f : 1.0f;
-    const int q0 = max(-32639, min(32639, (int)rintf(v0 / delta)));
-    const int q1 = max(-32639, min(32639, (int)rintf(v1 / delta)));
-    int s0 = q0, s1 = q1;
-    for (int o = 32; o > 0; o >>= 1) {
-      s0 += __shfl_xor(s0, o, 64);
-      s1 += __shfl_xor(s1, o, 64);
-    }
-    if (lane == 0) {
-      qc[k][h][0] = delta;
-      qc[k][h][1] = delta * (float)s0;   // |sum| < 2^24: exact
-      qc[k][h][2] = delta * (float)s1;
-      qc[k][h][3] = 0.f;
-    }
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int c = lane + 64 * half;
-      const int qi = half ? q1 : q0;
-      const int lo = (int)(int8_t)(qi & 0xFF);
-      const int hi = (qi - lo) >> 8;
-      const int kg = c >> 5, ks = (c >> 4) & 1, bb8 = (c >> 2) & 3, sb = c & 3;
-      const int g = c >> 6;
-      int8_t *base = (int8_t *)(aq[k] + ks * 64);
-      const int r = 4 * h + 2 * g;
-      base[(r + 16 * kg) * 16 + 4 * sb + bb8] = (int8_t)hi;
-      base[(r + 1 + 16 * kg) * 16 + 4 * sb + bb8] = (int8_t)lo;
     }
   }
   __syncthreads();
@@ -630,9 +531,16 @@ struct ScanSmem {
     float pw[kPageTokens][4];              // p * scale, p * zero (VALU)
     float tile[GH][kD];                    // BF16 tile probabilities, then its o
   };
+  struct EpiSmem {                         // split epilogue (one M-tile, after every wave's pages)
+    float zs[GH][kD];                      // history sum, bit-reversal permuted, then butterflied
+    float ot[GH][kD];                      // history sum in the original basis
+    float ob[GH][kD];                      // BF16 tile sum
+    float hm[GH], hl[GH], bm[GH], bl[GH];
+  };
   union {
     WaveScratch wave[NW];
     QSmem<MT, GH> q;                       // query preparation (before the scan)
+    EpiSmem e;
   };
   float qsum[GH][2];                       // VALU: per-group sums of q~
   float m[NW][MT * 4], l[NW][MT * 4], z[NW][MT * 4][2];
@@ -696,9 +604,8 @@ __device__ __forceinline__ void dma_page(uint64_t base, uint32_t lds, uint32_t l
   if (lane_off < 512u) dma_1k(base + 4096u, lds + 4096u, lane_off);
 }
 
-template <int GH, bool UVL = false>
+template <int GH>
 struct MergeSmem {
-  float uv[UVL ? kD : 1][kD];   // U_V of the KV head, staged by LDS DMA (UVL)
   float ml[kMaxParts * GH][2];  // (m, l) of partial p, head h at p * G + h: history splits, then BF16 tiles
   float wgt[kMaxParts][GH];     // merge weight of every partial
   float hs[GH][4];              // per head: history scale, tile scale, 1 / denominator
@@ -708,17 +615,29 @@ struct MergeSmem {
   alignas(16) float red[2][kMergeSlices * 4 * kD];   // per-slice sums (history, tiles)
 };
 
+// Plain merge of partials already in the original basis (see merge_plain).
+template <int GH>
+struct PlainMergeSmem {
+  float wgt[kMaxSplits][GH];
+  float inv[GH];
+  alignas(16) float red[kMergeSlices][GH * kD];
+};
+
 template <int MT, int GH, int NW, bool MFMA>
 union ScanUnion {
   ScanSmem<MT, GH, NW, MFMA> s;
   MergeSmem<GH> g;
+  PlainMergeSmem<GH> pm;
 };
 
 // BF16 window tiles: 16 tokens each, sink tiles first (kSinkTiles = sink / 16),
-// then the recent ring.  One wave computes one tile and writes its (m, l, o)
-// partial (log2 units, original basis) with coalesced stores.
+// then the recent ring.  One wave computes one tile: (m, l) per head (log2
+// units, row-uniform for head 4 q + i) and o = sum over the four token
+// phases of p V, staged in scratch[h][c] (original basis).  Returns the
+// number of valid tokens; with none, nothing is staged.
 template <int GH>
-__device__ void bf16_tile_partial(const DecArgs &a, int b, int kv, int u, float (*scratch)[kD], float *dst) {
+__device__ int bf16_tile_compute(const DecArgs &a, int b, int kv, int u, float (*scratch)[kD], float (&m)[4],
+                                 float (&l)[4]) {
   const PoolView &pv = a.pv;
   const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
   const int G = pv.hq / pv.hkv;
@@ -748,24 +667,19 @@ __device__ void bf16_tile_partial(const DecArgs &a, int b, int kv, int u, float 
     K = pv.recent_k + row;
     V = pv.recent_v + row;
   }
-  float m[4], l[4], o[GH][8];
-  if (valid > 0) {
-    v8bf Aq[4];
-    load_bf16_query(a.q + ((size_t)b * pv.hq + (size_t)kv * G) * kD, G, Aq);
-    bf16_tile<GH>(K, V, valid, G, Aq, pv.sm_scale * kLog2e, m, l, o, scratch);
-  } else {
+  if (valid == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       m[i] = -INFINITY;
       l[i] = 0.f;
     }
-#pragma unroll
-    for (int h = 0; h < GH; ++h) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) o[h][c] = 0.f;
-    }
+    return 0;
   }
-  // sum the four token phases, stage o in LDS, store coalesced
+  float o[GH][8];
+  v8bf Aq[4];
+  load_bf16_query(a.q + ((size_t)b * pv.hq + (size_t)kv * G) * kD, G, Aq);
+  bf16_tile<GH>(K, V, valid, G, Aq, pv.sm_scale * kLog2e, m, l, o, scratch);
+  // sum the four token phases and stage o in LDS
 #pragma unroll
   for (int h = 0; h < GH; ++h) {
     if (h < G) {
@@ -778,6 +692,17 @@ __device__ void bf16_tile_partial(const DecArgs &a, int b, int kv, int u, float 
       }
     }
   }
+  wave_lds_sync();
+  return valid;
+}
+
+// One BF16 tile as its own (m, l, o) partial, written with coherent stores.
+template <int GH>
+__device__ void bf16_tile_partial(const DecArgs &a, int b, int kv, int u, float (*scratch)[kD], float *dst) {
+  const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+  const int G = a.pv.hq / a.pv.hkv;
+  float m[4], l[4];
+  const int valid = bf16_tile_compute<GH>(a, b, kv, u, scratch, m, l);
   if (n == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -788,8 +713,48 @@ __device__ void bf16_tile_partial(const DecArgs &a, int b, int kv, int u, float 
       }
     }
   }
+  for (int e = lane; e < G * kD; e += 64)
+    st_coherent(dst + (size_t)(e / kD) * kPartStride + kPartO + e % kD, valid ? scratch[e / kD][e % kD] : 0.f);
   wave_lds_sync();
-  for (int e = lane; e < G * kD; e += 64) st_coherent(dst + (size_t)(e / kD) * kPartStride + kPartO + e % kD, scratch[e / kD][e % kD]);
+}
+
+// One BF16 tile folded into a wave's running BF16 state acc (LDS, one M-tile
+// of heads): acc[kAccO + 128 h + c] = o, acc[kAccM + h] = m (log2 units),
+// acc[kAccL + h] = l, online-softmax style.
+constexpr int kAccHist = 0, kAccO = 512, kAccM = 1024, kAccL = 1028, kAccTm = 1032, kAccTl = 1036, kAccFloats = 1040;
+template <int GH>
+__device__ void bf16_tile_fold(const DecArgs &a, int b, int kv, int u, float (*scratch)[kD], float *acc) {
+  static_assert(GH == 4, "one M-tile of heads");
+  const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+  const int G = a.pv.hq / a.pv.hkv;
+  float m[4], l[4];
+  if (bf16_tile_compute<GH>(a, b, kv, u, scratch, m, l) == 0) return;
+  if (n == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[kAccTm + 4 * q + i] = m[i];
+      acc[kAccTl + 4 * q + i] = l[i];
+    }
+  }
+  wave_lds_sync();
+  float al[4], be[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const float ma = acc[kAccM + h], mt = acc[kAccTm + h];
+    const float mx = fmaxf(ma, mt);   // finite: the tile has a valid token
+    al[h] = ma > -INFINITY ? exp2_fast(ma - mx) : 0.f;
+    be[h] = exp2_fast(mt - mx);
+    if (lane == h) {
+      acc[kAccL + h] = fmaf(acc[kAccL + h], al[h], acc[kAccTl + h] * be[h]);
+    }
+  }
+  wave_lds_sync();
+  if (lane < 4) acc[kAccM + lane] = fmaxf(acc[kAccM + lane], acc[kAccTm + lane]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int e = lane + 64 * j, h = e >> 7;
+    if (h < G) acc[kAccO + e] = fmaf(acc[kAccO + e], al[h], scratch[h][e & (kD - 1)] * be[h]);
+  }
   wave_lds_sync();
 }
 
@@ -1074,6 +1039,149 @@ __device__ void flush_partial(ScanSmem<MT, GH, NW, true> &sm, HistState<MT> &st,
   write_split_partial<MT, GH, NW, true>(sm, G, dst, true);
 }
 
+// End of a split for one M-tile of heads (G <= 4).  Each wave, once its
+// pages are done, stores its history state in its own (now idle) page
+// buffers, loads its share of U_V (the last 512 threads, one quarter row
+// each) and takes BF16 tiles from the workgroup's counter, folding them into
+// a running BF16 state next to its history state.  Then the workgroup
+// combines the waves, takes the history sum out of the rotated basis (bit
+// reversal, Walsh-Hadamard butterfly, U_V^T / sqrt(d): R_V^T is linear, so
+// applying it to every split's sum equals applying it once to the merged
+// sum) and adds the BF16 part.  With one split the output is written here;
+// otherwise one (m, l, o) partial in the original basis goes to dst.
+template <int GH, int NW>
+__device__ void split_epilogue(const DecArgs &a, int b, int kv, int split, ScanSmem<1, GH, NW, true> &sm,
+                               const HistState<1> &st, const MetaSteps &ms, DynPages *dp, float *dst) {
+  static_assert(GH == 4 && NW * 64 >= 512 + 256, "one M-tile of heads, 12 waves");
+  constexpr int NT = NW * 64;
+  const PoolView &pv = a.pv;
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, q = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = pv.hq / pv.hkv;
+  const int S = a.n_splits;
+  static_assert(sizeof(sm.pbuf[0]) >= kAccFloats * sizeof(float), "wave state fits in its page buffers");
+  float *reg = reinterpret_cast<float *>(&sm.pbuf[wave][0][0]);
+  // 1) this wave's history state: o = facc b_V + zero-point sums, per head q
+  {
+    const float l16 = row16_sum(st.lsum[0]);
+    const float z0 = row16_sum(st.z0[0]), z1 = row16_sum(st.z1[0]);
+    const float zz0 = fmaf(z0, ms.va, -ms.vtau * l16), zz1 = fmaf(z1, ms.va, -ms.vtau * l16);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) reg[kAccHist + q * kD + 16 * nt + n] = fmaf(st.facc[0][nt], ms.vb, nt < 4 ? zz0 : zz1);
+    if (n == 0) {
+      sm.m[wave][q] = st.mref[0];
+      sm.l[wave][q] = l16;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) reg[kAccO + lane + 64 * j] = 0.f;
+    if (lane < 4) {
+      reg[kAccM + lane] = -INFINITY;
+      reg[kAccL + lane] = 0.f;
+    }
+  }
+  // 2) U_V rows for step 5: thread t >= NT - 512 owns row (t - (NT - 512)) / 4,
+  // columns 32 ((t - (NT - 512)) % 4) .. + 32
+  const int ut = tid - (NT - 512);
+  const bool uown = ut >= 0;
+  const int krow = (uown ? ut : 0) >> 2, upart = (uown ? ut : 0) & 3;
+  float4 u[8];
+  if (uown) {
+    const float4 *urow = (const float4 *)(a.rv.U_V + ((size_t)kv * kD + krow) * kD + 32 * upart);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) u[i] = urow[i];
+  }
+  wave_lds_sync();
+  // 3) BF16 tiles u = split + S k, k < n_tiles, handed out as waves finish
+  const int n_tiles = split < a.n_chunks ? (a.n_chunks - 1 - split) / S + 1 : 0;
+  for (;;) {
+    int k = 0;
+    if (lane == 0) k = atomicAdd(&dp->next_tile, 1);
+    k = __builtin_amdgcn_readfirstlane(k);
+    if (k >= n_tiles) break;
+    bf16_tile_fold<GH>(a, b, kv, split + S * k, sm.wave[wave].tile, reg);
+  }
+  __syncthreads();
+  // 4) combine the waves (history: rotated basis, permuted for the butterfly)
+  for (int idx = tid; idx < G * kD; idx += NT) {
+    const int h = idx >> 7, c = idx & (kD - 1);
+    float M = -INFINITY, Mb = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      M = fmaxf(M, sm.m[w][h]);
+      Mb = fmaxf(Mb, reinterpret_cast<const float *>(&sm.pbuf[w][0][0])[kAccM + h]);
+    }
+    float o = 0.f, l = 0.f, ob = 0.f, lb = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float *rw = reinterpret_cast<const float *>(&sm.pbuf[w][0][0]);
+      const float mw = sm.m[w][h], mb = rw[kAccM + h];
+      if (mw > -INFINITY) {
+        const float sc = exp2_fast(mw - M);
+        o = fmaf(sc, rw[kAccHist + idx], o);
+        l = fmaf(sc, sm.l[w][h], l);
+      }
+      if (mb > -INFINITY) {
+        const float sc = exp2_fast(mb - Mb);
+        ob = fmaf(sc, rw[kAccO + idx], ob);
+        lb = fmaf(sc, rw[kAccL + h], lb);
+      }
+    }
+    sm.e.zs[h][bitrev7(c)] = o;   // (o P)[j] = o[bitrev(j)]
+    sm.e.ob[h][c] = ob;
+    if (c == 0) {
+      sm.e.hm[h] = M;
+      sm.e.hl[h] = l;
+      sm.e.bm[h] = Mb;
+      sm.e.bl[h] = lb;
+    }
+  }
+  __syncthreads();
+  // 5) Walsh-Hadamard butterfly per head (one wave each), then U_V^T
+  if (wave < G) {
+    float x0 = sm.e.zs[wave][lane], x1 = sm.e.zs[wave][lane + 64];
+    fwht_lane_stages(x0, x1, lane);
+    sm.e.zs[wave][lane] = x0 + x1;
+    sm.e.zs[wave][lane + 64] = x0 - x1;
+  }
+  __syncthreads();
+  if (uown) {
+    for (int h = 0; h < G; ++h) {
+      const float4 *zr = (const float4 *)(&sm.e.zs[h][32 * upart]);
+      float sa = 0.f, sb = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const float4 za = zr[i], zb = zr[i + 1];
+        sa = fmaf(za.x, u[i].x, fmaf(za.y, u[i].y, fmaf(za.z, u[i].z, fmaf(za.w, u[i].w, sa))));
+        sb = fmaf(zb.x, u[i + 1].x, fmaf(zb.y, u[i + 1].y, fmaf(zb.z, u[i + 1].z, fmaf(zb.w, u[i + 1].w, sb))));
+      }
+      float sum = sa + sb;
+      sum += lane_xor<1>(sum);
+      sum += lane_xor<2>(sum);
+      if (upart == 0) sm.e.ot[h][krow] = sum * kInvSqrtDf;
+    }
+  }
+  __syncthreads();
+  // 6) history and BF16 parts together
+  for (int idx = tid; idx < G * kD; idx += NT) {
+    const int h = idx >> 7, c = idx & (kD - 1);
+    const float Mh = sm.e.hm[h], Mb = sm.e.bm[h], Mt = fmaxf(Mh, Mb);
+    const float ah = Mh > -INFINITY ? exp2_fast(Mh - Mt) : 0.f;
+    const float ab = Mb > -INFINITY ? exp2_fast(Mb - Mt) : 0.f;
+    const float l = fmaf(ah, sm.e.hl[h], ab * sm.e.bl[h]);
+    const float o = fmaf(ah, sm.e.ot[h][c], ab * sm.e.ob[h][c]);
+    if (S == 1) {
+      a.out[((size_t)b * pv.hq + (size_t)kv * G + h) * kD + c] = l > 0.f ? o / l : 0.f;
+    } else {
+      float *d = dst + (size_t)h * kPartStride;
+      if (c == 0) {
+        st_coherent(d, Mt);
+        st_coherent(d + 1, l);
+      }
+      st_coherent(d + kPartO + c, o);
+    }
+  }
+}
+
 template <int MT, int GH, int NW, bool DYN>
 __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float *dst,
                               ScanSmem<MT, GH, NW, true> &sm, DynPages *dp) {
@@ -1105,7 +1213,8 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   // out dynamically
   const int npg_wg = pg1 - pg0;
   const bool long_scan = npg_wg >= 16 * NW;
-  const int early = long_scan ? 0 : 4;
+  // one M-tile of heads: every tile runs after the pages (split_epilogue)
+  const int early = (MT == 1 || long_scan) ? 0 : 4;
   const bool dyn = DYN && npg_wg >= 2 * NW * PF && npg_wg <= kDynMaxPages;
   // pages [pg0, pg0 + nfull) hold 64 tokens (only the history's last page can hold fewer)
   const int nfull = max(0, min(pg1, n_hist / kPageTokens) - pg0);
@@ -1121,16 +1230,15 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   }
   query_prep<MT, GH>(a, b, kv, sm.q, nullptr, [&] {
     bt_settle(pipe, tk, tv);
-    if (dyn) {   // published by the barrier that follows in the preparation
+    // published by the barrier that follows in the preparation
+    if (dp && tid == 0) dp->next_tile = early;   // tiles k < early run on waves 0..3 before their pages
+    if (dyn) {
 #pragma unroll
       for (int r = 0; r < kDynPer; ++r) {
         const int i = tid + r * 64 * NW;
         if (i < npg_wg) dp->bt[i] = dbt[r];
       }
-      if (tid == 0) {
-        dp->next_page = NW * PF;
-        dp->next_tile = early;   // tiles k < early run on waves 0..3 before their pages
-      }
+      if (tid == 0) dp->next_page = NW * PF;
     }
     if (wave >= 4) pipe_prologue(pipe, pv, lane);
   });
@@ -1150,7 +1258,7 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   // (The tile scratch overlaps the query scratch, which is dead after the
   // barrier above.)
   const int S = a.n_splits;
-  float *parts = a.part + (size_t)bh * (S + a.n_chunks) * G * kPartStride;
+  float *parts = a.part + (size_t)bh * a.n_parts * G * kPartStride;
   if (wave < 4) {
     const int u = split + S * (early - 1 - wave);
     if (wave < early && u < a.n_chunks)
@@ -1186,6 +1294,10 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
     pipe_scan<MT, NW, PF>(pipe, pv, n_hist, qo, st, wl, lane);
   }
   if (pipe.bad && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
+  if constexpr (MT == 1) {
+    split_epilogue<GH, NW>(a, b, kv, split, sm, st, ms, dp, dst);
+    return;
+  }
   if (dyn) {
     // this workgroup's tiles are u = split + S k, k < n_tiles; the counter
     // starts past the early ones
@@ -1268,9 +1380,9 @@ __device__ void run_scan_valu(const DecArgs &a, int b, int kv, int split, float 
 // partial.  The U_V rows are loaded once the partial loads are out, by
 // threads that do not compute the per-head weights, so that their latency
 // overlaps the weights and the weighted sums.
-template <int GH, int NT, bool UVL = false>
+template <int GH, int NT>
 __device__ void merge_item(const DecArgs &a, int b, int kv, const float *hist, int n_hist_parts, const float *tiles,
-                           int n_tile_parts, MergeSmem<GH, UVL> &sm) {
+                           int n_tile_parts, MergeSmem<GH> &sm) {
   // (head, channel quad) items per thread when each item takes all partials
   // (quads padded to whole waves)
   constexpr int kItems = ((GH * (kD / 4) + 63) / 64 * 64 + NT - 1) / NT;
@@ -1300,17 +1412,7 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *hist, i
   const bool uown = ut >= 0;
   const int krow = (ut >= 0 ? ut : 0) / kLPR, upart = (ut >= 0 ? ut : 0) % kLPR;
   const float4 *urow = (const float4 *)(a.rv.U_V + (size_t)kv * kD * kD + (size_t)krow * kD + kCPL * upart);
-  float4 u[UVL ? 1 : kCPL / 4];
-  if constexpr (UVL) {
-    // 64 KB of U_V into LDS, 1 KB per DMA copy, spread over the waves; the
-    // copies complete before step 4 reads them (explicit wait there).  They
-    // go first: the compiler's waits for the loads below cover them anyway.
-    const uint64_t src = (uint64_t)(uintptr_t)(a.rv.U_V + (size_t)kv * kD * kD);
-    const uint32_t dst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float *) & sm.uv[0][0];
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
-    for (int c = wv; c < kD * kD * 4 / 1024; c += nwaves) dma_1k(src + 1024u * c, dst + 1024u * c, 16u * lane);
-    asm volatile("" ::: "memory");
-  }
+  float4 u[kCPL / 4];
   // 1) one round of device-coherent loads: the first kPer partials of each
   // thread's slice (thread -> head, channel quad, slice; 16 bytes each) into
   // registers, and the (m, l) headers of every partial into LDS.  Further
@@ -1346,12 +1448,10 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *hist, i
   // U_V rows once every wave has issued its partial loads (the memory
   // pipeline serves a CU's loads in order, so earlier they would delay the
   // loads that step 2 waits for); they are needed only in step 4
-  if constexpr (!UVL) {
-    asm volatile("" ::: "memory");
-    if (uown) {
+  asm volatile("" ::: "memory");
+  if (uown) {
 #pragma unroll
-      for (int i = 0; i < kCPL / 4; ++i) u[i] = urow[i];
-    }
+    for (int i = 0; i < kCPL / 4; ++i) u[i] = urow[i];
   }
   // 2) per head: maxima, weights, denominators
   for (int h = wave; h < G; h += nwaves) {
@@ -1446,22 +1546,16 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *hist, i
   }
   __syncthreads();
   // 4) o_hist[h][k] = sum_j z[h][j] U_V[k][j] / sqrt(d)
-  if constexpr (UVL) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
   // two partial sums per head (independent FMA chains), then the kLPR
   // lanes of a row are added
   if (uown) {
-    const float4 *ul = (const float4 *)(&sm.uv[UVL ? krow : 0][kCPL * upart]);
     for (int h = 0; h < G; ++h) {
       const float4 *zr = (const float4 *)(&sm.zs[h][kCPL * upart]);
       float sa = 0.f, sb = 0.f;
 #pragma unroll
       for (int i = 0; i < kCPL / 4; i += 2) {
         const float4 za = zr[i], zb = zr[i + 1];
-        const float4 ua = UVL ? ul[i] : u[UVL ? 0 : i];
-        const float4 ub = UVL ? ul[i + 1] : u[UVL ? 0 : i + 1];
+        const float4 ua = u[i], ub = u[i + 1];
         sa = fmaf(za.x, ua.x, fmaf(za.y, ua.y, fmaf(za.z, ua.z, fmaf(za.w, ua.w, sa))));
         sb = fmaf(zb.x, ub.x, fmaf(zb.y, ub.y, fmaf(zb.z, ub.z, fmaf(zb.w, ub.w, sb))));
       }
@@ -1480,6 +1574,89 @@ __device__ void merge_item(const DecArgs &a, int b, int kv, const float *hist, i
   }
 }
 
+// Merge of the S partials of one (sequence, KV head) whose splits have
+// already left the rotated basis and folded in the BF16 tiles: a plain
+// log-sum-exp merge, by the last workgroup to finish.  Waves 0..G-1 form one
+// head's weights each; meanwhile every thread has its first kPer partial
+// loads (16 bytes each, device-coherent) in flight.
+template <int GH, int NT>
+__device__ void merge_plain(const DecArgs &a, int b, int kv, const float *parts, int S, PlainMergeSmem<GH> &sm) {
+  constexpr int kPer = 8;
+  const PoolView &pv = a.pv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = pv.hq / pv.hkv;
+  const int pstride = G * kPartStride;
+  const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(parts, (uint32_t)(S * pstride * 4));
+  // thread -> (head, channel quad) item of slice sl (quads padded to whole
+  // waves, so the slice is wave-uniform); slice sl takes partials sl + nsl j
+  const int nq = G * (kD / 4);
+  const int nqp = (nq + 63) & ~63;
+  const int nsl = min(kMergeSlices, max(1, NT / nqp));
+  const bool item = tid < nqp * nsl;
+  const int qd = tid % nqp;
+  const int sl = __builtin_amdgcn_readfirstlane(tid / nqp);
+  const bool act = item && qd < nq;
+  const int h = act ? qd >> 5 : 0, c = 4 * (qd & 31);
+  const uint32_t off = 4u * (uint32_t)(h * kPartStride + kPartO + c);
+  float4 v[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int p = sl + nsl * j;
+    v[j] = item && p < S ? ld_coherent4(rs, off, (uint32_t)(p * pstride * 4)) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (wave < G) {
+    float mx = -INFINITY;
+    float2 ml[kMaxSplits / 64];
+#pragma unroll
+    for (int r = 0; r < kMaxSplits / 64; ++r) {
+      const int p = lane + 64 * r;
+      ml[r] = p < S ? ld_coherent2(parts + (size_t)p * pstride + (size_t)wave * kPartStride) : make_float2(-INFINITY, 0.f);
+      mx = fmaxf(mx, ml[r].x);
+    }
+    mx = wave_max(mx);
+    float den = 0.f;
+#pragma unroll
+    for (int r = 0; r < kMaxSplits / 64; ++r) {
+      const int p = lane + 64 * r;
+      const float w = ml[r].x > -INFINITY ? exp2_fast(ml[r].x - mx) : 0.f;
+      if (p < S) sm.wgt[p][wave] = w;
+      den = fmaf(w, ml[r].y, den);
+    }
+    den = wave_sum(den);
+    if (lane == 0) sm.inv[wave] = den > 0.f ? 1.0f / den : 0.f;
+  }
+  __syncthreads();
+  if (item) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int p0 = 0; p0 < S; p0 += nsl * kPer) {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int p = p0 + sl + nsl * j;
+        if (p0 > 0)
+          v[j] = p < S ? ld_coherent4(rs, off, (uint32_t)(p * pstride * 4)) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int p = p0 + sl + nsl * j;
+        if (p < S) {
+          const float w = sm.wgt[p][h];
+          acc.x = fmaf(w, v[j].x, acc.x);
+          acc.y = fmaf(w, v[j].y, acc.y);
+          acc.z = fmaf(w, v[j].z, acc.z);
+          acc.w = fmaf(w, v[j].w, acc.w);
+        }
+      }
+    }
+    if (act) *(float4 *)(sm.red[sl] + h * kD + c) = acc;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * kD; idx += blockDim.x) {
+    float acc = 0.f;
+    for (int k = 0; k < nsl; ++k) acc += sm.red[k][idx];
+    a.out[((size_t)b * pv.hq + (size_t)kv * G) * kD + idx] = acc * sm.inv[idx / kD];
+  }
+}
+
 // Register budget: three waves per SIMD for one M-tile of heads (G <= 4), two
 // otherwise; the VALU reference takes what it needs.
 template <int MT, int GH, bool MFMA>
@@ -1494,7 +1671,7 @@ decode_scan_kernel(DecArgs a) {
   const int G = pv.hq / pv.hkv;
   const int wave = threadIdx.x >> 6;
   const int S = a.n_splits;
-  float *parts = a.part + (size_t)bh * (S + a.n_chunks) * G * kPartStride;
+  float *parts = a.part + (size_t)bh * a.n_parts * G * kPartStride;
   __shared__ ScanUnion<MT, GH, NW, MFMA> sm;
   if constexpr (!MFMA) {
     // BF16 tile u runs on workgroup u % S, wave (u / S) % NW, before its pages
@@ -1504,16 +1681,21 @@ decode_scan_kernel(DecArgs a) {
     }
   }
   float *dst = parts + (size_t)split * G * kPartStride;
+  __shared__ int last_flag;
   if constexpr (MFMA && MT == 1) {
+    // the split's partial leaves the rotated basis in the split itself; with
+    // one split the output is already written
     __shared__ DynPages dp;
     run_scan_mfma<MT, GH, NW, true>(a, b, kv, split, dst, sm.s, &dp);
+    if (S == 1 || !arrive_last(&a.counters[bh], S, &last_flag)) return;
+    merge_plain<GH, 64 * NW>(a, b, kv, parts, S, sm.pm);
+    return;
   } else if constexpr (MFMA) {
     // several M-tiles (8 waves, heavier pages): the static page order
     // measured faster on the GQA-12 shared-prefix workload
     run_scan_mfma<MT, GH, NW, false>(a, b, kv, split, dst, sm.s, nullptr);
   }
   else run_scan_valu<MT, GH, NW>(a, b, kv, split, dst, sm.s);
-  __shared__ int last_flag;
   if (S == 1) {
     // the only workgroup of its (sequence, KV head): no counter round trip,
     // only its own partial stores completed before any thread reads them
@@ -1526,213 +1708,6 @@ decode_scan_kernel(DecArgs a) {
 }
 
 
-// ===========================================================================
-// balanced scan (one M-tile of heads, MFMA): every workgroup takes an equal
-// share of all work units (per (sequence, KV head): n_tiles BF16 tiles, then
-// its history pages), computed on the device from seq_lens, so sequences of
-// different lengths load the workgroups evenly.  A workgroup's share splits
-// into segments, one per (sequence, KV head) it touches; each segment yields
-// one history partial (slot = workgroup + bh, unique and ordered) and the
-// tile partials of the tiles it covers.  The last contributor of a
-// (sequence, KV head) merges after its own segments are done.
-// ===========================================================================
-// The balanced scan is switched off: an earlier build of its page copies
-// faulted the device (a sign-extended source address, corrected in dma_1k),
-// and this corrected build has not yet been run on the device.  Every shape
-// takes the grid path meanwhile.
-constexpr bool kBalancedScan = false;
-constexpr int kFlatPrep = 3;     // segments whose query operands are prepared together
-constexpr int kFlatMaxSeg = 96;  // segments per workgroup
-constexpr int kFlatMaxBatch = 4096;
-
-struct FlatSeg {
-  int b, kv, t0, t1, p0, p1, first_blk, last_blk;
-};
-
-template <int GH, int NW>
-struct FlatPrep {
-  v4i aq[kFlatPrep][2 * 64];
-  float qc[kFlatPrep][4][4];
-};
-
-template <int GH, int NW>
-union FlatUnion {
-  ScanSmem<1, GH, NW, true> s;
-  MergeSmem<GH, true> g;
-};
-
-__device__ __forceinline__ int seq_pages(const PoolView &pv, int b) {
-  const int L = max(0, pv.seq_lens[b]);
-  const int nh = max(0, L - pv.sink - pv.recent);
-  return min((nh + kPageTokens - 1) / kPageTokens, pv.max_pages);
-}
-
-// workgroup i owns units [start(i), start(i + 1)), start(i) = i U / NB
-__device__ __forceinline__ long long flat_start(long long i, long long U, long long NB) { return i * U / NB; }
-__device__ __forceinline__ int flat_block_of(long long x, long long U, int NB) {
-  long long i = x * NB / U;
-  if (i > NB - 1) i = NB - 1;
-  while (i + 1 < NB && flat_start(i + 1, U, NB) <= x) ++i;
-  while (i > 0 && flat_start(i, U, NB) > x) --i;
-  return (int)i;
-}
-
-template <int GH>
-__global__ void __launch_bounds__((64 * scan_waves<1, true>())) __attribute__((amdgpu_waves_per_eu(3)))
-decode_flat_kernel(DecArgs a) {
-  constexpr int NW = scan_waves<1, true>();
-  constexpr int PF = ScanSmem<1, GH, NW, true>::PF;
-  const PoolView &pv = a.pv;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = pv.hq / pv.hkv, Hkv = pv.hkv, B = pv.batch, NT = a.n_chunks, NB = a.n_blocks;
-  __shared__ FlatUnion<GH, NW> sm;
-  __shared__ FlatPrep<GH, NW> prep;
-  __shared__ FlatSeg segs[kFlatMaxSeg];
-  __shared__ int seg_info[4];   // nseg, nmerge
-  __shared__ int merge_list[kFlatMaxSeg];
-  __shared__ int last_flag;
-  __shared__ int wtot[NW];
-
-  // 1) units per sequence and their prefix sums (LDS scratch in the wave area)
-  int *pre = (int *)&sm.s.wave[0];   // [B + 1]
-  static_assert(sizeof(sm.s.wave) >= (kFlatMaxBatch + 1) * sizeof(int), "prefix scratch");
-  {
-    int carry = 0;
-    for (int base = 0; base < B; base += blockDim.x) {
-      const int b = base + tid;
-      int v = 0;
-      if (b < B) {
-        v = Hkv * (NT + seq_pages(pv, b));
-        if (blockIdx.x == 0 && pv.err) {
-          const int L = max(0, pv.seq_lens[b]);
-          const int nh = max(0, L - pv.sink - pv.recent);
-          if ((nh + kPageTokens - 1) / kPageTokens > pv.max_pages) atomicOr(pv.err, OSCAR_DEVERR_LENGTH);
-        }
-      }
-      for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(v, o, 64);
-        if (lane >= o) v += t;
-      }
-      if (lane == 63) wtot[wave] = v;
-      __syncthreads();
-      int off = carry;
-      for (int w2 = 0; w2 < wave; ++w2) off += wtot[w2];
-      if (b < B) pre[b + 1] = v + off;
-      int tot = 0;
-      for (int w2 = 0; w2 < NW; ++w2) tot += wtot[w2];
-      carry += tot;
-      __syncthreads();
-    }
-    if (tid == 0) pre[0] = 0;
-    __syncthreads();
-  }
-  const long long U = pre[B];
-  // workgroups in use: every one of them owns at least one unit, so each
-  // workgroup in [first_blk, last_blk] of a (sequence, KV head) contributes
-  const int NBe = (int)min((long long)NB, U);
-  if ((int)blockIdx.x >= NBe) return;
-  const long long start = flat_start(blockIdx.x, U, NBe), end = flat_start(blockIdx.x + 1, U, NBe);
-  // 2) segments (thread 0)
-  if (tid == 0) {
-    int lo = 0, hi = B - 1;   // sequence b with pre[b] <= start < pre[b + 1]
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (pre[mid] <= start) lo = mid;
-      else hi = mid - 1;
-    }
-    int b = lo, n = 0;
-    long long x = start;
-    while (x < end && n < kFlatMaxSeg) {
-      const int ub = (pre[b + 1] - pre[b]) / Hkv;   // units of one (b, kv)
-      const int kv = (int)((x - pre[b]) / ub);
-      const long long u0 = pre[b] + (long long)kv * ub;   // first unit of (b, kv)
-      const int a0 = (int)(x - u0), a1 = (int)min((long long)ub, end - u0);
-      FlatSeg sg;
-      sg.b = b;
-      sg.kv = kv;
-      sg.t0 = min(a0, NT);
-      sg.t1 = min(a1, NT);
-      sg.p0 = max(a0, NT) - NT;
-      sg.p1 = max(a1, NT) - NT;
-      sg.first_blk = flat_block_of(u0, U, NBe);
-      sg.last_blk = flat_block_of(u0 + ub - 1, U, NBe);
-      segs[n++] = sg;
-      x = u0 + ub;
-      if (kv + 1 == Hkv) ++b;
-    }
-    seg_info[0] = n;
-    seg_info[1] = 0;
-  }
-  __syncthreads();
-  const int nseg = __builtin_amdgcn_readfirstlane(seg_info[0]);
-  const float sl2 = pv.sm_scale * kLog2e;
-
-  // 3) per segment: its page copies start, then (every kFlatPrep segments)
-  // the query operands of the next kFlatPrep segments are prepared side by
-  // side while the copies land
-  PagePipe<NW, PF> pipe;
-  v4i *wl = sm.s.wave[wave].wl;
-  for (int si = 0; si < nseg; ++si) {
-    FlatSeg sg = segs[si];
-    sg.b = __builtin_amdgcn_readfirstlane(sg.b);
-    sg.kv = __builtin_amdgcn_readfirstlane(sg.kv);
-    sg.t0 = __builtin_amdgcn_readfirstlane(sg.t0);
-    sg.t1 = __builtin_amdgcn_readfirstlane(sg.t1);
-    sg.p0 = __builtin_amdgcn_readfirstlane(sg.p0);
-    sg.p1 = __builtin_amdgcn_readfirstlane(sg.p1);
-    sg.first_blk = __builtin_amdgcn_readfirstlane(sg.first_blk);
-    sg.last_blk = __builtin_amdgcn_readfirstlane(sg.last_blk);
-    const int bh = sg.b * Hkv + sg.kv;
-    pipe_init(pipe, pv, sg.b, sg.kv, sg.p0, sg.p1, sm.s.pbuf[wave], wave, lane);
-    bt_settle(pipe);
-    pipe_prologue(pipe, pv, lane);
-    if (si % kFlatPrep == 0) {
-      int bb[kFlatPrep], kk[kFlatPrep];
-#pragma unroll
-      for (int k = 0; k < kFlatPrep; ++k) {
-        const int sk = min(si + k, nseg - 1);
-        bb[k] = __builtin_amdgcn_readfirstlane(segs[sk].b);
-        kk[k] = __builtin_amdgcn_readfirstlane(segs[sk].kv);
-      }
-      query_prep_multi<kFlatPrep>(a, bb, kk, min(nseg - si, kFlatPrep), (float(*)[4][kD]) & sm.s.wave[0],
-                                  prep.aq, prep.qc);
-    }
-    const int slot = si % kFlatPrep;
-    const MetaSteps ms = meta_steps(a.rv, sg.kv);
-    QueryOps<1> qo;
-    load_query_ops<1, GH>(prep.aq[slot], prep.qc[slot], G, sl2, ms, lane, qo);
-    __syncthreads();   // operands read; the wave scratch is reused below
-    // BF16 tiles of this segment, from the last wave down
-    float *tile_parts = a.part_tile + (size_t)bh * NT * G * kPartStride;
-    for (int t = sg.t0; t < sg.t1; ++t)
-      if (NW - 1 - (t - sg.t0) % NW == wave)
-        bf16_tile_partial<GH>(a, sg.b, sg.kv, t, sm.s.wave[wave].tile, tile_parts + (size_t)t * G * kPartStride);
-    HistState<1> st;
-    hist_reset(st);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) wl[i * 64 + lane] = v4i{0, 0, 0, 0};
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    const int L = max(0, pv.seq_lens[sg.b]);
-    pipe_scan<1, NW, PF>(pipe, pv, max(0, L - pv.sink - pv.recent), qo, st, wl, lane);
-    if (pipe.bad && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
-    flush_partial<1, GH, NW>(sm.s, st, G, ms, a.part + ((size_t)blockIdx.x + bh) * G * kPartStride);
-    if (arrive_last(&a.counters[bh], sg.last_blk - sg.first_blk + 1, &last_flag) && tid == 0)
-      merge_list[seg_info[1]++] = si;
-    __syncthreads();
-  }
-  // 4) merges of the (sequence, KV head) pairs this workgroup completed
-  const int nmerge = seg_info[1];
-  for (int mi = 0; mi < nmerge; ++mi) {
-    const FlatSeg sg = segs[merge_list[mi]];
-    const int bh = sg.b * Hkv + sg.kv;
-    merge_item<GH, 64 * NW, true>(a, sg.b, sg.kv, a.part + ((size_t)sg.first_blk + bh) * G * kPartStride,
-                            sg.last_blk - sg.first_blk + 1, a.part_tile + (size_t)bh * NT * G * kPartStride, NT,
-                            sm.g);
-    __syncthreads();
-  }
-}
-
 }  // namespace
 
 namespace {
@@ -1740,8 +1715,7 @@ namespace {
 int target_blocks(int blocks) { return blocks > 0 ? blocks : 256; }
 int mt_of(int G) { return (G + 3) / 4; }
 int gh_of(int G) { return 4 * mt_of(G); }
-// variant 0: MFMA scan (balanced partition where it applies, else grid);
-// 2: MFMA scan on the grid partition only; 1: VALU scan on the grid
+// variants 0 and 2: MFMA scan; 1: VALU scan
 bool is_mfma(int variant) { return variant != 1; }
 int nw_of(int G, int variant) { return !is_mfma(variant) ? 4 : (mt_of(G) == 1 ? 12 : 8); }
 }  // namespace
@@ -1754,27 +1728,6 @@ DecodePlan make_decode_plan(int batch, int hkv, int hq, int max_pages, int sink,
   const int bh = batch * hkv;
   p.n_chunks = (sink + recent) / kTileTokens;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  // balanced path: one M-tile of heads on the MFMA scan, bounded segments
-  const long long NB = target_blocks(blocks);
-  const long long units_max = (long long)bh * (p.n_chunks + max(max_pages, 0));
-  const long long seg_bound = (units_max / NB + 1 + p.n_chunks - 1) / p.n_chunks + 2;
-  p.flat = kBalancedScan && variant == 0 && MT == 1 && batch <= kFlatMaxBatch && seg_bound <= kFlatMaxSeg &&
-           NB + p.n_chunks <= kMaxParts && units_max < (1LL << 30);
-  size_t off = 0;
-  p.off_counters = off;
-  off = al(off + (size_t)bh * sizeof(int));
-  if (p.flat) {
-    p.n_blocks = (int)NB;
-    p.n_splits = 0;
-    p.pages_per_split = 0;
-    p.off_qconst = p.off_qrot = off;
-    p.off_part = off;
-    off = al(off + (size_t)(NB + bh) * G * kPartStride * sizeof(float));
-    p.off_tile = off;
-    off = al(off + (size_t)bh * p.n_chunks * G * kPartStride * sizeof(float));
-    p.total = off;
-    return p;
-  }
   int S = (target_blocks(blocks) + bh - 1) / bh;
   const int max_by_pages = max_pages > 0 ? (max_pages + NW - 1) / NW : 1;   // >= 1 page per wave
   S = S < 1 ? 1 : S;
@@ -1782,15 +1735,18 @@ DecodePlan make_decode_plan(int batch, int hkv, int hq, int max_pages, int sink,
   S = S > kMaxSplits ? kMaxSplits : S;
   S = S > kMaxParts - p.n_chunks ? kMaxParts - p.n_chunks : S;
   p.n_splits = S;
-  p.n_blocks = 0;
+  // one M-tile of heads on MFMA: one partial per split (BF16 tiles folded in)
+  p.n_parts = (is_mfma(variant) && MT == 1) ? S : S + p.n_chunks;
   p.pages_per_split = max_pages > 0 ? (max_pages + S - 1) / S : 1;
+  size_t off = 0;
+  p.off_counters = off;
+  off = al(off + (size_t)bh * sizeof(int));
   p.off_qconst = off;
-  off = al(off + (size_t)bh * GH * 4 * sizeof(float));
+  off = al(off + (is_mfma(variant) ? 0 : (size_t)bh * GH * 4 * sizeof(float)));
   p.off_qrot = off;
-  off = al(off + (size_t)bh * GH * kD * sizeof(float));
+  off = al(off + (is_mfma(variant) ? 0 : (size_t)bh * GH * kD * sizeof(float)));
   p.off_part = off;
-  off = al(off + (size_t)bh * (S + p.n_chunks) * G * kPartStride * sizeof(float));
-  p.off_tile = off;
+  off = al(off + (size_t)bh * p.n_parts * G * kPartStride * sizeof(float));
   p.total = off;
   return p;
 }
@@ -1800,14 +1756,10 @@ hipError_t launch_decode(const PoolView &pv, const RotView &rv, const uint16_t *
   const int G = pv.hq / pv.hkv;
   const int BH = pv.batch * pv.hkv;
   DecArgs a{pv, rv, q, out, counters, (float *)(ws + plan.off_qconst),
-            (float *)(ws + plan.off_qrot), (float *)(ws + plan.off_part), (float *)(ws + plan.off_tile),
-            plan.n_splits, plan.n_chunks, plan.pages_per_split, plan.n_blocks};
+            (float *)(ws + plan.off_qrot), (float *)(ws + plan.off_part),
+            plan.n_splits, plan.n_chunks, plan.pages_per_split, plan.n_parts};
   const bool mfma = is_mfma(variant);
   hipError_t e;
-  if (plan.flat) {
-    hipLaunchKernelGGL(decode_flat_kernel<4>, dim3(plan.n_blocks), dim3(64 * scan_waves<1, true>()), 0, s, a);
-    return hipGetLastError();
-  }
   const dim3 sgrid(BH * plan.n_splits);
 #define OSCAR_LAUNCH(MT, GH)                                                                         \
   do {                                                                                               \

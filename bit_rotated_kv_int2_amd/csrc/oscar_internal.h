@@ -110,16 +110,14 @@ struct RotView {
 
 // Decode workspace carve-up (offsets in bytes from the workspace base).
 struct DecodePlan {
-  int flat;              // balanced scan (one M-tile of heads, MFMA)
-  int n_blocks;          // balanced scan: workgroups
-  int n_splits;          // grid scan: history splits per (sequence, kv head)
+  int n_splits;          // history splits per (sequence, kv head)
+  int n_parts;           // partials per (sequence, kv head)
   int n_chunks;          // 16-token BF16 tiles (sink + recent window)
   int pages_per_split;
   size_t off_counters;   // int [B*Hkv] completion counters, zero between calls
-  size_t off_qconst;     // float [B*Hkv][GH][4]
-  size_t off_qrot;       // float [B*Hkv][GH][128]
-  size_t off_part;       // float partials (layout per path, see DecArgs)
-  size_t off_tile;       // balanced scan: float [B*Hkv][n_chunks][G][kPartStride]
+  size_t off_qconst;     // float [B*Hkv][GH][4] (VALU variant)
+  size_t off_qrot;       // float [B*Hkv][GH][128] (VALU variant)
+  size_t off_part;       // float partials [B*Hkv][n_parts][G][kPartStride]
   size_t total;
 };
 

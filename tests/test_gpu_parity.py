@@ -236,15 +236,12 @@ def test_decode_group_sizes(G):
     assert int(pool.error_flags.cpu()[0]) == 0
 
 
-@pytest.mark.skip(reason="balanced-partition scan switched off in the library: an earlier build of its "
-                         "page copies faulted the device (sign-extended DMA source address, corrected "
-                         "since) and the corrected build has not run on the device yet")
-def test_balanced_partition_ragged_batch():
+def test_ragged_batch_empty_and_short_sequences():
     """Sixteen sequences x eight KV heads (G = 4) of very different lengths
-    (empty, windows only, one partial page, up to 41 pages), pages scattered:
-    the balanced partition gives many workgroups two or three (sequence, KV
-    head) segments, and some segments tiles only.  Variant 0 (balanced) and
-    variant 2 (grid) must both match the oracle."""
+    (empty, windows only, one partial page, up to 41 pages), pages scattered,
+    two splits per (sequence, KV head): some splits have no pages, some only
+    BF16 tiles.  Every decode variant must match the oracle; empty sequences
+    give zeros."""
     wl = synth.Workload(91, "test-balanced", 16, 8, 32, 128, 0, 2950, n_cal=512, outliers="pairs10",
                         scattered_pages=True)
     cals = oracle_calibration(wl, n_cal=512)
@@ -260,7 +257,7 @@ def test_balanced_partition_ragged_batch():
         if lens[b]:
             append_sequence(params, rot, pool, b, kb, vb)
     q = synth.decode_queries(wl, 0)
-    for variant in (0, 2):
+    for variant in (0, 1, 2):
         out = _decode_gpu(params, rot, pool, q, variant)
         for b in range(wl.batch):
             if lens[b] == 0:
@@ -402,8 +399,11 @@ def test_bf16_baseline_decode(tiny):
 
 
 def test_decode_repeat_same_workspace(tiny):
-    """Consecutive decodes sharing one workspace give identical results (the
-    completion counters return to zero after every call)."""
+    """Consecutive decodes sharing one workspace all match the oracle and one
+    another (the completion counters return to zero after every call; a
+    counter left behind would skip or misplace a later call's merge).  The
+    BF16 tiles go to the waves of a workgroup in the order they finish their
+    pages, so repeats may differ in summation order only."""
     torch = _torch()
     wl, cals, rot, params, kb, vb, q = tiny
     pool = _fresh_pool(params, 59)
@@ -416,10 +416,13 @@ def test_decode_repeat_same_workspace(tiny):
         O.decode_attention(params, rot, pool, qt, out, ws)
         outs.append(out)
     torch.cuda.synchronize()
-    for o in outs[1:]:
-        assert torch.equal(o, outs[0])
     ref, _ = _oracle_decode(wl, cals, kb, vb, q[0])
-    assert decode_check(outs[0].cpu().numpy()[0], ref) <= TOL
+    first = outs[0].cpu().numpy()[0]
+    for o in outs:
+        o = o.cpu().numpy()[0]
+        assert decode_check(o, ref) <= TOL
+        assert decode_check(o, first) <= 1e-5
+
 
 
 @pytest.mark.parametrize("kind", ["naive", "clip", "hadamard"])
