@@ -268,6 +268,7 @@ def run_workload(wb, steps, warmup, decode_reps, bf16_fit=None):
 
     hist_mean_us = float(np.mean(hist_us))
     hist_bytes_mean = float(np.mean(hist_launch_bytes))
+    kv_elements = float(np.mean([np.sum(base + s + 1) for s in range(warmup, total)])) * wl.n_kv * D * 2
     return {
         "step_ms": step_ms,
         "wall_ms_per_step": wall * 1e3 / steps,
@@ -275,6 +276,7 @@ def run_workload(wb, steps, warmup, decode_reps, bf16_fit=None):
         "scan_kernel_us": hist_mean_us,
         "scan_kernel_us_p10_p90": [float(np.percentile(hist_us, 10)), float(np.percentile(hist_us, 90))],
         "scan_kernel_bytes": hist_bytes_mean,
+        "kv_elements": kv_elements,
         "scan_kernel_gbps": hist_bytes_mean / (hist_mean_us * 1e-6) / 1e9,
         "decode_us_per_layer": decode_us,
         "decode_gbps": decode_bytes / (decode_us * 1e-6) / 1e9,
@@ -365,18 +367,74 @@ def run_prefix(n_cal, write_reps=5, decode_reps=20):
 
 
 # ---------------------------------------------------------------------------
+# 32K context, batch 1: one decode step plus one single-token append
+# ---------------------------------------------------------------------------
+
+def run_32k(n_cal, reps=50):
+    """One layer of 32768 tokens, 8 KV / 32 query heads.  A single layer
+    (22 MB) stays in the 256 MB last-level cache across repeats, so these
+    are cache-warm figures: decode alone, the single-token append (one token
+    x 8 KV heads through the fused rotate-clip-quantise-pack-demote kernel)
+    alone, and the two back to back as one step."""
+    import torch
+    from bit_rotated_kv_int2_amd import oscar as O
+    from bit_rotated_kv_int2_amd import synth
+    wl = synth.WORKLOADS["qwen3-8b-32k-b1"]
+    params = O.make_params(wl.n_kv, wl.n_q)
+    rot = calibrate_layer(O, synth, wl, 0, params, n_cal)
+    lengths = synth.sequence_lengths(wl)
+    bt, total = synth.block_table(wl, lengths, 3 * reps + 8)
+    pool = O.KVPool(params, 1, total, bt, zero_pages=False)
+    k, v = gpu_kv(torch, synth, wl, 0, 0, int(lengths[0]))
+    O.quantize_append(params, rot, pool, k[None], v[None], seq=0)
+    del k, v
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4321)
+    kn = torch.randn((3 * reps + 2, 1, 1, wl.n_kv, D), generator=g, device="cuda").to(torch.bfloat16).view(torch.int16)
+    vn = torch.randn((3 * reps + 2, 1, 1, wl.n_kv, D), generator=g, device="cuda").to(torch.bfloat16).view(torch.int16)
+    q = torch.randn((1, wl.n_q, D), generator=g, device="cuda").to(torch.bfloat16).view(torch.int16).contiguous()
+    ws = O.alloc_workspace(O.decode_workspace_size(params, 1, pool.max_pages))
+    out = torch.zeros((1, wl.n_q, D), dtype=torch.float32, device="cuda")
+    O.decode_attention(params, rot, pool, q, out, ws)
+    O.quantize_append(params, rot, pool, kn[0].contiguous(), vn[0].contiguous())
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    e = [ev() for _ in range(6)]
+    e[0].record()
+    for _ in range(reps):
+        O.decode_attention(params, rot, pool, q, out, ws)
+    e[1].record()
+    for i in range(reps):
+        O.quantize_append(params, rot, pool, kn[1 + i].contiguous(), vn[1 + i].contiguous())
+    e[2].record()
+    for i in range(reps):
+        O.quantize_append(params, rot, pool, kn[1 + reps + i].contiguous(), vn[1 + reps + i].contiguous())
+        O.decode_attention(params, rot, pool, q, out, ws)
+    e[3].record()
+    torch.cuda.synchronize()
+    assert int(pool.error_flags.item()) == 0
+    dec_us = e[0].elapsed_time(e[1]) * 1e3 / reps
+    app_us = e[1].elapsed_time(e[2]) * 1e3 / reps
+    step_us = e[2].elapsed_time(e[3]) * 1e3 / reps
+    L = int(pool.seq_lens.item())
+    dec_bytes = (max(0, L - 320) * HIST_BYTES_PER_TOKEN_HEAD + min(L, 320) * WIN_BYTES_PER_TOKEN_HEAD) * wl.n_kv \
+        + wl.n_q * D * 4
+    return {"workload": wl.name, "context": L, "cache": "warm (one 22 MB layer fits the 256 MB last-level cache)",
+            "decode_us": dec_us, "decode_gbps": dec_bytes / (dec_us * 1e-6) / 1e9,
+            "append_one_token_us": app_us, "step_us": step_us}
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline: the oracle's decode on a bounded sample of the same workload
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(wl, pairs, reps):
+def _oracle_decode_times(wl, pairs, reps, host_kv=False):
+    """Wall seconds of `reps` oracle decodes of each (sequence, KV head) pair
+    at full length, and the algorithmic bytes those decodes stand for.  The
+    pool of each pair is built (oracle write path) outside the timed calls."""
     import torch
     from bit_rotated_kv_int2_amd import synth
     from oracle import oscar_ref as R
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
     lengths = synth.sequence_lengths(wl)
     G = wl.n_q // wl.n_kv
     q_all = synth.decode_queries(wl, 0)
@@ -385,10 +443,14 @@ def cpu_baseline(wl, pairs, reps):
     times, nbytes = [], 0
     for (b, h) in pairs:
         L = int(lengths[b])
-        k, v = gpu_kv(torch, synth, wl, 0, b, L)
-        kh = f(k[:, h].cpu().numpy().view(np.uint16)).astype(np.float64)
-        vh = f(v[:, h].cpu().numpy().view(np.uint16)).astype(np.float64)
-        del k, v
+        if host_kv:
+            kb, vb = synth.kv_tokens(wl, 0, b, 0, L)
+            kh, vh = f(kb[:, h]).astype(np.float64), f(vb[:, h]).astype(np.float64)
+        else:
+            k, v = gpu_kv(torch, synth, wl, 0, b, L)
+            kh = f(k[:, h].cpu().numpy().view(np.uint16)).astype(np.float64)
+            vh = f(v[:, h].cpu().numpy().view(np.uint16)).astype(np.float64)
+            del k, v
         cal = R.calibrate_head(f(qc[h * G:(h + 1) * G]), f(kc[h]), f(vc[h]), 1 / np.sqrt(D))
         pool = R.build_head_pool(kh, vh, cal)
         q = f(q_all[b, h * G:(h + 1) * G]).astype(np.float64)
@@ -397,13 +459,43 @@ def cpu_baseline(wl, pairs, reps):
             R.decode_head_dense(q, pool, cal, 1 / np.sqrt(D))
             times.append(time.perf_counter() - t0)
         nbytes += reps * (max(0, L - 320) * HIST_BYTES_PER_TOKEN_HEAD + min(L, 320) * WIN_BYTES_PER_TOKEN_HEAD)
+    return times, nbytes
+
+
+def cpu_baseline(wl, pairs, reps):
+    """The oracle (never tuned for speed) timed on the host cores, on a bounded
+    sample of the benchmark workload with every BLAS thread, then single
+    threaded, plus one-pair samples of the other decode workloads."""
+    from bit_rotated_kv_int2_amd import synth
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        blas_threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    except Exception:       # no thread control: numpy runs as configured
+        threadpool_limits, blas_threads = None, None
+    times, nbytes = _oracle_decode_times(wl, pairs, reps)
     total = float(np.sum(times))
-    return {"value": nbytes / total / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "seconds": total,
-            "us_per_head_decode": total / len(times) * 1e6,
-            "sample": f"oracle fp64 decode (dequantise + inverse-rotate + softmax attention) of "
-                      f"{len(pairs)} (sequence, KV head) pairs of {wl.name} at full length, "
-                      f"{reps} runs each; GB/s over the same algorithmic bytes as the GPU"}
+    out = {"value": nbytes / total / 1e9, "unit": "GB/s", "cores": blas_threads, "kind": "oracle",
+           "host_cpus": os.cpu_count(), "seconds": total,
+           "us_per_head_decode": total / len(times) * 1e6,
+           "sample": f"oracle fp64 decode (dequantise + inverse-rotate + softmax attention) of "
+                     f"{len(pairs)} (sequence, KV head) pairs of {wl.name} at full length, "
+                     f"{reps} runs each, {blas_threads} BLAS threads; GB/s over the same algorithmic "
+                     f"bytes as the GPU"}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            t1, b1 = _oracle_decode_times(wl, pairs[:2], 2)
+        out["single_thread"] = {"value": b1 / float(np.sum(t1)) / 1e9, "unit": "GB/s", "cores": 1,
+                                "us_per_head_decode": float(np.mean(t1)) * 1e6,
+                                "sample": f"2 pairs of {wl.name}, 2 runs each, one thread"}
+    others = {}
+    for name, host in (("tiny-4k", True), ("qwen3-8b-32k-b1", False), ("qwen3-8b-100k-b1-36l", False)):
+        w = synth.WORKLOADS[name]
+        prs = [(0, 0)] if w.n_kv == 1 else [(0, 0), (0, 3)]
+        t, nb = _oracle_decode_times(w, prs, 5 if w.max_len > 10000 else 20, host_kv=host)
+        others[name] = {"us_per_head_decode": float(np.mean(t)) * 1e6, "gbps": nb / float(np.sum(t)) / 1e9,
+                        "pairs": len(prs)}
+    out["other_workloads"] = others
+    return out
 
 
 def effective_bpe(L, sink=64, recent=256, history_bits=2.0 + 16.0 / 64):
@@ -516,6 +608,11 @@ def main():
         del wb1
         torch.cuda.empty_cache()
 
+    ctx32k = None
+    if not args.no_batch1:
+        ctx32k = run_32k(args.n_cal)
+        log(f"32k: {json.dumps(ctx32k)}")
+
     prefix = None
     if not args.no_prefix:
         prefix = run_prefix(args.n_cal)
@@ -527,11 +624,13 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        # about 15 s of oracle decode: 8 (sequence, KV head) pairs at full length, 20 runs each
+        # about 7 s of oracle decode: 8 (sequence, KV head) pairs at full length, 10 runs each,
+        # then a few seconds single threaded and on the other decode workloads
         pairs = ([(b, (3 * b) % wl.n_kv) for b in range(8)] if wl.batch >= 8 else
                  [(0, h) for h in range(min(8, wl.n_kv))])
-        cpu = cpu_baseline(wl, pairs, reps=20)
+        cpu = cpu_baseline(wl, pairs, reps=10)
 
+    traffic = measured_traffic(wl.name)
     line = {
         "metric": METRIC,
         "value": r["value_gbps"],
@@ -556,7 +655,10 @@ def main():
         "decode_frac_of_peak": r["decode_gbps"] / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "kernel": "decode_scan_kernel (split-K INT2 history + BF16 windows + merge)",
                      "achieved": r["scan_kernel_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": r["scan_kernel_gbps"] / HBM_PEAK_GBPS, "traffic": measured_traffic(wl.name),
+                     "frac": r["scan_kernel_gbps"] / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kv_elements_per_launch": r["kv_elements"],
+                     "algorithmic_bytes_per_kv_element": r["scan_kernel_bytes"] / r["kv_elements"],
+                     "fetched_bytes_per_kv_element": (None if traffic is None else traffic / r["kv_elements"]),
                      "bytes_per_launch": r["scan_kernel_bytes"], "us_per_launch": r["scan_kernel_us"],
                      "us_p10_p90": r["scan_kernel_us_p10_p90"],
                      "stream_read_ceiling_gbps": ceiling["gbps"],
@@ -571,6 +673,7 @@ def main():
         "effective_bits_per_kv_element": round(effective_bpe(float(np.mean(synth.sequence_lengths(wl)))), 4),
         "pages_bits_per_kv_element": 2.28,
         "batch1": batch1,
+        "ctx32k_batch1": ctx32k,
         "long_prefix": prefix,
         "cpu_baseline": cpu,
     }

@@ -120,6 +120,9 @@ def kv_tokens(wl: Workload, layer: int, seq: int, start: int, count: int):
     Returns (k_bits, v_bits) uint16 [count, n_kv, head_dim].  Tokens are drawn
     in fixed blocks of 1024 positions so any sub-range is reproducible.
     """
+    if count <= 0:
+        empty = np.zeros((0, wl.n_kv, wl.head_dim), np.uint16)
+        return empty, empty.copy()
     out = []
     for tensor, stream in ((0, STREAM_K), (1, STREAM_V)):
         sc = outlier_scale(wl, layer, tensor)
