@@ -181,6 +181,38 @@ int32_t oscar_decode_attention(const oscar_params *p, const oscar_rotation *rot,
   return ok();
 }
 
+int32_t oscar_decode_attention_noalloc(const oscar_params *p, const oscar_rotation *rot,
+                                       const oscar_kv_pool *pool, const uint16_t *q, float *out,
+                                       const oscar_decode_options *opts, void *stream) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if ((rc = check_rot(rot)) || (rc = check_pool(p, pool))) return rc;
+  oscar_decode_options o;
+  if ((rc = check_opts(opts, &o))) return rc;
+  if (!q || !out) return fail(OSCAR_EINVAL, "q/out is NULL");
+  if (misaligned(q) || misaligned(out)) return fail(OSCAR_EINVAL, "q/out must be 16-byte aligned");
+  const oscar::DecodePlan plan = oscar::make_decode_plan(pool->batch, p->num_kv_heads, p->num_q_heads,
+                                                          pool->max_pages, p->sink, p->recent, o.variant, o.blocks);
+  // the plan's counters go to the buffer's counter region, everything after
+  // them (from off_qconst on) to the rest of the buffer
+  const size_t counters = (size_t)pool->batch * p->num_kv_heads * sizeof(int);
+  const size_t cbytes = oscar::noalloc_counter_bytes();
+  const size_t rest = plan.total - plan.off_qconst;
+  if (counters > cbytes || rest > (size_t)OSCAR_NOALLOC_SCRATCH_BYTES - cbytes)
+    return fail(OSCAR_EWORKSPACE,
+                "no-alloc decode needs %zu counter bytes and %zu scratch bytes; the library holds %zu and %zu",
+                counters, rest, cbytes, (size_t)OSCAR_NOALLOC_SCRATCH_BYTES - cbytes);
+  uint8_t *base = nullptr;
+  hipError_t e = oscar::noalloc_scratch((hipStream_t)stream, &base);
+  if (e != hipSuccess) return fail(OSCAR_EHIP, "no-alloc decode buffer: %s", hipGetErrorString(e));
+  oscar::PoolView pv = make_pv(p, pool);
+  oscar::RotView rv{rot->U_K, rot->U_V, rot->tau_K, rot->tau_V};
+  e = oscar::launch_decode(pv, rv, q, out, base + cbytes - plan.off_qconst, (int *)base, plan, o.variant,
+                           (hipStream_t)stream);
+  if (e != hipSuccess) return fail(OSCAR_EHIP, "decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t oscar_bf16_decode_workspace_size(const oscar_params *p, int32_t batch, int32_t max_pages) {
   if (check_params(p) || batch < 1 || max_pages < 0) return 0;
   return oscar::make_bf16_plan(batch, p->num_kv_heads, p->num_q_heads, max_pages).total;

@@ -33,6 +33,8 @@
 //           than a factor 2, so no per-page max or scale reduction is needed.
 //   Codes enter unscaled: the zero point is added as z * sum(q) (logits) and
 //   sum(p * z) (values).
+#include <mutex>
+
 #include "oscar_wave.h"
 
 namespace oscar {
@@ -1780,6 +1782,51 @@ hipError_t launch_decode(const PoolView &pv, const RotView &rv, const uint16_t *
   else OSCAR_LAUNCH(4, 16);
 #undef OSCAR_LAUNCH
   return hipGetLastError();
+}
+
+// ===========================================================================
+// Decode without a caller-provided workspace
+// ===========================================================================
+namespace {
+// The buffer of oscar_decode_attention_noalloc, one per GPU for the life of
+// the process.  [0, kNoAllocCounterBytes) holds the completion counters
+// only: zero when the code object is loaded, cleared once more by the first
+// call on each device, and returned to zero by every call; the rest holds
+// the query operands and partials of the current call.
+constexpr size_t kNoAllocCounterBytes = 64 * 1024;
+static_assert(OSCAR_NOALLOC_SCRATCH_BYTES % 256 == 0 && OSCAR_NOALLOC_SCRATCH_BYTES > kNoAllocCounterBytes, "");
+__device__ __align__(256) uint8_t scratch[OSCAR_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t *g_scratch[kMaxDevices] = {};   // device address of `scratch` per device, once known
+
+__global__ void __launch_bounds__(256) zero_words_kernel(uint32_t *p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+}  // namespace
+
+size_t noalloc_counter_bytes() { return kNoAllocCounterBytes; }
+
+hipError_t noalloc_scratch(hipStream_t s, uint8_t **base) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    // the array's name is a host-side stand-in: only this address may be
+    // passed to kernels or copies
+    void *ptr = nullptr;
+    if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    hipLaunchKernelGGL(zero_words_kernel, dim3(16), dim3(256), 0, s, (uint32_t *)ptr,
+                       (int)(kNoAllocCounterBytes / 4));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    g_scratch[dev] = (uint8_t *)ptr;
+  }
+  *base = g_scratch[dev];
+  return hipSuccess;
 }
 
 }  // namespace oscar

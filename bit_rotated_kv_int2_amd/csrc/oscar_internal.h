@@ -132,6 +132,12 @@ hipError_t launch_append(const PoolView &pv, const RotView &rv, const uint16_t *
 // (ws + plan.off_counters for a caller's workspace).
 hipError_t launch_decode(const PoolView &pv, const RotView &rv, const uint16_t *q, float *out,
                          uint8_t *ws, int *counters, const DecodePlan &plan, int variant, hipStream_t s);
+// Device address of the library's own decode buffer on the current device
+// (OSCAR_NOALLOC_SCRATCH_BYTES): counters in the first noalloc_counter_bytes(),
+// the rest free for one call's query operands and partials.  The first call
+// on a device looks the address up and enqueues a clear of the counters on s.
+hipError_t noalloc_scratch(hipStream_t s, uint8_t **base);
+size_t noalloc_counter_bytes();
 
 struct Bf16View {
   const uint16_t *k_pages, *v_pages;

@@ -29,6 +29,7 @@ EXPORTED = [
     "oscar_calibrate_rotation", "oscar_quantize_append", "oscar_decode_attention",
     "oscar_decode_workspace_size", "oscar_bf16_decode_attention",
     "oscar_bf16_decode_workspace_size", "oscar_last_error", "oscar_version",
+    "oscar_decode_attention_noalloc",
 ]
 
 
@@ -96,6 +97,8 @@ def lib():
     L.oscar_decode_attention.argtypes = [P(Params), P(Rotation), P(KVPoolC), vp, vp, P(DecodeOptions), vp, sz, vp]
     L.oscar_decode_attention.restype = i32
     L.oscar_decode_workspace_size.argtypes = [P(Params), i32, i32, P(DecodeOptions)]
+    L.oscar_decode_attention_noalloc.argtypes = [P(Params), P(Rotation), P(KVPoolC), vp, vp, P(DecodeOptions), vp]
+    L.oscar_decode_attention_noalloc.restype = i32
     L.oscar_decode_workspace_size.restype = sz
     L.oscar_bf16_decode_attention.argtypes = [P(Params), P(Bf16CacheC), vp, vp, vp, sz, vp]
     L.oscar_bf16_decode_attention.restype = i32
@@ -272,6 +275,17 @@ def decode_attention(params: Params, rot: RotationTensors, pool: KVPool, q, out,
     _check(lib().oscar_decode_attention(ctypes.byref(params), ctypes.byref(r), ctypes.byref(pc), _ptr(q),
                                         _ptr(out), ctypes.byref(opts), _ptr(workspace), workspace.numel(),
                                         _stream_ptr(stream)))
+
+
+def decode_attention_noalloc(params: Params, rot: RotationTensors, pool: KVPool, q, out, stream=None,
+                             variant: int = 0, blocks: int = 0):
+    """As decode_attention, on the library's own per-GPU buffer instead of a
+    workspace (no allocation; calls that overlap on one GPU race)."""
+    assert q.is_contiguous() and out.is_contiguous() and q.element_size() == 2
+    r, pc = rot.c(), pool.c()
+    opts = decode_options(variant, blocks)
+    _check(lib().oscar_decode_attention_noalloc(ctypes.byref(params), ctypes.byref(r), ctypes.byref(pc), _ptr(q),
+                                                _ptr(out), ctypes.byref(opts), _stream_ptr(stream)))
 
 
 class Bf16Cache:

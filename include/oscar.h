@@ -230,6 +230,27 @@ size_t oscar_decode_workspace_size(const oscar_params *p, int32_t batch, int32_t
                                    const oscar_decode_options *opts);
 
 /*
+ * oscar_decode_attention without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, results and
+ * errors as oscar_decode_attention with the same options; it calls no
+ * allocating routine.  Instead of a workspace it uses a buffer the library
+ * holds in each GPU's memory for the life of the process,
+ * OSCAR_NOALLOC_SCRATCH_BYTES bytes: the first 64 KiB hold completion
+ * counters (at most 16384 sequence x KV-head pairs), the rest one call's
+ * query operands and partials, i.e. oscar_decode_workspace_size(...) minus
+ * the counters.  Larger shapes are rejected with OSCAR_EWORKSPACE before
+ * anything is launched.  Every call on one GPU shares that GPU's buffer, so
+ * calls that overlap on one GPU (different streams or threads without
+ * ordering) race; calls ordered on one stream do not.  The first call on a
+ * device enqueues a clear of the counters on `stream` before its decode.
+ */
+#define OSCAR_NOALLOC_SCRATCH_BYTES (32u << 20)
+int32_t oscar_decode_attention_noalloc(const oscar_params *p, const oscar_rotation *rot,
+                                       const oscar_kv_pool *pool, const uint16_t *q, float *out,
+                                       const oscar_decode_options *opts, void *stream);
+
+/*
  * In-house BF16 decode baseline on a paged all-BF16 cache (the comparison
  * every speedup is quoted against): k_pages, v_pages bf16
  * [n_pages][Hkv][64][d]; token position t of sequence b lives in page
