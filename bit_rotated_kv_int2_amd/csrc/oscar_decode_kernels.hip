@@ -525,6 +525,17 @@ constexpr int scan_waves() { return MFMA ? (MT == 1 ? 12 : 8) : 4; }
 template <int MT>
 constexpr int scan_prefetch() { return 2; }
 
+// A running BF16 state (LDS, one M-tile of heads) is o[128 h + c] and 16
+// floats st: m[h] (log2 units) at st[h], l[h] at st[4 + h], and a tile's m
+// and l staged at st[8 + h], st[12 + h].  A wave's page buffers hold, once
+// its pages are done, its history state at kAccHist, a BF16 state at kAccO
+// (o) and kAccM (st).
+constexpr int kAccHist = 0, kAccO = 512, kAccM = 1024, kAccFloats = 1040;
+constexpr int kStM = 0, kStL = 4, kStTm = 8, kStTl = 12;
+// Waves that run the BF16 tiles of a long scan before their pages, each into
+// a BF16 state of its own outside the page buffers.
+constexpr int kTileWaves = 4;
+
 template <int MT, int GH, int NW, bool MFMA>
 struct ScanSmem {
   static constexpr int PF = MFMA ? scan_prefetch<MT>() : 1;
@@ -551,6 +562,7 @@ struct ScanSmem {
     float o[NW][MT * 4][kD];                          // per-wave value sums (after it)
   };
   float vacc[MFMA ? 1 : NW][GH][64][2];    // VALU: per-wave running sums
+  float tacc[MFMA && MT == 1 ? kTileWaves : 1][kD * 4 + 16];   // BF16 states of the tile waves (long scans)
 };
 
 // Page copies into LDS are issued as inline assembly so that the compiler
@@ -633,28 +645,32 @@ union ScanUnion {
 };
 
 // BF16 window tiles: 16 tokens each, sink tiles first (kSinkTiles = sink / 16),
-// then the recent ring.  One wave computes one tile: (m, l) per head (log2
-// units, row-uniform for head 4 q + i) and o = sum over the four token
-// phases of p V, staged in scratch[h][c] (original basis).  Returns the
-// number of valid tokens; with none, nothing is staged.
-template <int GH>
-__device__ int bf16_tile_compute(const DecArgs &a, int b, int kv, int u, float (*scratch)[kD], float (&m)[4],
-                                 float (&l)[4]) {
-  const PoolView &pv = a.pv;
-  const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
-  const int G = pv.hq / pv.hkv;
-  const int L = max(0, pv.seq_lens[b]);
-  const int n_sink_tiles = pv.sink / kTileTokens;
-  const int slot = pv.sink_slot[b];
-  const bool slot_ok = slot >= 0 && slot < pv.n_sink_slots;
+// then the recent ring.  tile_source gives tile u's K and V rows and its
+// number of valid tokens (0: nothing to do).
+struct TileSrc {
   const uint16_t *K, *V;
   int valid;
-  if (u < n_sink_tiles) {
+};
+// A sequence's length and sink slot, loaded once for all its tiles (each
+// tile's row loads then cost one memory round trip, not two).
+struct TileCtx {
+  int L, slot;
+};
+__device__ __forceinline__ TileCtx tile_ctx(const PoolView &pv, int b) {
+  return TileCtx{max(0, pv.seq_lens[b]), pv.sink_slot[b]};
+}
+__device__ __forceinline__ void tile_source(const PoolView &pv, const TileCtx &tc, int b, int kv, int u, TileSrc &t) {
+  const int lane = threadIdx.x & 63;
+  const int L = tc.L;
+  const int n_sink_tiles = pv.sink / kTileTokens;
+  const bool sink_tile = u < n_sink_tiles;
+  size_t row;
+  if (sink_tile) {
+    const int slot = tc.slot;
+    const bool slot_ok = slot >= 0 && slot < pv.n_sink_slots;
     if (!slot_ok && L > 0 && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_SINKSLOT);
-    valid = slot_ok ? max(0, min(kTileTokens, min(L, pv.sink) - u * kTileTokens)) : 0;
-    const size_t row = (((size_t)max(slot, 0) * pv.hkv + kv) * pv.sink + (size_t)u * kTileTokens) * kD;
-    K = pv.sink_k + row;
-    V = pv.sink_v + row;
+    t.valid = slot_ok ? max(0, min(kTileTokens, min(L, pv.sink) - u * kTileTokens)) : 0;
+    row = (((size_t)max(slot, 0) * pv.hkv + kv) * pv.sink + (size_t)u * kTileTokens) * kD;
   } else {
     // recent ring: valid slots are [a0, a0 + nr) mod W, a prefix of every
     // tile (a0 is 0 mod 64 while the ring is filling; all slots once full)
@@ -664,24 +680,29 @@ __device__ int bf16_tile_compute(const DecArgs &a, int b, int kv, int u, float (
     const int lo = (u - n_sink_tiles) * kTileTokens, hi = lo + kTileTokens;
     const int e1 = min(a0 + nr, pv.recent);
     const int e2 = max(0, a0 + nr - pv.recent);
-    valid = max(0, min(hi, e1) - max(lo, a0)) + max(0, min(hi, e2) - lo);
-    const size_t row = (((size_t)b * pv.hkv + kv) * pv.recent + lo) * kD;
-    K = pv.recent_k + row;
-    V = pv.recent_v + row;
+    t.valid = max(0, min(hi, e1) - max(lo, a0)) + max(0, min(hi, e2) - lo);
+    row = (((size_t)b * pv.hkv + kv) * pv.recent + lo) * kD;
   }
-  if (valid == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      m[i] = -INFINITY;
-      l[i] = 0.f;
-    }
-    return 0;
-  }
+  // the four base pointers are first pinned in scalar registers: a choice
+  // between the struct fields themselves was compiled into an indexed copy
+  // of the struct in scratch memory, one more memory round trip per tile
+  uint64_t sk = (uint64_t)(uintptr_t)pv.sink_k, sv = (uint64_t)(uintptr_t)pv.sink_v;
+  uint64_t rk = (uint64_t)(uintptr_t)pv.recent_k, rv = (uint64_t)(uintptr_t)pv.recent_v;
+  asm volatile("" : "+s"(sk), "+s"(sv), "+s"(rk), "+s"(rv));
+  t.K = reinterpret_cast<const uint16_t *>(sink_tile ? sk : rk) + row;
+  t.V = reinterpret_cast<const uint16_t *>(sink_tile ? sv : rv) + row;
+}
+
+// One wave computes one tile from its loaded rows: (m, l) per head (log2
+// units, row-uniform for head 4 q + i) and o = sum over the four token
+// phases of p V, staged in scratch[h][c] (original basis).
+template <int GH>
+__device__ __forceinline__ void bf16_tile_finish(const DecArgs &a, const TileRegs &r, int valid, const v8bf (&Aq)[4],
+                                 float (*scratch)[kD], float (&m)[4], float (&l)[4]) {
+  const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
+  const int G = a.pv.hq / a.pv.hkv;
   float o[GH][8];
-  v8bf Aq[4];
-  load_bf16_query(a.q + ((size_t)b * pv.hq + (size_t)kv * G) * kD, G, Aq);
-  bf16_tile<GH>(K, V, valid, G, Aq, pv.sm_scale * kLog2e, m, l, o, scratch);
-  // sum the four token phases and stage o in LDS
+  bf16_tile_math<GH>(r, valid, G, Aq, a.pv.sm_scale * kLog2e, m, l, o, scratch);
 #pragma unroll
   for (int h = 0; h < GH; ++h) {
     if (h < G) {
@@ -695,16 +716,40 @@ __device__ int bf16_tile_compute(const DecArgs &a, int b, int kv, int u, float (
     }
   }
   wave_lds_sync();
-  return valid;
+}
+
+// The same for tile u, loads included; returns its number of valid tokens
+// (with none, m = -inf, l = 0 and nothing is staged).
+template <int GH>
+__device__ __forceinline__ int bf16_tile_compute(const DecArgs &a, const TileCtx &tc, int b, int kv, int u,
+                                                 float (*scratch)[kD], float (&m)[4], float (&l)[4]) {
+  const PoolView &pv = a.pv;
+  TileSrc t;
+  tile_source(pv, tc, b, kv, u, t);
+  if (t.valid == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m[i] = -INFINITY;
+      l[i] = 0.f;
+    }
+    return 0;
+  }
+  TileRegs r;
+  bf16_tile_load(t.K, t.V, t.valid, r);
+  v8bf Aq[4];
+  load_bf16_query(a.q + ((size_t)b * pv.hq + (size_t)kv * (pv.hq / pv.hkv)) * kD, pv.hq / pv.hkv, Aq);
+  bf16_tile_finish<GH>(a, r, t.valid, Aq, scratch, m, l);
+  return t.valid;
 }
 
 // One BF16 tile as its own (m, l, o) partial, written with coherent stores.
 template <int GH>
-__device__ void bf16_tile_partial(const DecArgs &a, int b, int kv, int u, float (*scratch)[kD], float *dst) {
+__device__ void bf16_tile_partial(const DecArgs &a, const TileCtx &tc, int b, int kv, int u, float (*scratch)[kD],
+                                  float *dst) {
   const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
   const int G = a.pv.hq / a.pv.hkv;
   float m[4], l[4];
-  const int valid = bf16_tile_compute<GH>(a, b, kv, u, scratch, m, l);
+  const int valid = bf16_tile_compute<GH>(a, tc, b, kv, u, scratch, m, l);
   if (n == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -720,44 +765,49 @@ __device__ void bf16_tile_partial(const DecArgs &a, int b, int kv, int u, float 
   wave_lds_sync();
 }
 
-// One BF16 tile folded into a wave's running BF16 state acc (LDS, one M-tile
-// of heads): acc[kAccO + 128 h + c] = o, acc[kAccM + h] = m (log2 units),
-// acc[kAccL + h] = l, online-softmax style.
-constexpr int kAccHist = 0, kAccO = 512, kAccM = 1024, kAccL = 1028, kAccTm = 1032, kAccTl = 1036, kAccFloats = 1040;
+
+// Fold a tile staged by bf16_tile_finish (m, l per head, o in scratch) into
+// the running state (o, st), online-softmax style.
 template <int GH>
-__device__ void bf16_tile_fold(const DecArgs &a, int b, int kv, int u, float (*scratch)[kD], float *acc) {
+__device__ __forceinline__ void bf16_fold_staged(int G, const float (&m)[4], const float (&l)[4], float (*scratch)[kD],
+                                                 float *o, float *st) {
   static_assert(GH == 4, "one M-tile of heads");
-  const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
-  const int G = a.pv.hq / a.pv.hkv;
-  float m[4], l[4];
-  if (bf16_tile_compute<GH>(a, b, kv, u, scratch, m, l) == 0) return;
-  if (n == 0) {
+  const int lane = threadIdx.x & 63;
+  // heads 0..3 are the C rows of lane group 0 (the other rows are padding)
+  if (lane == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc[kAccTm + 4 * q + i] = m[i];
-      acc[kAccTl + 4 * q + i] = l[i];
+      st[kStTm + i] = m[i];
+      st[kStTl + i] = l[i];
     }
   }
   wave_lds_sync();
   float al[4], be[4];
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
-    const float ma = acc[kAccM + h], mt = acc[kAccTm + h];
+    const float ma = st[kStM + h], mt = st[kStTm + h];
     const float mx = fmaxf(ma, mt);   // finite: the tile has a valid token
     al[h] = ma > -INFINITY ? exp2_fast(ma - mx) : 0.f;
     be[h] = exp2_fast(mt - mx);
-    if (lane == h) {
-      acc[kAccL + h] = fmaf(acc[kAccL + h], al[h], acc[kAccTl + h] * be[h]);
-    }
+    if (lane == h) st[kStL + h] = fmaf(st[kStL + h], al[h], st[kStTl + h] * be[h]);
   }
   wave_lds_sync();
-  if (lane < 4) acc[kAccM + lane] = fmaxf(acc[kAccM + lane], acc[kAccTm + lane]);
+  if (lane < 4) st[kStM + lane] = fmaxf(st[kStM + lane], st[kStTm + lane]);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int e = lane + 64 * j, h = e >> 7;
-    if (h < G) acc[kAccO + e] = fmaf(acc[kAccO + e], al[h], scratch[h][e & (kD - 1)] * be[h]);
+    if (h < G) o[e] = fmaf(o[e], al[h], scratch[h][e & (kD - 1)] * be[h]);
   }
   wave_lds_sync();
+}
+
+// Tile u of one (sequence, KV head) folded into a wave's running BF16 state.
+template <int GH>
+__device__ __forceinline__ void bf16_tile_fold(const DecArgs &a, const TileCtx &tc, int b, int kv, int u,
+                                               float (*scratch)[kD], float *o, float *st) {
+  float m[4], l[4];
+  if (bf16_tile_compute<GH>(a, tc, b, kv, u, scratch, m, l))
+    bf16_fold_staged<GH>(a.pv.hq / a.pv.hkv, m, l, scratch, o, st);
 }
 
 // Combine the NW waves' history state into the split's partial.
@@ -1044,8 +1094,9 @@ __device__ void flush_partial(ScanSmem<MT, GH, NW, true> &sm, HistState<MT> &st,
 // End of a split for one M-tile of heads (G <= 4).  Each wave, once its
 // pages are done, stores its history state in its own (now idle) page
 // buffers, loads its share of U_V (the last 512 threads, one quarter row
-// each) and takes BF16 tiles from the workgroup's counter, folding them into
-// a running BF16 state next to its history state.  Then the workgroup
+// each) after taking BF16 tiles from the workgroup's counter (unless the
+// tile wave has run them already: tiles_here false) and folding them into a
+// running BF16 state next to its history state.  Then the workgroup
 // combines the waves, takes the history sum out of the rotated basis (bit
 // reversal, Walsh-Hadamard butterfly, U_V^T / sqrt(d): R_V^T is linear, so
 // applying it to every split's sum equals applying it once to the merged
@@ -1053,7 +1104,8 @@ __device__ void flush_partial(ScanSmem<MT, GH, NW, true> &sm, HistState<MT> &st,
 // otherwise one (m, l, o) partial in the original basis goes to dst.
 template <int GH, int NW>
 __device__ void split_epilogue(const DecArgs &a, int b, int kv, int split, ScanSmem<1, GH, NW, true> &sm,
-                               const HistState<1> &st, const MetaSteps &ms, DynPages *dp, float *dst) {
+                               const HistState<1> &st, const MetaSteps &ms, DynPages *dp, float *dst,
+                               bool tiles_here, const TileCtx &tc) {
   static_assert(GH == 4 && NW * 64 >= 512 + 256, "one M-tile of heads, 12 waves");
   constexpr int NT = NW * 64;
   const PoolView &pv = a.pv;
@@ -1077,12 +1129,25 @@ __device__ void split_epilogue(const DecArgs &a, int b, int kv, int split, ScanS
 #pragma unroll
     for (int j = 0; j < 8; ++j) reg[kAccO + lane + 64 * j] = 0.f;
     if (lane < 4) {
-      reg[kAccM + lane] = -INFINITY;
-      reg[kAccL + lane] = 0.f;
+      reg[kAccM + kStM + lane] = -INFINITY;
+      reg[kAccM + kStL + lane] = 0.f;
     }
   }
-  // 2) U_V rows for step 5: thread t >= NT - 512 owns row (t - (NT - 512)) / 4,
-  // columns 32 ((t - (NT - 512)) % 4) .. + 32
+  wave_lds_sync();
+  // 3) BF16 tiles u = split + S k, k < n_tiles, handed out as waves finish
+  // (one at a time: fetching two together, with both tiles' loads in flight,
+  // measured no faster and needs 40 more registers)
+  const int n_tiles = split < a.n_chunks ? (a.n_chunks - 1 - split) / S + 1 : 0;
+  while (tiles_here) {
+    int k = 0;
+    if (lane == 0) k = atomicAdd(&dp->next_tile, 1);
+    k = __builtin_amdgcn_readfirstlane(k);
+    if (k >= n_tiles) break;
+    bf16_tile_fold<GH>(a, tc, b, kv, split + S * k, sm.wave[wave].tile, reg + kAccO, reg + kAccM);
+  }
+  // 4) U_V rows for step 6: thread t >= NT - 512 owns row (t - (NT - 512)) / 4,
+  // columns 32 ((t - (NT - 512)) % 4) .. + 32; the loads overlap the wait
+  // for the other waves and the combine
   const int ut = tid - (NT - 512);
   const bool uown = ut >= 0;
   const int krow = (uown ? ut : 0) >> 2, upart = (uown ? ut : 0) & 3;
@@ -1092,31 +1157,33 @@ __device__ void split_epilogue(const DecArgs &a, int b, int kv, int split, ScanS
 #pragma unroll
     for (int i = 0; i < 8; ++i) u[i] = urow[i];
   }
-  wave_lds_sync();
-  // 3) BF16 tiles u = split + S k, k < n_tiles, handed out as waves finish
-  const int n_tiles = split < a.n_chunks ? (a.n_chunks - 1 - split) / S + 1 : 0;
-  for (;;) {
-    int k = 0;
-    if (lane == 0) k = atomicAdd(&dp->next_tile, 1);
-    k = __builtin_amdgcn_readfirstlane(k);
-    if (k >= n_tiles) break;
-    bf16_tile_fold<GH>(a, b, kv, split + S * k, sm.wave[wave].tile, reg);
-  }
   __syncthreads();
-  // 4) combine the waves (history: rotated basis, permuted for the butterfly)
+  // 5) combine the waves (history: rotated basis, permuted for the butterfly)
   for (int idx = tid; idx < G * kD; idx += NT) {
     const int h = idx >> 7, c = idx & (kD - 1);
+    // BF16 states: the tile waves' (long scans; else empty) and every wave's own
     float M = -INFINITY, Mb = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kTileWaves; ++t) Mb = fmaxf(Mb, sm.tacc[t][4 * kD + kStM + h]);
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       M = fmaxf(M, sm.m[w][h]);
-      Mb = fmaxf(Mb, reinterpret_cast<const float *>(&sm.pbuf[w][0][0])[kAccM + h]);
+      Mb = fmaxf(Mb, reinterpret_cast<const float *>(&sm.pbuf[w][0][0])[kAccM + kStM + h]);
     }
     float o = 0.f, l = 0.f, ob = 0.f, lb = 0.f;
 #pragma unroll
+    for (int t = 0; t < kTileWaves; ++t) {
+      const float mt = sm.tacc[t][4 * kD + kStM + h];
+      if (mt > -INFINITY) {
+        const float sc = exp2_fast(mt - Mb);
+        ob = fmaf(sc, sm.tacc[t][idx], ob);
+        lb = fmaf(sc, sm.tacc[t][4 * kD + kStL + h], lb);
+      }
+    }
+#pragma unroll
     for (int w = 0; w < NW; ++w) {
       const float *rw = reinterpret_cast<const float *>(&sm.pbuf[w][0][0]);
-      const float mw = sm.m[w][h], mb = rw[kAccM + h];
+      const float mw = sm.m[w][h], mb = rw[kAccM + kStM + h];
       if (mw > -INFINITY) {
         const float sc = exp2_fast(mw - M);
         o = fmaf(sc, rw[kAccHist + idx], o);
@@ -1125,7 +1192,7 @@ __device__ void split_epilogue(const DecArgs &a, int b, int kv, int split, ScanS
       if (mb > -INFINITY) {
         const float sc = exp2_fast(mb - Mb);
         ob = fmaf(sc, rw[kAccO + idx], ob);
-        lb = fmaf(sc, rw[kAccL + h], lb);
+        lb = fmaf(sc, rw[kAccM + kStL + h], lb);
       }
     }
     sm.e.zs[h][bitrev7(c)] = o;   // (o P)[j] = o[bitrev(j)]
@@ -1138,7 +1205,7 @@ __device__ void split_epilogue(const DecArgs &a, int b, int kv, int split, ScanS
     }
   }
   __syncthreads();
-  // 5) Walsh-Hadamard butterfly per head (one wave each), then U_V^T
+  // 6) Walsh-Hadamard butterfly per head (one wave each), then U_V^T
   if (wave < G) {
     float x0 = sm.e.zs[wave][lane], x1 = sm.e.zs[wave][lane + 64];
     fwht_lane_stages(x0, x1, lane);
@@ -1163,7 +1230,7 @@ __device__ void split_epilogue(const DecArgs &a, int b, int kv, int split, ScanS
     }
   }
   __syncthreads();
-  // 6) history and BF16 parts together
+  // 7) history and BF16 parts together
   for (int idx = tid; idx < G * kD; idx += NT) {
     const int h = idx >> 7, c = idx & (kD - 1);
     const float Mh = sm.e.hm[h], Mb = sm.e.bm[h], Mt = fmaxf(Mh, Mb);
@@ -1207,6 +1274,7 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   // 0..255) the query preparation's loads.  The waves without preparation
   // work start their copies as soon as those land.
   float tk = a.rv.tau_K[kv], tv = a.rv.tau_V[kv];
+  const TileCtx tc{max(0, L), pv.sink_slot[b]};
   PagePipe<NW, PF> pipe;
   pipe_init(pipe, pv, b, kv, pg0, pg1, sm.pbuf[wave], wave, lane);
   // long scans (16 pages per wave and more) take every BF16 tile after the
@@ -1215,8 +1283,17 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   // out dynamically
   const int npg_wg = pg1 - pg0;
   const bool long_scan = npg_wg >= 16 * NW;
-  // one M-tile of heads: every tile runs after the pages (split_epilogue)
+  // one M-tile of heads: on long scans the last wave runs every BF16 tile
+  // first (into its own running state, outside the page buffers) and then
+  // joins the page stream; otherwise the tiles run after the pages
+  // (split_epilogue)
   const int early = (MT == 1 || long_scan) ? 0 : 4;
+  // one M-tile of heads, scans of 48 pages per wave and more: the last
+  // kTileWaves waves run the BF16 tiles first (a tile takes several
+  // microseconds once the page stream fills the memory pipeline, so one wave
+  // alone would outlast the pages)
+  const bool tile_waves = MT == 1 && npg_wg >= 48 * NW;
+  const int tw = tile_waves ? wave - (NW - kTileWaves) : -1;   // this wave's tile-wave index, or < 0
   const bool dyn = DYN && npg_wg >= 2 * NW * PF && npg_wg <= kDynMaxPages;
   // pages [pg0, pg0 + nfull) hold 64 tokens (only the history's last page can hold fewer)
   const int nfull = max(0, min(pg1, n_hist / kPageTokens) - pg0);
@@ -1242,7 +1319,13 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
       }
       if (tid == 0) dp->next_page = NW * PF;
     }
-    if (wave >= 4) pipe_prologue(pipe, pv, lane);
+    if constexpr (MT == 1) {
+      if (tid < 4 * kTileWaves) {   // the tile waves' states start empty
+        sm.tacc[tid >> 2][4 * kD + kStM + (tid & 3)] = -INFINITY;
+        sm.tacc[tid >> 2][4 * kD + kStL + (tid & 3)] = 0.f;
+      }
+    }
+    if (wave >= 4 && tw < 0) pipe_prologue(pipe, pv, lane);
   });
   const MetaSteps ms = meta_steps(tk, tv);
   QueryOps<MT> qo;
@@ -1264,11 +1347,23 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   if (wave < 4) {
     const int u = split + S * (early - 1 - wave);
     if (wave < early && u < a.n_chunks)
-      bf16_tile_partial<GH>(a, b, kv, u, sm.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
+      bf16_tile_partial<GH>(a, tc, b, kv, u, sm.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
     // the preparing waves start their copies only now: issuing them inside
     // the preparation would stall those waves (the CU accepts copy requests
     // at the memory rate) and with them every wave waiting on the preparation
     pipe_prologue(pipe, pv, lane);
+  }
+  if constexpr (MT == 1) {
+    if (tw >= 0) {
+      // tiles u = split + S k with k = tw mod kTileWaves, one after the
+      // other, then the pages
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sm.tacc[tw][lane + 64 * j] = 0.f;
+      wave_lds_sync();
+      for (int u = split + S * tw; u < a.n_chunks; u += S * kTileWaves)
+        bf16_tile_fold<GH>(a, tc, b, kv, u, sm.wave[wave].tile, &sm.tacc[tw][0], &sm.tacc[tw][4 * kD]);
+      pipe_prologue(pipe, pv, lane);
+    }
   }
   HistState<MT> st;
   hist_reset(st);
@@ -1297,7 +1392,7 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   }
   if (pipe.bad && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
   if constexpr (MT == 1) {
-    split_epilogue<GH, NW>(a, b, kv, split, sm, st, ms, dp, dst);
+    split_epilogue<GH, NW>(a, b, kv, split, sm, st, ms, dp, dst, !tile_waves, tc);
     return;
   }
   if (dyn) {
@@ -1310,13 +1405,13 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
       k = __builtin_amdgcn_readfirstlane(k);
       if (k >= n_tiles) break;
       const int u = split + S * k;
-      bf16_tile_partial<GH>(a, b, kv, u, sm.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
+      bf16_tile_partial<GH>(a, tc, b, kv, u, sm.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
     }
   } else {
     for (int u = split + S * early; u < a.n_chunks; u += S) {
       const int k = u / S - early;
       if ((long_scan ? k % 4 : NW - 1 - k % NW) == wave)
-        bf16_tile_partial<GH>(a, b, kv, u, sm.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
+        bf16_tile_partial<GH>(a, tc, b, kv, u, sm.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
     }
   }
   flush_partial<MT, GH, NW>(sm, st, G, ms, dst);
@@ -1677,9 +1772,10 @@ decode_scan_kernel(DecArgs a) {
   __shared__ ScanUnion<MT, GH, NW, MFMA> sm;
   if constexpr (!MFMA) {
     // BF16 tile u runs on workgroup u % S, wave (u / S) % NW, before its pages
+    const TileCtx tc = tile_ctx(pv, b);
     for (int u = split; u < a.n_chunks; u += S) {
       if (((u / S) % NW) == wave)
-        bf16_tile_partial<GH>(a, b, kv, u, sm.s.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
+        bf16_tile_partial<GH>(a, tc, b, kv, u, sm.s.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
     }
   }
   float *dst = parts + (size_t)split * G * kPartStride;

@@ -258,27 +258,33 @@ __device__ __forceinline__ void bf16_chunk(const uint16_t *K, const uint16_t *V,
   wave_lds_sync();
 }
 
-// BF16 attention of one 16-token tile for one wave, from a fresh state.
+// BF16 attention of one 16-token tile for one wave, from a fresh state, in
+// two parts so that several tiles' loads can be in flight together.
 //   K, V: 16 bf16 rows of 128 channels; the first `valid` (1..16) are real
-//   tokens (rows past them are re-read from row valid - 1 and masked).  All
-//   eight 16-byte loads per lane are issued together.  Outputs (log2 units):
-//   m[i], l[i] for head 4 q + i (row-uniform), o[h][8] = sum over this
-//   lane's token phase (tokens q, q + 4, q + 8, q + 12) of p V for channels
-//   8 n .. 8 n + 7, relative to m.  ps: [GH][>= 16] LDS scratch of the wave.
-template <int GH>
-__device__ __forceinline__ void bf16_tile(const uint16_t *K, const uint16_t *V, int valid, int G,
-                                          const v8bf (&Aq)[4], float sl2, float (&m)[4], float (&l)[4],
-                                          float (&o)[GH][8], float (*ps)[kD]) {
+//   tokens (rows past them are re-read from row valid - 1 and masked).
+//   bf16_tile_load issues all eight 16-byte loads of a lane; bf16_tile_math
+//   gives (log2 units) m[i], l[i] for head 4 q + i (row-uniform), o[h][8] =
+//   sum over this lane's token phase (tokens q, q + 4, q + 8, q + 12) of p V
+//   for channels 8 n .. 8 n + 7, relative to m.  ps: [GH][>= 16] LDS scratch
+//   of the wave.
+struct TileRegs {
+  uint4 kk[4], vv[4];
+};
+__device__ __forceinline__ void bf16_tile_load(const uint16_t *K, const uint16_t *V, int valid, TileRegs &r) {
   const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
   const uint16_t *kr = K + (size_t)min(n, valid - 1) * kD + 32 * q;
-  uint4 kk[4], vv[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) kk[ks] = *(const uint4 *)(kr + 8 * ks);
+  for (int ks = 0; ks < 4; ++ks) r.kk[ks] = *(const uint4 *)(kr + 8 * ks);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) vv[i] = *(const uint4 *)(V + (size_t)min(q + 4 * i, valid - 1) * kD + 8 * n);
+  for (int i = 0; i < 4; ++i) r.vv[i] = *(const uint4 *)(V + (size_t)min(q + 4 * i, valid - 1) * kD + 8 * n);
+}
+template <int GH>
+__device__ __forceinline__ void bf16_tile_math(const TileRegs &r, int valid, int G, const v8bf (&Aq)[4], float sl2,
+                                               float (&m)[4], float (&l)[4], float (&o)[GH][8], float (*ps)[kD]) {
+  const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
   v4f C = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) C = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aq[ks], as_v8bf(kk[ks]), C, 0, 0, 0);
+  for (int ks = 0; ks < 4; ++ks) C = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Aq[ks], as_v8bf(r.kk[ks]), C, 0, 0, 0);
   const bool ok = n < valid;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -298,14 +304,14 @@ __device__ __forceinline__ void bf16_tile(const uint16_t *K, const uint16_t *V, 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float vf[8];
-    vf[0] = __uint_as_float(vv[i].x << 16);
-    vf[1] = __uint_as_float(vv[i].x & 0xFFFF0000u);
-    vf[2] = __uint_as_float(vv[i].y << 16);
-    vf[3] = __uint_as_float(vv[i].y & 0xFFFF0000u);
-    vf[4] = __uint_as_float(vv[i].z << 16);
-    vf[5] = __uint_as_float(vv[i].z & 0xFFFF0000u);
-    vf[6] = __uint_as_float(vv[i].w << 16);
-    vf[7] = __uint_as_float(vv[i].w & 0xFFFF0000u);
+    vf[0] = __uint_as_float(r.vv[i].x << 16);
+    vf[1] = __uint_as_float(r.vv[i].x & 0xFFFF0000u);
+    vf[2] = __uint_as_float(r.vv[i].y << 16);
+    vf[3] = __uint_as_float(r.vv[i].y & 0xFFFF0000u);
+    vf[4] = __uint_as_float(r.vv[i].z << 16);
+    vf[5] = __uint_as_float(r.vv[i].z & 0xFFFF0000u);
+    vf[6] = __uint_as_float(r.vv[i].w << 16);
+    vf[7] = __uint_as_float(r.vv[i].w & 0xFFFF0000u);
 #pragma unroll
     for (int h = 0; h < GH; ++h) {
       if (h >= G) break;
@@ -315,6 +321,14 @@ __device__ __forceinline__ void bf16_tile(const uint16_t *K, const uint16_t *V, 
     }
   }
   wave_lds_sync();
+}
+template <int GH>
+__device__ __forceinline__ void bf16_tile(const uint16_t *K, const uint16_t *V, int valid, int G,
+                                          const v8bf (&Aq)[4], float sl2, float (&m)[4], float (&l)[4],
+                                          float (&o)[GH][8], float (*ps)[kD]) {
+  TileRegs r;
+  bf16_tile_load(K, V, valid, r);
+  bf16_tile_math<GH>(r, valid, G, Aq, sl2, m, l, o, ps);
 }
 
 // Load the bf16 query rows of the G heads of one KV head as the A operand.
