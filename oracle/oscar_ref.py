@@ -248,6 +248,8 @@ class HeadCalibration:
     tau_V: np.float32
     eig_K: np.ndarray = field(repr=False, default=None)
     eig_V: np.ndarray = field(repr=False, default=None)
+    levels_K: np.ndarray = None   # uint8 [4] reconstruction levels n / 32 (None: the uniform grid)
+    levels_V: np.ndarray = None
 
 
 def calibrate_head(q_heads: np.ndarray, k_cal: np.ndarray, v_cal: np.ndarray,
@@ -314,6 +316,7 @@ class QuantizedTokens:
     z8: np.ndarray         # uint8 [n, d // group]: zero code
     scale: np.ndarray      # float32 [n, d // group]: decoded scale  s8 * b
     zero: np.ndarray       # float32 [n, d // group]: decoded zero   z8 * a - tau
+    levels: np.ndarray = None   # uint8 [4]: code k stands for levels[k] / 32 (None: k)
 
 
 META_LEVELS = 255          # largest 8-bit zero / scale code
@@ -334,7 +337,7 @@ def metadata_steps(tau: np.float32):
     return a, b
 
 
-def quantize_int2(xr: np.ndarray, tau: np.float32, group: int = GROUP_CHANNELS) -> QuantizedTokens:
+def quantize_int2(xr: np.ndarray, tau: np.float32, group: int = GROUP_CHANNELS, levels=None) -> QuantizedTokens:
     """Clip to +-tau and quantise per token, per group of ``group`` channels.
 
     [B] serving: per-token asymmetric INT2 with G_K = 64 channels per group,
@@ -350,6 +353,13 @@ def quantize_int2(xr: np.ndarray, tau: np.float32, group: int = GROUP_CHANNELS) 
     the decoded values z^ = z8 a - tau and s^ = s8 b: code = rint((x - z^) /
     s^) clamped to [0, 3], all codes 0 if s^ == 0.  All steps in float32
     (IEEE add, subtract, multiply and divide; round half to even).
+
+    With ``levels`` (a Lloyd-Max codebook, see ``codebook_levels``) code k
+    stands for the value z^ + s^ levels[k] / 32 instead of z^ + s^ k: the
+    code of u = (x - z^) / s^ is the nearest level, the thresholds being the
+    midpoints t_k = (levels[k] + levels[k+1]) / 64, with a tie at the middle
+    threshold going up and at the outer ones down.  For the uniform grid
+    levels = (0, 32, 64, 96) that is exactly the rounding above.
     """
     xr = np.asarray(xr, dtype=np.float32)
     n, d = xr.shape
@@ -369,10 +379,16 @@ def quantize_int2(xr: np.ndarray, tau: np.float32, group: int = GROUP_CHANNELS) 
     zf = z8.astype(np.float32) * a - t
     sf = s8.astype(np.float32) * b
     with np.errstate(divide="ignore", invalid="ignore"):
-        q = np.rint((xc - zf[..., None]) / sf[..., None])
+        u = (xc - zf[..., None]) / sf[..., None]
+    if levels is None:
+        q = np.rint(u)
+    else:
+        t = level_thresholds(levels)
+        q = ((u > t[0]).astype(np.int32) + (u >= t[1]).astype(np.int32) + (u > t[2]).astype(np.int32)).astype(np.float32)
     q = np.where(sf[..., None] == 0, np.float32(0), q)
     codes = np.clip(q, 0, INT2_LEVELS - 1).astype(np.uint8).reshape(n, d)
-    return QuantizedTokens(codes=codes, s8=s8, z8=z8, scale=sf, zero=zf)
+    return QuantizedTokens(codes=codes, s8=s8, z8=z8, scale=sf, zero=zf,
+                           levels=None if levels is None else np.asarray(levels, np.uint8).copy())
 
 
 def pack_codes(codes: np.ndarray) -> np.ndarray:
@@ -396,18 +412,108 @@ def unpack_codes(packed: np.ndarray) -> np.ndarray:
 
 
 def dequantize_int2(codes: np.ndarray, scale: np.ndarray, zero: np.ndarray,
-                    group: int = GROUP_CHANNELS) -> np.ndarray:
-    """x^ = code * s + z per group, in float64 from the decoded float32 s, z."""
+                    group: int = GROUP_CHANNELS, levels=None) -> np.ndarray:
+    """x^ = code * s + z per group, in float64 from the decoded float32 s, z
+    (with a codebook: levels[code] / 32 in place of the code)."""
     c = np.asarray(codes, dtype=np.float64)
+    if levels is not None:
+        c = np.asarray(levels, dtype=np.float64)[np.asarray(codes, dtype=np.int64)] / LEVEL_DENOM
     n, d = c.shape
     s = np.asarray(scale, dtype=np.float64)[..., None]
     z = np.asarray(zero, dtype=np.float64)[..., None]
     return (c.reshape(n, d // group, group) * s + z).reshape(n, d)
 
 
-def write_history(x: np.ndarray, U32: np.ndarray, tau: np.float32) -> QuantizedTokens:
+def write_history(x: np.ndarray, U32: np.ndarray, tau: np.float32, levels=None) -> QuantizedTokens:
     """Whole write path for history tokens: rotate, clip, quantise."""
-    return quantize_int2(rotate_for_write(x, U32), tau)
+    return quantize_int2(rotate_for_write(x, U32), tau, levels=levels)
+
+
+# ---------------------------------------------------------------------------
+# Lloyd-Max codebook ([A] summary and outlook: the latest code base adds a
+# Lloyd-Max codebook for the 2-bit codes; the pages say nothing more)
+# ---------------------------------------------------------------------------
+#
+# Reading taken: rotation, clip and the per-token, per-group zero and scale
+# (with their 8-bit codes) stay as they are; only the four reconstruction
+# levels of a code change.  On the uniform grid code k stands for
+# z^ + s^ k.  With a codebook it stands for z^ + s^ c_k, where c_0..c_3 are
+# the Lloyd-Max levels of the normalised values u = (x - z^) / s^ in [0, 3]
+# of one head's calibration tokens (keys and values separately).  The levels
+# are stored as integers n_k = c_k * 32 in [0, 96], strictly increasing
+# (8 bits each, 32 bits per head and tensor), so that the grid stays exact
+# in float32 and in the integer products of the decode kernels.
+
+LEVEL_DENOM = 32
+UNIFORM_LEVELS = np.array([0, 32, 64, 96], dtype=np.uint8)
+
+
+def level_thresholds(levels) -> np.ndarray:
+    """Midpoints between consecutive levels, in float32 (exact: integers / 64)."""
+    n = np.asarray(levels, dtype=np.float64)
+    return ((n[:-1] + n[1:]) / (2 * LEVEL_DENOM)).astype(np.float32)
+
+
+def lloyd_max(samples: np.ndarray, levels0, iters: int = 1000, tol: float = 1e-12) -> np.ndarray:
+    """Lloyd-Max scalar quantiser of 1-D samples (float64): alternately assign
+    each sample to the nearest level (cells bounded by the midpoints) and move
+    each level to the mean of its cell, from the ascending levels0, until no
+    level moves by more than tol.  A cell without samples keeps its level."""
+    x = np.sort(np.asarray(samples, dtype=np.float64).ravel())
+    c = np.array(levels0, dtype=np.float64)
+    csum = np.concatenate([[0.0], np.cumsum(x)])
+    for _ in range(iters):
+        t = (c[:-1] + c[1:]) / 2
+        edges = np.concatenate([[0], np.searchsorted(x, t, side="left"), [x.size]])
+        new = c.copy()
+        for k in range(c.size):
+            lo, hi = edges[k], edges[k + 1]
+            if hi > lo:
+                new[k] = (csum[hi] - csum[lo]) / (hi - lo)
+        done = np.max(np.abs(new - c)) <= tol
+        c = new
+        if done:
+            break
+    return c
+
+
+def codebook_levels(u: np.ndarray) -> np.ndarray:
+    """Stored levels (uint8 [4]) of the normalised values u in [0, 3]: the
+    Lloyd-Max levels from the uniform start (0, 1, 2, 3), each rounded to the
+    nearest 1/32 (half to even) and clamped to [0, 96], then made strictly
+    increasing by raising each level to at least one step above the one
+    below it and lowering it to leave room for the ones above."""
+    c = lloyd_max(u, [0.0, 1.0, 2.0, 3.0])
+    n = np.clip(np.rint(c * LEVEL_DENOM), 0, 3 * LEVEL_DENOM).astype(np.int64)
+    for k in range(1, 4):
+        n[k] = max(n[k], n[k - 1] + 1)
+    for k in range(3, -1, -1):
+        n[k] = min(n[k], 3 * LEVEL_DENOM - (3 - k))
+        if k < 3:
+            n[k] = min(n[k], n[k + 1] - 1)
+    return n.astype(np.uint8)
+
+
+def normalised_values(x: np.ndarray, U32: np.ndarray, tau: np.float32, group: int = GROUP_CHANNELS) -> np.ndarray:
+    """u = (x~ - z^) / s^ (float32) of every element of tokens x [n, d]
+    through the write path up to the code (rotate, clip, group metadata),
+    for the groups whose decoded scale is not zero."""
+    xr = rotate_for_write(x, U32)
+    qt = quantize_int2(xr, tau, group)
+    t = np.float32(tau)
+    n, d = xr.shape
+    xc = np.clip(xr, -t, t).reshape(n, d // group, group)
+    keep = qt.scale > 0
+    u = (xc - qt.zero[..., None]) / np.where(keep, qt.scale, np.float32(1))[..., None]
+    return u[keep].ravel()
+
+
+def calibrate_codebook(cal: HeadCalibration, k_cal: np.ndarray, v_cal: np.ndarray) -> HeadCalibration:
+    """``cal`` with Lloyd-Max levels for keys and values, from the head's
+    calibration tokens (the same ones that set tau)."""
+    import dataclasses
+    return dataclasses.replace(cal, levels_K=codebook_levels(normalised_values(k_cal, cal.U_K, cal.tau_K)),
+                               levels_V=codebook_levels(normalised_values(v_cal, cal.U_V, cal.tau_V)))
 
 
 # ---------------------------------------------------------------------------
@@ -450,8 +556,8 @@ def build_head_pool(k: np.ndarray, v: np.ndarray, cal: HeadCalibration,
     L = k.shape[0]
     (s0, s1), (h0, h1), (r0, r1) = pool_regions(L, sink, recent)
     return HeadPool(sink_k=k[s0:s1], sink_v=v[s0:s1],
-                    hist_k=write_history(k[h0:h1], cal.U_K, cal.tau_K),
-                    hist_v=write_history(v[h0:h1], cal.U_V, cal.tau_V),
+                    hist_k=write_history(k[h0:h1], cal.U_K, cal.tau_K, cal.levels_K),
+                    hist_v=write_history(v[h0:h1], cal.U_V, cal.tau_V, cal.levels_V),
                     recent_k=k[r0:r1], recent_v=v[r0:r1])
 
 
@@ -459,8 +565,8 @@ def dequantized_head_cache(pool: HeadPool, cal: HeadCalibration):
     """Full L x d float64 K^ and V^ with history inverse-rotated (x~ @ R^T)."""
     RK = composite_rotation(cal.U_K)
     RV = composite_rotation(cal.U_V)
-    hk = dequantize_int2(pool.hist_k.codes, pool.hist_k.scale, pool.hist_k.zero) @ RK.T
-    hv = dequantize_int2(pool.hist_v.codes, pool.hist_v.scale, pool.hist_v.zero) @ RV.T
+    hk = dequantize_int2(pool.hist_k.codes, pool.hist_k.scale, pool.hist_k.zero, levels=pool.hist_k.levels) @ RK.T
+    hv = dequantize_int2(pool.hist_v.codes, pool.hist_v.scale, pool.hist_v.zero, levels=pool.hist_v.levels) @ RV.T
     K = np.concatenate([pool.sink_k, hk, pool.recent_k], axis=0)
     V = np.concatenate([pool.sink_v, hv, pool.recent_v], axis=0)
     return K, V
@@ -533,8 +639,10 @@ def decode_head_segmented(q: np.ndarray, pool: HeadPool, cal: HeadCalibration,
     n_hist = pool.hist_k.codes.shape[0]
     for start in range(0, n_hist, page_tokens):
         sl = slice(start, min(n_hist, start + page_tokens))
-        hk = dequantize_int2(pool.hist_k.codes[sl], pool.hist_k.scale[sl], pool.hist_k.zero[sl]) @ RK.T
-        hv = dequantize_int2(pool.hist_v.codes[sl], pool.hist_v.scale[sl], pool.hist_v.zero[sl]) @ RV.T
+        hk = dequantize_int2(pool.hist_k.codes[sl], pool.hist_k.scale[sl], pool.hist_k.zero[sl],
+                             levels=pool.hist_k.levels) @ RK.T
+        hv = dequantize_int2(pool.hist_v.codes[sl], pool.hist_v.scale[sl], pool.hist_v.zero[sl],
+                             levels=pool.hist_v.levels) @ RV.T
         parts.append(segment_partial(q, hk, hv, sm_scale))
     parts.append(segment_partial(q, pool.recent_k, pool.recent_v, sm_scale))
     merged = lse_merge(parts)

@@ -555,3 +555,106 @@ def test_decode_sequence_gqa_head_mapping():
         torch.from_numpy(q)[None, :, None, :], Kt.repeat(1, G, 1, 1), Vt.repeat(1, G, 1, 1),
         scale=1 / np.sqrt(D))[0, :, 0]
     assert np.max(np.abs(out - wrong.numpy())) > 0.1
+
+
+# --- Lloyd-Max codebook -------------------------------------------------------
+
+def test_lloyd_max_gaussian_fixed_point():
+    """On the unit Gaussian the 4-level Lloyd-Max quantiser converges to the
+    textbook levels +-0.4528, +-1.5104 with thresholds 0, +-0.9816 (Max's
+    table).  The distribution is a fine deterministic quantile grid."""
+    from scipy.stats import norm
+    N = 400_000
+    x = norm.ppf((np.arange(N) + 0.5) / N)
+    c = O.lloyd_max(x, [-1.5, -0.5, 0.5, 1.5])
+    assert np.max(np.abs(c - np.array([-1.5104, -0.4528, 0.4528, 1.5104]))) < 3e-4
+    t = (c[:-1] + c[1:]) / 2
+    assert np.max(np.abs(t - np.array([-0.9816, 0.0, 0.9816]))) < 3e-4
+
+
+def test_lloyd_max_uniform_equally_spaced():
+    """On a uniform distribution over [0, 3] the optimum is the four cell
+    centres 3/8, 9/8, 15/8, 21/8 (equal cells of width 3/4)."""
+    N = 120_000
+    x = (np.arange(N) + 0.5) / N * 3.0
+    c = O.lloyd_max(x, [0.0, 1.0, 2.0, 3.0])
+    assert np.max(np.abs(c - np.array([3, 9, 15, 21]) / 8.0)) < 1e-4
+
+
+def test_uniform_codebook_is_the_rounding_quantiser():
+    """The codebook (0, 32, 64, 96) / 32 reproduces the plain quantiser bit for
+    bit: its thresholds 0.5, 1.5, 2.5 with the tie rule (middle up, outer
+    down) equal clamp(rint(u), 0, 3) with rounding half to even, exact
+    half-way values included; end to end on random tokens too."""
+    t = O.level_thresholds(O.UNIFORM_LEVELS)
+    assert np.array_equal(t, np.array([0.5, 1.5, 2.5], np.float32))
+    u = np.concatenate([np.arange(-8, 40, dtype=np.float32) / 8,
+                        np.nextafter(np.float32([0.5, 1.5, 2.5]), np.float32(9)),
+                        np.nextafter(np.float32([0.5, 1.5, 2.5]), np.float32(-9))])
+    by_threshold = (u > t[0]).astype(int) + (u >= t[1]).astype(int) + (u > t[2]).astype(int)
+    assert np.array_equal(by_threshold, np.clip(np.rint(u), 0, 3).astype(int))
+    g = np.random.default_rng(30)
+    x = g.standard_normal((300, D)).astype(np.float32) * 2
+    tau = np.float32(4.0)
+    base = O.quantize_int2(x, tau)
+    a = O.quantize_int2(x, tau, levels=O.UNIFORM_LEVELS)
+    assert np.array_equal(a.codes, base.codes) and np.array_equal(a.s8, base.s8) and np.array_equal(a.z8, base.z8)
+    assert np.array_equal(O.dequantize_int2(a.codes, a.scale, a.zero, levels=a.levels),
+                          O.dequantize_int2(base.codes, base.scale, base.zero))
+
+
+def test_codebook_code_choice_by_hand():
+    """Levels (0, 20, 50, 96) / 32: thresholds 0.3125, 1.09375, 2.28125; a tie
+    at the middle threshold goes up, at the outer ones down; the decoded value
+    is z^ + s^ n[code] / 32."""
+    lv = np.array([0, 20, 50, 96], np.uint8)
+    t = O.level_thresholds(lv)
+    assert np.array_equal(t, np.array([0.3125, 1.09375, 2.28125], np.float32))
+    # one group with z^ = -2 (z8 = 0 at tau = 2... grid a = 4/255) and a value per probe
+    tau = np.float32(2.0)
+    a, b = O.metadata_steps(tau)
+    x = np.full((1, D), -2.0, np.float32)
+    x[0, 1] = 2.0                       # group 0 spans [-2, 2]: z8 = 0, s = 4/3
+    probes = [0.0, 0.3125, 0.4, 1.09375, 1.2, 2.28125, 2.5, 3.0]
+    qt0 = O.quantize_int2(x, tau)
+    zf, sf = qt0.zero[0, 0], qt0.scale[0, 0]
+    for i, u in enumerate(probes):
+        x[0, 2 + i] = zf + sf * np.float32(u)
+    qt = O.quantize_int2(x, tau, levels=lv)
+    zf, sf = qt.zero[0, 0], qt.scale[0, 0]
+    for i, u in enumerate(probes):
+        uu = (x[0, 2 + i] - zf) / sf                          # float32, as the quantiser sees it
+        want = int(uu > t[0]) + int(uu >= t[1]) + int(uu > t[2])
+        assert qt.codes[0, 2 + i] == want, (u, uu)
+    deq = O.dequantize_int2(qt.codes, qt.scale, qt.zero, levels=lv)
+    assert deq[0, 1] == float(zf) + float(sf) * 96 / 32
+
+
+def test_codebook_levels_calibrated():
+    """Calibrated levels are strictly increasing integers in [0, 96] and, being
+    the Lloyd-Max levels of the calibration values, lower the reconstruction
+    error of those values below the uniform grid's."""
+    wl = synth.WORKLOADS["tiny-4k"]
+    q, k, v = synth.calibration_set(wl, 0, n_cal=1024)
+    f = synth.bf16_bits_to_f32
+    cal = O.calibrate_head(f(q), f(k)[0], f(v)[0], 1 / np.sqrt(D))
+    cb = O.calibrate_codebook(cal, f(k)[0], f(v)[0])
+    for lv in (cb.levels_K, cb.levels_V):
+        assert lv.dtype == np.uint8 and np.all(np.diff(lv.astype(int)) >= 1) and lv[-1] <= 96
+    for x, U, tau, lv in ((f(k)[0], cal.U_K, cal.tau_K, cb.levels_K), (f(v)[0], cal.U_V, cal.tau_V, cb.levels_V)):
+        xr = O.rotate_for_write(x.astype(np.float64), U).astype(np.float64)
+        xc = np.clip(xr, -float(tau), float(tau))
+        errs = []
+        for levels in (None, lv):
+            qt = O.quantize_int2(xr.astype(np.float32), tau, levels=levels)
+            errs.append(np.mean((O.dequantize_int2(qt.codes, qt.scale, qt.zero, levels=levels) - xc) ** 2))
+        assert errs[1] < 0.95 * errs[0], errs
+
+
+def test_codebook_levels_degenerate_samples():
+    """All samples equal: every cell but one stays at its start, and the
+    stored levels are still strictly increasing inside [0, 96]."""
+    lv = O.codebook_levels(np.full(1000, 3.0))
+    assert np.all(np.diff(lv.astype(int)) >= 1) and lv[0] >= 0 and lv[-1] <= 96
+    lv = O.codebook_levels(np.zeros(1000))
+    assert np.all(np.diff(lv.astype(int)) >= 1) and lv[0] == 0
