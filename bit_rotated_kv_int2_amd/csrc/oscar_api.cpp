@@ -131,6 +131,18 @@ int32_t oscar_calibrate_rotation(const oscar_params *p, const float *q_cal, int6
   return ok();
 }
 
+int32_t oscar_calibrate_codebook(const oscar_params *p, const float *U, const float *tau, const float *x_cal,
+                                 int64_t n, uint32_t *levels) {
+  int rc = check_params(p);
+  if (rc) return rc;
+  if (!U || !tau || !x_cal || !levels) return fail(OSCAR_EINVAL, "codebook pointer is NULL");
+  if (n < 1) return fail(OSCAR_EINVAL, "need at least one calibration token");
+  char msg[256] = "";
+  rc = oscar::calibrate_codebook_host(p->head_dim, p->num_kv_heads, U, tau, x_cal, n, levels, msg, sizeof(msg));
+  if (rc) return fail(rc, "%s", msg);
+  return ok();
+}
+
 int32_t oscar_quantize_append(const oscar_params *p, const oscar_rotation *rot,
                               const oscar_kv_pool *pool, const uint16_t *k_new,
                               const uint16_t *v_new, int32_t n_new, void *stream) {
@@ -141,7 +153,7 @@ int32_t oscar_quantize_append(const oscar_params *p, const oscar_rotation *rot,
   if (!k_new || !v_new) return fail(OSCAR_EINVAL, "k_new/v_new is NULL");
   if (misaligned(k_new) || misaligned(v_new)) return fail(OSCAR_EINVAL, "k_new/v_new must be 16-byte aligned");
   oscar::PoolView pv = make_pv(p, pool);
-  oscar::RotView rv{rot->U_K, rot->U_V, rot->tau_K, rot->tau_V};
+  oscar::RotView rv{rot->U_K, rot->U_V, rot->tau_K, rot->tau_V, rot->levels_K, rot->levels_V};
   hipError_t e = oscar::launch_append(pv, rv, k_new, v_new, n_new, (hipStream_t)stream);
   if (e != hipSuccess) return fail(OSCAR_EHIP, "append launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -173,7 +185,7 @@ int32_t oscar_decode_attention(const oscar_params *p, const oscar_rotation *rot,
     return fail(OSCAR_EWORKSPACE, "workspace of %zu bytes needed, %zu given", plan.total, workspace_bytes);
   if (((uintptr_t)workspace) & 255) return fail(OSCAR_EINVAL, "workspace must be 256-byte aligned");
   oscar::PoolView pv = make_pv(p, pool);
-  oscar::RotView rv{rot->U_K, rot->U_V, rot->tau_K, rot->tau_V};
+  oscar::RotView rv{rot->U_K, rot->U_V, rot->tau_K, rot->tau_V, rot->levels_K, rot->levels_V};
   hipError_t e = oscar::launch_decode(pv, rv, q, out, (uint8_t *)workspace,
                                       (int *)((uint8_t *)workspace + plan.off_counters), plan, o.variant,
                                       (hipStream_t)stream);
@@ -206,7 +218,7 @@ int32_t oscar_decode_attention_noalloc(const oscar_params *p, const oscar_rotati
   hipError_t e = oscar::noalloc_scratch((hipStream_t)stream, &base);
   if (e != hipSuccess) return fail(OSCAR_EHIP, "no-alloc decode buffer: %s", hipGetErrorString(e));
   oscar::PoolView pv = make_pv(p, pool);
-  oscar::RotView rv{rot->U_K, rot->U_V, rot->tau_K, rot->tau_V};
+  oscar::RotView rv{rot->U_K, rot->U_V, rot->tau_K, rot->tau_V, rot->levels_K, rot->levels_V};
   e = oscar::launch_decode(pv, rv, q, out, base + cbytes - plan.off_qconst, (int *)base, plan, o.variant,
                            (hipStream_t)stream);
   if (e != hipSuccess) return fail(OSCAR_EHIP, "decode launch failed: %s", hipGetErrorString(e));

@@ -258,4 +258,120 @@ int calibrate_host(int d, int hkv, int hq, float sm_scale, const float *q_cal, i
   return OSCAR_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Lloyd-Max codebook ([A] summary and outlook: a Lloyd-Max codebook for the
+// 2-bit codes).  Every calibration token takes the write path up to its codes
+// (the arithmetic order of the append kernels), the normalised values
+// u = (x - zero) / scale of its groups with a non-zero scale are collected,
+// and a 4-level Lloyd-Max quantiser of them, rounded to the 1/32 grid, gives
+// the head's levels.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr double kInvSqrt128 = 0x1.6a09e667f3bcdp-4;   // nearest double to 1/sqrt(128)
+
+#pragma clang fp contract(off)
+// u values of one token x [d] (float32 holding bf16), d = 128.
+void token_normalised(int d, const float *x, const float *U, float tau, std::vector<float> &out) {
+  double y[128];
+  for (int j = 0; j < d; ++j) y[j] = 0.0;
+  for (int k = 0; k < d; ++k) {   // S1: k ascending, one accumulator per output
+    const double xk = (double)x[k];
+    const float *ur = U + (size_t)k * d;
+    for (int j = 0; j < d; ++j) y[j] += xk * (double)ur[j];
+  }
+  for (int h = 1; h < d; h <<= 1)   // S2: butterfly stages 1, 2, ..., 64
+    for (int i = 0; i < d; ++i)
+      if ((i & h) == 0) {
+        const double a = y[i], b = y[i + h];
+        y[i] = a + b;
+        y[i + h] = a - b;
+      }
+  float xr[128];
+  for (int pos = 0; pos < d; ++pos) {   // S3, S4, S5, S6
+    const int src = bitrev7(pos);
+    const float v = (float)(y[src] * kInvSqrt128);
+    xr[pos] = std::fmin(std::fmax(v, -tau), tau);
+  }
+  const float za = (tau + tau) / 255.0f, sb = (tau + tau) / 765.0f;
+  for (int g = 0; g < d / 64; ++g) {   // S7: group metadata, then u
+    const float *xg = xr + 64 * g;
+    float mx = xg[0], mn = xg[0];
+    for (int c = 1; c < 64; ++c) {
+      mx = std::fmax(mx, xg[c]);
+      mn = std::fmin(mn, xg[c]);
+    }
+    const float sg = (mx - mn) / 3.0f;
+    float z8 = 0.0f, s8 = 0.0f;
+    if (za > 0.0f) z8 = std::fmin(std::fmax(std::nearbyint((mn + tau) / za), 0.0f), 255.0f);
+    if (sb > 0.0f) s8 = std::fmin(std::fmax(std::nearbyint(sg / sb), 0.0f), 255.0f);
+    const float zf = z8 * za - tau;
+    const float sf = s8 * sb;
+    if (sf == 0.0f) continue;
+    for (int c = 0; c < 64; ++c) out.push_back((xg[c] - zf) / sf);
+  }
+}
+#pragma clang fp contract(on)
+
+// Lloyd-Max levels of the sorted samples x, from (0, 1, 2, 3).
+void lloyd_max4(const std::vector<double> &x, double c[4]) {
+  std::vector<double> csum(x.size() + 1, 0.0);
+  for (size_t i = 0; i < x.size(); ++i) csum[i + 1] = csum[i] + x[i];
+  for (int k = 0; k < 4; ++k) c[k] = (double)k;
+  for (int it = 0; it < 1000; ++it) {
+    size_t edges[5];
+    edges[0] = 0;
+    edges[4] = x.size();
+    for (int k = 0; k < 3; ++k) {
+      const double t = (c[k] + c[k + 1]) / 2;
+      edges[k + 1] = (size_t)(std::lower_bound(x.begin(), x.end(), t) - x.begin());
+    }
+    double nc[4], moved = 0.0;
+    for (int k = 0; k < 4; ++k) {
+      nc[k] = c[k];
+      if (edges[k + 1] > edges[k])
+        nc[k] = (csum[edges[k + 1]] - csum[edges[k]]) / (double)(edges[k + 1] - edges[k]);
+      moved = std::max(moved, std::fabs(nc[k] - c[k]));
+    }
+    for (int k = 0; k < 4; ++k) c[k] = nc[k];
+    if (moved <= 1e-12) break;
+  }
+}
+
+}  // namespace
+
+int calibrate_codebook_host(int d, int hkv, const float *U, const float *tau, const float *x_cal, int64_t n,
+                            uint32_t *levels, char *err, size_t err_len) {
+  if (d != 128) {
+    snprintf(err, err_len, "codebook calibration needs head_dim 128");
+    return OSCAR_ENOTSUP;
+  }
+  for (int h = 0; h < hkv; ++h) {
+    if (!(tau[h] >= 0.0f) || !std::isfinite(tau[h])) {
+      snprintf(err, err_len, "tau of head %d is not a finite non-negative value", h);
+      return OSCAR_EINVAL;
+    }
+  }
+  parallel_for(hkv, [&](int, int64_t h) {
+    const float *Uh = U + (size_t)h * d * d;
+    const float *xh = x_cal + (size_t)h * n * d;
+    std::vector<float> u;
+    u.reserve((size_t)n * d);
+    for (int64_t t = 0; t < n; ++t) token_normalised(d, xh + (size_t)t * d, Uh, tau[h], u);
+    std::vector<double> x(u.begin(), u.end());
+    std::sort(x.begin(), x.end());
+    double c[4];
+    lloyd_max4(x, c);
+    int nk[4];
+    for (int k = 0; k < 4; ++k) nk[k] = (int)std::min(96.0, std::max(0.0, std::nearbyint(c[k] * 32.0)));
+    for (int k = 1; k < 4; ++k) nk[k] = std::max(nk[k], nk[k - 1] + 1);
+    for (int k = 3; k >= 0; --k) {
+      nk[k] = std::min(nk[k], 96 - (3 - k));
+      if (k < 3) nk[k] = std::min(nk[k], nk[k + 1] - 1);
+    }
+    levels[h] = (uint32_t)nk[0] | ((uint32_t)nk[1] << 8) | ((uint32_t)nk[2] << 16) | ((uint32_t)nk[3] << 24);
+  });
+  return OSCAR_OK;
+}
+
 }  // namespace oscar

@@ -94,6 +94,13 @@ __device__ __forceinline__ v4i unpack16_v(uint32_t w) {
   return r;
 }
 
+// Every byte of w (a 2-bit code 0..3) replaced by byte `code` of the codebook
+// word lut (its level n_code, <= 96): one v_perm_b32.
+__device__ __forceinline__ int lut_bytes(int w, uint32_t lut) { return (int)__builtin_amdgcn_perm(0u, lut, (uint32_t)w); }
+__device__ __forceinline__ v4i lut4(v4i r, uint32_t lut) {
+  return v4i{lut_bytes(r[0], lut), lut_bytes(r[1], lut), lut_bytes(r[2], lut), lut_bytes(r[3], lut)};
+}
+
 // Byte i of a word as a float (one v_cvt_f32_ubyte<i>).
 __device__ __forceinline__ float ubyte_f(uint32_t w, int i) { return (float)((w >> (8 * i)) & 0xFFu); }
 
@@ -302,6 +309,7 @@ template <int MT>
 struct QueryOps {
   v4i A[MT][2];
   float qa[MT], qb0[MT], qb1[MT], qc[MT];
+  uint32_t lutk, lutv;   // codebook words (LUT scans)
 };
 
 // One 64-token history page for MT M-tiles of 4 query heads.
@@ -315,13 +323,17 @@ struct QueryOps {
 // codes on the int8 MFMA.  Small weights must survive: at long context most
 // of the softmax mass can sit in weights far below the page maximum.  The
 // zero-point part sum(w * zero) stays in float.
-template <int MT, bool FULL>
+// With LUT the codes stand for codebook levels: every unpacked code byte is
+// replaced by its level n (<= 96) before the products, the 1/32 of the
+// level grid is in qa and the page's weight step, and the value results are
+// combined in float (an int32 of three byte planes could overflow).
+template <int MT, bool FULL, bool LUT>
 __device__ __forceinline__ void int2_page(const PageRegs &r, int valid, const QueryOps<MT> &qo, HistState<MT> &st,
                                           v4i *wl) {
   const int lane = threadIdx.x & 63, n = lane & 15, q = lane >> 4;
   // this lane's weights meet value-code register n % 4 (see unpack16_v)
   // (kWScale / 4^s for s = n % 4 < 3, else kWScale: exponent steps 0, 2, 4, 0)
-  const float wsc = __int_as_float(__float_as_int(kWScale) - (int)(((0x00040200u >> (8 * (n & 3))) & 0xFFu) << 23));
+  const float wsc = LUT ? kWScale : __int_as_float(__float_as_int(kWScale) - (int)(((0x00040200u >> (8 * (n & 3))) & 0xFFu) << 23));
   const uint32_t kmw[4] = {r.km.x, r.km.y, r.km.z, r.km.w};
   const uint32_t vmw[4] = {r.vm.x, r.vm.y, r.vm.z, r.vm.w};
   float lg[MT][4];
@@ -329,8 +341,12 @@ __device__ __forceinline__ void int2_page(const PageRegs &r, int valid, const Qu
   v4i CK[4][MT];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
-    const v4i B0 = unpack16(r.kc[tt].x);
-    const v4i B1 = unpack16(r.kc[tt].y);
+    v4i B0 = unpack16(r.kc[tt].x);
+    v4i B1 = unpack16(r.kc[tt].y);
+    if constexpr (LUT) {
+      B0 = lut4(B0, qo.lutk);
+      B1 = lut4(B1, qo.lutk);
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
       CK[tt][mt] = mfma_i8(qo.A[mt][1], B1, mfma_i8(qo.A[mt][0], B0, v4i{0, 0, 0, 0}));
@@ -383,7 +399,7 @@ __device__ __forceinline__ void int2_page(const PageRegs &r, int valid, const Qu
     // approximate reciprocal: kq may exceed kWScale / wmax by an ulp, which
     // the margin in kWScale absorbs; pscale is exact in the same sense
     const float kq = wmax > 0.f ? wsc * __builtin_amdgcn_rcpf(wmax) : 0.f;
-    pscale[mt] = wmax * (1.0f / kWScale);
+    pscale[mt] = wmax * (LUT ? 1.0f / (32.0f * kWScale) : 1.0f / kWScale);
     uint32_t u0[4], u1[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
@@ -414,7 +430,7 @@ __device__ __forceinline__ void int2_page(const PageRegs &r, int valid, const Qu
   v4i C[8][MT];
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
-    const v4i Bv = unpack16_v(r.vc[nt]);
+    const v4i Bv = LUT ? lut4(unpack16(r.vc[nt]), qo.lutv) : unpack16_v(r.vc[nt]);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) C[nt][mt] = mfma_i8(Aw[mt][nt >> 2], Bv, v4i{0, 0, 0, 0});
   }
@@ -422,13 +438,20 @@ __device__ __forceinline__ void int2_page(const PageRegs &r, int valid, const Qu
   for (int nt = 0; nt < 8; ++nt) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      // sum over 64 tokens of u * code <= 8355000 * 3 * 64 < 2^31: exact in int32
-      // two shift-adds; the empty asm (on a VALU result) keeps the compiler
-      // from re-associating them into two shifts and a three-way add
-      int t = (int)(((unsigned)C[nt][mt][0] << 8) + (unsigned)C[nt][mt][1]);
-      asm("" : "+v"(t));
-      const int val = (int)(((unsigned)t << 8) + (unsigned)C[nt][mt][2]);
-      st.facc[mt][nt] = fmaf((float)val, pscale[mt], st.facc[mt][nt]);
+      if constexpr (LUT) {
+        // each byte plane's sum (at most 128 * 96 * 64 in magnitude) is exact
+        // in int32; the planes are weighted in float
+        const float val = fmaf((float)C[nt][mt][0], 65536.0f, fmaf((float)C[nt][mt][1], 256.0f, (float)C[nt][mt][2]));
+        st.facc[mt][nt] = fmaf(val, pscale[mt], st.facc[mt][nt]);
+      } else {
+        // sum over 64 tokens of u * code <= 8355000 * 3 * 64 < 2^31: exact in int32
+        // two shift-adds; the empty asm (on a VALU result) keeps the compiler
+        // from re-associating them into two shifts and a three-way add
+        int t = (int)(((unsigned)C[nt][mt][0] << 8) + (unsigned)C[nt][mt][1]);
+        asm("" : "+v"(t));
+        const int val = (int)(((unsigned)t << 8) + (unsigned)C[nt][mt][2]);
+        st.facc[mt][nt] = fmaf((float)val, pscale[mt], st.facc[mt][nt]);
+      }
     }
   }
 }
@@ -439,10 +462,16 @@ struct ValuWave {
   float (*acc)[64][2];   // [GH][lane][2]
 };
 
+// The reconstruction level of a code (byte `code` of the codebook word / 32;
+// the code itself on the uniform grid).
+__device__ __forceinline__ float level_f(uint32_t lut, uint32_t code) {
+  return (float)((lut >> (8 * code)) & 0xFFu) * (1.0f / 32.0f);
+}
+
 template <bool FULL>
 __device__ __forceinline__ void int2_page_valu(const uint8_t *P, int valid, int G, const float *qrot,
                                                const float (*qsum)[2], float sl2, const MetaSteps &ms,
-                                               ValuWave st, float (*pw)[4]) {
+                                               ValuWave st, float (*pw)[4], uint32_t lutk, uint32_t lutv) {
   const int lane = threadIdx.x & 63;
   const int t = lane;
   const uint4 k0 = *(const uint4 *)(P + kKCodes + t * 32);
@@ -467,7 +496,7 @@ __device__ __forceinline__ void int2_page_valu(const uint8_t *P, int valid, int 
     for (int w = 0; w < 8; ++w) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float code = (float)((kw[w] >> (2 * j)) & 3u);
+        const float code = level_f(lutk, (kw[w] >> (2 * j)) & 3u);
         if (w < 4) d0 = fmaf(qr[16 * w + j], code, d0);
         else d1 = fmaf(qr[16 * w + j], code, d1);
       }
@@ -501,8 +530,8 @@ __device__ __forceinline__ void int2_page_valu(const uint8_t *P, int valid, int 
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
           const int tt = 16 * bb + 4 * j + s4, sh = 8 * bb + 2 * s4;
-          const float cd0 = (float)((w0[j] >> sh) & 3u);
-          const float cd1 = (float)((w1[j] >> sh) & 3u);
+          const float cd0 = level_f(lutv, (w0[j] >> sh) & 3u);
+          const float cd1 = level_f(lutv, (w1[j] >> sh) & 3u);
           const float ps = pw[tt][2 * g], pz = pw[tt][2 * g + 1];
           a0 = fmaf(ps, cd0, a0 + pz);
           a1 = fmaf(ps, cd1, a1 + pz);
@@ -936,7 +965,7 @@ __device__ __forceinline__ void pipe_prologue(PagePipe<NW, PF> &p, const PoolVie
 // One page of the pipeline: wait for its copy, read it, refill the pipeline
 // and fold the page into the state.  A page whose copy was never issued (its
 // block-table entry is out of range) is skipped.
-template <int MT, int NW, int PF, bool FULL>
+template <int MT, int NW, int PF, bool FULL, bool LUT>
 __device__ __forceinline__ void pipe_step(PagePipe<NW, PF> &p, const PoolView &pv, int i, int n_hist,
                                           const QueryOps<MT> &qo, HistState<MT> &st, v4i *wl, int lane) {
   const int n = lane & 15, q = lane >> 4;
@@ -953,21 +982,21 @@ __device__ __forceinline__ void pipe_step(PagePipe<NW, PF> &p, const PoolView &p
   }
   if (ok) {
     const int valid = FULL ? kPageTokens : min(kPageTokens, n_hist - (p.first + i * NW) * kPageTokens);
-    int2_page<MT, FULL>(cur, valid, qo, st, wl);
+    int2_page<MT, FULL, LUT>(cur, valid, qo, st, wl);
   }
 }
 
 // Consume every page of the pipeline (the prologue must have been issued).
 // Only the last page of the history can be partly filled, so every page of
 // the wave but possibly its last runs the full-page path.
-template <int MT, int NW, int PF>
+template <int MT, int NW, int PF, bool LUT>
 __device__ __forceinline__ void pipe_scan(PagePipe<NW, PF> &p, const PoolView &pv, int n_hist, const QueryOps<MT> &qo,
                                           HistState<MT> &st, v4i *wl, int lane) {
   const int full_pages = n_hist / kPageTokens;   // global pages [0, full_pages) hold 64 tokens
   const int nfull = min(p.npg, max(0, (full_pages - p.first + NW - 1) / NW));
   int i = 0;
-  for (; i < nfull; ++i) pipe_step<MT, NW, PF, true>(p, pv, i, n_hist, qo, st, wl, lane);
-  for (; i < p.npg; ++i) pipe_step<MT, NW, PF, false>(p, pv, i, n_hist, qo, st, wl, lane);
+  for (; i < nfull; ++i) pipe_step<MT, NW, PF, true, LUT>(p, pv, i, n_hist, qo, st, wl, lane);
+  for (; i < p.npg; ++i) pipe_step<MT, NW, PF, false, LUT>(p, pv, i, n_hist, qo, st, wl, lane);
 }
 
 // Dynamic page order within a workgroup (48 to kDynMaxPages pages, one
@@ -991,7 +1020,7 @@ struct DynPages {
 // block-table entry is read together with the page.  Returns true on the
 // wave that drew index nfull: it owns the workgroup's partly filled last
 // page, if any.
-template <int MT, int NW, int PF>
+template <int MT, int NW, int PF, bool LUT>
 __device__ __forceinline__ bool pipe_scan_dyn(PagePipe<NW, PF> &p, const PoolView &pv, int nfull, DynPages *dp,
                                               const QueryOps<MT> &qo, HistState<MT> &st, v4i *wl, int lane) {
   static_assert(PF == 2, "the dynamic order is written for two page buffers");
@@ -1023,7 +1052,7 @@ __device__ __forceinline__ bool pipe_scan_dyn(PagePipe<NW, PF> &p, const PoolVie
       }
       if (lane == 0) jn = atomicAdd(&dp->next_page, 1);
     }
-    if (ok) int2_page<MT, true>(cur, kPageTokens, qo, st, wl);
+    if (ok) int2_page<MT, true, LUT>(cur, kPageTokens, qo, st, wl);
     have_cur = have_nxt;
     have_nxt = have_new;
     c ^= 1;
@@ -1045,7 +1074,7 @@ __device__ __forceinline__ void hist_reset(HistState<MT> &st) {
 // Query operands of one head group into registers, from prepared LDS copies
 // (qc[h] = {delta, Q_0, Q_1}), with the K metadata steps of the KV head
 // folded in (see QueryOps).
-template <int MT, int GH>
+template <int MT, int GH, bool LUT>
 __device__ __forceinline__ void load_query_ops(const v4i *aq, const float (*qc)[4], int G, float sl2,
                                                const MetaSteps &ms, int lane, QueryOps<MT> &qo) {
   const int q = lane >> 4;
@@ -1056,7 +1085,7 @@ __device__ __forceinline__ void load_query_ops(const v4i *aq, const float (*qc)[
     const int h = min(4 * mt + q, GH - 1);
     const bool hv = 4 * mt + q < G;
     const float q0 = hv ? qc[h][1] * sl2 : 0.f, q1 = hv ? qc[h][2] * sl2 : 0.f;
-    qo.qa[mt] = hv ? qc[h][0] * sl2 * ms.kb : 0.f;
+    qo.qa[mt] = hv ? qc[h][0] * sl2 * ms.kb * (LUT ? 1.0f / 32.0f : 1.0f) : 0.f;
     qo.qb0[mt] = q0 * ms.ka;
     qo.qb1[mt] = q1 * ms.ka;
     qo.qc[mt] = -ms.ktau * (q0 + q1);
@@ -1251,7 +1280,7 @@ __device__ void split_epilogue(const DecArgs &a, int b, int kv, int split, ScanS
   }
 }
 
-template <int MT, int GH, int NW, bool DYN>
+template <int MT, int GH, int NW, bool DYN, bool LUT>
 __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float *dst,
                               ScanSmem<MT, GH, NW, true> &sm, DynPages *dp) {
   constexpr int PF = ScanSmem<MT, GH, NW, true>::PF;
@@ -1274,6 +1303,8 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   // 0..255) the query preparation's loads.  The waves without preparation
   // work start their copies as soon as those land.
   float tk = a.rv.tau_K[kv], tv = a.rv.tau_V[kv];
+  const uint32_t lutk = LUT ? levels_of(a.rv, kv, false) : OSCAR_UNIFORM_LEVELS;
+  const uint32_t lutv = LUT ? levels_of(a.rv, kv, true) : OSCAR_UNIFORM_LEVELS;
   const TileCtx tc{max(0, L), pv.sink_slot[b]};
   PagePipe<NW, PF> pipe;
   pipe_init(pipe, pv, b, kv, pg0, pg1, sm.pbuf[wave], wave, lane);
@@ -1329,7 +1360,9 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   });
   const MetaSteps ms = meta_steps(tk, tv);
   QueryOps<MT> qo;
-  load_query_ops<MT, GH>(sm.q.aq, sm.q.qc, G, pv.sm_scale * kLog2e, ms, lane, qo);
+  load_query_ops<MT, GH, LUT>(sm.q.aq, sm.q.qc, G, pv.sm_scale * kLog2e, ms, lane, qo);
+  qo.lutk = lutk;
+  qo.lutv = lutv;
   __syncthreads();   // the query scratch is reused by the weights and the BF16 tiles
   // BF16 tiles: this workgroup takes tiles u = split + S k.  Short scans
   // (under 16 pages per wave): tiles k < 4 run first on waves 3..0 (the
@@ -1372,7 +1405,7 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
 #pragma unroll
   for (int i = 0; i < MT * 2; ++i) wl[i * 64 + lane] = v4i{0, 0, 0, 0};
   if (dyn) {
-    if (pipe_scan_dyn<MT, NW, PF>(pipe, pv, nfull, dp, qo, st, wl, lane) && nfull < npg_wg) {
+    if (pipe_scan_dyn<MT, NW, PF, LUT>(pipe, pv, nfull, dp, qo, st, wl, lane) && nfull < npg_wg) {
       // the partly filled last page, on the wave that drew its index (its
       // buffers are idle: every copy it issued has been consumed)
       const int ph = __builtin_amdgcn_readfirstlane(dp->bt[nfull]);
@@ -1382,13 +1415,13 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
         PageRegs cur;
         load_page(cur, (const uint8_t *)pipe.bufs[0], lane & 15, lane >> 4);
         wait_lds_reads();
-        int2_page<MT, false>(cur, n_hist - (pg0 + nfull) * kPageTokens, qo, st, wl);
+        int2_page<MT, false, LUT>(cur, n_hist - (pg0 + nfull) * kPageTokens, qo, st, wl);
       } else {
         pipe.bad = true;
       }
     }
   } else {
-    pipe_scan<MT, NW, PF>(pipe, pv, n_hist, qo, st, wl, lane);
+    pipe_scan<MT, NW, PF, LUT>(pipe, pv, n_hist, qo, st, wl, lane);
   }
   if (pipe.bad && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
   if constexpr (MT == 1) {
@@ -1451,6 +1484,7 @@ __device__ void run_scan_valu(const DecArgs &a, int b, int kv, int split, float 
   const ValuWave st{sm.m[wave], sm.l[wave], sm.vacc[wave]};
   const float sl2 = pv.sm_scale * kLog2e;
   const MetaSteps ms = meta_steps(a.rv, kv);
+  const uint32_t lutk = levels_of(a.rv, kv, false), lutv = levels_of(a.rv, kv, true);
   const int32_t *btab = pv.block_table + (size_t)b * pv.max_pages;
   bool bad = false;
   for (int pg = pg0 + wave; pg < pg1; pg += NW) {
@@ -1461,8 +1495,8 @@ __device__ void run_scan_valu(const DecArgs &a, int b, int kv, int split, float 
     }
     const uint8_t *P = pv.pages + ((size_t)ph * pv.hkv + kv) * kPageBytes;
     const int valid = min(kPageTokens, n_hist - pg * kPageTokens);
-    if (valid == kPageTokens) int2_page_valu<true>(P, valid, G, qrot, sm.qsum, sl2, ms, st, sm.wave[wave].pw);
-    else int2_page_valu<false>(P, valid, G, qrot, sm.qsum, sl2, ms, st, sm.wave[wave].pw);
+    if (valid == kPageTokens) int2_page_valu<true>(P, valid, G, qrot, sm.qsum, sl2, ms, st, sm.wave[wave].pw, lutk, lutv);
+    else int2_page_valu<false>(P, valid, G, qrot, sm.qsum, sl2, ms, st, sm.wave[wave].pw, lutk, lutv);
   }
   if (bad && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
   __syncthreads();
@@ -1756,7 +1790,7 @@ __device__ void merge_plain(const DecArgs &a, int b, int kv, const float *parts,
 
 // Register budget: three waves per SIMD for one M-tile of heads (G <= 4), two
 // otherwise; the VALU reference takes what it needs.
-template <int MT, int GH, bool MFMA>
+template <int MT, int GH, bool MFMA, bool LUT>
 __global__ void __launch_bounds__((64 * scan_waves<MT, MFMA>()))
 __attribute__((amdgpu_waves_per_eu(MFMA ? (MT == 1 ? 3 : 2) : 1)))
 decode_scan_kernel(DecArgs a) {
@@ -1784,14 +1818,14 @@ decode_scan_kernel(DecArgs a) {
     // the split's partial leaves the rotated basis in the split itself; with
     // one split the output is already written
     __shared__ DynPages dp;
-    run_scan_mfma<MT, GH, NW, true>(a, b, kv, split, dst, sm.s, &dp);
+    run_scan_mfma<MT, GH, NW, true, LUT>(a, b, kv, split, dst, sm.s, &dp);
     if (S == 1 || !arrive_last(&a.counters[bh], S, &last_flag)) return;
     merge_plain<GH, 64 * NW>(a, b, kv, parts, S, sm.pm);
     return;
   } else if constexpr (MFMA) {
     // several M-tiles (8 waves, heavier pages): the static page order
     // measured faster on the GQA-12 shared-prefix workload
-    run_scan_mfma<MT, GH, NW, false>(a, b, kv, split, dst, sm.s, nullptr);
+    run_scan_mfma<MT, GH, NW, false, LUT>(a, b, kv, split, dst, sm.s, nullptr);
   }
   else run_scan_valu<MT, GH, NW>(a, b, kv, split, dst, sm.s);
   if (S == 1) {
@@ -1857,6 +1891,9 @@ hipError_t launch_decode(const PoolView &pv, const RotView &rv, const uint16_t *
             (float *)(ws + plan.off_qrot), (float *)(ws + plan.off_part),
             plan.n_splits, plan.n_chunks, plan.pages_per_split, plan.n_parts};
   const bool mfma = is_mfma(variant);
+  // the codebook scans when either tensor has a codebook (the other then
+  // takes the uniform levels through the same lookup)
+  const bool lut = rv.lev_K != nullptr || rv.lev_V != nullptr;
   hipError_t e;
   const dim3 sgrid(BH * plan.n_splits);
 #define OSCAR_LAUNCH(MT, GH)                                                                         \
@@ -1864,13 +1901,15 @@ hipError_t launch_decode(const PoolView &pv, const RotView &rv, const uint16_t *
     if (!mfma) {                                                                                     \
       hipLaunchKernelGGL((decode_pre_kernel<MT, GH>), dim3(BH), dim3(256), 0, s, a);                 \
       if ((e = hipGetLastError()) != hipSuccess) return e;                                           \
-    }                                                                                                \
-    if (mfma)                                                                                        \
-      hipLaunchKernelGGL((decode_scan_kernel<MT, GH, true>), sgrid, dim3(64 * scan_waves<MT, true>()), \
-                         0, s, a);                                                                   \
-    else                                                                                             \
-      hipLaunchKernelGGL((decode_scan_kernel<MT, GH, false>), sgrid,                                 \
+      hipLaunchKernelGGL((decode_scan_kernel<MT, GH, false, true>), sgrid,                           \
                          dim3(64 * scan_waves<MT, false>()), 0, s, a);                               \
+    } else if (lut) {                                                                                \
+      hipLaunchKernelGGL((decode_scan_kernel<MT, GH, true, true>), sgrid,                            \
+                         dim3(64 * scan_waves<MT, true>()), 0, s, a);                                \
+    } else {                                                                                         \
+      hipLaunchKernelGGL((decode_scan_kernel<MT, GH, true, false>), sgrid,                           \
+                         dim3(64 * scan_waves<MT, true>()), 0, s, a);                                \
+    }                                                                                                \
   } while (0)
   if (G <= 4) OSCAR_LAUNCH(1, 4);
   else if (G <= 8) OSCAR_LAUNCH(2, 8);

@@ -106,7 +106,30 @@ struct PoolView {
 
 struct RotView {
   const float *U_K, *U_V, *tau_K, *tau_V;
+  const uint32_t *lev_K, *lev_V;   // codebooks (NULL: uniform grid)
 };
+
+// The codebook word (byte k = n_k) of KV head h, key or value tensor.
+__device__ __forceinline__ uint32_t levels_of(const RotView &rv, int h, bool is_v) {
+  const uint32_t *p = is_v ? rv.lev_V : rv.lev_K;
+  return p ? p[h] : OSCAR_UNIFORM_LEVELS;
+}
+
+// Code of a normalised group value u = (x - zero) / scale: the nearest of the
+// four levels n_k / 32, thresholds at the midpoints (n_k + n_{k+1}) / 64
+// (exact in float32), a tie at the middle threshold going up and at the outer
+// ones down.  On the uniform grid this is rint(u) clamped to [0, 3].
+struct CodeThresholds {
+  float t0, t1, t2;
+};
+__host__ __device__ inline CodeThresholds code_thresholds(uint32_t lev) {
+  const float n0 = (float)(lev & 0xFFu), n1 = (float)((lev >> 8) & 0xFFu);
+  const float n2 = (float)((lev >> 16) & 0xFFu), n3 = (float)(lev >> 24);
+  return CodeThresholds{(n0 + n1) * (1.0f / 64.0f), (n1 + n2) * (1.0f / 64.0f), (n2 + n3) * (1.0f / 64.0f)};
+}
+__host__ __device__ inline uint32_t level_code(float u, const CodeThresholds &t) {
+  return (uint32_t)(u > t.t0) + (uint32_t)(u >= t.t1) + (uint32_t)(u > t.t2);
+}
 
 // Decode workspace carve-up (offsets in bytes from the workspace base).
 struct DecodePlan {
@@ -153,6 +176,10 @@ struct Bf16Plan {
 Bf16Plan make_bf16_plan(int batch, int hkv, int hq, int max_pages);
 hipError_t launch_bf16_decode(const Bf16View &v, const uint16_t *q, float *out, uint8_t *ws,
                               const Bf16Plan &plan, hipStream_t s);
+
+// Host Lloyd-Max codebook of one tensor (float64 iteration).
+int calibrate_codebook_host(int d, int hkv, const float *U, const float *tau, const float *x_cal, int64_t n,
+                            uint32_t *levels, char *err, size_t err_len);
 
 // Host calibration (float64).
 int calibrate_host(int d, int hkv, int hq, float sm_scale, const float *q_cal, int64_t n_q,

@@ -20,8 +20,9 @@
 //   S7 per 64-channel group: s = (max - min) / 3 (float32 IEEE); with
 //      a = (tau + tau) / 255 and b = (tau + tau) / 765: z8 = clamp(rint((min +
 //      tau) / a), 0, 255), s8 = clamp(rint(s / b), 0, 255) (0 if tau is 0);
-//      zero = z8 a - tau, scale = s8 b; code = clamp(rint((x - zero) /
-//      scale), 0, 3), all codes 0 if scale == 0.  Everything float32 (16
+//      zero = z8 a - tau, scale = s8 b; code = the nearest codebook level
+//      of u = (x - zero) / scale (level_code: on the uniform grid
+//      clamp(rint(u), 0, 3)), all codes 0 if scale == 0.  Everything float32 (16
 //      metadata bits per group: the density of the pages' 2.28 bits per
 //      element at 128K; the encoding relative to tau is this library's);
 //   S8 pack four codes per byte (page layout in oscar.h).
@@ -52,8 +53,9 @@ struct AppendArgs {
 // lane).  Zero and scale are 8-bit codes on grids over [-tau, tau] and
 // [0, 2 tau / 3] (steps a = 2 tau / 255, b = 2 tau / 765): z8 = rint((min +
 // tau) / a), s8 = rint(s / b), clamped to [0, 255] (0 when tau is 0); codes
-// use the decoded zero z8 a - tau and scale s8 b.
-__device__ __forceinline__ uint32_t quantize_group(float v, float tau, uint32_t &meta) {
+// use the decoded zero z8 a - tau and scale s8 b, and the head's codebook
+// thresholds (level_code; on the uniform grid rint(u) clamped to [0, 3]).
+__device__ __forceinline__ uint32_t quantize_group(float v, float tau, const CodeThresholds &th, uint32_t &meta) {
   v = fminf(fmaxf(v, -tau), tau);
   const float mx = wave_max(v), mn = wave_min(v);
   const float s = __fdiv_rn(mx - mn, 3.0f);
@@ -63,21 +65,17 @@ __device__ __forceinline__ uint32_t quantize_group(float v, float tau, uint32_t 
   if (b > 0.0f) s8 = (uint32_t)fminf(fmaxf(rintf(__fdiv_rn(s, b)), 0.0f), 255.0f);
   const float zf = (float)z8 * a - tau;
   const float sf = (float)s8 * b;
-  uint32_t code = 0;
-  if (sf != 0.0f) {
-    float r = rintf(__fdiv_rn(v - zf, sf));
-    r = fminf(fmaxf(r, 0.0f), 3.0f);
-    code = (uint32_t)r;
-  }
+  const uint32_t code = sf != 0.0f ? level_code(__fdiv_rn(v - zf, sf), th) : 0u;
   meta = s8 | (z8 << 8);
   return code;
 }
 
 // As quantize_group for output channel p; lane p % 64 == 0 stores the
 // group's metadata to meta[p / 64] (the 4-byte entry of the token).
-__device__ __forceinline__ uint32_t quantize_code(float v, float tau, int p, uint16_t *meta) {
+__device__ __forceinline__ uint32_t quantize_code(float v, float tau, const CodeThresholds &th, int p,
+                                                  uint16_t *meta) {
   uint32_t m;
-  const uint32_t code = quantize_group(v, tau, m);
+  const uint32_t code = quantize_group(v, tau, th, m);
   if ((p & 63) == 0) meta[p >> 6] = (uint16_t)m;
   return code;
 }
@@ -210,6 +208,7 @@ append_demote_kernel(AppendArgs a) {
   // S3, S5: the float32 values of the wave's 16 slots, in butterfly order,
   // staged in its own rows of xs (free after S1).  Row stride 132 floats.
   const float tau = (is_v ? a.rv.tau_V : a.rv.tau_K)[h];
+  const CodeThresholds th = code_thresholds(levels_of(a.rv, h, is_v));
   constexpr int kRow = 132;
   float *ys = (float *)&xs[16 * w][0];
   float4 *stat = (float4 *)(ys + 16 * kRow);       // per slot: zero0, scale0, zero1, scale1
@@ -269,8 +268,8 @@ append_demote_kernel(AppendArgs a) {
     const float v0 = fminf(fmaxf(ys[i * kRow + e0], -tau), tau);
     const float v1 = fminf(fmaxf(ys[i * kRow + e1], -tau), tau);
     uint32_t code0 = 0, code1 = 0;
-    if (st.y != 0.0f) code0 = (uint32_t)fminf(fmaxf(rintf(__fdiv_rn(v0 - st.x, st.y)), 0.0f), 3.0f);
-    if (st.w != 0.0f) code1 = (uint32_t)fminf(fmaxf(rintf(__fdiv_rn(v1 - st.z, st.w)), 0.0f), 3.0f);
+    if (st.y != 0.0f) code0 = level_code(__fdiv_rn(v0 - st.x, st.y), th);
+    if (st.w != 0.0f) code1 = level_code(__fdiv_rn(v1 - st.z, st.w), th);
     if (lane == 0) *(uint32_t *)(page + (is_v ? kVMeta : kKMeta) + meta_entry(slot) * 4) = smeta[i];
     if (!is_v) {
       // K row: dword q holds channels 16 q .. 16 q + 15, two bits each
@@ -335,6 +334,7 @@ __global__ void __launch_bounds__(kThreads) append_one_kernel(AppendArgs a) {
   // 128 loads at once.  The length then decides the ring slot and the page.
   const uint16_t nb = (is_v ? a.v_new : a.k_new)[((size_t)b * pv.hkv + h) * kD + j];
   const float tau = (is_v ? a.rv.tau_V : a.rv.tau_K)[h];
+  const CodeThresholds th = code_thresholds(levels_of(a.rv, h, is_v));
   const float *U = (is_v ? a.rv.U_V : a.rv.U_K) + (size_t)h * kD * kD + j;
   float u[kD];
 #pragma unroll
@@ -401,7 +401,8 @@ __global__ void __launch_bounds__(kThreads) append_one_kernel(AppendArgs a) {
       // S3..S8: thread j = output channel p
       const int p = j;
       const float v = (float)(ys[bitrev7(p)] * kInvSqrtD);
-      const uint32_t code = quantize_code(v, tau, p, (uint16_t *)(page + (is_v ? kVMeta : kKMeta) + meta_entry(slot) * 4));
+      const uint32_t code =
+          quantize_code(v, tau, th, p, (uint16_t *)(page + (is_v ? kVMeta : kKMeta) + meta_entry(slot) * 4));
       if (!is_v) {
         uint32_t c = code << (2 * (p & 3));
         c |= (uint32_t)lane_xor_i<1>((int)c);

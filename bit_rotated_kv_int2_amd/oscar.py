@@ -29,8 +29,9 @@ EXPORTED = [
     "oscar_calibrate_rotation", "oscar_quantize_append", "oscar_decode_attention",
     "oscar_decode_workspace_size", "oscar_bf16_decode_attention",
     "oscar_bf16_decode_workspace_size", "oscar_last_error", "oscar_version",
-    "oscar_decode_attention_noalloc",
+    "oscar_decode_attention_noalloc", "oscar_calibrate_codebook",
 ]
+UNIFORM_LEVELS = 0x60402000
 
 
 class OscarLibraryMissing(RuntimeError):
@@ -52,7 +53,8 @@ class Params(ctypes.Structure):
 
 class Rotation(ctypes.Structure):
     _fields_ = [("U_K", ctypes.c_void_p), ("U_V", ctypes.c_void_p),
-                ("tau_K", ctypes.c_void_p), ("tau_V", ctypes.c_void_p)]
+                ("tau_K", ctypes.c_void_p), ("tau_V", ctypes.c_void_p),
+                ("levels_K", ctypes.c_void_p), ("levels_V", ctypes.c_void_p)]
 
 
 class KVPoolC(ctypes.Structure):
@@ -92,6 +94,8 @@ def lib():
     vp, i32, i64, f64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_size_t
     L.oscar_calibrate_rotation.argtypes = [P(Params), vp, i64, vp, vp, i64, f64, f64, vp, vp, vp, vp]
     L.oscar_calibrate_rotation.restype = i32
+    L.oscar_calibrate_codebook.argtypes = [P(Params), vp, vp, vp, i64, vp]
+    L.oscar_calibrate_codebook.restype = i32
     L.oscar_quantize_append.argtypes = [P(Params), P(Rotation), P(KVPoolC), vp, vp, i32, vp]
     L.oscar_quantize_append.restype = i32
     L.oscar_decode_attention.argtypes = [P(Params), P(Rotation), P(KVPoolC), vp, vp, P(DecodeOptions), vp, sz, vp]
@@ -163,6 +167,24 @@ def calibrate_rotation(params: Params, q_cal: np.ndarray, k_cal: np.ndarray, v_c
     return UK, UV, tK, tV
 
 
+def calibrate_codebook(params: Params, U: np.ndarray, tau: np.ndarray, x_cal: np.ndarray) -> np.ndarray:
+    """Lloyd-Max codebook words (uint32 [Hkv]) of one tensor: U float32
+    [Hkv][d][d], tau float32 [Hkv], x_cal float32 [Hkv][n][d] (host)."""
+    Uc = np.ascontiguousarray(U, dtype=np.float32)
+    tc = np.ascontiguousarray(tau, dtype=np.float32)
+    xc = np.ascontiguousarray(x_cal, dtype=np.float32)
+    out = np.zeros(params.num_kv_heads, np.uint32)
+    vp = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    _check(lib().oscar_calibrate_codebook(ctypes.byref(params), vp(Uc), vp(tc), vp(xc), xc.shape[1], vp(out)))
+    return out
+
+
+def levels_word(levels) -> int:
+    """Four level integers n_k (code k stands for n_k / 32) as the codebook word."""
+    n = [int(x) for x in levels]
+    return n[0] | (n[1] << 8) | (n[2] << 16) | (n[3] << 24)
+
+
 # ---------------------------------------------------------------------------
 # Device-side pool and calls
 # ---------------------------------------------------------------------------
@@ -173,15 +195,20 @@ class RotationTensors:
     U_V: "torch.Tensor"
     tau_K: "torch.Tensor"    # float32 [Hkv]
     tau_V: "torch.Tensor"
+    levels_K: Optional["torch.Tensor"] = None   # int32 [Hkv] codebook words, None = uniform grid
+    levels_V: Optional["torch.Tensor"] = None
 
     def c(self) -> Rotation:
-        return Rotation(_ptr(self.U_K), _ptr(self.U_V), _ptr(self.tau_K), _ptr(self.tau_V))
+        return Rotation(_ptr(self.U_K), _ptr(self.U_V), _ptr(self.tau_K), _ptr(self.tau_V),
+                        _ptr(self.levels_K), _ptr(self.levels_V))
 
     @staticmethod
-    def from_numpy(UK, UV, tK, tV, device):
+    def from_numpy(UK, UV, tK, tV, device, levels_K=None, levels_V=None):
         import torch
         f = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
-        return RotationTensors(f(UK), f(UV), f(tK), f(tV))
+        w = lambda a: None if a is None else torch.from_numpy(
+            np.ascontiguousarray(np.asarray(a, dtype=np.uint32).view(np.int32))).to(device)
+        return RotationTensors(f(UK), f(UV), f(tK), f(tV), w(levels_K), w(levels_V))
 
 
 class KVPool:

@@ -106,13 +106,29 @@ typedef struct oscar_params {
  * descending eigenvalue.  The composite rotation of a row vector x is
  * x -> bitrev(FWHT(x U) / sqrt(d)).  tau_* are float32 [Hkv], finite,
  * in (0, 60000].
+ *
+ * levels_K, levels_V (optional, uint32 [Hkv]; NULL = the uniform grid): the
+ * 2-bit codebook of each KV head ([A] summary and outlook: a Lloyd-Max
+ * codebook).  Byte k of a head's word is n_k, and code k stands for
+ * zero + scale * n_k / 32 instead of zero + scale * k; the n_k are strictly
+ * increasing in [0, 96].  The uniform grid is n = (0, 32, 64, 96), i.e. the
+ * word 0x60402000.  A token is given the code of the level nearest to
+ * u = (x - zero) / scale, the thresholds being the midpoints
+ * (n_k + n_{k+1}) / 64, with a tie at the middle threshold going up and at
+ * the outer ones down (on the uniform grid: u rounded half to even and
+ * clamped to [0, 3]).  The same levels must be given to appends and decodes
+ * of a pool.  oscar_calibrate_codebook computes them.
  */
 typedef struct oscar_rotation {
   const float *U_K;
   const float *U_V;
   const float *tau_K;
   const float *tau_V;
+  const uint32_t *levels_K;
+  const uint32_t *levels_V;
 } oscar_rotation;
+
+#define OSCAR_UNIFORM_LEVELS 0x60402000u
 
 /*
  * Mixed-precision KV pool of one layer ([A] token pool; [B] serving):
@@ -159,6 +175,26 @@ int32_t oscar_calibrate_rotation(const oscar_params *p, const float *q_cal, int6
                                  const float *k_cal, const float *v_cal, int64_t n_kv,
                                  double quantile_k, double quantile_v, float *U_K, float *U_V,
                                  float *tau_K, float *tau_V);
+
+/*
+ * Offline Lloyd-Max codebook of one tensor (keys or values) of one layer
+ * ([A] summary and outlook).  HOST pointers, synchronous, float64 Lloyd-Max
+ * iteration.  U [Hkv][d][d] and tau [Hkv] are that tensor's rotation factor
+ * and clip threshold (as in oscar_rotation); x_cal [Hkv][n][d] are float32
+ * holding the bf16 calibration tokens.  Every calibration token goes through
+ * the write path up to its codes (rotation, clip, 8-bit zero and scale per
+ * 64-channel group, exactly as an append computes them); the normalised
+ * values u = (x - zero) / scale of the groups whose scale is not zero feed
+ * a 4-level Lloyd-Max quantiser started from (0, 1, 2, 3) (nearest-level
+ * cells, cell means, until no level moves by more than 1e-12; an empty cell
+ * keeps its level).  Each level is rounded to the nearest 1/32 (half to
+ * even), clamped to [0, 96] and the four made strictly increasing (each
+ * raised to one step above the one below, then lowered to leave one step
+ * for each above).  Output: levels [Hkv] in the format of
+ * oscar_rotation.levels_K.  OSCAR_EINVAL for NULL pointers or n < 1.
+ */
+int32_t oscar_calibrate_codebook(const oscar_params *p, const float *U, const float *tau, const float *x_cal,
+                                 int64_t n, uint32_t *levels);
 
 /*
  * Append n_new tokens to every sequence of the pool ([A] token pool: new

@@ -76,11 +76,17 @@ def oracle_calibration(wl: synth.Workload, layer: int = 0, n_cal: int = 512):
 
 
 def rotation_tensors(cals, device="cuda"):
+    """Device rotation artifact of per-head oracle calibrations; their
+    codebooks, when they have them, as the library's level words."""
     UK = np.stack([c.U_K for c in cals])
     UV = np.stack([c.U_V for c in cals])
     tK = np.array([c.tau_K for c in cals], np.float32)
     tV = np.array([c.tau_V for c in cals], np.float32)
-    return O.RotationTensors.from_numpy(UK, UV, tK, tV, device)
+    lk = lv = None
+    if cals[0].levels_K is not None:
+        lk = np.array([O.levels_word(c.levels_K) for c in cals], np.uint32)
+        lv = np.array([O.levels_word(c.levels_V) for c in cals], np.uint32)
+    return O.RotationTensors.from_numpy(UK, UV, tK, tV, device, levels_K=lk, levels_V=lv)
 
 
 def pool_view(pool: O.KVPool, b: int) -> O.KVPoolC:

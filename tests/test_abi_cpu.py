@@ -130,3 +130,22 @@ def test_calibration_matches_oracle():
     assert np.max(np.abs(UV[0] - ref.U_V)) <= 2e-7
     assert abs(float(tK[0]) - float(ref.tau_K)) <= 2 * np.spacing(np.float32(ref.tau_K))
     assert abs(float(tV[0]) - float(ref.tau_V)) <= 2 * np.spacing(np.float32(ref.tau_V))
+
+
+@pytest.mark.slow
+def test_codebook_calibration_matches_oracle():
+    """oscar_calibrate_codebook (host C++) against the oracle's Lloyd-Max
+    codebook on the same rotation artifact and calibration tokens."""
+    wl = synth.WORKLOADS["tiny-4k"]
+    q, k, v = synth.calibration_set(wl, 0, n_cal=512)
+    f = synth.bf16_bits_to_f32
+    qf, kf, vf = f(q), f(k), f(v)
+    cal = R.calibrate_head(qf, kf[0], vf[0], 1 / np.sqrt(128))
+    cb = R.calibrate_codebook(cal, kf[0], vf[0])
+    p = O.make_params(1, 4)
+    wk = O.calibrate_codebook(p, cal.U_K[None], np.array([cal.tau_K], np.float32), kf)
+    wv = O.calibrate_codebook(p, cal.U_V[None], np.array([cal.tau_V], np.float32), vf)
+    assert int(wk[0]) == O.levels_word(cb.levels_K), (hex(int(wk[0])), cb.levels_K)
+    assert int(wv[0]) == O.levels_word(cb.levels_V), (hex(int(wv[0])), cb.levels_V)
+    with pytest.raises(O.OscarError):
+        O.calibrate_codebook(p, cal.U_K[None], np.array([cal.tau_K], np.float32), kf[:, :0])
