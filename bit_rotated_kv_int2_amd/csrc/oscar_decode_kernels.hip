@@ -34,6 +34,7 @@
 //   Codes enter unscaled: the zero point is added as z * sum(q) (logits) and
 //   sum(p * z) (values).
 #include <mutex>
+#include <type_traits>
 
 #include "oscar_wave.h"
 
@@ -136,18 +137,36 @@ struct QSmem {
   float qc[GH][4];         // delta, Q0, Q1 (per-group sums of the fixed-point q~)
 };
 
-// Query preparation for one (sequence, KV head), by the whole workgroup (any
-// multiple of 64 threads >= 256): q~ = bitrev(FWHT(q U_K) / sqrt(d)) for its
-// G query heads, then per head a 15-bit fixed-point copy split into hi/lo
-// int8 bytes laid out as the A operand of the logit MFMA (rows: head h ->
-// 4h + {group 0 hi, group 0 lo, group 1 hi, group 1 lo}).  Results stay in
-// `sm`; with `qrot` non-null the float q~ is also written there.
-// after_loads() runs on every thread once the global loads of the
-// preparation (threads 0..255) have been consumed, before the first barrier.
+// Barrier among waves 0..3 of a workgroup (the other waves take no part): a
+// shared counter, zero at the workgroup's first s_barrier, that each of the
+// four waves raises by one and then polls until it reaches `target` (4 for
+// the first such barrier, 8 for a second one, ...).
+__device__ __forceinline__ void four_wave_sync(int *ctr, int target) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) __builtin_amdgcn_s_sleep(1);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Query preparation for one (sequence, KV head): q~ = bitrev(FWHT(q U_K) /
+// sqrt(d)) for its G query heads, then per head a 15-bit fixed-point copy
+// split into hi/lo int8 bytes laid out as the A operand of the logit MFMA
+// (rows: head h -> 4h + {group 0 hi, group 0 lo, group 1 hi, group 1 lo}).
+// Results stay in `sm`; with `qrot` non-null the float q~ is also written
+// there.  after_loads() runs on every thread once the global loads of the
+// preparation (threads 0..255) have been consumed.
+// With four_ctr null the whole workgroup (any multiple of 64 threads >= 256)
+// takes part and synchronises with s_barrier.  Otherwise (G <= 4) waves 0..3
+// alone finish the preparation, synchronising through four_wave_sync on
+// *four_ctr, while every other wave returns right after after_loads(): a wave
+// held up issuing page copies then delays no one.  The caller publishes the
+// results with a barrier of its own (none is taken at the end here).
 template <int MT, int GH, typename AfterLoads>
-__device__ void query_prep(const DecArgs &a, int b, int kv, QSmem<MT, GH> &sm, float *qrot, AfterLoads after_loads) {
+__device__ void query_prep(const DecArgs &a, int b, int kv, QSmem<MT, GH> &sm, float *qrot, AfterLoads after_loads,
+                           int *four_ctr = nullptr) {
   const PoolView &pv = a.pv;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nw = four_ctr ? 4 : blockDim.x >> 6;   // waves taking part
   const int G = pv.hq / pv.hkv;
   const float *U = a.rv.U_K + (size_t)kv * kD * kD;
   const uint16_t *qb = a.q + ((size_t)b * pv.hq + (size_t)kv * G) * kD;
@@ -205,8 +224,10 @@ __device__ void query_prep(const DecArgs &a, int b, int kv, QSmem<MT, GH> &sm, f
     }
   }
   after_loads();
-  for (int e = tid; e < MT * 2 * 64 * 4; e += blockDim.x) ((uint32_t *)sm.aq)[e] = 0;
-  __syncthreads();
+  if (four_ctr && w >= 4) return;
+  for (int e = tid; e < MT * 2 * 64 * 4; e += 64 * nw) ((uint32_t *)sm.aq)[e] = 0;
+  if (four_ctr) four_wave_sync(four_ctr, 4);
+  else __syncthreads();
   // one wave per head: Walsh-Hadamard butterfly (lane l holds elements l and
   // l + 64; stages 1..32 by lane exchange, stage 64 in registers), then the
   // rotated, permuted q~ -> fixed point -> operands
@@ -249,7 +270,7 @@ __device__ void query_prep(const DecArgs &a, int b, int kv, QSmem<MT, GH> &sm, f
       base[(r + 1 + 16 * kg) * 16 + 4 * s + bb] = (int8_t)lo;
     }
   }
-  __syncthreads();
+  if (!four_ctr) __syncthreads();
 }
 
 // Query preparation for the VALU scan variant, which reads the float q~ and
@@ -557,12 +578,11 @@ constexpr int scan_prefetch() { return 2; }
 // A running BF16 state (LDS, one M-tile of heads) is o[128 h + c] and 16
 // floats st: m[h] (log2 units) at st[h], l[h] at st[4 + h], and a tile's m
 // and l staged at st[8 + h], st[12 + h].  A wave's page buffers hold, once
-// its pages are done, its history state at kAccHist, a BF16 state at kAccO
-// (o) and kAccM (st).
-constexpr int kAccHist = 0, kAccO = 512, kAccM = 1024, kAccFloats = 1040;
+// its pages are done, its history state (o, 128 floats per head) at kAccHist.
+constexpr int kAccHist = 0, kAccFloats = 512;
 constexpr int kStM = 0, kStL = 4, kStTm = 8, kStTl = 12;
-// Waves that run the BF16 tiles of a long scan before their pages, each into
-// a BF16 state of its own outside the page buffers.
+// Waves that run the BF16 tiles (one M-tile of heads) before their pages,
+// each into a BF16 state of its own outside the page buffers.
 constexpr int kTileWaves = 4;
 
 template <int MT, int GH, int NW, bool MFMA>
@@ -581,17 +601,26 @@ struct ScanSmem {
   };
   union {
     WaveScratch wave[NW];
-    QSmem<MT, GH> q;                       // query preparation (before the scan)
+    QSmem<MT, GH> q;                       // query preparation, several M-tiles (before the scan)
     EpiSmem e;
   };
+  // query preparation, one M-tile of heads: its own space (the tile waves
+  // read it only after their tiles, while the other waves are scanning)
+  struct NoQ {};
+  std::conditional_t<MFMA && MT == 1, QSmem<MT, GH>, NoQ> q1;
+  __device__ QSmem<MT, GH> &qprep() {
+    if constexpr (MFMA && MT == 1) return q1;
+    else return q;
+  }
   float qsum[GH][2];                       // VALU: per-group sums of q~
+  int prep_ctr, ready;                     // one M-tile: four_wave_sync counter; parts ready before the scan
   float m[NW][MT * 4], l[NW][MT * 4], z[NW][MT * 4][2];
   union {
     uint4 pbuf[MFMA ? NW : 1][PF][kPageBytes / 16];   // page copies (during the scan)
     float o[NW][MT * 4][kD];                          // per-wave value sums (after it)
   };
   float vacc[MFMA ? 1 : NW][GH][64][2];    // VALU: per-wave running sums
-  float tacc[MFMA && MT == 1 ? kTileWaves : 1][kD * 4 + 16];   // BF16 states of the tile waves (long scans)
+  float tacc[MFMA && MT == 1 ? kTileWaves : 1][kD * 4 + 16];   // BF16 states of the tile waves
 };
 
 // Page copies into LDS are issued as inline assembly so that the compiler
@@ -1008,7 +1037,7 @@ __device__ __forceinline__ void pipe_scan(PagePipe<NW, PF> &p, const PoolView &p
 // the same way afterwards.
 constexpr int kDynMaxPages = 2048;
 struct DynPages {
-  int next_page, next_tile;
+  int next_page;
   int bt[kDynMaxPages];   // block-table entries of pages pg0 + i
 };
 
@@ -1122,19 +1151,16 @@ __device__ void flush_partial(ScanSmem<MT, GH, NW, true> &sm, HistState<MT> &st,
 
 // End of a split for one M-tile of heads (G <= 4).  Each wave, once its
 // pages are done, stores its history state in its own (now idle) page
-// buffers, loads its share of U_V (the last 512 threads, one quarter row
-// each) after taking BF16 tiles from the workgroup's counter (unless the
-// tile wave has run them already: tiles_here false) and folding them into a
-// running BF16 state next to its history state.  Then the workgroup
-// combines the waves, takes the history sum out of the rotated basis (bit
-// reversal, Walsh-Hadamard butterfly, U_V^T / sqrt(d): R_V^T is linear, so
-// applying it to every split's sum equals applying it once to the merged
+// buffers and loads its share of U_V (the last 512 threads, one quarter row
+// each).  Then the workgroup combines the waves' history states and the
+// tile waves' BF16 states, takes the history sum out of the rotated basis
+// (bit reversal, Walsh-Hadamard butterfly, U_V^T / sqrt(d): R_V^T is linear,
+// so applying it to every split's sum equals applying it once to the merged
 // sum) and adds the BF16 part.  With one split the output is written here;
 // otherwise one (m, l, o) partial in the original basis goes to dst.
 template <int GH, int NW>
 __device__ void split_epilogue(const DecArgs &a, int b, int kv, int split, ScanSmem<1, GH, NW, true> &sm,
-                               const HistState<1> &st, const MetaSteps &ms, DynPages *dp, float *dst,
-                               bool tiles_here, const TileCtx &tc) {
+                               const HistState<1> &st, const MetaSteps &ms, float *dst) {
   static_assert(GH == 4 && NW * 64 >= 512 + 256, "one M-tile of heads, 12 waves");
   constexpr int NT = NW * 64;
   const PoolView &pv = a.pv;
@@ -1155,26 +1181,8 @@ __device__ void split_epilogue(const DecArgs &a, int b, int kv, int split, ScanS
       sm.m[wave][q] = st.mref[0];
       sm.l[wave][q] = l16;
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) reg[kAccO + lane + 64 * j] = 0.f;
-    if (lane < 4) {
-      reg[kAccM + kStM + lane] = -INFINITY;
-      reg[kAccM + kStL + lane] = 0.f;
-    }
   }
-  wave_lds_sync();
-  // 3) BF16 tiles u = split + S k, k < n_tiles, handed out as waves finish
-  // (one at a time: fetching two together, with both tiles' loads in flight,
-  // measured no faster and needs 40 more registers)
-  const int n_tiles = split < a.n_chunks ? (a.n_chunks - 1 - split) / S + 1 : 0;
-  while (tiles_here) {
-    int k = 0;
-    if (lane == 0) k = atomicAdd(&dp->next_tile, 1);
-    k = __builtin_amdgcn_readfirstlane(k);
-    if (k >= n_tiles) break;
-    bf16_tile_fold<GH>(a, tc, b, kv, split + S * k, sm.wave[wave].tile, reg + kAccO, reg + kAccM);
-  }
-  // 4) U_V rows for step 6: thread t >= NT - 512 owns row (t - (NT - 512)) / 4,
+  // 2) U_V rows for step 4: thread t >= NT - 512 owns row (t - (NT - 512)) / 4,
   // columns 32 ((t - (NT - 512)) % 4) .. + 32; the loads overlap the wait
   // for the other waves and the combine
   const int ut = tid - (NT - 512);
@@ -1187,18 +1195,14 @@ __device__ void split_epilogue(const DecArgs &a, int b, int kv, int split, ScanS
     for (int i = 0; i < 8; ++i) u[i] = urow[i];
   }
   __syncthreads();
-  // 5) combine the waves (history: rotated basis, permuted for the butterfly)
+  // 3) combine the waves (history: rotated basis, permuted for the butterfly)
   for (int idx = tid; idx < G * kD; idx += NT) {
     const int h = idx >> 7, c = idx & (kD - 1);
-    // BF16 states: the tile waves' (long scans; else empty) and every wave's own
     float M = -INFINITY, Mb = -INFINITY;
 #pragma unroll
     for (int t = 0; t < kTileWaves; ++t) Mb = fmaxf(Mb, sm.tacc[t][4 * kD + kStM + h]);
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      M = fmaxf(M, sm.m[w][h]);
-      Mb = fmaxf(Mb, reinterpret_cast<const float *>(&sm.pbuf[w][0][0])[kAccM + kStM + h]);
-    }
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.m[w][h]);
     float o = 0.f, l = 0.f, ob = 0.f, lb = 0.f;
 #pragma unroll
     for (int t = 0; t < kTileWaves; ++t) {
@@ -1211,17 +1215,11 @@ __device__ void split_epilogue(const DecArgs &a, int b, int kv, int split, ScanS
     }
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float *rw = reinterpret_cast<const float *>(&sm.pbuf[w][0][0]);
-      const float mw = sm.m[w][h], mb = rw[kAccM + kStM + h];
+      const float mw = sm.m[w][h];
       if (mw > -INFINITY) {
         const float sc = exp2_fast(mw - M);
-        o = fmaf(sc, rw[kAccHist + idx], o);
+        o = fmaf(sc, reinterpret_cast<const float *>(&sm.pbuf[w][0][0])[kAccHist + idx], o);
         l = fmaf(sc, sm.l[w][h], l);
-      }
-      if (mb > -INFINITY) {
-        const float sc = exp2_fast(mb - Mb);
-        ob = fmaf(sc, rw[kAccO + idx], ob);
-        lb = fmaf(sc, rw[kAccM + kStL + h], lb);
       }
     }
     sm.e.zs[h][bitrev7(c)] = o;   // (o P)[j] = o[bitrev(j)]
@@ -1234,7 +1232,7 @@ __device__ void split_epilogue(const DecArgs &a, int b, int kv, int split, ScanS
     }
   }
   __syncthreads();
-  // 6) Walsh-Hadamard butterfly per head (one wave each), then U_V^T
+  // 4) Walsh-Hadamard butterfly per head (one wave each), then U_V^T
   if (wave < G) {
     float x0 = sm.e.zs[wave][lane], x1 = sm.e.zs[wave][lane + 64];
     fwht_lane_stages(x0, x1, lane);
@@ -1259,7 +1257,7 @@ __device__ void split_epilogue(const DecArgs &a, int b, int kv, int split, ScanS
     }
   }
   __syncthreads();
-  // 7) history and BF16 parts together
+  // 5) history and BF16 parts together
   for (int idx = tid; idx < G * kD; idx += NT) {
     const int h = idx >> 7, c = idx & (kD - 1);
     const float Mh = sm.e.hm[h], Mb = sm.e.bm[h], Mt = fmaxf(Mh, Mb);
@@ -1301,71 +1299,106 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   // copies start is therefore issued first and completed in one round trip:
   // the clip thresholds, the first block-table entries and (threads
   // 0..255) the query preparation's loads.  The waves without preparation
-  // work start their copies as soon as those land.
+  // work start their copies as soon as those land (the tile waves of one
+  // M-tile of heads after their tiles).
   float tk = a.rv.tau_K[kv], tv = a.rv.tau_V[kv];
   const uint32_t lutk = LUT ? levels_of(a.rv, kv, false) : OSCAR_UNIFORM_LEVELS;
   const uint32_t lutv = LUT ? levels_of(a.rv, kv, true) : OSCAR_UNIFORM_LEVELS;
   const TileCtx tc{max(0, L), pv.sink_slot[b]};
+  const int S = a.n_splits;
   PagePipe<NW, PF> pipe;
   pipe_init(pipe, pv, b, kv, pg0, pg1, sm.pbuf[wave], wave, lane);
-  // long scans (16 pages per wave and more) take every BF16 tile after the
-  // pages; where the workgroup has two rounds of prologue pages or more and
-  // its block-table entries fit in LDS, pages and the late tiles are handed
-  // out dynamically
+  // several M-tiles: long scans (16 pages per wave and more) take every BF16
+  // tile after the pages, short ones four of them first (on waves 0..3)
   const int npg_wg = pg1 - pg0;
   const bool long_scan = npg_wg >= 16 * NW;
-  // one M-tile of heads: on long scans the last wave runs every BF16 tile
-  // first (into its own running state, outside the page buffers) and then
-  // joins the page stream; otherwise the tiles run after the pages
-  // (split_epilogue)
   const int early = (MT == 1 || long_scan) ? 0 : 4;
-  // one M-tile of heads, scans of 48 pages per wave and more: the last
-  // kTileWaves waves run the BF16 tiles first (a tile takes several
-  // microseconds once the page stream fills the memory pipeline, so one wave
-  // alone would outlast the pages)
-  const bool tile_waves = MT == 1 && npg_wg >= 48 * NW;
-  const int tw = tile_waves ? wave - (NW - kTileWaves) : -1;   // this wave's tile-wave index, or < 0
+  // one M-tile of heads: the last kTileWaves waves run every BF16 tile first,
+  // from the start (a tile needs the query only in its original basis, and
+  // its loads then go out ahead of the wave's page copies), each wave into a
+  // running state of its own outside the page buffers, and then join the
+  // page stream
+  const int tw = MT == 1 ? wave - (NW - kTileWaves) : -1;   // this wave's tile-wave index, or < 0
+  // where the workgroup has two rounds of prologue pages or more and its
+  // block-table entries fit in LDS, pages are handed out dynamically
   const bool dyn = DYN && npg_wg >= 2 * NW * PF && npg_wg <= kDynMaxPages;
   // pages [pg0, pg0 + nfull) hold 64 tokens (only the history's last page can hold fewer)
   const int nfull = max(0, min(pg1, n_hist / kPageTokens) - pg0);
-  constexpr int kDynPer = (kDynMaxPages + 64 * NW - 1) / (64 * NW);
+  // threads that load the workgroup's block-table entries into LDS (the
+  // tile waves do not)
+  constexpr int kBtThreads = 64 * (MT == 1 ? NW - kTileWaves : NW);
+  constexpr int kDynPer = (kDynMaxPages + kBtThreads - 1) / kBtThreads;
   int dbt[kDynPer];
-  if (dyn) {
+  if (dyn && tid < kBtThreads) {
     const int32_t *row = pv.block_table + (size_t)b * pv.max_pages + pg0;
 #pragma unroll
     for (int r = 0; r < kDynPer; ++r) {
-      const int i = tid + r * 64 * NW;
+      const int i = tid + r * kBtThreads;
       dbt[r] = i < npg_wg ? row[i] : -1;
     }
   }
-  query_prep<MT, GH>(a, b, kv, sm.q, nullptr, [&] {
+  // block-table entries to LDS and the prologue copies of waves 4.. once the
+  // first loads have landed (published by the barrier or readiness count
+  // that follows the preparation)
+  auto after_loads = [&] {
     bt_settle(pipe, tk, tv);
-    // published by the barrier that follows in the preparation
-    if (dp && tid == 0) dp->next_tile = early;   // tiles k < early run on waves 0..3 before their pages
     if (dyn) {
 #pragma unroll
       for (int r = 0; r < kDynPer; ++r) {
-        const int i = tid + r * 64 * NW;
+        const int i = tid + r * kBtThreads;
         if (i < npg_wg) dp->bt[i] = dbt[r];
       }
       if (tid == 0) dp->next_page = NW * PF;
     }
-    if constexpr (MT == 1) {
-      if (tid < 4 * kTileWaves) {   // the tile waves' states start empty
-        sm.tacc[tid >> 2][4 * kD + kStM + (tid & 3)] = -INFINITY;
-        sm.tacc[tid >> 2][4 * kD + kStL + (tid & 3)] = 0.f;
-      }
+    if (wave >= 4) pipe_prologue(pipe, pv, lane);
+  };
+  QSmem<MT, GH> &qs = sm.qprep();
+  if constexpr (MT == 1) {
+    // No barrier between the start and the pages: waves 0..3 prepare the
+    // query (synchronising among themselves), waves 4..7 start their copies,
+    // the tile waves run their tiles and then start their copies.  Waves
+    // 0..7 each raise sm.ready once their part (query operands of their head,
+    // block-table entries) is in LDS; every wave waits for all eight before
+    // it reads the query operands.  Both counters start at zero.
+    if (tid == 0) {
+      sm.prep_ctr = 0;
+      sm.ready = 0;
     }
-    if (wave >= 4 && tw < 0) pipe_prologue(pipe, pv, lane);
-  });
+    __syncthreads();
+    if (tw >= 0) {
+      // tiles u = split + S k with k = tw mod kTileWaves, one after the other
+      float *to = &sm.tacc[tw][0], *tst = &sm.tacc[tw][4 * kD];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) to[lane + 64 * j] = 0.f;
+      if (lane < 4) {
+        tst[kStM + lane] = -INFINITY;
+        tst[kStL + lane] = 0.f;
+      }
+      wave_lds_sync();
+      for (int u = split + S * tw; u < a.n_chunks; u += S * kTileWaves)
+        bf16_tile_fold<GH>(a, tc, b, kv, u, sm.wave[wave].tile, to, tst);
+      bt_settle(pipe, tk, tv);
+      pipe_prologue(pipe, pv, lane);
+    } else {
+      query_prep<MT, GH>(a, b, kv, qs, nullptr, after_loads, &sm.prep_ctr);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      if (lane == 0) __hip_atomic_fetch_add(&sm.ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    while (__hip_atomic_load(&sm.ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < NW - kTileWaves)
+      __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  } else {
+    query_prep<MT, GH>(a, b, kv, qs, nullptr, after_loads);
+  }
   const MetaSteps ms = meta_steps(tk, tv);
   QueryOps<MT> qo;
-  load_query_ops<MT, GH, LUT>(sm.q.aq, sm.q.qc, G, pv.sm_scale * kLog2e, ms, lane, qo);
+  load_query_ops<MT, GH, LUT>(qs.aq, qs.qc, G, pv.sm_scale * kLog2e, ms, lane, qo);
   qo.lutk = lutk;
   qo.lutv = lutv;
-  __syncthreads();   // the query scratch is reused by the weights and the BF16 tiles
-  // BF16 tiles: this workgroup takes tiles u = split + S k.  Short scans
-  // (under 16 pages per wave): tiles k < 4 run first on waves 3..0 (the
+  // several M-tiles: the query scratch is reused by the weights and the BF16 tiles
+  if constexpr (MT != 1) __syncthreads();
+  // Several M-tiles, BF16 tiles u = split + S k of this workgroup: on short
+  // scans (under 16 pages per wave) tiles k < 4 run first on waves 3..0 (the
   // preparing waves, whose history pages are the last to arrive, and which
   // finish their pages before the others); the rest run after the history
   // pages, from the last wave down.  An early tile goes before the wave's
@@ -1375,7 +1408,6 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   // issue priority), so the tiles hide behind the remaining page stream.
   // (The tile scratch overlaps the query scratch, which is dead after the
   // barrier above.)
-  const int S = a.n_splits;
   float *parts = a.part + (size_t)bh * a.n_parts * G * kPartStride;
   if (wave < 4) {
     const int u = split + S * (early - 1 - wave);
@@ -1385,18 +1417,6 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
     // the preparation would stall those waves (the CU accepts copy requests
     // at the memory rate) and with them every wave waiting on the preparation
     pipe_prologue(pipe, pv, lane);
-  }
-  if constexpr (MT == 1) {
-    if (tw >= 0) {
-      // tiles u = split + S k with k = tw mod kTileWaves, one after the
-      // other, then the pages
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sm.tacc[tw][lane + 64 * j] = 0.f;
-      wave_lds_sync();
-      for (int u = split + S * tw; u < a.n_chunks; u += S * kTileWaves)
-        bf16_tile_fold<GH>(a, tc, b, kv, u, sm.wave[wave].tile, &sm.tacc[tw][0], &sm.tacc[tw][4 * kD]);
-      pipe_prologue(pipe, pv, lane);
-    }
   }
   HistState<MT> st;
   hist_reset(st);
@@ -1425,27 +1445,13 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   }
   if (pipe.bad && lane == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
   if constexpr (MT == 1) {
-    split_epilogue<GH, NW>(a, b, kv, split, sm, st, ms, dp, dst, !tile_waves, tc);
+    split_epilogue<GH, NW>(a, b, kv, split, sm, st, ms, dst);
     return;
   }
-  if (dyn) {
-    // this workgroup's tiles are u = split + S k, k < n_tiles; the counter
-    // starts past the early ones
-    const int n_tiles = split < a.n_chunks ? (a.n_chunks - 1 - split) / S + 1 : 0;
-    for (;;) {
-      int k = 0;
-      if (lane == 0) k = atomicAdd(&dp->next_tile, 1);
-      k = __builtin_amdgcn_readfirstlane(k);
-      if (k >= n_tiles) break;
-      const int u = split + S * k;
+  for (int u = split + S * early; u < a.n_chunks; u += S) {
+    const int k = u / S - early;
+    if ((long_scan ? k % 4 : NW - 1 - k % NW) == wave)
       bf16_tile_partial<GH>(a, tc, b, kv, u, sm.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
-    }
-  } else {
-    for (int u = split + S * early; u < a.n_chunks; u += S) {
-      const int k = u / S - early;
-      if ((long_scan ? k % 4 : NW - 1 - k % NW) == wave)
-        bf16_tile_partial<GH>(a, tc, b, kv, u, sm.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
-    }
   }
   flush_partial<MT, GH, NW>(sm, st, G, ms, dst);
 }
