@@ -213,7 +213,7 @@ __device__ __forceinline__ void bf16_chunk(const uint16_t *K, const uint16_t *V,
   wave_lds_sync();
 #pragma unroll
   for (int h = 0; h < GH; ++h) {
-    if (h >= G) break;
+    if (h >= G) continue;
     const int i = h & 3;
     const float v = (i == 0) ? pm[0] : (i == 1) ? pm[1] : (i == 2) ? pm[2] : pm[3];
     const float mh = __shfl(v, 16 * (h >> 2), 64);
@@ -248,7 +248,7 @@ __device__ __forceinline__ void bf16_chunk(const uint16_t *K, const uint16_t *V,
       vf[7] = __uint_as_float(u[i].w & 0xFFFF0000u);
 #pragma unroll
       for (int h = 0; h < GH; ++h) {
-        if (h >= G) break;
+        if (h >= G) continue;
         const float p = ps[h][t];
 #pragma unroll
         for (int c = 0; c < 8; ++c) o[h][c] = fmaf(p, vf[c], o[h][c]);
@@ -314,7 +314,13 @@ __device__ __forceinline__ void bf16_tile_math(const TileRegs &r, int valid, int
     vf[7] = __uint_as_float(r.vv[i].w & 0xFFFF0000u);
 #pragma unroll
     for (int h = 0; h < GH; ++h) {
-      if (h >= G) break;
+      // heads past G: continue keeps the loop fully unrolled (with break, twelve
+      // heads kept o in scratch memory); sixteen heads fully unrolled fail to
+      // compile with this toolchain, so they keep the early exit
+      if (h >= G) {
+        if constexpr (GH <= 12) continue;
+        else break;
+      }
       const float p = ps[h][q + 4 * i];
 #pragma unroll
       for (int c = 0; c < 8; ++c) o[h][c] = fmaf(p, vf[c], o[h][c]);
@@ -351,7 +357,7 @@ __device__ __forceinline__ void bf16_block_combine(int G, const float (&m)[4], c
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, n = lane & 15, q = lane >> 4;
 #pragma unroll
   for (int h = 0; h < GH; ++h) {
-    if (h >= G) break;
+    if (h >= G) continue;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       float v = o[h][c];
@@ -363,7 +369,7 @@ __device__ __forceinline__ void bf16_block_combine(int G, const float (&m)[4], c
   if (q == 0) {
 #pragma unroll
     for (int h = 0; h < GH; ++h) {
-      if (h >= G) break;
+      if (h >= G) continue;
 #pragma unroll
       for (int c = 0; c < 8; ++c) sm_o[wave][h][8 * n + c] = o[h][c];
     }
