@@ -604,7 +604,8 @@ def main():
                   "scan_kernel_us": r1["scan_kernel_us"], "scan_kernel_gbps": r1["scan_kernel_gbps"],
                   "scan_kernel_frac_of_peak": r1["scan_kernel_gbps"] / HBM_PEAK_GBPS,
                   "bf16_us_per_layer": r1["bf16_us_per_layer"], "bf16_gbps": r1["bf16_gbps"],
-                  "speedup_vs_bf16_decode": r1["speedup_vs_bf16_decode"]}
+                  "speedup_vs_bf16_decode": r1["speedup_vs_bf16_decode"],
+                  "scan_kernel_traffic": measured_traffic(wl1.name)}
         del wb1
         torch.cuda.empty_cache()
 
@@ -616,6 +617,9 @@ def main():
     prefix = None
     if not args.no_prefix:
         prefix = run_prefix(args.n_cal)
+        # HBM bytes the scan fetched and wrote per launch (counters), next to
+        # the logical and unique bytes
+        prefix["scan_kernel_traffic"] = measured_traffic(prefix["workload"])
         log(f"prefix: {json.dumps(prefix)}")
         torch.cuda.empty_cache()
 
