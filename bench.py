@@ -559,7 +559,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefix", action="store_true",
                     help="skip the long shared-prefix workload (bulk quantise-pack + decode)")
-    ap.add_argument("--variant", type=int, default=0, help="0 = MFMA int8 history kernel, 1 = VALU, 2 = MFMA on the split grid only")
+    ap.add_argument("--variant", type=int, default=0, help="0 = MFMA int8 history kernel, 1 = VALU reference")
     ap.add_argument("--bf16-budget-gb", type=float, default=48.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="end with one plain device-to-device copy of this many MiB (scales HBM counters)")

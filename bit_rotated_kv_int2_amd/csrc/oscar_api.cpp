@@ -72,8 +72,7 @@ int check_rot(const oscar_rotation *r) {
 int check_opts(const oscar_decode_options *o, oscar_decode_options *out) {
   *out = oscar_decode_options{0, 0};
   if (!o) return OSCAR_OK;
-  if (o->variant < 0 || o->variant > 2)
-    return fail(OSCAR_EINVAL, "options.variant must be 0 (MFMA), 1 (VALU) or 2 (MFMA, grid partition)");
+  if (o->variant < 0 || o->variant > 1) return fail(OSCAR_EINVAL, "options.variant must be 0 (MFMA) or 1 (VALU)");
   if (o->blocks < 0 || o->blocks > 65536) return fail(OSCAR_EINVAL, "options.blocks must be in [0, 65536]");
   *out = *o;
   return OSCAR_OK;

@@ -1854,7 +1854,7 @@ int target_blocks(int blocks) { return blocks > 0 ? blocks : 256; }
 int mt_of(int G) { return (G + 3) / 4; }
 int gh_of(int G) { return 4 * mt_of(G); }
 // variants 0 and 2: MFMA scan; 1: VALU scan
-bool is_mfma(int variant) { return variant != 1; }
+bool is_mfma(int variant) { return variant == 0; }
 int nw_of(int G, int variant) { return !is_mfma(variant) ? 4 : (mt_of(G) == 1 ? 12 : 8); }
 }  // namespace
 

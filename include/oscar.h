@@ -216,15 +216,11 @@ int32_t oscar_quantize_append(const oscar_params *p, const oscar_rotation *rot,
  * Per-call choices of the decode kernels.  Pass NULL for the defaults
  * (every field 0).  Nothing is kept between calls: the library holds no
  * process-wide decode settings.
- *   variant: 0 = MFMA int8 history scan (default); for G <= 4 it may split
- *            the work evenly over a fixed grid of workgroups (balanced
- *            partition, where built in), else one workgroup per (sequence,
- *            KV head, split);
- *            1 = VALU history scan (float arithmetic, reference speed);
- *            2 = MFMA int8 history scan, always on the per-(sequence, KV
- *            head) split grid.
- *            Results of 0 and 2 differ only in floating-point summation
- *            order.  OSCAR_EINVAL for other values.
+ *   variant: 0 = MFMA int8 history scan (default), one workgroup per
+ *            (sequence, KV head, split);
+ *            1 = VALU history scan (float arithmetic, reference speed), on
+ *            the same grid after a query-preparation kernel.
+ *            OSCAR_EINVAL for other values.
  *   blocks:  history-scan workgroups the split grid aims for: each
  *            (sequence, KV head) gets ceil(blocks / (batch * Hkv)) splits,
  *            capped so every wave keeps at least one page.  0 aims for one
@@ -252,8 +248,8 @@ typedef struct oscar_decode_options {
  * aligned, ZERO-FILLED by the caller before its first use.  It holds
  * completion counters that every call returns to zero, so it can be reused
  * without clearing; calls that share a workspace must not overlap (same
- * stream, or ordered).  With variant 0 or 2 the call is one kernel launch
- * on `stream`.
+ * stream, or ordered).  With variant 0 the call is one kernel launch on
+ * `stream`.
  */
 int32_t oscar_decode_attention(const oscar_params *p, const oscar_rotation *rot,
                                const oscar_kv_pool *pool, const uint16_t *q, float *out,

@@ -92,7 +92,7 @@ def test_validation_errors():
     assert L.oscar_quantize_append(ctypes.byref(p), ctypes.byref(rot), ctypes.byref(pool),
                                    0x1000, 0x1010 + 2, 1, None) == O.OSCAR_EINVAL
     # per-call decode options: checked before anything else is looked at
-    for bad_opts in (O.decode_options(7, 0), O.decode_options(-1, 0), O.decode_options(0, -1),
+    for bad_opts in (O.decode_options(2, 0), O.decode_options(7, 0), O.decode_options(-1, 0), O.decode_options(0, -1),
                      O.decode_options(0, 65537)):
         assert _call_decode(p, opts=bad_opts) == O.OSCAR_EINVAL
         assert b"options" in L.oscar_last_error()
