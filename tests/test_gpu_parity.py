@@ -200,7 +200,7 @@ def test_ragged_batch_mixed_page_orders():
         toks.append((kb, vb))
         append_sequence(params, rot, pool, b, kb, vb)
     q = synth.decode_queries(wl, 0)
-    out = _decode_gpu(params, rot, pool, q, 2, blocks=2 * wl.batch * wl.n_kv)   # two splits per (sequence, KV head)
+    out = _decode_gpu(params, rot, pool, q, 0, blocks=2 * wl.batch * wl.n_kv)   # two splits per (sequence, KV head)
     for b in range(wl.batch):
         ref, _ = _oracle_decode(wl, cals, toks[b][0], toks[b][1], q[b])
         assert decode_check(out[b], ref) <= TOL, b
@@ -311,7 +311,7 @@ def test_single_workgroup_long_history(tiny):
     perm = np.random.default_rng(7).permutation(n_pages).astype(np.int32)
     pool = O.KVPool(params, 1, n_pages, perm[None])
     append_sequence(params, rot, pool, 0, kb, vb)
-    out = _decode_gpu(params, rot, pool, q, 2, blocks=1)
+    out = _decode_gpu(params, rot, pool, q, 0, blocks=1)
     ref, _ = _oracle_decode(wl, cals, kb, vb, q[0])
     err = decode_check(out[0], ref)
     print(f"150K tokens, one workgroup: err/||o|| = {err:.3e}")
@@ -334,7 +334,7 @@ def test_dynamic_page_order(tiny, blocks):
     perm = np.random.default_rng(11).permutation(n_pages).astype(np.int32)
     pool = O.KVPool(params, 1, n_pages, perm[None])
     append_sequence(params, rot, pool, 0, kb, vb)
-    out = _decode_gpu(params, rot, pool, q, 2, blocks=blocks)
+    out = _decode_gpu(params, rot, pool, q, 0, blocks=blocks)
     ref, _ = _oracle_decode(wl, cals, kb, vb, q[0])
     err = decode_check(out[0], ref)
     print(f"40037 tokens, {blocks} workgroup(s): err/||o|| = {err:.3e}")
@@ -356,7 +356,7 @@ def test_dynamic_page_order_bad_entries_flagged(tiny):
     for i in (5, 300, n_pages - 1):
         pool.block_table[0, i] = 1 << 20
     try:
-        out = _decode_gpu(params, rot, pool, q, 2, blocks=1)
+        out = _decode_gpu(params, rot, pool, q, 0, blocks=1)
     finally:
         pool.block_table.copy_(bt)
     assert np.all(np.isfinite(out))
