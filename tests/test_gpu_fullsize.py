@@ -149,3 +149,24 @@ def test_prefix_128k_gqa12_sampled():
     for b, h in ((0, 1), (9, 4)):
         err = _check_pair(wl, cals, pool, bt, b, h, int(lengths[b]), q, out)
         print(f"prefix seq {b} kv {h}: err/||o|| = {err:.3e}")
+
+
+def test_qwen3_100k_batch1_codebook_sampled():
+    """Batch 1 at 102400 tokens with Lloyd-Max codebooks (levels calibrated
+    by the oracle on the calibration tokens): the write kernels' threshold
+    codes bit-exact and the level-lookup scan within tolerance, two KV
+    heads."""
+    wl = synth.WORKLOADS["qwen3-8b-100k-b1-36l"]
+    lengths = synth.sequence_lengths(wl)
+    cals = oracle_calibration(wl, n_cal=2048)
+    _, kc, vc = synth.calibration_set(wl, 0, n_cal=2048)
+    f = synth.bf16_bits_to_f32
+    cals = [R.calibrate_codebook(c, f(kc)[h], f(vc)[h]) for h, c in enumerate(cals)]
+    assert any(not np.array_equal(c.levels_K, R.UNIFORM_LEVELS) for c in cals)
+    params, rot, pool, bt = _build_pool(wl, lengths, cals)
+    q = synth.decode_queries(wl, 0)
+    out = _decode(params, rot, pool, q)
+    k, v = synth.gpu_sequence_kv(wl, 0, 0, int(lengths[0]))
+    for h in (1, 5):
+        err = _check_pair(wl, cals, pool, bt, 0, h, int(lengths[0]), q, out, k, v)
+        print(f"batch1 codebook kv {h} levels K {cals[h].levels_K} V {cals[h].levels_V}: err/||o|| = {err:.3e}")
