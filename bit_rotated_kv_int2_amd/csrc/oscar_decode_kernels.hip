@@ -1033,8 +1033,7 @@ __device__ __forceinline__ void pipe_scan(PagePipe<NW, PF> &p, const PoolView &p
 // LDS and each wave takes the next page index from a shared counter
 // whenever it frees a buffer, so the waves of a SIMD (which otherwise
 // finish in age order, the oldest having issue priority) all run until the
-// pages are gone.  The BF16 tiles not taken before the pages are handed out
-// the same way afterwards.
+// pages are gone.
 constexpr int kDynMaxPages = 2048;
 struct DynPages {
   int next_page;

@@ -39,6 +39,11 @@ namespace {
 constexpr int kThreads = 128;     // single-token append: one thread per channel
 constexpr int kPageThreads = 256; // bulk demotion: four waves of 16 page slots
 constexpr double kInvSqrtD = 0x1.6a09e667f3bcdp-4;  // nearest double to 1/sqrt(128)
+// Row stride (floats) of the bulk kernel's token rows in LDS: the matrix
+// core's A operand reads 16 rows x 4 columns at once, and a stride of 4 mod
+// 64 floats puts those 64 reads in 64 different banks.
+constexpr int kXRow = 132;
+typedef double v4d __attribute__((ext_vector_type(4)));
 
 struct AppendArgs {
   PoolView pv;
@@ -82,8 +87,8 @@ __device__ __forceinline__ uint32_t quantize_code(float v, float tau, const Code
 
 // Bulk demotion, one 64-token history page of one (KV head, K|V) per
 // workgroup.  grid: (pages, Hkv * 2, batch); block: 256 threads.  Wave w owns
-// page slots 16 w .. 16 w + 15; lane l owns butterfly elements l and l + 64
-// of each of them (S1, S2) and output channels l and l + 64 (S5..S8).
+// page slots 16 w .. 16 w + 15 (S1..S5 on the fp64 matrix core and in its
+// lanes) and lane l output channels l and l + 64 of each (S6..S8).
 // Demotes every position x with max(S0, p0 - W) <= x < p0 + n_new - W.
 __global__ void __launch_bounds__(kPageThreads) __attribute__((amdgpu_waves_per_eu(2)))
 append_demote_kernel(AppendArgs a) {
@@ -113,89 +118,102 @@ append_demote_kernel(AppendArgs a) {
     if (tid == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
     return;
   }
-  __shared__ __align__(16) double xs[kPageTokens][kD];   // bf16 sources as float64, token-major
+  __shared__ __align__(16) float xs[kPageTokens][kXRow];    // bf16 sources as float32 (exact), token-major
+  __shared__ __align__(16) float4 stat_s[kPageThreads / 64][16];   // per wave and slot: zero0, scale0, zero1, scale1
+  __shared__ uint32_t smeta_s[kPageThreads / 64][16];     // per wave and slot: s8_0 | z8_0 << 8 | s8_1 << 16 | z8_1 << 24
   __shared__ __align__(16) uint8_t vst[kD][16];           // V code bytes of the page, channel-major
 
   // Gather: each wave its own 16 slots (zeros outside [t0, t1)); lane l
-  // reads channels 2 l and 2 l + 1 of the token row.
-  const uint16_t *ring = is_v ? pv.recent_v : pv.recent_k;
-  const uint16_t *fresh = is_v ? a.v_new : a.k_new;
-  for (int i = 0; i < 16; ++i) {
-    const int hx = c0 + 16 * w + i;   // history index of the slot
-    double2 d = {0.0, 0.0};
-    if (hx >= t0 && hx < t1) {
-      const int x = hx + pv.sink;
-      const uint16_t *row = x < p0 ? ring + (((size_t)b * pv.hkv + h) * pv.recent + (x % pv.recent)) * kD
-                                   : fresh + (((size_t)b * a.n_new + (x - p0)) * pv.hkv + h) * kD;
-      const uint32_t bits = ((const uint32_t *)row)[lane];
-      d.x = (double)bf16_to_f32((uint16_t)(bits & 0xFFFFu));
-      d.y = (double)bf16_to_f32((uint16_t)(bits >> 16));
+  // reads channels 2 l and 2 l + 1 of the token row.  The 16 loads are
+  // issued together: a slot outside the range reads the row of t0 (valid)
+  // and drops it.
+  const uint16_t *ring = (is_v ? pv.recent_v : pv.recent_k) + ((size_t)b * pv.hkv + h) * pv.recent * kD;
+  const uint16_t *fresh = (is_v ? a.v_new : a.k_new) + ((size_t)b * a.n_new * pv.hkv + h) * kD;
+  const size_t fresh_stride = (size_t)pv.hkv * kD;   // between consecutive new tokens
+  auto row_of = [&](int x, int rp) -> const uint16_t * {
+    return x < p0 ? ring + (size_t)rp * kD : fresh + (size_t)(x - p0) * fresh_stride;
+  };
+  const int xw = c0 + 16 * w + pv.sink;   // position of the wave's first slot
+  const uint16_t *row_t0 = row_of(t0 + pv.sink, (t0 + pv.sink) % pv.recent);
+  uint32_t bits[16];
+  {
+    int rp = xw % pv.recent;   // ring slot of position xw + i
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int hx = xw + i - pv.sink;
+      const uint16_t *row = (hx >= t0 && hx < t1) ? row_of(xw + i, rp) : row_t0;
+      bits[i] = ((const uint32_t *)row)[lane];
+      rp = rp + 1 == pv.recent ? 0 : rp + 1;
     }
-    *(double2 *)&xs[16 * w + i][2 * lane] = d;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int hx = xw + i - pv.sink;
+    float2 f = {0.0f, 0.0f};
+    if (hx >= t0 && hx < t1) {
+      f.x = bf16_to_f32((uint16_t)(bits[i] & 0xFFFFu));
+      f.y = bf16_to_f32((uint16_t)(bits[i] >> 16));
+    }
+    *(float2 *)&xs[16 * w + i][2 * lane] = f;
   }
   __syncthreads();
 
-  // S1: y_j = sum_k x_k U[k][j], float64, k ascending.  Half-wave hw takes
-  // slots 16 w + 8 hw + i (i < 8) and lane l = lane % 32 output columns
-  // 4 l .. 4 l + 3, so every 16-byte LDS read of two x values feeds eight
-  // FMAs (LDS delivery, not the FMA rate, bounded the one-read-per-four
-  // layout).  U rows of the next eight k are loaded while the current eight
-  // are used.
+  // S1: y_n = sum_k x_k U[k][n], float64, k ascending, on the fp64 matrix
+  // core: each wave the 16 x 128 block Y = X U of its slots as eight 16 x 16
+  // tiles, 32 steps of v_mfma_f64_16x16x4f64 over k.  One step adds the
+  // products of k = 4 ks .. 4 ks + 3 in that order, rounding after each, so
+  // the chain equals one fma chain over k ascending bit for bit (the
+  // products of bf16 and float32 values are exact in float64; checked
+  // against a plain fma chain on the device over wide exponent ranges).
+  // Tile nt, column j holds output n = 8 j + nt: the eight B values of a
+  // lane are adjacent floats of one U row (two 16-byte loads per step).
+  // Operand lanes: A (16 x 4) lane l = X[slot l % 16][k = l / 16]; B (4 x 16)
+  // lane l = U[k = l / 16][column l % 16]; D lane l, register r = slot
+  // l / 16 + 4 r, column l % 16.
   const float *U = (is_v ? a.rv.U_V : a.rv.U_K) + (size_t)h * kD * kD;
-  const int hw = lane >> 5, lq = lane & 31;
-  double acc[8][4];
+  const int mi = lane & 15, kq = lane >> 4;
+  const float *urow = U + (size_t)kq * kD + 8 * mi;   // row 4 ks + kq, columns 8 mi .. 8 mi + 7
+  v4d acc[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i][0] = acc[i][1] = acc[i][2] = acc[i][3] = 0.0;
-  float4 uc[8], un[8];
+  for (int nt = 0; nt < 8; ++nt) acc[nt] = v4d{0.0, 0.0, 0.0, 0.0};
+  float4 u0 = *(const float4 *)urow, u1 = *(const float4 *)(urow + 4);
+#pragma unroll 4
+  for (int ks = 0; ks < kD / 4; ++ks) {
+    const int kn = ks + 1 < kD / 4 ? ks + 1 : ks;   // the last step reloads its own row (unused)
+    const float4 n0 = *(const float4 *)(urow + (size_t)4 * kn * kD);
+    const float4 n1 = *(const float4 *)(urow + (size_t)4 * kn * kD + 4);
+    const double av = (double)xs[16 * w + mi][4 * ks + kq];
+    const double bv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) uc[kk] = *(const float4 *)(U + kk * kD + 4 * lq);
-  for (int kb = 0; kb < kD / 8; ++kb) {
-    const int kn = kb + 1 < kD / 8 ? 8 * (kb + 1) : 8 * kb;   // last block reloads itself (unused)
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) un[kk] = *(const float4 *)(U + (kn + kk) * kD + 4 * lq);
-#pragma unroll
-    for (int kp = 0; kp < 4; ++kp) {
-      const int k = 8 * kb + 2 * kp;
-      const double u0[4] = {uc[2 * kp].x, uc[2 * kp].y, uc[2 * kp].z, uc[2 * kp].w};
-      const double u1[4] = {uc[2 * kp + 1].x, uc[2 * kp + 1].y, uc[2 * kp + 1].z, uc[2 * kp + 1].w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const double2 xv = *(const double2 *)&xs[16 * w + 8 * hw + i][k];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          acc[i][c] = fma(xv.x, u0[c], acc[i][c]);
-          acc[i][c] = fma(xv.y, u1[c], acc[i][c]);
-        }
-      }
-    }
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) uc[kk] = un[kk];
+    for (int nt = 0; nt < 8; ++nt) acc[nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv[nt], acc[nt], 0, 0, 0);
+    u0 = n0;
+    u1 = n1;
   }
 
-  // S2: butterfly stages h = 1, 2 inside the lane's four columns, then
-  // h = 4 .. 64 across lanes of the half-wave (bit-exact lane moves), in
-  // ascending order of h: element pairs (a, b) at (e, e + h) -> (a + b, a - b).
+  // S2: butterfly stages h = 1, 2, 4 (element bits 0..2: the tiles of the
+  // lane) and h = 8 .. 64 (bits 3..6: lanes j ^ (h / 8) of a 16-lane row),
+  // in ascending order of h: pairs (a, b) at (e, e + h) -> (a + b, a - b).
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int hs = 1; hs <= 4; hs <<= 1) {
 #pragma unroll
-    for (int hs = 1; hs <= 2; hs <<= 1) {
+    for (int nt = 0; nt < 8; ++nt) {
+      if (nt & hs) continue;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (c & hs) continue;
-        const double x0 = acc[i][c], x1 = acc[i][c + hs];
-        acc[i][c] = x0 + x1;
-        acc[i][c + hs] = x0 - x1;
+      for (int r = 0; r < 4; ++r) {
+        const double x0 = acc[nt][r], x1 = acc[nt + hs][r];
+        acc[nt][r] = x0 + x1;
+        acc[nt + hs][r] = x0 - x1;
       }
     }
   }
   auto stage = [&](auto M) {
-    constexpr int m = decltype(M)::value;   // element bit 4 m <-> lane bit m
+    constexpr int m = decltype(M)::value;   // element bit 3 + log2(m) <-> lane bit log2(m)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int nt = 0; nt < 8; ++nt) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const double o = lane_xor_d<m>(acc[i][c]);
-        acc[i][c] = (lq & m) ? o - acc[i][c] : acc[i][c] + o;
+      for (int r = 0; r < 4; ++r) {
+        const double o = lane_xor_d<m>(acc[nt][r]);
+        acc[nt][r] = (mi & m) ? o - acc[nt][r] : acc[nt][r] + o;
       }
     }
   };
@@ -203,20 +221,23 @@ append_demote_kernel(AppendArgs a) {
   stage(std::integral_constant<int, 2>{});
   stage(std::integral_constant<int, 4>{});
   stage(std::integral_constant<int, 8>{});
-  stage(std::integral_constant<int, 16>{});
 
   // S3, S5: the float32 values of the wave's 16 slots, in butterfly order,
   // staged in its own rows of xs (free after S1).  Row stride 132 floats.
   const float tau = (is_v ? a.rv.tau_V : a.rv.tau_K)[h];
   const CodeThresholds th = code_thresholds(levels_of(a.rv, h, is_v));
   constexpr int kRow = 132;
-  float *ys = (float *)&xs[16 * w][0];
-  float4 *stat = (float4 *)(ys + 16 * kRow);       // per slot: zero0, scale0, zero1, scale1
-  uint32_t *smeta = (uint32_t *)(stat + 16);       // per slot: s8_0 | z8_0 << 8 | s8_1 << 16 | z8_1 << 24
+  float *ys = &xs[16 * w][0];
+  float4 *stat = stat_s[w];
+  uint32_t *smeta = smeta_s[w];
+  static_assert(kRow == kXRow, "staging reuses the wave's rows");
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) ys[(8 * hw + i) * kRow + 4 * lq + c] = (float)(acc[i][c] * kInvSqrtD);
+  for (int r = 0; r < 4; ++r) {
+    float *row = ys + (kq + 4 * r) * kRow + 8 * mi;   // elements 8 mi .. 8 mi + 7 of slot kq + 4 r
+    *(float4 *)row = make_float4((float)(acc[0][r] * kInvSqrtD), (float)(acc[1][r] * kInvSqrtD),
+                                 (float)(acc[2][r] * kInvSqrtD), (float)(acc[3][r] * kInvSqrtD));
+    *(float4 *)(row + 4) = make_float4((float)(acc[4][r] * kInvSqrtD), (float)(acc[5][r] * kInvSqrtD),
+                                       (float)(acc[6][r] * kInvSqrtD), (float)(acc[7][r] * kInvSqrtD));
   }
   wave_lds_sync();
   // S6, S7 per slot and group, lane i < 16 taking slot 16 w + i.  Output
