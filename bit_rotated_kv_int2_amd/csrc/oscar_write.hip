@@ -40,10 +40,44 @@ constexpr int kThreads = 128;     // single-token append: one thread per channel
 constexpr int kPageThreads = 256; // bulk demotion: four waves of 16 page slots
 constexpr double kInvSqrtD = 0x1.6a09e667f3bcdp-4;  // nearest double to 1/sqrt(128)
 // Row stride (floats) of the bulk kernel's token rows in LDS: the matrix
-// core's A operand reads 16 rows x 4 columns at once, and a stride of 4 mod
+// core's B operand reads 4 columns x 16 rows at once, and a stride of 4 mod
 // 64 floats puts those 64 reads in 64 different banks.
 constexpr int kXRow = 132;
 typedef double v4d __attribute__((ext_vector_type(4)));
+
+// Exchanges x of the upper lanes with y of the lower lanes, where lower and
+// upper are the two halves of each 32-lane group (M == 1: lane bit 4 clear /
+// set) or of the wave (M == 2: lane bit 5): afterwards a lower lane holds
+// (own x, partner's x) and an upper lane (partner's y, own y).
+template <int M>
+__device__ __forceinline__ void half_swap(uint32_t &x, uint32_t &y) {
+  static_assert(M == 1 || M == 2, "half_swap: M");
+  if constexpr (M == 1) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+    x = r[0];
+    y = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+    x = r[0];
+    y = r[1];
+  }
+}
+template <int M>
+__device__ __forceinline__ void half_swap(double &x, double &y) {
+  const uint64_t bx = __builtin_bit_cast(uint64_t, x), by = __builtin_bit_cast(uint64_t, y);
+  uint32_t xl = (uint32_t)bx, xh = (uint32_t)(bx >> 32), yl = (uint32_t)by, yh = (uint32_t)(by >> 32);
+  half_swap<M>(xl, yl);
+  half_swap<M>(xh, yh);
+  x = __builtin_bit_cast(double, ((uint64_t)xh << 32) | xl);
+  y = __builtin_bit_cast(double, ((uint64_t)yh << 32) | yl);
+}
+template <int M>
+__device__ __forceinline__ void half_swap(float &x, float &y) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = __builtin_bit_cast(uint32_t, y);
+  half_swap<M>(a, b);
+  x = __builtin_bit_cast(float, a);
+  y = __builtin_bit_cast(float, b);
+}
 
 struct AppendArgs {
   PoolView pv;
@@ -87,8 +121,8 @@ __device__ __forceinline__ uint32_t quantize_code(float v, float tau, const Code
 
 // Bulk demotion, one 64-token history page of one (KV head, K|V) per
 // workgroup.  grid: (pages, Hkv * 2, batch); block: 256 threads.  Wave w owns
-// page slots 16 w .. 16 w + 15 (S1..S5 on the fp64 matrix core and in its
-// lanes) and lane l output channels l and l + 64 of each (S6..S8).
+// page slots 16 w .. 16 w + 15; from S2 on, the 128 elements of slot
+// 16 w + (l % 16) sit in the four lanes l % 16 + 16 j, 32 in each.
 // Demotes every position x with max(S0, p0 - W) <= x < p0 + n_new - W.
 __global__ void __launch_bounds__(kPageThreads) __attribute__((amdgpu_waves_per_eu(2)))
 append_demote_kernel(AppendArgs a) {
@@ -159,17 +193,19 @@ append_demote_kernel(AppendArgs a) {
   __syncthreads();
 
   // S1: y_n = sum_k x_k U[k][n], float64, k ascending, on the fp64 matrix
-  // core: each wave the 16 x 128 block Y = X U of its slots as eight 16 x 16
-  // tiles, 32 steps of v_mfma_f64_16x16x4f64 over k.  One step adds the
-  // products of k = 4 ks .. 4 ks + 3 in that order, rounding after each, so
-  // the chain equals one fma chain over k ascending bit for bit (the
+  // core: each wave the 128 x 16 block Y^T = U^T X^T of its slots as eight
+  // 16 x 16 tiles, 32 steps of v_mfma_f64_16x16x4f64 over k.  One step adds
+  // the products of k = 4 ks .. 4 ks + 3 in that order, rounding after each,
+  // so the chain equals one fma chain over k ascending bit for bit (the
   // products of bf16 and float32 values are exact in float64; checked
   // against a plain fma chain on the device over wide exponent ranges).
-  // Tile nt, column j holds output n = 8 j + nt: the eight B values of a
-  // lane are adjacent floats of one U row (two 16-byte loads per step).
-  // Operand lanes: A (16 x 4) lane l = X[slot l % 16][k = l / 16]; B (4 x 16)
-  // lane l = U[k = l / 16][column l % 16]; D lane l, register r = slot
-  // l / 16 + 4 r, column l % 16.
+  // Tile nt, row i holds output n = 8 i + nt: the eight A values of a lane
+  // are adjacent floats of one U row (two 16-byte loads per step).
+  // Operand lanes: A (16 x 4) lane l = U[k = l / 16][n = 8 (l % 16) + nt];
+  // B (4 x 16) lane l = X[slot l % 16][k = l / 16]; D lane l, register r =
+  // row l / 16 + 4 r, slot l % 16.  So lane (mi = l % 16, kq = l / 16) ends
+  // with n = 8 (kq + 4 r) + nt of slot mi in acc[nt][r]: n bits 0..2 = nt,
+  // bits 3, 4 = lane bits 4, 5, bits 5, 6 = r.
   const float *U = (is_v ? a.rv.U_V : a.rv.U_K) + (size_t)h * kD * kD;
   const int mi = lane & 15, kq = lane >> 4;
   const float *urow = U + (size_t)kq * kD + 8 * mi;   // row 4 ks + kq, columns 8 mi .. 8 mi + 7
@@ -182,17 +218,16 @@ append_demote_kernel(AppendArgs a) {
     const int kn = ks + 1 < kD / 4 ? ks + 1 : ks;   // the last step reloads its own row (unused)
     const float4 n0 = *(const float4 *)(urow + (size_t)4 * kn * kD);
     const float4 n1 = *(const float4 *)(urow + (size_t)4 * kn * kD + 4);
-    const double av = (double)xs[16 * w + mi][4 * ks + kq];
-    const double bv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    const double xv = (double)xs[16 * w + mi][4 * ks + kq];
+    const double uv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) acc[nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv[nt], acc[nt], 0, 0, 0);
+    for (int nt = 0; nt < 8; ++nt) acc[nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(uv[nt], xv, acc[nt], 0, 0, 0);
     u0 = n0;
     u1 = n1;
   }
 
-  // S2: butterfly stages h = 1, 2, 4 (element bits 0..2: the tiles of the
-  // lane) and h = 8 .. 64 (bits 3..6: lanes j ^ (h / 8) of a 16-lane row),
-  // in ascending order of h: pairs (a, b) at (e, e + h) -> (a + b, a - b).
+  // S2: butterfly stages in ascending order of h, pairs (a, b) at (e, e + h)
+  // -> (a + b, a - b).  h = 1, 2, 4: registers acc[nt] and acc[nt + h].
 #pragma unroll
   for (int hs = 1; hs <= 4; hs <<= 1) {
 #pragma unroll
@@ -206,119 +241,146 @@ append_demote_kernel(AppendArgs a) {
       }
     }
   }
-  auto stage = [&](auto M) {
-    constexpr int m = decltype(M)::value;   // element bit 3 + log2(m) <-> lane bit log2(m)
+  // h = 8, 16 (element bits 3, 4: lane bits 4, 5).  The pair of registers
+  // (acc[nt], acc[nt + m]) with nt & m == 0, m = 1 for h = 8 and 2 for h = 16,
+  // holds elements that differ in bit 0 (resp. 1), whose stages are done.
+  // half_swap gives every lane one (a, b) pair: the lower lane that of the
+  // element with that bit clear, the upper lane the other; the sum goes to
+  // acc[nt], the difference to acc[nt + m].  From then on register bit m of
+  // nt stands for element bit 3 (resp. 4), and the lane bit for element bit 0
+  // (resp. 1).
+  auto cross = [&](auto M) {
+    constexpr int m = decltype(M)::value;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      if (nt & m) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        double x0 = acc[nt][r], x1 = acc[nt + m][r];
+        half_swap<m>(x0, x1);
+        acc[nt][r] = x0 + x1;
+        acc[nt + m][r] = x0 - x1;
+      }
+    }
+  };
+  cross(std::integral_constant<int, 1>{});
+  cross(std::integral_constant<int, 2>{});
+  // h = 32, 64 (element bits 5, 6): registers r and r + h / 32.
+#pragma unroll
+  for (int hr = 1; hr <= 2; hr <<= 1) {
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const double o = lane_xor_d<m>(acc[nt][r]);
-        acc[nt][r] = (mi & m) ? o - acc[nt][r] : acc[nt][r] + o;
+        if (r & hr) continue;
+        const double x0 = acc[nt][r], x1 = acc[nt][r + hr];
+        acc[nt][r] = x0 + x1;
+        acc[nt][r + hr] = x0 - x1;
       }
     }
-  };
-  stage(std::integral_constant<int, 1>{});
-  stage(std::integral_constant<int, 2>{});
-  stage(std::integral_constant<int, 4>{});
-  stage(std::integral_constant<int, 8>{});
+  }
+  // Now lane (mi, L4 = bit 4, L5 = bit 5) holds in acc[nt][r] element
+  // n = L4 + 2 L5 + 4 nt2 + 8 nt0 + 16 nt1 + 32 r0 + 64 r1 of slot 16 w + mi
+  // (ntj, rj: bit j of nt, r).  Output channel p takes element bitrev7(p),
+  // so p = 64 L4 + 32 L5 + 16 nt2 + 8 nt0 + 4 nt1 + 2 r0 + r1: the lane's
+  // 32 channels are 32 (2 L4 + L5) .. + 31, all in group g = L4.
 
-  // S3, S5: the float32 values of the wave's 16 slots, in butterfly order,
-  // staged in its own rows of xs (free after S1).  Row stride 132 floats.
+  // S3, S5, S6 clamp: float32 values clamped to [-tau, tau].
   const float tau = (is_v ? a.rv.tau_V : a.rv.tau_K)[h];
   const CodeThresholds th = code_thresholds(levels_of(a.rv, h, is_v));
-  constexpr int kRow = 132;
-  float *ys = &xs[16 * w][0];
-  float4 *stat = stat_s[w];
-  uint32_t *smeta = smeta_s[w];
-  static_assert(kRow == kXRow, "staging reuses the wave's rows");
+  float v[8][4];
+  float mx = -INFINITY, mn = INFINITY;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float *row = ys + (kq + 4 * r) * kRow + 8 * mi;   // elements 8 mi .. 8 mi + 7 of slot kq + 4 r
-    *(float4 *)row = make_float4((float)(acc[0][r] * kInvSqrtD), (float)(acc[1][r] * kInvSqrtD),
-                                 (float)(acc[2][r] * kInvSqrtD), (float)(acc[3][r] * kInvSqrtD));
-    *(float4 *)(row + 4) = make_float4((float)(acc[4][r] * kInvSqrtD), (float)(acc[5][r] * kInvSqrtD),
-                                       (float)(acc[6][r] * kInvSqrtD), (float)(acc[7][r] * kInvSqrtD));
-  }
-  wave_lds_sync();
-  // S6, S7 per slot and group, lane i < 16 taking slot 16 w + i.  Output
-  // channel p takes element bitrev(p), so group g (channels 64 g .. 64 g + 63)
-  // is the set of elements with e % 2 == g; min and max commute with the
-  // order and with the clamp to [-tau, tau] (monotone), which is applied to
-  // them.  Then the group metadata as in quantize_group.
-  if (lane < 16) {
-    const float4 *row = (const float4 *)(ys + lane * kRow);
-    float mx0 = -INFINITY, mn0 = INFINITY, mx1 = -INFINITY, mn1 = INFINITY;
-#pragma unroll 8
-    for (int j = 0; j < kD / 4; ++j) {
-      const float4 v = row[j];
-      mx0 = fmaxf(mx0, fmaxf(v.x, v.z));
-      mn0 = fminf(mn0, fminf(v.x, v.z));
-      mx1 = fmaxf(mx1, fmaxf(v.y, v.w));
-      mn1 = fminf(mn1, fminf(v.y, v.w));
-    }
-    float zf[2], sf[2];
-    uint32_t meta = 0;
-    const float mx[2] = {fminf(fmaxf(mx0, -tau), tau), fminf(fmaxf(mx1, -tau), tau)};
-    const float mn[2] = {fminf(fmaxf(mn0, -tau), tau), fminf(fmaxf(mn1, -tau), tau)};
-    const float za = meta_zero_step(tau), sb = meta_scale_step(tau);
+  for (int nt = 0; nt < 8; ++nt) {
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const float sg = __fdiv_rn(mx[g] - mn[g], 3.0f);
-      uint32_t z8 = 0, s8 = 0;
-      if (za > 0.0f) z8 = (uint32_t)fminf(fmaxf(rintf(__fdiv_rn(mn[g] + tau, za)), 0.0f), 255.0f);
-      if (sb > 0.0f) s8 = (uint32_t)fminf(fmaxf(rintf(__fdiv_rn(sg, sb)), 0.0f), 255.0f);
-      zf[g] = (float)z8 * za - tau;
-      sf[g] = (float)s8 * sb;
-      meta |= (s8 | (z8 << 8)) << (16 * g);
+    for (int r = 0; r < 4; ++r) {
+      v[nt][r] = fminf(fmaxf((float)(acc[nt][r] * kInvSqrtD), -tau), tau);
+      mx = fmaxf(mx, v[nt][r]);
+      mn = fminf(mn, v[nt][r]);
     }
-    stat[lane] = make_float4(zf[0], sf[0], zf[1], sf[1]);
-    smeta[lane] = meta;
   }
-  wave_lds_sync();
-
-  // S7 codes and S8 packing: lane l takes output channels l and l + 64
-  const int e0 = bitrev7(lane), e1 = bitrev7(lane + 64);
+  // S6 group statistics over the slot's 64 channels of group L4: the lanes
+  // l and l ^ 32.  First swap: a lower lane gets the partner's maximum, an
+  // upper lane the partner's minimum; second swap hands each result over.
+  {
+    float x = mx, y = mn;
+    half_swap<2>(x, y);
+    const float t = (lane & 32) ? fminf(x, y) : fmaxf(x, y);
+    float c = t, d = t;
+    half_swap<2>(c, d);
+    mx = c;
+    mn = d;
+  }
+  // Group metadata as in quantize_group.
+  const float za = meta_zero_step(tau), sb = meta_scale_step(tau);
+  uint32_t z8 = 0, s8 = 0;
+  {
+    const float sg = __fdiv_rn(mx - mn, 3.0f);
+    if (za > 0.0f) z8 = (uint32_t)fminf(fmaxf(rintf(__fdiv_rn(mn + tau, za)), 0.0f), 255.0f);
+    if (sb > 0.0f) s8 = (uint32_t)fminf(fmaxf(rintf(__fdiv_rn(sg, sb)), 0.0f), 255.0f);
+  }
+  const float zf = (float)z8 * za - tau, sf = (float)s8 * sb;
+  const int slot = 16 * w + mi;
+  const bool valid = c0 + slot >= t0 && c0 + slot < t1;
   uint8_t *page = pv.pages + ((size_t)phys * pv.hkv + h) * kPageBytes;
-  uint32_t vb[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};   // V: bytes 4 m + w of channels l, l + 64
+  {
+    // the token's 4-byte entry: s8_0 | z8_0 << 8 from lane bit 4 clear,
+    // s8_1 | z8_1 << 8 from the lane 16 above
+    uint32_t m0 = s8 | (z8 << 8), m1 = m0;
+    half_swap<1>(m0, m1);
+    if ((lane & 48) == 0 && valid)
+      *(uint32_t *)(page + (is_v ? kVMeta : kKMeta) + meta_entry(slot) * 4) = m0 | (m1 << 16);
+  }
+
+  // S7 codes, S8 packing.
+  uint32_t code[8][4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int slot = 16 * w + i;
-    const bool valid = c0 + slot >= t0 && c0 + slot < t1;   // wave-uniform
-    if (!valid) continue;
-    const float4 st = stat[i];
-    const float v0 = fminf(fmaxf(ys[i * kRow + e0], -tau), tau);
-    const float v1 = fminf(fmaxf(ys[i * kRow + e1], -tau), tau);
-    uint32_t code0 = 0, code1 = 0;
-    if (st.y != 0.0f) code0 = level_code(__fdiv_rn(v0 - st.x, st.y), th);
-    if (st.w != 0.0f) code1 = level_code(__fdiv_rn(v1 - st.z, st.w), th);
-    if (lane == 0) *(uint32_t *)(page + (is_v ? kVMeta : kKMeta) + meta_entry(slot) * 4) = smeta[i];
-    if (!is_v) {
-      // K row: dword q holds channels 16 q .. 16 q + 15, two bits each
-      uint32_t k0 = code0 << (2 * (lane & 15)), k1 = code1 << (2 * (lane & 15));
-      k0 |= (uint32_t)lane_xor_i<1>((int)k0);
-      k1 |= (uint32_t)lane_xor_i<1>((int)k1);
-      k0 |= (uint32_t)lane_xor_i<2>((int)k0);
-      k1 |= (uint32_t)lane_xor_i<2>((int)k1);
-      k0 |= (uint32_t)lane_xor_i<4>((int)k0);
-      k1 |= (uint32_t)lane_xor_i<4>((int)k1);
-      k0 |= (uint32_t)lane_xor_i<8>((int)k0);
-      k1 |= (uint32_t)lane_xor_i<8>((int)k1);
-      if ((lane & 15) == 0) {
-        uint32_t *row = (uint32_t *)(page + kKCodes + slot * 32);
-        row[lane >> 4] = k0;
-        row[4 + (lane >> 4)] = k1;
-      }
-    } else {
-      // V: slot 16 w + i sits in byte 4 (i / 4) + w of each channel row, bits 2 (i % 4)
-      vb[0][i >> 2] |= code0 << (2 * (i & 3));
-      vb[1][i >> 2] |= code1 << (2 * (i & 3));
+  for (int nt = 0; nt < 8; ++nt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) code[nt][r] = sf != 0.0f ? level_code(__fdiv_rn(v[nt][r] - zf, sf), th) : 0u;
+  }
+  if (!is_v) {
+    // K row: dword q holds channels 16 q .. 16 q + 15, two bits each; the
+    // lane owns dwords 4 L4 + 2 L5 + nt2, whole.
+    uint32_t kw[2] = {0, 0};
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        kw[nt >> 2] |= code[nt][r] << (2 * (8 * (nt & 1) + 4 * ((nt >> 1) & 1) + 2 * (r & 1) + (r >> 1)));
+    }
+    if (valid) *(uint2 *)(page + kKCodes + slot * 32 + 4 * (4 * ((lane >> 4) & 1) + 2 * (lane >> 5))) = make_uint2(kw[0], kw[1]);
+    return;
+  }
+  // V: slot 16 w + mi sits in byte 4 (mi / 4) + w of each channel row, bits
+  // 2 (mi % 4).  Word j / 4 of the lane collects channel 32 (2 L4 + L5) + j
+  // in byte j % 4; the four lanes mi ^ 1, mi ^ 2 merge theirs, then lane
+  // mi % 4 == q stores words 2 q, 2 q + 1.
+  uint32_t vw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = 16 * (nt >> 2) + 8 * (nt & 1) + 4 * ((nt >> 1) & 1) + 2 * (r & 1) + (r >> 1);
+      vw[j >> 2] |= code[nt][r] << (8 * (j & 3) + 2 * (mi & 3));
     }
   }
-  if (!is_v) return;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    vst[lane][4 * m + w] = (uint8_t)vb[0][m];
-    vst[lane + 64][4 * m + w] = (uint8_t)vb[1][m];
+  for (int j = 0; j < 8; ++j) {
+    vw[j] |= (uint32_t)lane_xor_i<1>((int)vw[j]);
+    vw[j] |= (uint32_t)lane_xor_i<2>((int)vw[j]);
+  }
+  {
+    const int q = mi & 3;
+    const uint32_t wa = q == 0 ? vw[0] : q == 1 ? vw[2] : q == 2 ? vw[4] : vw[6];
+    const uint32_t wb = q == 0 ? vw[1] : q == 1 ? vw[3] : q == 2 ? vw[5] : vw[7];
+    const int ch = 32 * (2 * ((lane >> 4) & 1) + (lane >> 5)) + 8 * q;   // channel of byte 0 of wa
+    const int byte = 4 * (mi >> 2) + w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      vst[ch + j][byte] = (uint8_t)(wa >> (8 * j));
+      vst[ch + 4 + j][byte] = (uint8_t)(wb >> (8 * j));
+    }
   }
   __syncthreads();
   if (tid < kD) {
