@@ -131,6 +131,39 @@ __host__ __device__ inline uint32_t level_code(float u, const CodeThresholds &t)
   return (uint32_t)(u > t.t0) + (uint32_t)(u >= t.t1) + (uint32_t)(u > t.t2);
 }
 
+// level_code(fl(a / s), th) for s > 0 as three comparisons of a with float
+// cutoffs.  Each term of level_code is "fl(a / s) >= T" for one float T
+// (u > t is u >= nextafter(t, +inf)).  Rounding is monotone, so the term
+// holds from some float a on: fl(q) >= T exactly when q exceeds the
+// midpoint m of prev(T) and T, or equals it and the tie goes to T (T has an
+// even last bit).  m s is exact in float64 (25 x 24 significant bits), so
+// the term is a >= B with B = m s, or a > B when the tie goes down, and the
+// cutoff is the smallest float not below that bound.
+__host__ __device__ inline uint32_t float_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
+struct CodeCuts {
+  double m[3];     // midpoints of prev(T) and T
+  bool up[3];      // the tie at m rounds to T
+};
+__host__ __device__ inline CodeCuts code_cuts(const CodeThresholds &th) {
+  const float T[3] = {nextafterf(th.t0, INFINITY), th.t1, nextafterf(th.t2, INFINITY)};
+  CodeCuts c;
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    c.m[j] = 0.5 * ((double)nextafterf(T[j], -INFINITY) + (double)T[j]);
+    c.up[j] = (float_bits(T[j]) & 1u) == 0;
+  }
+  return c;
+}
+// Cutoff of term j for scale s > 0: the smallest float a with a >= m s (tie
+// up) or a > m s (tie down).
+__host__ __device__ inline float code_cut(const CodeCuts &c, int j, float s) {
+  double b = c.m[j] * (double)s;
+  if (!c.up[j]) b = nextafter(b, (double)INFINITY);
+  float f = (float)b;
+  if ((double)f < b) f = nextafterf(f, INFINITY);
+  return f;
+}
+
 // Decode workspace carve-up (offsets in bytes from the workspace base).
 struct DecodePlan {
   int n_splits;          // history splits per (sequence, kv head)

@@ -287,7 +287,7 @@ append_demote_kernel(AppendArgs a) {
 
   // S3, S5, S6 clamp: float32 values clamped to [-tau, tau].
   const float tau = (is_v ? a.rv.tau_V : a.rv.tau_K)[h];
-  const CodeThresholds th = code_thresholds(levels_of(a.rv, h, is_v));
+  const CodeCuts cuts = code_cuts(code_thresholds(levels_of(a.rv, h, is_v)));
   float v[8][4];
   float mx = -INFINITY, mn = INFINITY;
 #pragma unroll
@@ -332,12 +332,19 @@ append_demote_kernel(AppendArgs a) {
       *(uint32_t *)(page + (is_v ? kVMeta : kKMeta) + meta_entry(slot) * 4) = m0 | (m1 << 16);
   }
 
-  // S7 codes, S8 packing.
+  // S7 codes (level_code of fl(fl(v - zero) / scale), all 0 when the scale
+  // is 0) through the cutoffs of code_cut; S8 packing.
+  float cut[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) cut[j] = sf != 0.0f ? code_cut(cuts, j, sf) : INFINITY;
   uint32_t code[8][4];
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) code[nt][r] = sf != 0.0f ? level_code(__fdiv_rn(v[nt][r] - zf, sf), th) : 0u;
+    for (int r = 0; r < 4; ++r) {
+      const float d = v[nt][r] - zf;
+      code[nt][r] = (uint32_t)(d >= cut[0]) + (uint32_t)(d >= cut[1]) + (uint32_t)(d >= cut[2]);
+    }
   }
   if (!is_v) {
     // K row: dword q holds channels 16 q .. 16 q + 15, two bits each; the
