@@ -70,11 +70,25 @@ int check_rot(const oscar_rotation *r) {
 
 // Decode options: NULL means every field 0 (the defaults).
 int check_opts(const oscar_decode_options *o, oscar_decode_options *out) {
-  *out = oscar_decode_options{0, 0};
+  *out = oscar_decode_options{0, 0, 0};
   if (!o) return OSCAR_OK;
   if (o->variant < 0 || o->variant > 1) return fail(OSCAR_EINVAL, "options.variant must be 0 (MFMA) or 1 (VALU)");
   if (o->blocks < 0 || o->blocks > 65536) return fail(OSCAR_EINVAL, "options.blocks must be in [0, 65536]");
+  if (o->prefix_pages < 0) return fail(OSCAR_EINVAL, "options.prefix_pages must be >= 0");
   *out = *o;
+  return OSCAR_OK;
+}
+
+// The shared-prefix options against the shape (n_pages < 0: pool not known yet).
+int check_prefix(const oscar_params *p, int32_t max_pages, int32_t n_pages, const oscar_decode_options &o) {
+  if (o.prefix_pages == 0) return OSCAR_OK;
+  if (o.variant != 0) return fail(OSCAR_EINVAL, "options.prefix_pages needs variant 0");
+  if (p->num_q_heads / p->num_kv_heads <= 4)
+    return fail(OSCAR_EINVAL, "options.prefix_pages needs more than 4 query heads per KV head");
+  if (o.prefix_pages > max_pages) return fail(OSCAR_EINVAL, "options.prefix_pages exceeds max_pages");
+  if (o.prefix_pages > oscar::kMaxPrefixPages)
+    return fail(OSCAR_EINVAL, "options.prefix_pages exceeds %d", oscar::kMaxPrefixPages);
+  if (n_pages == 0) return fail(OSCAR_EINVAL, "options.prefix_pages needs a pool with pages");
   return OSCAR_OK;
 }
 
@@ -161,9 +175,10 @@ int32_t oscar_quantize_append(const oscar_params *p, const oscar_rotation *rot,
 size_t oscar_decode_workspace_size(const oscar_params *p, int32_t batch, int32_t max_pages,
                                    const oscar_decode_options *opts) {
   oscar_decode_options o;
-  if (check_params(p) || batch < 1 || max_pages < 0 || check_opts(opts, &o)) return 0;
+  if (check_params(p) || batch < 1 || max_pages < 0 || check_opts(opts, &o) || check_prefix(p, max_pages, -1, o))
+    return 0;
   return oscar::make_decode_plan(batch, p->num_kv_heads, p->num_q_heads, max_pages, p->sink, p->recent, o.variant,
-                                 o.blocks)
+                                 o.blocks, o.prefix_pages)
       .total;
 }
 
@@ -175,11 +190,12 @@ int32_t oscar_decode_attention(const oscar_params *p, const oscar_rotation *rot,
   if (rc) return rc;
   if ((rc = check_rot(rot)) || (rc = check_pool(p, pool))) return rc;
   oscar_decode_options o;
-  if ((rc = check_opts(opts, &o))) return rc;
+  if ((rc = check_opts(opts, &o)) || (rc = check_prefix(p, pool->max_pages, pool->n_pages, o))) return rc;
   if (!q || !out) return fail(OSCAR_EINVAL, "q/out is NULL");
   if (misaligned(q) || misaligned(out)) return fail(OSCAR_EINVAL, "q/out must be 16-byte aligned");
   const oscar::DecodePlan plan = oscar::make_decode_plan(pool->batch, p->num_kv_heads, p->num_q_heads,
-                                                          pool->max_pages, p->sink, p->recent, o.variant, o.blocks);
+                                                          pool->max_pages, p->sink, p->recent, o.variant, o.blocks,
+                                                          o.prefix_pages);
   if (!workspace || workspace_bytes < plan.total)
     return fail(OSCAR_EWORKSPACE, "workspace of %zu bytes needed, %zu given", plan.total, workspace_bytes);
   if (((uintptr_t)workspace) & 255) return fail(OSCAR_EINVAL, "workspace must be 256-byte aligned");
@@ -199,11 +215,12 @@ int32_t oscar_decode_attention_noalloc(const oscar_params *p, const oscar_rotati
   if (rc) return rc;
   if ((rc = check_rot(rot)) || (rc = check_pool(p, pool))) return rc;
   oscar_decode_options o;
-  if ((rc = check_opts(opts, &o))) return rc;
+  if ((rc = check_opts(opts, &o)) || (rc = check_prefix(p, pool->max_pages, pool->n_pages, o))) return rc;
   if (!q || !out) return fail(OSCAR_EINVAL, "q/out is NULL");
   if (misaligned(q) || misaligned(out)) return fail(OSCAR_EINVAL, "q/out must be 16-byte aligned");
   const oscar::DecodePlan plan = oscar::make_decode_plan(pool->batch, p->num_kv_heads, p->num_q_heads,
-                                                          pool->max_pages, p->sink, p->recent, o.variant, o.blocks);
+                                                          pool->max_pages, p->sink, p->recent, o.variant, o.blocks,
+                                                          o.prefix_pages);
   // the plan's counters go to the buffer's counter region, everything after
   // them (from off_qconst on) to the rest of the buffer
   const size_t counters = (size_t)pool->batch * p->num_kv_heads * sizeof(int);

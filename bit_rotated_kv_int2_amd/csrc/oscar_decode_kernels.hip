@@ -63,9 +63,12 @@ struct DecArgs {
   int *counters;       // [BH]
   float *qconst;       // [BH][GH][4]: delta, Q0, Q1 (VALU variant)
   float *qrot;         // [BH][GH][kD] float q~ (VALU variant)
-  float *part;         // [BH][n_parts][G][kPartStride]: history splits, then (several M-tiles, VALU)
-                       // BF16 tiles; one M-tile on MFMA folds its tiles into its split's partial
+  float *part;         // [BH][n_parts][G][kPartStride]: history splits, shared-prefix chunks, then
+                       // (several M-tiles, VALU) BF16 tiles; one M-tile on MFMA folds its tiles
+                       // into its split's partial
   int n_splits, n_chunks, pages_per_split, n_parts;
+  int prefix_pages, n_prefix, prefix_per_chunk;   // shared prefix (0 pages: none)
+  float *pq;           // shared prefix: query operands per (sequence, KV head)
 };
 
 __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
@@ -1289,7 +1292,7 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   const int L = pv.seq_lens[b];
   const int n_hist = max(0, L - pv.sink - pv.recent);
   const int n_pages = (n_hist + kPageTokens - 1) / kPageTokens;
-  const int pg0 = split * a.pages_per_split;
+  const int pg0 = a.prefix_pages + split * a.pages_per_split;   // the shared prefix has a scan of its own
   const int pg1 = min(min(n_pages, pg0 + a.pages_per_split), pv.max_pages);
   if (n_pages > pv.max_pages && split == 0 && tid == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_LENGTH);
 
@@ -1411,7 +1414,7 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   if (wave < 4) {
     const int u = split + S * (early - 1 - wave);
     if (wave < early && u < a.n_chunks)
-      bf16_tile_partial<GH>(a, tc, b, kv, u, sm.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
+      bf16_tile_partial<GH>(a, tc, b, kv, u, sm.wave[wave].tile, parts + (size_t)(S + a.n_prefix + u) * G * kPartStride);
     // the preparing waves start their copies only now: issuing them inside
     // the preparation would stall those waves (the CU accepts copy requests
     // at the memory rate) and with them every wave waiting on the preparation
@@ -1450,7 +1453,7 @@ __device__ void run_scan_mfma(const DecArgs &a, int b, int kv, int split, float 
   for (int u = split + S * early; u < a.n_chunks; u += S) {
     const int k = u / S - early;
     if ((long_scan ? k % 4 : NW - 1 - k % NW) == wave)
-      bf16_tile_partial<GH>(a, tc, b, kv, u, sm.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
+      bf16_tile_partial<GH>(a, tc, b, kv, u, sm.wave[wave].tile, parts + (size_t)(S + a.n_prefix + u) * G * kPartStride);
   }
   flush_partial<MT, GH, NW>(sm, st, G, ms, dst);
 }
@@ -1465,7 +1468,7 @@ __device__ void run_scan_valu(const DecArgs &a, int b, int kv, int split, float 
   const int L = pv.seq_lens[b];
   const int n_hist = max(0, L - pv.sink - pv.recent);
   const int n_pages = (n_hist + kPageTokens - 1) / kPageTokens;
-  const int pg0 = split * a.pages_per_split;
+  const int pg0 = a.prefix_pages + split * a.pages_per_split;   // the shared prefix has a scan of its own
   const int pg1 = min(min(n_pages, pg0 + a.pages_per_split), pv.max_pages);
   if (n_pages > pv.max_pages && split == 0 && tid == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_LENGTH);
   const float *qrot = a.qrot + (size_t)bh * GH * kD;
@@ -1814,7 +1817,7 @@ decode_scan_kernel(DecArgs a) {
     const TileCtx tc = tile_ctx(pv, b);
     for (int u = split; u < a.n_chunks; u += S) {
       if (((u / S) % NW) == wave)
-        bf16_tile_partial<GH>(a, tc, b, kv, u, sm.s.wave[wave].tile, parts + (size_t)(S + u) * G * kPartStride);
+        bf16_tile_partial<GH>(a, tc, b, kv, u, sm.s.wave[wave].tile, parts + (size_t)(S + a.n_prefix + u) * G * kPartStride);
     }
   }
   float *dst = parts + (size_t)split * G * kPartStride;
@@ -1841,7 +1844,163 @@ decode_scan_kernel(DecArgs a) {
   } else if (!arrive_last(&a.counters[bh], S, &last_flag)) {
     return;
   }
-  merge_item<GH, 64 * NW>(a, b, kv, parts, S, parts + (size_t)S * G * kPartStride, a.n_chunks, sm.g);
+  // the shared-prefix chunks' partials (rotated basis, written by the
+  // prefix scan before this launch) merge as further history splits
+  const int SH = S + a.n_prefix;
+  merge_item<GH, 64 * NW>(a, b, kv, parts, SH, parts + (size_t)SH * G * kPartStride, a.n_chunks, sm.g);
+}
+
+
+// ===========================================================================
+// shared-prefix scan
+// ===========================================================================
+// The leading prefix_pages history pages are the same physical pages for
+// every sequence.  They are scanned once per KV head for up to kPfxWaves
+// sequences at a time: a workgroup takes one chunk of those pages and one
+// group of sequences, streams each page into LDS once, and every wave
+// folds it into the state of its own sequence (all its query heads, the
+// page math of the per-sequence scan).  Each wave then writes its
+// sequence's (m, l, o) partial of the chunk, rotated basis, into the
+// history-split slots n_splits + chunk; the per-sequence scan, launched
+// after this one, merges them with its own splits.
+constexpr int kPfxWaves = 8;          // sequences per workgroup, one per wave
+constexpr int kPfxBufs = 3;           // pages in flight per workgroup
+constexpr int kPfxMaxChunk = 1024;    // pages per chunk (block-table entries in LDS)
+static_assert(kMaxPrefixPages <= kPfxMaxChunk * (kMaxParts / 4), "the largest prefix fits the chunk limits");
+
+// Query operands of one (sequence, KV head) in the workspace: the A
+// operands of the logit MFMA, then {delta, Q_0, Q_1, 0} per head.
+template <int MT, int GH>
+constexpr size_t pq_floats() { return (size_t)MT * 2 * 64 * 4 + (size_t)GH * 4; }
+
+// grid: B * Hkv; block: 256.
+template <int MT, int GH>
+__global__ void __launch_bounds__(256) prefix_prep_kernel(DecArgs a) {
+  __shared__ QSmem<MT, GH> sm;
+  const int bh = blockIdx.x;
+  query_prep<MT, GH>(a, bh / a.pv.hkv, bh % a.pv.hkv, sm, nullptr, [] {});   // ends with a barrier
+  float *dst = a.pq + (size_t)bh * pq_floats<MT, GH>();
+  for (int e = threadIdx.x; e < MT * 2 * 64; e += blockDim.x) ((v4i *)dst)[e] = sm.aq[e];
+  for (int e = threadIdx.x; e < GH * 4; e += blockDim.x) dst[MT * 2 * 64 * 4 + e] = (&sm.qc[0][0])[e];
+}
+
+template <int MT>
+struct PfxSmem {
+  uint4 pbuf[kPfxBufs][kPageBytes / 16];
+  v4i wl[kPfxWaves][MT * 2 * 64];
+  int bt[kPfxMaxChunk];   // block-table entries of the chunk (sequence 0)
+};
+
+// grid: 8 * ceil(n_prefix * Hkv / 8) * ceil(B / kPfxWaves) blocks of
+// kPfxWaves waves.  Block i -> XCD x = i % 8 (the hardware deals blocks to
+// the eight XCDs in turn) and slot j = i / 8; (chunk, KV head) item
+// 8 (j / nsg) + x, sequence group j % nsg.  The groups of one item are thus
+// 8 blocks apart and run on the same XCD, whose L2 serves their reads of
+// the item's pages after the first.
+template <int MT, int GH, bool LUT>
+__global__ void __launch_bounds__(64 * kPfxWaves) __attribute__((amdgpu_waves_per_eu(2)))
+prefix_scan_kernel(DecArgs a) {
+  const PoolView &pv = a.pv;
+  const int nsg = (pv.batch + kPfxWaves - 1) / kPfxWaves;
+  const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int item = 8 * (j / nsg) + x, sg = j % nsg;
+  if (item >= a.n_prefix * pv.hkv) return;   // padding block (the whole block leaves)
+  const int kv = item % pv.hkv, chunk = item / pv.hkv;
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, q = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = pv.hq / pv.hkv;
+  const int b = sg * kPfxWaves + wave;
+  const bool active = b < pv.batch;
+  const int pg0 = chunk * a.prefix_per_chunk;
+  const int npg = max(0, min(a.prefix_pages, pg0 + a.prefix_per_chunk) - pg0);
+  __shared__ PfxSmem<MT> sm;
+  // block-table entries of the chunk (sequence 0's), and this wave's
+  // sequence: its entries must be the same and its history must hold the
+  // whole prefix
+  const int32_t *bt0 = pv.block_table + pg0;
+  for (int i = tid; i < npg; i += blockDim.x) sm.bt[i] = bt0[i];
+  __syncthreads();
+  if (active) {
+    const int32_t *btb = pv.block_table + (size_t)b * pv.max_pages + pg0;
+    bool diff = false;
+    for (int i = lane; i < npg; i += 64) diff = diff || btb[i] != sm.bt[i];
+    const bool any_diff = __builtin_amdgcn_ballot_w64(diff) != 0;
+    const int n_hist = max(0, pv.seq_lens[b] - pv.sink - pv.recent);
+    if (lane == 0 && pv.err) {
+      if (any_diff) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
+      if (chunk == 0 && n_hist < a.prefix_pages * kPageTokens) atomicOr(pv.err, OSCAR_DEVERR_LENGTH);
+    }
+  }
+  // this wave's query operands (a padding wave takes sequence 0's and
+  // computes nothing)
+  const int bq = active ? b : 0;
+  const size_t bh = (size_t)bq * pv.hkv + kv;
+  const float *pq = a.pq + bh * pq_floats<MT, GH>();
+  const MetaSteps ms = meta_steps(a.rv, kv);
+  QueryOps<MT> qo;
+  load_query_ops<MT, GH, LUT>((const v4i *)pq, (const float (*)[4])(pq + MT * 2 * 64 * 4), G,
+                              pv.sm_scale * kLog2e, ms, lane, qo);
+  qo.lutk = LUT ? levels_of(a.rv, kv, false) : OSCAR_UNIFORM_LEVELS;
+  qo.lutv = LUT ? levels_of(a.rv, kv, true) : OSCAR_UNIFORM_LEVELS;
+  HistState<MT> st;
+  hist_reset(st);
+  v4i *wl = sm.wl[wave];
+#pragma unroll
+  for (int i = 0; i < MT * 2; ++i) wl[i * 64 + lane] = v4i{0, 0, 0, 0};
+  // every load above has landed before the first copy is issued (wave 0
+  // counts only its copies in vmcnt from here on)
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  const uint8_t *pbase = pv.pages + (size_t)kv * kPageBytes;
+  const size_t pstride = (size_t)pv.hkv * kPageBytes;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4 *)sm.pbuf[0];
+  // page i -> buffer i % kPfxBufs; an entry out of range copies pool page 0
+  // instead (in bounds, so that every page is one copy) and is skipped
+  auto page_ok = [&](int i) {
+    const int ph = sm.bt[i];
+    return ph >= 0 && ph < pv.n_pages;
+  };
+  auto issue = [&](int i) {
+    const int ph = page_ok(i) ? sm.bt[i] : 0;
+    dma_page((uint64_t)(uintptr_t)(pbase + (size_t)ph * pstride), lds0 + (uint32_t)(i % kPfxBufs) * kPageBytes,
+             16u * lane);
+  };
+  if (wave == 0)
+    for (int i = 0; i < kPfxBufs && i < npg; ++i) issue(i);
+  bool bad = false;
+  for (int i = 0; i < npg; ++i) {
+    // copies issued after page i: min(npg, i + kPfxBufs) - i - 1 (at most 2)
+    if (wave == 0) wait_pages(min(npg, i + kPfxBufs) - i - 1);
+    __syncthreads();   // page i is in LDS
+    PageRegs cur;
+    load_page(cur, (const uint8_t *)sm.pbuf[i % kPfxBufs], n, q);
+    wait_lds_reads();
+    __syncthreads();   // every wave has read its buffer
+    if (wave == 0 && i + kPfxBufs < npg) issue(i + kPfxBufs);
+    const bool ok = page_ok(i);
+    bad = bad || !ok;
+    if (active && ok) int2_page<MT, true, LUT>(cur, kPageTokens, qo, st, wl);
+  }
+  if (bad && tid == 0 && pv.err) atomicOr(pv.err, OSCAR_DEVERR_PAGE);
+  if (!active) return;
+  // the wave's partial: value sums in metadata code units become o = sum w
+  // (s8 b) code + sum w (z8 a - tau), per head
+  float *dst = a.part + (bh * a.n_parts + a.n_splits + chunk) * G * kPartStride;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const float l16 = row16_sum(st.lsum[mt]);
+    const float z0 = row16_sum(st.z0[mt]), z1 = row16_sum(st.z1[mt]);
+    const int hh = 4 * mt + q;
+    if (hh < G) {
+      const float zz0 = fmaf(z0, ms.va, -ms.vtau * l16), zz1 = fmaf(z1, ms.va, -ms.vtau * l16);
+      float *d = dst + (size_t)hh * kPartStride;
+      if (n == 0) {
+        d[0] = st.mref[mt];
+        d[1] = l16;
+      }
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) d[kPartO + 16 * nt + n] = fmaf(st.facc[mt][nt], ms.vb, nt < 4 ? zz0 : zz1);
+    }
+  }
 }
 
 
@@ -1858,23 +2017,37 @@ int nw_of(int G, int variant) { return !is_mfma(variant) ? 4 : (mt_of(G) == 1 ? 
 }  // namespace
 
 DecodePlan make_decode_plan(int batch, int hkv, int hq, int max_pages, int sink, int recent, int variant,
-                            int blocks) {
+                            int blocks, int prefix_pages) {
   DecodePlan p{};
   const int G = hq / hkv;
   const int MT = mt_of(G), GH = gh_of(G), NW = nw_of(G, variant);
   const int bh = batch * hkv;
   p.n_chunks = (sink + recent) / kTileTokens;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  // shared prefix: chunks of pages such that chunks x KV heads x sequence
+  // groups is about the target grid, each chunk at most kPfxMaxChunk pages
+  p.prefix_pages = prefix_pages;
+  if (prefix_pages > 0) {
+    const int nsg = (batch + kPfxWaves - 1) / kPfxWaves;
+    int C = (target_blocks(blocks) + hkv * nsg - 1) / (hkv * nsg);
+    C = C < 1 ? 1 : C;
+    C = C > prefix_pages ? prefix_pages : C;
+    C = C < (prefix_pages + kPfxMaxChunk - 1) / kPfxMaxChunk ? (prefix_pages + kPfxMaxChunk - 1) / kPfxMaxChunk : C;
+    C = C > kMaxParts / 4 ? kMaxParts / 4 : C;
+    p.prefix_per_chunk = (prefix_pages + C - 1) / C;
+    p.n_prefix = (prefix_pages + p.prefix_per_chunk - 1) / p.prefix_per_chunk;   // no empty chunk
+  }
+  const int own_pages = max_pages - prefix_pages;   // pages the per-sequence scan covers at most
   int S = (target_blocks(blocks) + bh - 1) / bh;
-  const int max_by_pages = max_pages > 0 ? (max_pages + NW - 1) / NW : 1;   // >= 1 page per wave
+  const int max_by_pages = own_pages > 0 ? (own_pages + NW - 1) / NW : 1;   // >= 1 page per wave
   S = S < 1 ? 1 : S;
   S = S > max_by_pages ? max_by_pages : S;
   S = S > kMaxSplits ? kMaxSplits : S;
-  S = S > kMaxParts - p.n_chunks ? kMaxParts - p.n_chunks : S;
+  S = S > kMaxParts - p.n_chunks - p.n_prefix ? kMaxParts - p.n_chunks - p.n_prefix : S;
   p.n_splits = S;
   // one M-tile of heads on MFMA: one partial per split (BF16 tiles folded in)
-  p.n_parts = (is_mfma(variant) && MT == 1) ? S : S + p.n_chunks;
-  p.pages_per_split = max_pages > 0 ? (max_pages + S - 1) / S : 1;
+  p.n_parts = (is_mfma(variant) && MT == 1) ? S : S + p.n_prefix + p.n_chunks;
+  p.pages_per_split = own_pages > 0 ? (own_pages + S - 1) / S : 1;
   size_t off = 0;
   p.off_counters = off;
   off = al(off + (size_t)bh * sizeof(int));
@@ -1884,6 +2057,8 @@ DecodePlan make_decode_plan(int batch, int hkv, int hq, int max_pages, int sink,
   off = al(off + (is_mfma(variant) ? 0 : (size_t)bh * GH * kD * sizeof(float)));
   p.off_part = off;
   off = al(off + (size_t)bh * p.n_parts * G * kPartStride * sizeof(float));
+  p.off_pq = off;
+  off = al(off + (p.n_prefix > 0 ? (size_t)bh * ((size_t)MT * 2 * 64 * 4 + (size_t)GH * 4) * sizeof(float) : 0));
   p.total = off;
   return p;
 }
@@ -1894,15 +2069,33 @@ hipError_t launch_decode(const PoolView &pv, const RotView &rv, const uint16_t *
   const int BH = pv.batch * pv.hkv;
   DecArgs a{pv, rv, q, out, counters, (float *)(ws + plan.off_qconst),
             (float *)(ws + plan.off_qrot), (float *)(ws + plan.off_part),
-            plan.n_splits, plan.n_chunks, plan.pages_per_split, plan.n_parts};
+            plan.n_splits, plan.n_chunks, plan.pages_per_split, plan.n_parts,
+            plan.prefix_pages, plan.n_prefix, plan.prefix_per_chunk, (float *)(ws + plan.off_pq)};
   const bool mfma = is_mfma(variant);
   // the codebook scans when either tensor has a codebook (the other then
   // takes the uniform levels through the same lookup)
   const bool lut = rv.lev_K != nullptr || rv.lev_V != nullptr;
   hipError_t e;
   const dim3 sgrid(BH * plan.n_splits);
+  // shared prefix (several M-tiles of heads, MFMA): the query operands, then
+  // the prefix pages, both before the per-sequence scan that merges them
+  const int nsg = (pv.batch + kPfxWaves - 1) / kPfxWaves;
+  const dim3 pgrid(8 * ((plan.n_prefix * pv.hkv + 7) / 8) * nsg);
+#define OSCAR_PREFIX(MT, GH, LUT)                                                                    \
+  do {                                                                                               \
+    hipLaunchKernelGGL((prefix_prep_kernel<MT, GH>), dim3(BH), dim3(256), 0, s, a);                  \
+    if ((e = hipGetLastError()) != hipSuccess) return e;                                             \
+    hipLaunchKernelGGL((prefix_scan_kernel<MT, GH, LUT>), pgrid, dim3(64 * kPfxWaves), 0, s, a);     \
+    if ((e = hipGetLastError()) != hipSuccess) return e;                                             \
+  } while (0)
 #define OSCAR_LAUNCH(MT, GH)                                                                         \
   do {                                                                                               \
+    if constexpr (MT > 1) {                                                                          \
+      if (mfma && plan.n_prefix > 0) {                                                               \
+        if (lut) OSCAR_PREFIX(MT, GH, true);                                                         \
+        else OSCAR_PREFIX(MT, GH, false);                                                            \
+      }                                                                                              \
+    }                                                                                                \
     if (!mfma) {                                                                                     \
       hipLaunchKernelGGL((decode_pre_kernel<MT, GH>), dim3(BH), dim3(256), 0, s, a);                 \
       if ((e = hipGetLastError()) != hipSuccess) return e;                                           \
@@ -1921,6 +2114,7 @@ hipError_t launch_decode(const PoolView &pv, const RotView &rv, const uint16_t *
   else if (G <= 12) OSCAR_LAUNCH(3, 12);
   else OSCAR_LAUNCH(4, 16);
 #undef OSCAR_LAUNCH
+#undef OSCAR_PREFIX
   return hipGetLastError();
 }
 

@@ -21,6 +21,7 @@ constexpr int kVMeta = OSCAR_PAGE_VMETA;
 constexpr int kMaxGroupHeads = 16;          // Hq / Hkv supported
 constexpr int kPartStride = 132;            // floats per partial: m, l, 2 pad, o[128]
 constexpr int kPartO = 4;                   // offset of o in a partial (16-byte aligned)
+constexpr int kMaxPrefixPages = 131072;     // shared-prefix pages (128 chunks of at most 1024)
 constexpr int kTileTokens = 16;             // BF16 window tokens per decode tile
 
 // Bit reversal of a 7-bit channel index (d = 128).
@@ -170,16 +171,22 @@ struct DecodePlan {
   int n_parts;           // partials per (sequence, kv head)
   int n_chunks;          // 16-token BF16 tiles (sink + recent window)
   int pages_per_split;
+  int prefix_pages;      // shared-prefix pages (0: none)
+  int n_prefix;          // shared-prefix chunks, one partial each per (sequence, kv head)
+  int prefix_per_chunk;  // pages per shared-prefix chunk
   size_t off_counters;   // int [B*Hkv] completion counters, zero between calls
   size_t off_qconst;     // float [B*Hkv][GH][4] (VALU variant)
   size_t off_qrot;       // float [B*Hkv][GH][128] (VALU variant)
-  size_t off_part;       // float partials [B*Hkv][n_parts][G][kPartStride]
+  size_t off_part;       // float partials [B*Hkv][n_parts][G][kPartStride]:
+                         // history splits, shared-prefix chunks, BF16 tiles
+  size_t off_pq;         // shared prefix: query operands [B*Hkv] (see prefix_prep_kernel)
   size_t total;
 };
 
-// blocks: scan workgroups the grid aims for (0 = the default, one per CU).
+// blocks: scan workgroups the grid aims for (0 = the default, one per CU);
+// prefix_pages: leading history pages shared by every sequence (0: none).
 DecodePlan make_decode_plan(int batch, int hkv, int hq, int max_pages, int sink, int recent,
-                            int variant, int blocks);
+                            int variant, int blocks, int prefix_pages);
 
 // Launchers (return hipError_t of the launches).
 hipError_t launch_append(const PoolView &pv, const RotView &rv, const uint16_t *k_new,

@@ -68,7 +68,7 @@ class KVPoolC(ctypes.Structure):
 
 
 class DecodeOptions(ctypes.Structure):
-    _fields_ = [("variant", ctypes.c_int32), ("blocks", ctypes.c_int32)]
+    _fields_ = [("variant", ctypes.c_int32), ("blocks", ctypes.c_int32), ("prefix_pages", ctypes.c_int32)]
 
 
 class Bf16CacheC(ctypes.Structure):
@@ -276,13 +276,14 @@ def quantize_append(params: Params, rot: RotationTensors, pool: KVPool, k_new, v
                                        _ptr(k_new), _ptr(v_new), n_new, _stream_ptr(stream)))
 
 
-def decode_options(variant: int = 0, blocks: int = 0) -> DecodeOptions:
+def decode_options(variant: int = 0, blocks: int = 0, prefix_pages: int = 0) -> DecodeOptions:
     """Per-call decode choices (see oscar_decode_options in include/oscar.h)."""
-    return DecodeOptions(int(variant), int(blocks))
+    return DecodeOptions(int(variant), int(blocks), int(prefix_pages))
 
 
-def decode_workspace_size(params: Params, batch: int, max_pages: int, variant: int = 0, blocks: int = 0) -> int:
-    opts = decode_options(variant, blocks)
+def decode_workspace_size(params: Params, batch: int, max_pages: int, variant: int = 0, blocks: int = 0,
+                          prefix_pages: int = 0) -> int:
+    opts = decode_options(variant, blocks, prefix_pages)
     return int(lib().oscar_decode_workspace_size(ctypes.byref(params), batch, max_pages, ctypes.byref(opts)))
 
 
@@ -293,24 +294,24 @@ def alloc_workspace(nbytes: int, device="cuda"):
 
 
 def decode_attention(params: Params, rot: RotationTensors, pool: KVPool, q, out, workspace, stream=None,
-                     variant: int = 0, blocks: int = 0):
+                     variant: int = 0, blocks: int = 0, prefix_pages: int = 0):
     """q: bf16 bits [B, Hq, d]; out: float32 [B, Hq, d]; workspace: uint8 device tensor
-    sized by decode_workspace_size with the same variant and blocks."""
+    sized by decode_workspace_size with the same options."""
     assert q.is_contiguous() and out.is_contiguous() and q.element_size() == 2
     r, pc = rot.c(), pool.c()
-    opts = decode_options(variant, blocks)
+    opts = decode_options(variant, blocks, prefix_pages)
     _check(lib().oscar_decode_attention(ctypes.byref(params), ctypes.byref(r), ctypes.byref(pc), _ptr(q),
                                         _ptr(out), ctypes.byref(opts), _ptr(workspace), workspace.numel(),
                                         _stream_ptr(stream)))
 
 
 def decode_attention_noalloc(params: Params, rot: RotationTensors, pool: KVPool, q, out, stream=None,
-                             variant: int = 0, blocks: int = 0):
+                             variant: int = 0, blocks: int = 0, prefix_pages: int = 0):
     """As decode_attention, on the library's own per-GPU buffer instead of a
     workspace (no allocation; calls that overlap on one GPU race)."""
     assert q.is_contiguous() and out.is_contiguous() and q.element_size() == 2
     r, pc = rot.c(), pool.c()
-    opts = decode_options(variant, blocks)
+    opts = decode_options(variant, blocks, prefix_pages)
     _check(lib().oscar_decode_attention_noalloc(ctypes.byref(params), ctypes.byref(r), ctypes.byref(pc), _ptr(q),
                                                 _ptr(out), ctypes.byref(opts), _stream_ptr(stream)))
 

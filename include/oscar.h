@@ -52,8 +52,10 @@ enum {
 
 /* Bits OR-ed into *oscar_kv_pool.error_flags by the kernels. */
 enum {
-  OSCAR_DEVERR_PAGE = 1,     /* block-table entry outside [0, n_pages) */
-  OSCAR_DEVERR_LENGTH = 2,   /* sequence needs more pages than max_pages */
+  OSCAR_DEVERR_PAGE = 1,     /* block-table entry outside [0, n_pages), or a shared-prefix
+                                entry that differs from sequence 0's */
+  OSCAR_DEVERR_LENGTH = 2,   /* sequence needs more pages than max_pages, or its history is
+                                shorter than the shared prefix */
   OSCAR_DEVERR_SINKSLOT = 4  /* sink_slot entry outside [0, n_sink_slots) */
 };
 
@@ -227,11 +229,29 @@ int32_t oscar_quantize_append(const oscar_params *p, const oscar_rotation *rot,
  *            workgroup per compute unit (256).  Results differ only in
  *            floating-point summation order.  OSCAR_EINVAL outside
  *            [0, 65536].
- * The workspace size depends on both, so size it with the same options.
+ *   prefix_pages: shared-prefix decode ([A] serving with a prefix cache:
+ *            many sequences on the same prompt pages).  0 (default): every
+ *            sequence scans all of its history pages.  P > 0: the first P
+ *            history pages of every sequence in the batch are the same
+ *            physical pages (equal block-table entries) and every sequence
+ *            holds at least 64 P history tokens.  Those P pages are then
+ *            read once per KV head for up to 8 sequences at a time: one
+ *            workgroup streams each page into LDS and each of its waves
+ *            scores it for one sequence's query heads; the workgroups of
+ *            the other sequences of the same pages run on the same XCD, so
+ *            HBM serves each page once.  Each sequence's own scan covers
+ *            pages P.. only, and one merge combines both.  Needs variant 0
+ *            and Hq/Hkv > 4, P <= max_pages, P <= 131072 and a pool with
+ *            pages; OSCAR_EINVAL otherwise.
+ *            On the device, a sequence shorter than the prefix sets
+ *            OSCAR_DEVERR_LENGTH and one whose entries differ from sequence
+ *            0's sets OSCAR_DEVERR_PAGE (the pages of sequence 0 are used).
+ * The workspace size depends on all three, so size it with the same options.
  */
 typedef struct oscar_decode_options {
   int32_t variant;
   int32_t blocks;
+  int32_t prefix_pages;
 } oscar_decode_options;
 
 /*
