@@ -376,19 +376,25 @@ def run_prefix(n_cal, write_reps=5, decode_reps=20):
         del k, v
     torch.cuda.synchronize()
     assert int(pool.error_flags.item()) == 0
-    ws = O.alloc_workspace(O.decode_workspace_size(params, wl.batch, pool.max_pages))
     out = torch.zeros((wl.batch, wl.n_q, D), dtype=torch.float32, device="cuda")
     q = torch.from_numpy(synth.decode_queries(wl, 0).view(np.int16)).cuda()
-    O.decode_attention(params, rot, pool, q, out, ws)
-    d0 = torch.cuda.Event(enable_timing=True)
-    d1 = torch.cuda.Event(enable_timing=True)
-    d0.record()
-    for _ in range(decode_reps):
-        O.decode_attention(params, rot, pool, q, out, ws)
-    d1.record()
-    torch.cuda.synchronize()
-    assert int(pool.error_flags.item()) == 0
-    dec_us = d0.elapsed_time(d1) * 1e3 / decode_reps
+    shared_pages = (P - wl.sink) // 64   # whole 64-token pages after the sink
+
+    def time_decode(prefix_pages):
+        ws = O.alloc_workspace(O.decode_workspace_size(params, wl.batch, pool.max_pages, prefix_pages=prefix_pages))
+        O.decode_attention(params, rot, pool, q, out, ws, prefix_pages=prefix_pages)
+        d0 = torch.cuda.Event(enable_timing=True)
+        d1 = torch.cuda.Event(enable_timing=True)
+        d0.record()
+        for _ in range(decode_reps):
+            O.decode_attention(params, rot, pool, q, out, ws, prefix_pages=prefix_pages)
+        d1.record()
+        torch.cuda.synchronize()
+        assert int(pool.error_flags.item()) == 0
+        return d0.elapsed_time(d1) * 1e3 / decode_reps
+
+    dec_us = time_decode(0)
+    dec_shared_us = time_decode(shared_pages)
     n_hist = np.maximum(0, lengths.astype(np.int64) - wl.sink - wl.recent)
     win = np.minimum(lengths.astype(np.int64), wl.sink + wl.recent)
     out_bytes = wl.batch * wl.n_q * D * 4
@@ -403,7 +409,12 @@ def run_prefix(n_cal, write_reps=5, decode_reps=20):
             "decode_us_per_layer": dec_us,
             "decode_gbps_logical": logical / (dec_us * 1e-6) / 1e9,
             "decode_gbps_unique": unique / (dec_us * 1e-6) / 1e9,
-            "note": "one layer; logical bytes read the shared prefix once per sequence, unique bytes once"}
+            "shared_prefix_pages": shared_pages,
+            "decode_us_per_layer_shared_prefix": dec_shared_us,
+            "decode_gbps_unique_shared_prefix": unique / (dec_shared_us * 1e-6) / 1e9,
+            "note": "one layer; logical bytes read the shared prefix once per sequence, unique bytes once; "
+                    "decode_us_per_layer: every sequence scans all its pages, "
+                    "decode_us_per_layer_shared_prefix: decode option prefix_pages = the shared pages"}
 
 
 # ---------------------------------------------------------------------------

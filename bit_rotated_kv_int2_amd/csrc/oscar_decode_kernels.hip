@@ -1864,7 +1864,7 @@ decode_scan_kernel(DecArgs a) {
 // history-split slots n_splits + chunk; the per-sequence scan, launched
 // after this one, merges them with its own splits.
 constexpr int kPfxWaves = 8;          // sequences per workgroup, one per wave
-constexpr int kPfxBufs = 3;           // pages in flight per workgroup
+constexpr int kPfxBufs = 4;           // page buffers of the workgroup's ring
 constexpr int kPfxMaxChunk = 1024;    // pages per chunk (block-table entries in LDS)
 static_assert(kMaxPrefixPages <= kPfxMaxChunk * (kMaxParts / 4), "the largest prefix fits the chunk limits");
 
@@ -1889,7 +1889,15 @@ struct PfxSmem {
   uint4 pbuf[kPfxBufs][kPageBytes / 16];
   v4i wl[kPfxWaves][MT * 2 * 64];
   int bt[kPfxMaxChunk];   // block-table entries of the chunk (sequence 0)
+  int avail;              // pages 0 .. avail - 1 are in LDS (raised by wave 0)
+  int done[kPfxWaves];    // per wave: pages 0 .. done - 1 read into its registers
 };
+
+// Wait until at most n (<= 3) pages' copies are outstanding (5 loads each).
+__device__ __forceinline__ void wait_pages3(int n) {
+  if (n >= 3) asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+  else wait_pages(n);
+}
 
 // grid: 8 * ceil(n_prefix * Hkv / 8) * ceil(B / kPfxWaves) blocks of
 // kPfxWaves waves.  Block i -> XCD x = i % 8 (the hardware deals blocks to
@@ -1919,6 +1927,8 @@ prefix_scan_kernel(DecArgs a) {
   // whole prefix
   const int32_t *bt0 = pv.block_table + pg0;
   for (int i = tid; i < npg; i += blockDim.x) sm.bt[i] = bt0[i];
+  if (tid < kPfxWaves) sm.done[tid] = 0;
+  if (tid == 0) sm.avail = 0;
   __syncthreads();
   if (active) {
     const int32_t *btb = pv.block_table + (size_t)b * pv.max_pages + pg0;
@@ -1964,18 +1974,50 @@ prefix_scan_kernel(DecArgs a) {
     dma_page((uint64_t)(uintptr_t)(pbase + (size_t)ph * pstride), lds0 + (uint32_t)(i % kPfxBufs) * kPageBytes,
              16u * lane);
   };
-  if (wave == 0)
-    for (int i = 0; i < kPfxBufs && i < npg; ++i) issue(i);
+  auto ld = [&](int *c) { return __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP); };
+  // the fewest pages any wave has read
+  auto min_done = [&] {
+    int m = ld(&sm.done[0]);
+#pragma unroll
+    for (int w = 1; w < kPfxWaves; ++w) m = min(m, ld(&sm.done[w]));
+    return m;
+  };
+  // The ring without workgroup barriers: wave 0 copies page j into buffer
+  // j % kPfxBufs once every wave has read page j - kPfxBufs from it (every
+  // done[w] > j - kPfxBufs), and raises avail to i + 1 once its copy of page
+  // i has landed; a wave reads page i once avail > i and then sets its done
+  // to i + 1.  Wave 0 blocks only for the page it needs next, i, whose
+  // buffer waits for page i - kPfxBufs; every wave can read that page, as
+  // it waits only for pages up to i - 1, all of which wave 0 has published.
+  // So every wait ends, and the waves drift apart by up to the ring's depth
+  // instead of meeting at every page.
+  int issued = 0;
   bool bad = false;
   for (int i = 0; i < npg; ++i) {
-    // copies issued after page i: min(npg, i + kPfxBufs) - i - 1 (at most 2)
-    if (wave == 0) wait_pages(min(npg, i + kPfxBufs) - i - 1);
-    __syncthreads();   // page i is in LDS
+    if (wave == 0) {
+      // copy every page whose buffer is free, up to page i at least
+      while (issued < npg && issued < i + kPfxBufs) {
+        const int need = issued - kPfxBufs + 1;
+        if (min_done() < need) {
+          if (issued > i) break;   // not needed yet
+          while (min_done() < need) __builtin_amdgcn_s_sleep(1);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        issue(issued);
+        ++issued;
+      }
+      wait_pages3(issued - i - 1);   // copies issued after page i may stay outstanding
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      if (lane == 0) __hip_atomic_store(&sm.avail, i + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    } else {
+      while (ld(&sm.avail) <= i) __builtin_amdgcn_s_sleep(1);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
     PageRegs cur;
     load_page(cur, (const uint8_t *)sm.pbuf[i % kPfxBufs], n, q);
     wait_lds_reads();
-    __syncthreads();   // every wave has read its buffer
-    if (wave == 0 && i + kPfxBufs < npg) issue(i + kPfxBufs);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if (lane == 0) __hip_atomic_store(&sm.done[wave], i + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     const bool ok = page_ok(i);
     bad = bad || !ok;
     if (active && ok) int2_page<MT, true, LUT>(cur, kPageTokens, qo, st, wl);

@@ -48,12 +48,12 @@ def _build_pool(wl, lengths, cals, extra_tokens=0):
     return params, rot, pool, bt
 
 
-def _decode(params, rot, pool, q_bits):
+def _decode(params, rot, pool, q_bits, prefix_pages=0):
     import torch
-    ws = O.alloc_workspace(O.decode_workspace_size(params, pool.batch, pool.max_pages))
+    ws = O.alloc_workspace(O.decode_workspace_size(params, pool.batch, pool.max_pages, prefix_pages=prefix_pages))
     q = torch.from_numpy(q_bits.view(np.int16)).cuda().contiguous()
     out = torch.zeros((pool.batch, params.num_q_heads, D), dtype=torch.float32, device="cuda")
-    O.decode_attention(params, rot, pool, q, out, ws)
+    O.decode_attention(params, rot, pool, q, out, ws, prefix_pages=prefix_pages)
     torch.cuda.synchronize()
     assert int(pool.error_flags.item()) == 0
     return out.cpu().numpy()
@@ -137,7 +137,9 @@ def test_qwen3_100k_batch1_sampled():
 def test_prefix_128k_gqa12_sampled():
     """Batch 16 at 131072 tokens, GQA 12 (96 query heads), one shared
     98304-token prefix on shared pages and sink slot: two sequences that
-    share the prefix are checked."""
+    share the prefix are checked, for the plain decode and for the
+    shared-prefix decode (prefix_pages = 1535, as the benchmark times it),
+    which must also agree with the plain one within summation order."""
     wl = synth.WORKLOADS["prefix-128k-b16-gqa12"]
     lengths = synth.sequence_lengths(wl)
     cals = oracle_calibration(wl, n_cal=2048)
@@ -146,9 +148,13 @@ def test_prefix_128k_gqa12_sampled():
     assert np.array_equal(bt[0, :shared], bt[9, :shared]) and shared == 1535
     q = synth.decode_queries(wl, 0)
     out = _decode(params, rot, pool, q)
+    out_sh = _decode(params, rot, pool, q, prefix_pages=shared)
     for b, h in ((0, 1), (9, 4)):
         err = _check_pair(wl, cals, pool, bt, b, h, int(lengths[b]), q, out)
         print(f"prefix seq {b} kv {h}: err/||o|| = {err:.3e}")
+        err = _check_pair(wl, cals, pool, bt, b, h, int(lengths[b]), q, out_sh)
+        print(f"shared-prefix decode, seq {b} kv {h}: err/||o|| = {err:.3e}")
+    assert decode_check(out_sh, out) <= 1e-4
 
 
 def test_qwen3_100k_batch1_codebook_sampled():
