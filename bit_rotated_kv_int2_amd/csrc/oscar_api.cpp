@@ -83,8 +83,6 @@ int check_opts(const oscar_decode_options *o, oscar_decode_options *out) {
 int check_prefix(const oscar_params *p, int32_t max_pages, int32_t n_pages, const oscar_decode_options &o) {
   if (o.prefix_pages == 0) return OSCAR_OK;
   if (o.variant != 0) return fail(OSCAR_EINVAL, "options.prefix_pages needs variant 0");
-  if (p->num_q_heads / p->num_kv_heads <= 4)
-    return fail(OSCAR_EINVAL, "options.prefix_pages needs more than 4 query heads per KV head");
   if (o.prefix_pages > max_pages) return fail(OSCAR_EINVAL, "options.prefix_pages exceeds max_pages");
   if (o.prefix_pages > oscar::kMaxPrefixPages)
     return fail(OSCAR_EINVAL, "options.prefix_pages exceeds %d", oscar::kMaxPrefixPages);

@@ -1269,7 +1269,7 @@ __device__ void split_epilogue(const DecArgs &a, int b, int kv, int split, ScanS
     const float ab = Mb > -INFINITY ? exp2_fast(Mb - Mt) : 0.f;
     const float l = fmaf(ah, sm.e.hl[h], ab * sm.e.bl[h]);
     const float o = fmaf(ah, sm.e.ot[h][c], ab * sm.e.ob[h][c]);
-    if (S == 1) {
+    if (S == 1 && a.n_prefix == 0) {
       a.out[((size_t)b * pv.hq + (size_t)kv * G + h) * kD + c] = l > 0.f ? o / l : 0.f;
     } else {
       float *d = dst + (size_t)h * kPartStride;
@@ -1829,8 +1829,21 @@ decode_scan_kernel(DecArgs a) {
     // one split the output is already written
     __shared__ DynPages dp;
     run_scan_mfma<MT, GH, NW, true, LUT>(a, b, kv, split, dst, sm.s, &dp);
-    if (S == 1 || !arrive_last(&a.counters[bh], S, &last_flag)) return;
-    merge_plain<GH, 64 * NW>(a, b, kv, parts, S, sm.pm);
+    if (a.n_prefix == 0) {
+      if (S == 1 || !arrive_last(&a.counters[bh], S, &last_flag)) return;
+      merge_plain<GH, 64 * NW>(a, b, kv, parts, S, sm.pm);
+      return;
+    }
+    // shared prefix: the splits' partials (original basis, slots 0..S-1)
+    // and the prefix chunks' (rotated basis, slots S..), inverse-rotated
+    // once by the two-group merge
+    if (S == 1) {
+      stores_complete();
+      __syncthreads();
+    } else if (!arrive_last(&a.counters[bh], S, &last_flag)) {
+      return;
+    }
+    merge_item<GH, 64 * NW>(a, b, kv, parts + (size_t)S * G * kPartStride, a.n_prefix, parts, S, sm.g);
     return;
   } else if constexpr (MFMA) {
     // several M-tiles (8 waves, heavier pages): the static page order
@@ -2090,7 +2103,7 @@ DecodePlan make_decode_plan(int batch, int hkv, int hq, int max_pages, int sink,
   S = S > kMaxParts - p.n_chunks - p.n_prefix ? kMaxParts - p.n_chunks - p.n_prefix : S;
   p.n_splits = S;
   // one M-tile of heads on MFMA: one partial per split (BF16 tiles folded in)
-  p.n_parts = (is_mfma(variant) && MT == 1) ? S : S + p.n_prefix + p.n_chunks;
+  p.n_parts = (is_mfma(variant) && MT == 1) ? S + p.n_prefix : S + p.n_prefix + p.n_chunks;
   p.pages_per_split = own_pages > 0 ? (own_pages + S - 1) / S : 1;
   size_t off = 0;
   p.off_counters = off;
@@ -2134,11 +2147,9 @@ hipError_t launch_decode(const PoolView &pv, const RotView &rv, const uint16_t *
   } while (0)
 #define OSCAR_LAUNCH(MT, GH)                                                                         \
   do {                                                                                               \
-    if constexpr (MT > 1) {                                                                          \
-      if (mfma && plan.n_prefix > 0) {                                                               \
-        if (lut) OSCAR_PREFIX(MT, GH, true);                                                         \
-        else OSCAR_PREFIX(MT, GH, false);                                                            \
-      }                                                                                              \
+    if (mfma && plan.n_prefix > 0) {                                                                 \
+      if (lut) OSCAR_PREFIX(MT, GH, true);                                                           \
+      else OSCAR_PREFIX(MT, GH, false);                                                              \
     }                                                                                                \
     if (!mfma) {                                                                                     \
       hipLaunchKernelGGL((decode_pre_kernel<MT, GH>), dim3(BH), dim3(256), 0, s, a);                 \

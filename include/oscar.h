@@ -240,9 +240,9 @@ int32_t oscar_quantize_append(const oscar_params *p, const oscar_rotation *rot,
  *            scores it for one sequence's query heads; the workgroups of
  *            the other sequences of the same pages run on the same XCD, so
  *            HBM serves each page once.  Each sequence's own scan covers
- *            pages P.. only, and one merge combines both.  Needs variant 0
- *            and Hq/Hkv > 4, P <= max_pages, P <= 131072 and a pool with
- *            pages; OSCAR_EINVAL otherwise.
+ *            pages P.. only, and one merge combines both.  Needs variant 0,
+ *            P <= max_pages, P <= 131072 and a pool with pages;
+ *            OSCAR_EINVAL otherwise.
  *            On the device, a sequence shorter than the prefix sets
  *            OSCAR_DEVERR_LENGTH and one whose entries differ from sequence
  *            0's sets OSCAR_DEVERR_PAGE (the pages of sequence 0 are used).

@@ -104,8 +104,7 @@ def test_validation_errors():
     assert 0 < ws(O.decode_options(0, 8)) < default_ws       # one split per (sequence, KV head): fewer partials
     assert ws(O.decode_options(0, -1)) == 0 and ws(O.decode_options(3, 0)) == 0
     assert ws(None) == default_ws                           # nothing is kept between calls
-    # shared-prefix decode: more than four query heads per KV head, MFMA
-    # variant, at most max_pages prefix pages
+    # shared-prefix decode: MFMA variant, at most max_pages prefix pages
     p12 = O.make_params(8, 96)
     ws12 = lambda opts, mp=1600: L.oscar_decode_workspace_size(ctypes.byref(p12), 16, mp, ctypes.byref(opts))
     assert ws12(O.decode_options(0, 0, 1535)) > ws12(O.decode_options(0, 0, 0)) > 0   # prefix partials + operands
@@ -113,12 +112,12 @@ def test_validation_errors():
     assert ws12(O.decode_options(0, 0, 1601)) == 0
     assert ws12(O.decode_options(1, 0, 10)) == 0
     assert ws12(O.decode_options(0, 0, -1)) == 0
-    assert ws(O.decode_options(0, 0, 10)) == 0               # G = 4
+    assert ws(O.decode_options(0, 0, 10)) > default_ws      # G = 4: prefix partials and query operands
     for bad_opts, what in ((O.decode_options(0, 0, -1), b"prefix_pages"), (O.decode_options(1, 0, 4), b"variant 0")):
         assert _call_decode(p12, opts=bad_opts) == O.OSCAR_EINVAL
         assert what in L.oscar_last_error()
-    assert _call_decode(p, opts=O.decode_options(0, 0, 4)) == O.OSCAR_EINVAL   # G = 4
-    assert b"query heads" in L.oscar_last_error()
+    assert _call_decode(p, opts=O.decode_options(0, 0, 5)) == O.OSCAR_EINVAL   # more than max_pages = 4
+    assert b"max_pages" in L.oscar_last_error()
     assert L.oscar_decode_workspace_size(ctypes.byref(O.make_params(8, 30)), 1, 10, None) == 0
     with pytest.raises(O.OscarError):
         O.calibrate_rotation(O.make_params(1, 1), np.zeros((1, 8, 128), np.float32),

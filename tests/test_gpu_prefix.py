@@ -79,12 +79,14 @@ def _oracle(wl, cals, kb, vb, q_b):
     return R.decode_sequence(_f64(q_b), pools, cals, 1 / np.sqrt(D))
 
 
-@pytest.mark.parametrize("n_q,batch,P", [(24, 10, 11), (16, 3, 6), (32, 9, 5)])
+@pytest.mark.parametrize("n_q,batch,P", [(24, 10, 11), (16, 3, 6), (32, 9, 5), (8, 10, 9), (4, 3, 4)])
 def test_prefix_decode_matches_oracle(n_q, batch, P):
-    """G = 12, 8 and 16; batches of 10 and 9 leave a second group of
+    """G = 12, 8, 16, 4 and 2; batches of 10 and 9 leave a second group of
     sequences with idle waves; ragged suffixes, some without private history
     pages and some ending in a partial page; scattered physical pages.
-    Default grid (several prefix chunks) and blocks = 8 (one chunk)."""
+    Default grid (several prefix chunks) and blocks = 8 (one chunk, and one
+    split per sequence and KV head, whose partial then goes to the merge
+    instead of the output)."""
     base = [256, 257, 300, 320, 383, 384, 448, 700, 1000, 1500]
     suffixes = [base[(3 * b + P) % len(base)] for b in range(batch)]
     wl, cals, rot, params, pool, toks, q = _build(2, n_q, batch, P, suffixes, seed=200 + n_q + P)
