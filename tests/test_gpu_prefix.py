@@ -151,3 +151,19 @@ def test_prefix_decode_flags_bad_input():
     pool.block_table.copy_(bt_ok)
     torch.cuda.synchronize()
     assert run(6) == 0
+
+
+@pytest.mark.parametrize("n_q,batch", [(8, 3), (24, 3), (24, 1)])
+def test_prefix_is_whole_history(n_q, batch):
+    """Every sequence's history is exactly the shared prefix (prefix_pages =
+    max_pages): the per-sequence scans have no pages of their own and only
+    their BF16 windows and the prefix partials reach the merge."""
+    P = 5
+    wl, cals, rot, params, pool, toks, q = _build(2, n_q, batch, P, [256] * batch, seed=400 + n_q + batch)
+    assert pool.max_pages == P
+    out = _decode(params, rot, pool, q, prefix_pages=P)
+    assert int(pool.error_flags.cpu()[0]) == 0
+    for b in range(batch):
+        e = decode_check(out[b], _oracle(wl, cals, toks[b][0], toks[b][1], q[b]))
+        assert e <= TOL, (b, e)
+    assert decode_check(out, _decode(params, rot, pool, q)) <= 1e-4
