@@ -332,13 +332,14 @@ def run_workload(wb, steps, warmup, decode_reps, bf16_fit=None):
 # Long shared prefix: bulk quantise-pack of the prefix, then decode
 # ---------------------------------------------------------------------------
 
-def run_prefix(n_cal, write_reps=5, decode_reps=20):
+def run_prefix(n_cal, write_reps=10, decode_reps=20):
     """Batch 16 x 131072 tokens, 8 KV / 96 query heads, one 98304-token
     prefix on shared pages and one shared sink slot; one layer.
 
     - The bulk prefill-time quantise-pack of the prefix (one append of 98304
       tokens x 8 KV heads through the write kernels) is timed on its own,
-      write_reps times into the same pages (seq_lens reset in between).
+      write_reps times into the same pages (seq_lens reset in between; the
+      median is reported).
     - Then every sequence is completed and the decode attention timed.
       Logical bytes count the shared pages once per sequence; unique bytes
       count them once."""
@@ -364,7 +365,7 @@ def run_prefix(n_cal, write_reps=5, decode_reps=20):
         e1.record()
     torch.cuda.synchronize()
     assert int(pool.error_flags.item()) == 0 and int(pool.seq_lens[0].item()) == P
-    write_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    write_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
     del kp, vp
     # complete sequence 0 with its private suffix, then every other sequence
     k, v = gpu_kv(torch, synth, wl, 0, 0, int(lengths[0]))
