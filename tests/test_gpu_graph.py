@@ -104,3 +104,48 @@ def test_graph_replays_match_eager():
         err = decode_check(og[b], want)
         print(f"graph final seq {b}: err/||o|| = {err:.3e}", flush=True)
         assert err <= TOL
+
+
+@pytest.mark.parametrize("n_q", [8, 24])
+def test_graph_replays_prefix_decode(n_q):
+    """The shared-prefix decode (prefix_pages; query-operand, prefix-scan and
+    scan launches) captured in a graph, workspace and no-allocation entry
+    points: every replay, with eager work in between, equals the eager call
+    up to summation order, and the oracle within tolerance."""
+    import torch
+    from test_gpu_prefix import _build, _oracle
+    P = 6
+    suffixes = [300, 500, 256, 700, 1000]
+    wl, cals, rot, params, pool, toks, qb = _build(2, n_q, 5, P, suffixes, seed=501 + n_q)
+    q = torch.from_numpy(qb.view(np.int16)).cuda().contiguous()
+    ws = O.alloc_workspace(O.decode_workspace_size(params, pool.batch, pool.max_pages, prefix_pages=P))
+    outg = torch.zeros((pool.batch, params.num_q_heads, D), dtype=torch.float32, device="cuda")
+    outg_na, oute = torch.zeros_like(outg), torch.zeros_like(outg)
+
+    def dec(out, out_na):
+        O.decode_attention(params, rot, pool, q, out, ws, prefix_pages=P)
+        if out_na is not None:
+            O.decode_attention_noalloc(params, rot, pool, q, out_na, prefix_pages=P)
+
+    dec(oute, outg_na)   # eager, and sets up the no-allocation buffer
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dec(outg, outg_na)
+    for rep in range(3):
+        outg.zero_()
+        outg_na.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        junk = torch.randn(1 << 20, device="cuda").square().sum()
+        assert torch.isfinite(junk)
+        dec(oute, None)
+        torch.cuda.synchronize()
+        og, ogn, oe = outg.cpu().numpy(), outg_na.cpu().numpy(), oute.cpu().numpy()
+        e1, e2 = decode_check(og, oe), decode_check(ogn, oe)
+        print(f"G={n_q // 2} replay {rep}: graph vs eager {e1:.2e}, no-alloc graph vs eager {e2:.2e}", flush=True)
+        assert e1 <= 1e-5 and e2 <= 1e-5, (rep, e1, e2)
+    assert int(pool.error_flags.cpu()[0]) == 0
+    og = outg.cpu().numpy()
+    for b in range(pool.batch):
+        assert decode_check(og[b], _oracle(wl, cals, toks[b][0], toks[b][1], qb[b])) <= TOL, b
